@@ -1,0 +1,83 @@
+"""Mutation checks: a plausible mistake planted in the oracle (on the CPU) must fail a pin.
+
+Each case patches one oracle step, runs the pins that should catch it, and requires at least one
+of them to fail; the oracle is restored afterwards by monkeypatch.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import tests.test_oracle_pins as pins
+from oracle import ref
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except Exception:   # a failed assertion or a crash: either way the pin rejects it
+        return True
+    return False
+
+
+def _wrong_kv_head(h, num_q_heads, num_kv_heads):
+    # interleaved instead of consecutive grouping
+    return h % num_kv_heads
+
+
+def _window_off_by_one(L, window):
+    start = max(0, L - window + 1) if window > 0 else 0
+    return start, L
+
+
+def _slot_off_by_one(cache, block_table, b, kvh, start, stop, block_size):
+    t = np.arange(start, max(start, stop), dtype=np.int64)
+    phys = block_table[b, t // block_size].astype(np.int64)
+    return np.ascontiguousarray(cache[phys, kvh, (t + 1) % block_size, :])
+
+
+_orig_softmax = ref.softmax_attention
+
+
+def _sink_dropped(qv, K, V, scale, sink=None):
+    return _orig_softmax(qv, K, V, scale, None)
+
+
+def _scale_ignored(qv, K, V, scale, sink=None):
+    return _orig_softmax(qv, K, V, 1.0, sink)
+
+
+_orig_merge = ref.merge_partitions
+
+
+def _merge_drops_last(o, lse, counts):
+    return _orig_merge(o, lse, np.maximum(np.asarray(counts) - 1, 1))
+
+
+MUTATIONS = {
+    "gqa head map interleaved": ("kv_head_of", _wrong_kv_head,
+                           [(pins.test_paged_equals_dense_unpaged, 0, False, 8, 2),
+                            (pins.test_gqa_equals_mha_with_repeated_kv_heads,)]),
+    "window off by one": ("attended_range", _window_off_by_one,
+                          [(pins.test_window_one_is_last_v_row,),
+                           (pins.test_paged_equals_dense_unpaged, 5, False, 8, 2)]),
+    "slot index off by one": ("gather_rows", _slot_off_by_one,
+                              [(pins.test_paged_equals_dense_unpaged, 0, False, 4, 2),
+                               (pins.test_hand_worked_golden,)]),
+    "sink dropped": ("softmax_attention", _sink_dropped,
+                     [(pins.test_sink_single_token_logistic,),
+                      (pins.test_hand_worked_golden,)]),
+    "scale ignored": ("softmax_attention", _scale_ignored,
+                      [(pins.test_paged_equals_dense_unpaged, 0, False, 4, 2),
+                       (pins.test_hand_worked_golden,)]),
+    "merge drops last partition": ("merge_partitions", _merge_drops_last,
+                                   [(pins.test_split_merge_equals_unsplit, 8, 0, True)]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, bad, checks = MUTATIONS[name]
+    monkeypatch.setattr(ref, attr, bad)
+    caught = [_fails(c[0], *c[1:]) for c in checks]
+    assert all(caught), f"mutation '{name}' escaped: {caught}"
