@@ -1,0 +1,239 @@
+"""Decode-step benchmark: one paged-attention decode step (decode + split-KV reduce) over a
+synthetic Llama-8B-shaped batch, on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--partition P]
+
+Prints ONE JSON line.  value = algorithmic KV bytes per step / wall time per step (GB/s), with
+inputs resident in HBM; the timed region is K back-to-back steps bracketed by synchronisation.
+Several identical copies of the KV pools are rotated across steps so that no step finds its KV
+in the 256 MB last-level (MALL) cache.  roofline.achieved divides the same KV bytes by the
+decode kernel's own average duration (HIP events recorded on the launch stream around every
+decode launch of the timed region).  cpu_baseline times the fp64 oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV-read GB/s (% of HBM peak) + µs/decode step, bf16 d=128 GQA paged decode"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SOURCES = ["paged_kv_attention_attn_amd/csrc/pa_decode.hip",
+                  "paged_kv_attention_attn_amd/csrc/pa_device.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, partition: int):
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs, if they were taken
+    on the current kernel source for this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    if rec.get("workload") != workload or rec.get("partition_size") != partition:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl) -> dict:
+    """The fp64 oracle on this host, one thread, over the whole step's batch."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ref
+
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        ref.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
+                   wl.block_size, window=wl.window, sinks=wl.sinks)
+        dt = time.perf_counter() - t0
+    return {"value": round(wl.kv_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the whole step ({wl.num_seqs} sequences, all heads) of the same "
+                      f"workload, NumPy float64, 1 BLAS thread"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--head-dim", type=int, default=128)
+    ap.add_argument("--q-heads", type=int, default=None)
+    ap.add_argument("--partition", type=int, default=None,
+                    help="partition size (0 = unsplit); default: the library's suggestion")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this "
+              "single-GPU decode kernel build", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_attention_attn_amd as pa
+    from paged_kv_attention_attn_amd import debug
+    from workloads import make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(0)
+    print(f"[bench] device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}",
+          file=sys.stderr, flush=True)
+
+    kw = {}
+    if args.config == 3:
+        kw = dict(head_dim=args.head_dim, num_q_heads=args.q_heads or 32)
+    wl = make_config(args.config, **kw)
+    B, Hq, D = wl.q.shape
+    maxL = int(wl.seq_lens.max())
+    P = args.partition
+    if P is None:
+        P = wl.partition_size or pa.suggest_partition_size(B, wl.num_kv_heads, maxL,
+                                                           wl.block_size,
+                                                           props.multi_processor_count)
+    pmax = pa.num_partitions(maxL, P) if P > 0 else 0
+    kv_bytes = wl.kv_bytes()
+    pool_bytes = 2 * wl.k_cache.nbytes
+    copies = args.copies or max(2, min(8, math.ceil(1.5 * 2 ** 30 / pool_bytes) + 1))
+    print(f"[bench] {wl.name}: kv_bytes/step={kv_bytes / 1e6:.1f} MB, P={P}, pmax={pmax}, "
+          f"pool={pool_bytes / 1e6:.0f} MB x {copies} copies", file=sys.stderr, flush=True)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    q, bt, L = up(wl.q), up(wl.block_table), up(wl.seq_lens)
+    sinks = None if wl.sinks is None else up(wl.sinks)
+    k0, v0 = up(wl.k_cache), up(wl.v_cache)
+    ks = [k0] + [k0.clone() for _ in range(copies - 1)]
+    vs = [v0] + [v0.clone() for _ in range(copies - 1)]
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if P > 0:
+        part = torch.empty((B, Hq, pmax, D), dtype=torch.float32, device=dev)
+        plse = torch.empty((B, Hq, pmax), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    shape = pa.make_shape(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, P, pmax)
+    variant = pa.variant_name(shape, D, wl.block_size)
+
+    def step(i):
+        c = i % copies
+        if P > 0:
+            pa.decode(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window, sinks=sinks,
+                      partition_size=P, max_partitions=pmax, out=part, lse=plse, stream=stream)
+            pa.reduce(part, plse, L, partition_size=P, out=out, lse=lse, stream=stream)
+        else:
+            pa.decode(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window, sinks=sinks,
+                      out=out, lse=lse, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, HIP events on the launch stream around each decode launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        c = i % copies
+        ev[i][0].record(stream)
+        if P > 0:
+            pa.decode(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window, sinks=sinks,
+                      partition_size=P, max_partitions=pmax, out=part, lse=plse, stream=stream)
+            ev[i][1].record(stream)
+            pa.reduce(part, plse, L, partition_size=P, out=out, lse=lse, stream=stream)
+        else:
+            pa.decode(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window, sinks=sinks,
+                      out=out, lse=lse, stream=stream)
+            ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    value = kv_bytes / (wall / args.steps) / 1e9
+    achieved = kv_bytes / dec_avg_s / 1e9
+
+    # attainable streaming read on this device (context for the roofline fraction)
+    probe = torch.empty(2 ** 31, dtype=torch.uint8, device=dev)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        debug.stream_read(probe, 4096, sink)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(10):
+        debug.stream_read(probe, 4096, sink)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    attainable = probe.numel() * 10 / (s0.elapsed_time(s1) / 1e3) / 1e9
+    del probe
+
+    workload = f"config{args.config}" + (f"_d{D}_hq{Hq}" if args.config == 3 else "")
+    traffic = measured_traffic(workload, P)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{workload}: {wl.name}",
+            "batch": B, "q_heads": Hq, "kv_heads": wl.num_kv_heads, "head_dim": D,
+            "block_size": wl.block_size, "window": wl.window,
+            "sinks": wl.sinks is not None, "seq_len_sum": int(wl.seq_lens.sum()),
+            "max_seq_len": maxL, "partition_size": P, "kv_bytes_per_step": kv_bytes,
+            "variant": variant, "kv_pool_copies": copies, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": variant,
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "decode_us_avg": round(dec_avg_s * 1e6, 3),
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "attainable_stream_read_GBps": round(attainable, 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

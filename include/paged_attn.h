@@ -1,0 +1,165 @@
+/*
+ * paged_attn.h — C ABI of the MI355X (gfx950) single-token paged-attention decode library.
+ *
+ * The operation: for each sequence b and query head h, one new query token q[b][h] attends over
+ * the sequence's cached keys and values, which live in fixed-size physical blocks of a shared KV
+ * pool and are located through the sequence's block table.  The library computes
+ *
+ *     out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t,     lse[b][h] = ln(denominator)
+ *
+ * over the attended tokens t, with grouped-query sharing (Hq/Hkv query heads per KV head), an
+ * optional sliding window and optional per-head attention-sink logits.  Long sequences may be
+ * split into partitions that each emit a partial output plus a log-sum-exp, merged by a second
+ * call.  Sources for the definition:
+ *   - one-token split-KV decode with an optional LSE output and a reducer that takes the output,
+ *     the sequence lengths and the LSE buffer: ROCm/rocm-libraries PR #13700 "prepare saved paged
+ *     decode bindings once", Summary and review finding N1;
+ *   - online softmax that only changes the reduction order: vllm.cpp PR #564 "spec(BACKEND-ROCM):
+ *     the ROCm head_dim=128 decode arm", section "It is a mirror of merged work, not new design";
+ *   - GQA groups of query heads per KV head (qg = 2/4/8): same page, "What is deliberately not
+ *     here";
+ *   - sliding window with out-of-window blocks skipped, and attention sinks: randomvariable/vllm
+ *     issue #23 "Attention parity", table "Current state".
+ *
+ * Readings where the pages are silent (fixed here as the contract):
+ *   - KV pools k_cache and v_cache are bf16 [num_blocks][Hkv][block_size][head_dim], contiguous.
+ *     Token t of sequence b is slot (t % block_size) of physical block
+ *     block_table[b * block_table_stride + t / block_size].
+ *   - q is bf16 [num_seqs][Hq][head_dim]; query head h reads KV head h / (Hq / Hkv).
+ *   - out is fp32 [num_seqs][Hq][head_dim]; lse is fp32, natural log.
+ *   - window W > 0 keeps the last min(L, W) tokens, t in [L - W, L); W = 0 means no window.
+ *   - a sink is one fp32 logit per query head that joins the softmax max and denominator with a
+ *     zero value row; lse includes it.
+ *   - split mode: partition p covers tokens [p*P, (p+1)*P) of the attended range; a sequence of
+ *     length L owns max(1, ceil(L / P)) partitions; the sink is folded into the first non-empty
+ *     partition, floor(start / P); an empty partition writes o = 0 and lse = -inf.
+ *   - L = 0 yields out = 0 and lse = -inf (lse = sink when a sink is given).
+ *
+ * Ownership and concurrency: the caller owns every buffer.  The library allocates nothing, keeps
+ * no global state and is safe to call from several host threads.  Calls are asynchronous on the
+ * given stream (a hipStream_t passed as void*, NULL = the null stream); outputs are valid once
+ * that stream reaches the call.
+ *
+ * Errors: every check below runs on the host before anything is launched; a failed check
+ * returns its status and touches no memory.  Values that live in device memory (block-table
+ * entries, sequence lengths) cannot be checked on the host without a copy; the kernels check
+ * them and, instead of reading out of bounds, write NaN to every output of the affected
+ * (sequence, head): a physical block id outside [0, num_blocks), a length L < 0 or
+ * L > block_table_stride * block_size, or (split mode) a sequence needing more than
+ * max_partitions partitions.  paged_attn_check_tables() runs the same checks on host copies.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,          /* a required pointer is NULL                                     */
+  PA_ERR_SHAPE = -2,         /* sizes inconsistent or out of range                             */
+  PA_ERR_UNSUPPORTED = -3,   /* (head_dim, Hq/Hkv, block_size) outside the compiled set        */
+  PA_ERR_LSE_REQUIRED = -4,  /* split mode (partition_size > 0) without an lse buffer          */
+  PA_ERR_LAUNCH = -5,        /* the HIP runtime rejected the launch                            */
+  PA_ERR_TABLE = -6          /* paged_attn_check_tables found a bad entry or length            */
+} pa_status;
+
+/* Host-side sizes; nothing in here is read from device memory. */
+typedef struct {
+  int32_t num_seqs;            /* B >= 0                                                        */
+  int32_t num_q_heads;         /* Hq >= 1                                                       */
+  int32_t num_kv_heads;        /* Hkv >= 1, Hq % Hkv == 0                                       */
+  int32_t num_blocks;          /* physical blocks in each of k_cache / v_cache, >= 1            */
+  int32_t block_table_stride;  /* int32 entries per block-table row, >= 1                       */
+  int32_t partition_size;      /* 0 = unsplit; else tokens per partition, a multiple of 16      */
+  int32_t max_partitions;      /* split mode: partition slots per (b, h) in the partial buffers */
+} pa_shape;
+
+/*
+ * One decode step over the whole batch.
+ *
+ *   q            bf16 [B][Hq][head_dim]                                   device, read
+ *   k_cache      bf16 [num_blocks][Hkv][block_size][head_dim]             device, read
+ *   v_cache      bf16 [num_blocks][Hkv][block_size][head_dim]             device, read
+ *   block_table  int32 [B][block_table_stride]; entries past ceil(L/bs) are never read
+ *   seq_lens     int32 [B]                                                device, read
+ *   scale        fp32 multiplier on q.k (finite)
+ *   head_dim     64, 128 or 256;   Hq / Hkv in {1, 2, 4, 8}
+ *   block_size   16, 32, 64, 128 or 256 tokens
+ *   window       0 (none) or W > 0
+ *   sinks        fp32 [Hq] sink logits, or NULL
+ *   out          unsplit: fp32 [B][Hq][head_dim]
+ *                split:   partial outputs fp32 [B][Hq][max_partitions][head_dim], each normalised
+ *                         within its partition
+ *   lse          unsplit: fp32 [B][Hq], or NULL (then nothing but out is written)
+ *                split:   REQUIRED, fp32 [B][Hq][max_partitions]
+ *   stream       hipStream_t
+ *
+ * Slots p >= max(1, ceil(L/P)) of the partial buffers are not written.
+ */
+pa_status paged_attn_decode(const pa_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, float scale, int32_t head_dim,
+                            int32_t block_size, int32_t window, const float* sinks, float* out,
+                            float* lse, void* stream);
+
+/*
+ * Merge the split-mode partials of paged_attn_decode (same shape, partition_size > 0):
+ * for each (b, h) over its max(1, ceil(L/P)) partitions, M = max lse_p,
+ * w_p = exp(lse_p - M), out = sum w_p o_p / sum w_p, lse_out = M + ln sum w_p.  Partitions with
+ * lse = -inf carry no weight and their o is not read; if all are empty, out = 0, lse = -inf.
+ *
+ *   partials      fp32 [B][Hq][max_partitions][head_dim]   device, read
+ *   lse_partials  fp32 [B][Hq][max_partitions]             device, read
+ *   seq_lens      int32 [B]                                device, read (the same lengths)
+ *   out           fp32 [B][Hq][head_dim]                   device, written
+ *   lse_out       fp32 [B][Hq] or NULL                     device, written
+ */
+pa_status paged_attn_reduce(const pa_shape* shape, int32_t head_dim, const float* partials,
+                            const float* lse_partials, const int32_t* seq_lens, float* out,
+                            float* lse_out, void* stream);
+
+/* Partitions a sequence of length seq_len occupies: max(1, ceil(seq_len / partition_size));
+ * 1 when partition_size == 0; -1 for a negative length or partition size. */
+int32_t paged_attn_num_partitions(int32_t seq_len, int32_t partition_size);
+
+/* Name of the kernel variant paged_attn_decode would launch for these sizes, or NULL if the
+ * combination is unsupported.  The string is static. */
+const char* paged_attn_variant_name(const pa_shape* shape, int32_t head_dim, int32_t block_size);
+
+/* Static text for a status code. */
+const char* paged_attn_status_string(int32_t status);
+
+/*
+ * Host-side check of host copies of the block table and lengths against the shape: every
+ * length in [0, block_table_stride * block_size], every entry a sequence reads (the first
+ * ceil(L / block_size), or only those from the window start when window > 0) in
+ * [0, num_blocks), and in split mode max(1, ceil(L/P)) <= max_partitions.  Returns PA_OK or
+ * PA_ERR_TABLE (PA_ERR_NULL / PA_ERR_SHAPE for bad arguments).  Reads host memory only.
+ */
+pa_status paged_attn_check_tables(const pa_shape* shape, int32_t block_size, int32_t window,
+                                  const int32_t* host_block_table,
+                                  const int32_t* host_seq_lens);
+
+/*
+ * Suggested partition size for a batch: 0 (unsplit) when the batch alone fills the GPU,
+ * otherwise a multiple of block_size (and of 16) sized so that roughly
+ * num_seqs * num_kv_heads * partitions reaches several workgroups per compute unit.
+ * max_seq_len is a host-side upper bound on the lengths; num_cus the device's CU count.
+ */
+int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                          int32_t max_seq_len, int32_t block_size,
+                                          int32_t num_cus);
+
+/* ABI version, bumped on any incompatible change. */
+int32_t paged_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

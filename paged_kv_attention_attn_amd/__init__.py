@@ -1,0 +1,249 @@
+"""Python binding of the gfx950 paged-attention decode library (libpaged_attn.so).
+
+Argument marshalling only: every step of the decode runs in the HIP kernels behind the C ABI
+declared in include/paged_attn.h.  PyTorch provides device memory and the current stream.  If
+the library has not been built, importing this package raises; there is no fallback path.
+
+    from paged_kv_attention_attn_amd import decode, reduce
+    out, lse = decode(q, k_cache, v_cache, block_table, seq_lens, scale)          # unsplit
+    part, plse = decode(..., partition_size=512, max_partitions=256)              # split
+    out, lse = reduce(part, plse, seq_lens, partition_size=512)
+
+Tensor layouts (all on the GPU, contiguous): q bf16 [B][Hq][D]; k_cache / v_cache bf16
+[num_blocks][Hkv][block_size][D]; block_table int32 [B][stride]; seq_lens int32 [B];
+sinks fp32 [Hq]; out fp32 [B][Hq][D] (split: [B][Hq][max_partitions][D]); lse fp32 [B][Hq]
+(split: [B][Hq][max_partitions]).  bf16 tensors may also be passed as uint16/int16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
+
+PA_OK = 0
+STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
+                -4: "PA_ERR_LSE_REQUIRED", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_TABLE"}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} "
+                         f"({status_string(status)})")
+
+
+class PaShape(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("block_table_stride", ctypes.c_int32), ("partition_size", ctypes.c_int32),
+                ("max_partitions", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first "
+                          "(python -m paged_kv_attention_attn_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    sp = ctypes.POINTER(PaShape)
+    sigs = {
+        "paged_attn_decode": (i32, [sp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, vp]),
+        "paged_attn_reduce": (i32, [sp, i32, vp, vp, vp, vp, vp, vp]),
+        "paged_attn_num_partitions": (i32, [i32, i32]),
+        "paged_attn_variant_name": (ctypes.c_char_p, [sp, i32, i32]),
+        "paged_attn_status_string": (ctypes.c_char_p, [i32]),
+        "paged_attn_check_tables": (i32, [sp, i32, i32, vp, vp]),
+        "paged_attn_suggest_partition_size": (i32, [i32, i32, i32, i32, i32]),
+        "paged_attn_abi_version": (i32, []),
+        "paged_attn_gather_witness": (i32, [sp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]),
+        "paged_attn_stream_read": (i32, [vp, ctypes.c_size_t, i32, vp, vp]),
+        "paged_attn_copy": (i32, [vp, vp, ctypes.c_size_t, vp]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+EXPORTED = ("paged_attn_decode", "paged_attn_reduce", "paged_attn_num_partitions",
+            "paged_attn_variant_name", "paged_attn_status_string", "paged_attn_check_tables",
+            "paged_attn_suggest_partition_size", "paged_attn_abi_version",
+            "paged_attn_gather_witness", "paged_attn_stream_read", "paged_attn_copy")
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.paged_attn_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(_lib.paged_attn_abi_version())
+
+
+def num_partitions(seq_len: int, partition_size: int) -> int:
+    return int(_lib.paged_attn_num_partitions(int(seq_len), int(partition_size)))
+
+
+def suggest_partition_size(num_seqs: int, num_kv_heads: int, max_seq_len: int, block_size: int,
+                           num_cus: int) -> int:
+    return int(_lib.paged_attn_suggest_partition_size(num_seqs, num_kv_heads, max_seq_len,
+                                                      block_size, num_cus))
+
+
+def make_shape(num_seqs: int, num_q_heads: int, num_kv_heads: int, num_blocks: int,
+               block_table_stride: int, partition_size: int = 0,
+               max_partitions: int = 0) -> PaShape:
+    return PaShape(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(num_blocks),
+                   int(block_table_stride), int(partition_size), int(max_partitions))
+
+
+def variant_name(shape: PaShape, head_dim: int, block_size: int) -> Optional[str]:
+    r = _lib.paged_attn_variant_name(ctypes.byref(shape), int(head_dim), int(block_size))
+    return None if r is None else r.decode()
+
+
+def check_tables(shape: PaShape, block_size: int, window: int, block_table_host,
+                 seq_lens_host) -> int:
+    """Host-side table check on CPU int32 tensors / NumPy arrays; returns the status code."""
+    bt = torch.as_tensor(block_table_host, dtype=torch.int32).contiguous()
+    sl = torch.as_tensor(seq_lens_host, dtype=torch.int32).contiguous()
+    return int(_lib.paged_attn_check_tables(ctypes.byref(shape), int(block_size), int(window),
+                                            ctypes.c_void_p(bt.data_ptr()),
+                                            ctypes.c_void_p(sl.data_ptr())))
+
+
+# ---------------------------------------------------------------------------------------------
+# tensor marshalling
+# ---------------------------------------------------------------------------------------------
+_BF16_LIKE = (torch.bfloat16, torch.uint16, torch.int16)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device, stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float, *, window: int = 0,
+           sinks: Optional[torch.Tensor] = None, partition_size: int = 0,
+           max_partitions: Optional[int] = None, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+           stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """paged_attn_decode on torch tensors.  Unsplit: returns (out [B][Hq][D], lse [B][Hq] or
+    None).  Split (partition_size > 0): returns the partials ([B][Hq][Pmax][D], [B][Hq][Pmax]);
+    max_partitions must be given (or implied by ``out``)."""
+    _dev(q, "q", _BF16_LIKE)
+    _dev(k_cache, "k_cache", _BF16_LIKE)
+    _dev(v_cache, "v_cache", _BF16_LIKE)
+    _dev(block_table, "block_table", (torch.int32,))
+    _dev(seq_lens, "seq_lens", (torch.int32,))
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B][Hq][D]; k_cache/v_cache [num_blocks][Hkv][bs][D], equal")
+    B, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("inconsistent q / cache / block_table / seq_lens shapes")
+    split = partition_size > 0
+    if split:
+        if max_partitions is None:
+            if out is None:
+                raise ValueError("split mode needs max_partitions (or an out tensor)")
+            max_partitions = out.shape[2]
+    else:
+        max_partitions = 0
+    if sinks is not None:
+        _dev(sinks, "sinks", (torch.float32,))
+        if sinks.shape != (Hq,):
+            raise ValueError("sinks must be fp32 [Hq]")
+    if out is None:
+        shp = (B, Hq, max_partitions, D) if split else (B, Hq, D)
+        out = torch.empty(shp, dtype=torch.float32, device=q.device)
+    else:
+        _dev(out, "out", (torch.float32,))
+    if lse is None and (split or want_lse):
+        shp = (B, Hq, max_partitions) if split else (B, Hq)
+        lse = torch.empty(shp, dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", (torch.float32,))
+    shape = make_shape(B, Hq, Hkv, NB, block_table.shape[1], partition_size, max_partitions)
+    st = _lib.paged_attn_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(block_table), _ptr(seq_lens), float(scale), int(D),
+                                int(bs), int(window), _ptr(sinks), _ptr(out), _ptr(lse),
+                                _stream(q.device, stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "paged_attn_decode")
+    return out, lse
+
+
+def reduce(partials: torch.Tensor, lse_partials: torch.Tensor, seq_lens: torch.Tensor, *,
+           partition_size: int, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+           stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """paged_attn_reduce on torch tensors: merges [B][Hq][Pmax][D] partials into [B][Hq][D]."""
+    _dev(partials, "partials", (torch.float32,))
+    _dev(lse_partials, "lse_partials", (torch.float32,))
+    _dev(seq_lens, "seq_lens", (torch.int32,))
+    B, Hq, Pmax, D = partials.shape
+    if lse_partials.shape != (B, Hq, Pmax) or seq_lens.shape != (B,):
+        raise ValueError("inconsistent partial / lse / seq_lens shapes")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=partials.device)
+    else:
+        _dev(out, "out", (torch.float32,))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=partials.device)
+    elif lse is not None:
+        _dev(lse, "lse", (torch.float32,))
+    # the reducer reads only the sizes below from the shape
+    shape = make_shape(B, Hq, 1, 1, 1, partition_size, Pmax)
+    st = _lib.paged_attn_reduce(ctypes.byref(shape), int(D), _ptr(partials), _ptr(lse_partials),
+                                _ptr(seq_lens), _ptr(out), _ptr(lse),
+                                _stream(partials.device, stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "paged_attn_reduce")
+    return out, lse
+
+
+def paged_attention(q, k_cache, v_cache, block_table, seq_lens, scale, *, window: int = 0,
+                    sinks=None, partition_size: int = 0, max_seq_len: Optional[int] = None,
+                    want_lse: bool = True, stream=None):
+    """One decode step end to end: decode (+ reduce when partition_size > 0).  In split mode
+    ``max_seq_len`` (a host-side bound on seq_lens) sizes the partial buffers."""
+    if partition_size <= 0:
+        return decode(q, k_cache, v_cache, block_table, seq_lens, scale, window=window,
+                      sinks=sinks, want_lse=want_lse, stream=stream)
+    if max_seq_len is None:
+        raise ValueError("split mode needs max_seq_len")
+    pmax = num_partitions(int(max_seq_len), int(partition_size))
+    part, plse = decode(q, k_cache, v_cache, block_table, seq_lens, scale, window=window,
+                        sinks=sinks, partition_size=partition_size, max_partitions=pmax,
+                        stream=stream)
+    return reduce(part, plse, seq_lens, partition_size=partition_size, want_lse=want_lse,
+                  stream=stream)

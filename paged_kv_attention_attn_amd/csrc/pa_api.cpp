@@ -1,0 +1,254 @@
+// C ABI of the paged-attention decode library: host-side validation, variant selection and
+// launches.  Every check runs before any HIP call, so a rejected call touches no device state
+// (and can be exercised on a machine without a GPU).  Nothing is allocated.
+//
+// The shape-envelope checks fail loudly instead of falling back to another path: a head size
+// that silently fell to a slower kernel is the defect vllm.cpp PR #564 "spec(BACKEND-ROCM): the
+// ROCm head_dim=128 decode arm" specs ("The gap it specs"), and shapes outside a native envelope
+// silently taking another path is open gap 6 of randomvariable/vllm issue #23 "Attention parity".
+// Split mode without an LSE buffer is an error, as an LSE request without LSE emission raises in
+// ROCm/rocm-libraries PR #13700 "prepare saved paged decode bindings once", review finding N1.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstdio>
+
+#include "../../include/paged_attn.h"
+#include "../../include/paged_attn_debug.h"
+#include "pa_kernels.hpp"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kMaxGridYZ = 65535;
+
+int log2_exact(int32_t v) {
+  if (v <= 0 || (v & (v - 1)) != 0) return -1;
+  int k = 0;
+  while ((1 << k) < v) ++k;
+  return k;
+}
+
+bool block_size_ok(int32_t bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256; }
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
+
+pa_status check_shape(const pa_shape* s) {
+  if (s == nullptr) return PA_ERR_NULL;
+  if (s->num_seqs < 0 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->num_blocks < 1 ||
+      s->block_table_stride < 1 || s->partition_size < 0)
+    return PA_ERR_SHAPE;
+  if (s->num_q_heads % s->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (s->num_seqs > kMaxGridYZ || s->num_kv_heads > kMaxGridYZ) return PA_ERR_SHAPE;
+  if (s->partition_size > 0 && (s->partition_size % 16 != 0 || s->max_partitions < 1))
+    return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+bool debug_log() {
+  static const int on = [] {
+    const char* v = std::getenv("PA_LOG");
+    return (v != nullptr && v[0] == '1' && v[1] == '\0') ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t paged_attn_abi_version(void) { return kAbiVersion; }
+
+const char* paged_attn_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "sizes inconsistent or out of range";
+    case PA_ERR_UNSUPPORTED: return "head_dim / group / block_size combination not supported";
+    case PA_ERR_LSE_REQUIRED: return "split mode requires an lse buffer";
+    case PA_ERR_LAUNCH: return "HIP launch failed";
+    case PA_ERR_TABLE: return "block table or sequence lengths out of range";
+    default: return "unknown status";
+  }
+}
+
+int32_t paged_attn_num_partitions(int32_t seq_len, int32_t partition_size) {
+  if (seq_len < 0 || partition_size < 0) return -1;
+  if (partition_size == 0 || seq_len == 0) return 1;
+  return (int32_t)(((int64_t)seq_len + partition_size - 1) / partition_size);
+}
+
+const char* paged_attn_variant_name(const pa_shape* shape, int32_t head_dim, int32_t block_size) {
+  if (check_shape(shape) != PA_OK || !head_dim_ok(head_dim) || !block_size_ok(block_size))
+    return nullptr;
+  const int group = shape->num_q_heads / shape->num_kv_heads;
+  if (!pa::decode_supported(head_dim, group)) return nullptr;
+  return pa::decode_variant_name(head_dim, group, shape->partition_size > 0);
+}
+
+pa_status paged_attn_decode(const pa_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, float scale, int32_t head_dim,
+                            int32_t block_size, int32_t window, const float* sinks, float* out,
+                            float* lse, void* stream) {
+  const pa_status st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  const int group = shape->num_q_heads / shape->num_kv_heads;
+  if (!pa::decode_supported(head_dim, group)) return PA_ERR_UNSUPPORTED;
+  if (window < 0 || !std::isfinite(scale)) return PA_ERR_SHAPE;
+  const bool split = shape->partition_size > 0;
+  if (split && lse == nullptr) return PA_ERR_LSE_REQUIRED;
+  if (shape->num_seqs == 0) return PA_OK;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+      seq_lens == nullptr || out == nullptr)
+    return PA_ERR_NULL;
+
+  pa::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const char*>(k_cache);
+  p.v_cache = static_cast<const char*>(v_cache);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.sinks = sinks;
+  p.out = out;
+  p.lse = lse;
+  p.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.num_q_heads = shape->num_q_heads;
+  p.num_kv_heads = shape->num_kv_heads;
+  p.num_blocks = shape->num_blocks;
+  p.stride = shape->block_table_stride;
+  p.bs_log2 = log2_exact(block_size);
+  p.window = window;
+  p.psize = shape->partition_size;
+  p.max_parts = split ? shape->max_partitions : 1;
+  if (debug_log())
+    std::fprintf(stderr, "[paged_attn] decode %s B=%d Hq=%d Hkv=%d bs=%d P=%d Pmax=%d W=%d\n",
+                 pa::decode_variant_name(head_dim, group, split), shape->num_seqs,
+                 shape->num_q_heads, shape->num_kv_heads, block_size, p.psize, p.max_parts,
+                 window);
+  const hipError_t e = pa::launch_decode(p, head_dim, group, shape->num_seqs,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status paged_attn_reduce(const pa_shape* shape, int32_t head_dim, const float* partials,
+                            const float* lse_partials, const int32_t* seq_lens, float* out,
+                            float* lse_out, void* stream) {
+  const pa_status st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (!head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (shape->partition_size <= 0) return PA_ERR_SHAPE;
+  if (shape->num_q_heads > kMaxGridYZ * 32) return PA_ERR_SHAPE;
+  if (shape->num_seqs == 0) return PA_OK;
+  if (partials == nullptr || lse_partials == nullptr || seq_lens == nullptr || out == nullptr)
+    return PA_ERR_NULL;
+  pa::ReduceParams p{};
+  p.partials = partials;
+  p.lse_partials = lse_partials;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.lse = lse_out;
+  p.num_q_heads = shape->num_q_heads;
+  p.psize = shape->partition_size;
+  p.max_parts = shape->max_partitions;
+  const hipError_t e = pa::launch_reduce(p, head_dim, shape->num_seqs,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status paged_attn_check_tables(const pa_shape* shape, int32_t block_size, int32_t window,
+                                  const int32_t* host_block_table, const int32_t* host_seq_lens) {
+  const pa_status st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (!block_size_ok(block_size) || window < 0) return PA_ERR_SHAPE;
+  if (shape->num_seqs == 0) return PA_OK;
+  if (host_block_table == nullptr || host_seq_lens == nullptr) return PA_ERR_NULL;
+  const int64_t cap = (int64_t)shape->block_table_stride * block_size;
+  for (int32_t b = 0; b < shape->num_seqs; ++b) {
+    const int32_t L = host_seq_lens[b];
+    if (L < 0 || L > cap) return PA_ERR_TABLE;
+    if (shape->partition_size > 0 &&
+        paged_attn_num_partitions(L, shape->partition_size) > shape->max_partitions)
+      return PA_ERR_TABLE;
+    const int32_t start = (window > 0 && L > window) ? L - window : 0;
+    if (L == 0) continue;
+    const int32_t first = start / block_size;
+    const int32_t last = (L - 1) / block_size;
+    const int32_t* row = host_block_table + (size_t)b * shape->block_table_stride;
+    for (int32_t i = first; i <= last; ++i)
+      if (row[i] < 0 || row[i] >= shape->num_blocks) return PA_ERR_TABLE;
+  }
+  return PA_OK;
+}
+
+int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                          int32_t max_seq_len, int32_t block_size,
+                                          int32_t num_cus) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_seq_len <= 0 || num_cus <= 0 ||
+      !block_size_ok(block_size))
+    return 0;
+  // Aim for about 16 partition workgroups per CU, with partitions of 256..2048 tokens that are
+  // multiples of the block size; batches that already fill the GPU and are short stay unsplit.
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  const int64_t want = (int64_t)num_cus * 16;
+  if (units >= want && max_seq_len <= 1024) return 0;
+  int64_t parts = (want + units - 1) / units;
+  int64_t P = ((int64_t)max_seq_len + parts - 1) / parts;
+  if (P < 256) P = 256;
+  if (P > 2048) P = 2048;
+  const int64_t unit = block_size > 16 ? block_size : 16;
+  P = ((P + unit - 1) / unit) * unit;
+  return (int32_t)P;
+}
+
+pa_status paged_attn_gather_witness(const pa_shape* shape, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_table,
+                                    const int32_t* seq_lens, int32_t head_dim,
+                                    int32_t block_size, int32_t window, int32_t max_rows,
+                                    void* k_rows, void* v_rows, void* stream) {
+  const pa_status st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (window < 0 || max_rows < 1) return PA_ERR_SHAPE;
+  if (shape->num_seqs == 0) return PA_OK;
+  if (k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+      seq_lens == nullptr || k_rows == nullptr || v_rows == nullptr)
+    return PA_ERR_NULL;
+  pa::WitnessParams p{};
+  p.k_cache = static_cast<const char*>(k_cache);
+  p.v_cache = static_cast<const char*>(v_cache);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.k_rows = static_cast<char*>(k_rows);
+  p.v_rows = static_cast<char*>(v_rows);
+  p.num_kv_heads = shape->num_kv_heads;
+  p.num_blocks = shape->num_blocks;
+  p.stride = shape->block_table_stride;
+  p.bs_log2 = log2_exact(block_size);
+  p.window = window;
+  p.max_rows = max_rows;
+  const hipError_t e = pa::launch_witness(p, head_dim, shape->num_seqs,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status paged_attn_stream_read(const void* buf, size_t bytes, int32_t num_workgroups,
+                                 uint32_t* sink, void* stream) {
+  if (buf == nullptr || sink == nullptr) return PA_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0 || num_workgroups < 1) return PA_ERR_SHAPE;
+  const hipError_t e = pa::launch_stream_read(buf, bytes, num_workgroups, sink,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status paged_attn_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (dst == nullptr || src == nullptr) return PA_ERR_NULL;
+  if (bytes % 16 != 0) return PA_ERR_SHAPE;
+  const hipError_t e = pa::launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,205 @@
+// Device helpers for the gfx950 paged-attention kernels: wave64 cross-lane reductions, bf16
+// unpacking and the tile -> KV address generator shared by the decode and witness kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#if !defined(__HIP_DEVICE_COMPILE__) || defined(__gfx950__)
+#else
+#error "these kernels are written for gfx950 (CDNA4) only"
+#endif
+
+namespace pa {
+
+// ---------------------------------------------------------------------------------------------
+// Lane geometry.  A wave64 is four DPP rows of 16 lanes.  One KV row (head_dim bf16 values) is
+// spread over the 16 lanes of one DPP row, so one wave-wide load instruction covers four
+// consecutive rows, a contiguous 4 * head_dim * 2 bytes (1 KiB at head_dim 128).  A tile is
+// 16 consecutive tokens: row group r (lane / 16) handles tokens 4j + r, j = 0..3.
+// ---------------------------------------------------------------------------------------------
+constexpr int kWave = 64;
+constexpr int kRowLanes = 16;
+constexpr int kRows = kWave / kRowLanes;   // 4 row groups per wave
+constexpr int kTileTokens = 16;
+constexpr int kTileSteps = kTileTokens / kRows;   // 4 tokens per row group per tile
+
+static_assert(kWave == 64, "wave64 only");
+
+// 32-bit words (bf16 pairs) a lane holds of one row: 2 (8 B) at head_dim 64, 4 (16 B) at 128,
+// 8 (two 16 B pieces) at 256.
+template <int D>
+struct RowGeom {
+  static_assert(D == 64 || D == 128 || D == 256, "head_dim 64/128/256");
+  static constexpr int kWords = D / 32;
+  static constexpr int kElems = 2 * kWords;   // bf16 values per lane per row
+  static constexpr int kRowBytes = D * 2;
+  // head-dim index of element e held by lane c of a row group
+  __device__ __host__ static constexpr int dim(int c, int e) {
+    return D == 256 ? (e < 8 ? 8 * c + e : 128 + 8 * c + (e - 8)) : c * kElems + e;
+  }
+};
+
+// Load the kWords words lane c holds of the row starting at byte address `row`.
+template <int D>
+__device__ __forceinline__ void load_row(const char* __restrict__ row, int c,
+                                         uint32_t (&w)[RowGeom<D>::kWords]) {
+  if constexpr (D == 64) {
+    const uint2 x = *reinterpret_cast<const uint2*>(row + c * 8);
+    w[0] = x.x; w[1] = x.y;
+  } else if constexpr (D == 128) {
+    const uint4 x = *reinterpret_cast<const uint4*>(row + c * 16);
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4*>(row + c * 16);
+    const uint4 y = *reinterpret_cast<const uint4*>(row + 256 + c * 16);
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+    w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_row(char* __restrict__ row, int c,
+                                          const uint32_t (&w)[RowGeom<D>::kWords]) {
+  if constexpr (D == 64) {
+    *reinterpret_cast<uint2*>(row + c * 8) = make_uint2(w[0], w[1]);
+  } else if constexpr (D == 128) {
+    *reinterpret_cast<uint4*>(row + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    *reinterpret_cast<uint4*>(row + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(row + 256 + c * 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// bf16 pair -> two fp32 (exact: bf16 is the upper half of an fp32)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + a.x*b.x + a.y*b.y on two bf16 pairs, fp32 accumulate (v_dot2c_f32_bf16).  Products of
+// two bf16 values are exact in fp32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// ---------------------------------------------------------------------------------------------
+// wave64 reductions.
+//
+// row_sum16: sum over the 16 lanes of each DPP row, result in every lane of the row.  Four DPP
+// steps: row_mirror (i <-> 15-i), row_half_mirror (i <-> 7-i within each half), then the two
+// quad permutations xor 2 and xor 1.  After the two mirrors, the four lanes of each quad hold
+// sums over four disjoint 4-lane sets that together cover the row, so the quad steps finish the
+// sum.  DPP moves stay inside a 16-lane row, so this is the same on any wave size; the
+// cross-row steps below are what a 64-wide wave adds.
+// ---------------------------------------------------------------------------------------------
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<kDppRowMirror>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppQuadXor1>(x);
+  return x;
+}
+
+// Value of x in lane (lane ^ 16) and (lane ^ 32): crosses DPP rows, so it goes through the LDS
+// crossbar (ds_bpermute).  Both steps are needed to cover the four rows of a wave64; stopping at
+// xor 16 would only combine two rows.
+__device__ __forceinline__ float xor_lane(float x, int mask) {
+  const int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2,
+                                                                __builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ float rows_max(float x) {
+  x = fmaxf(x, xor_lane(x, 16));
+  return fmaxf(x, xor_lane(x, 32));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+  x += xor_lane(x, 16);
+  return x + xor_lane(x, 32);
+}
+
+// full-wave sum / max (every lane gets the result)
+__device__ __forceinline__ float wave_sum(float x) { return rows_sum(row_sum16(x)); }
+
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) { return rows_max(row_max16(x)); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------------------------
+// Tile addressing (block-table walk).  Tile t covers tokens [16t, 16t+16), which never straddle
+// a block because block_size is a multiple of 16.  Token 16t is slot (16t mod block_size) of
+// logical block 16t / block_size; its physical block comes from the sequence's block-table row.
+// Byte offset of the tile's first row in a pool [num_blocks][Hkv][block_size][D]:
+//   ((phys * Hkv + kvh) * block_size + slot) * D * 2, computed in 64 bits.
+// Returns -1 when the table entry is outside [0, num_blocks): the caller must not read.
+// All operands are wave-uniform, so this is scalar code.
+// ---------------------------------------------------------------------------------------------
+struct TileAddr {
+  const int32_t* __restrict__ bt_row;   // this sequence's block-table row
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t kvh;
+  int32_t bs_log2;
+  int32_t row_bytes;
+
+  __device__ __forceinline__ int64_t offset(int tile) const {
+    const int tok = tile * kTileTokens;
+    const int lb = tok >> bs_log2;
+    const int slot = tok & ((1 << bs_log2) - 1);
+    const int phys = __builtin_amdgcn_readfirstlane(bt_row[lb]);
+    if (phys < 0 || phys >= num_blocks) return -1;
+    return ((((int64_t)phys * num_kv_heads + kvh) << bs_log2) + slot) * (int64_t)row_bytes;
+  }
+};
+
+// Attended token range of partition `part` of a sequence of length L, and the validity of L.
+struct PartRange {
+  int lo, hi;        // tokens [lo, hi)
+  int first_part;    // partition that holds the sink (the first non-empty one)
+};
+
+__device__ __forceinline__ PartRange part_range(int L, int window, int part, int psize) {
+  PartRange r;
+  const int start = (window > 0 && L > window) ? L - window : 0;
+  if (psize > 0) {
+    const int64_t plo = (int64_t)part * psize;
+    const int64_t phi = plo + psize;
+    r.lo = (int)(plo > start ? plo : start);
+    r.hi = (int)(phi < L ? phi : L);
+    if (r.hi < r.lo) r.hi = r.lo;
+    r.first_part = start / psize;
+  } else {
+    r.lo = start;
+    r.hi = L;
+    r.first_part = 0;
+  }
+  return r;
+}
+
+}  // namespace pa

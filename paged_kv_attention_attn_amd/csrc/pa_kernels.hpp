@@ -1,0 +1,69 @@
+// Kernel parameter blocks and the host-side launch entry points of the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeParams {
+  const uint16_t* q;          // bf16 [B][Hq][D]
+  const char* k_cache;        // bf16 [NB][Hkv][bs][D]
+  const char* v_cache;
+  const int32_t* block_table; // [B][stride]
+  const int32_t* seq_lens;    // [B]
+  const float* sinks;         // [Hq] or null
+  float* out;                 // unsplit [B][Hq][D]; split [B][Hq][Pmax][D]
+  float* lse;                 // unsplit [B][Hq] or null; split [B][Hq][Pmax]
+  float qk_scale_log2;        // scale * log2(e)
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t stride;
+  int32_t bs_log2;
+  int32_t window;
+  int32_t psize;              // 0 = unsplit
+  int32_t max_parts;          // split: partition slots; unsplit: 1
+};
+
+struct ReduceParams {
+  const float* partials;      // [B][Hq][Pmax][D]
+  const float* lse_partials;  // [B][Hq][Pmax]
+  const int32_t* seq_lens;
+  float* out;                 // [B][Hq][D]
+  float* lse;                 // [B][Hq] or null
+  int32_t num_q_heads;
+  int32_t psize;
+  int32_t max_parts;
+};
+
+struct WitnessParams {
+  const char* k_cache;
+  const char* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  char* k_rows;               // bf16 [B][Hkv][max_rows][D]
+  char* v_rows;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t stride;
+  int32_t bs_log2;
+  int32_t window;
+  int32_t max_rows;
+};
+
+// Launchers return hipSuccess or the launch error.  Grid and variant choice is theirs; the
+// caller has validated the parameters.
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int num_seqs,
+                         hipStream_t stream);
+const char* decode_variant_name(int head_dim, int group, bool split);
+bool decode_supported(int head_dim, int group);
+
+hipError_t launch_reduce(const ReduceParams& p, int head_dim, int num_seqs, hipStream_t stream);
+
+hipError_t launch_witness(const WitnessParams& p, int head_dim, int num_seqs, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, size_t bytes, int num_wg, uint32_t* sink,
+                              hipStream_t stream);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace pa

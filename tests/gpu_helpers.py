@@ -1,0 +1,132 @@
+"""Shared helpers for the GPU parity tests: move a seeded workload to the device, run the HIP
+path through the C ABI (via the thin binding), and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import paged_kv_attention_attn_amd as pa
+from oracle import ref
+
+# Contract: max abs error <= 3e-2 against the fp64 oracle (bf16 inputs, fp32 accumulation).
+TOL = 3e-2
+# Regression gates, far tighter than the contract: fp32 accumulation lands ~1e-6 from fp64.
+REG_ABS = 1e-3
+REG_NMSE = 5e-4
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(wl):
+    d = torch.device("cuda")
+    t = dict(
+        q=torch.from_numpy(np.ascontiguousarray(wl.q).view(np.int16)).to(d),
+        k=torch.from_numpy(np.ascontiguousarray(wl.k_cache).view(np.int16)).to(d),
+        v=torch.from_numpy(np.ascontiguousarray(wl.v_cache).view(np.int16)).to(d),
+        bt=torch.from_numpy(np.ascontiguousarray(wl.block_table)).to(d),
+        L=torch.from_numpy(np.ascontiguousarray(wl.seq_lens)).to(d),
+        sinks=None if wl.sinks is None else torch.from_numpy(wl.sinks).to(d),
+    )
+    torch.cuda.synchronize()
+    return t
+
+
+def max_len(wl) -> int:
+    return int(wl.seq_lens.max()) if wl.num_seqs else 0
+
+
+def run_gpu(wl, t, partition_size: int = 0, max_partitions=None, poison_outputs=True):
+    """One decode step through the ABI; returns (out, lse) as NumPy float64.  Output buffers are
+    NaN-poisoned first so an unwritten element cannot pass."""
+    B, Hq, D = wl.q.shape
+    dev = t["q"].device
+    if partition_size <= 0:
+        out = torch.full((B, Hq, D), float("nan"), device=dev)
+        lse = torch.full((B, Hq), float("nan"), device=dev)
+        pa.decode(t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale), window=wl.window,
+                  sinks=t["sinks"], out=out, lse=lse)
+    else:
+        pmax = max_partitions or pa.num_partitions(max_len(wl), partition_size)
+        part = torch.full((B, Hq, pmax, D), float("nan"), device=dev)
+        plse = torch.full((B, Hq, pmax), float("nan"), device=dev)
+        pa.decode(t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale), window=wl.window,
+                  sinks=t["sinks"], partition_size=partition_size, max_partitions=pmax,
+                  out=part, lse=plse)
+        out = torch.full((B, Hq, D), float("nan"), device=dev)
+        lse = torch.full((B, Hq), float("nan"), device=dev)
+        pa.reduce(part, plse, t["L"], partition_size=partition_size, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_full(wl):
+    return ref.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
+                      wl.block_size, window=wl.window, sinks=wl.sinks)
+
+
+def oracle_pairs(wl, pairs):
+    outs, lses = [], []
+    for b, h in pairs:
+        o, l = ref.decode_one(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens,
+                              wl.scale, wl.block_size, b, h, window=wl.window, sinks=wl.sinks)
+        outs.append(o)
+        lses.append(l)
+    return np.array(outs), np.array(lses)
+
+
+def compare(got_out, got_lse, exp_out, exp_lse, tag: str, strict: bool = True) -> dict:
+    """Element-wise comparison; asserts the contract (and the regression gates when strict)."""
+    assert got_out.shape == exp_out.shape, (tag, got_out.shape, exp_out.shape)
+    assert np.isfinite(got_out).all(), f"{tag}: non-finite output at " \
+        f"{np.argwhere(~np.isfinite(got_out))[:4].tolist()}"
+    err = np.abs(got_out - exp_out)
+    i = np.unravel_index(int(np.argmax(err)), err.shape)
+    emax = float(err[i])
+    denom = float(np.sum(exp_out ** 2))
+    nmse = float(np.sum((got_out - exp_out) ** 2) / denom) if denom > 0 else 0.0
+    # lse: -inf where the oracle says so, else within tolerance
+    ninf = np.isneginf(exp_lse)
+    assert np.array_equal(np.isneginf(got_lse), ninf), f"{tag}: -inf lse pattern differs"
+    fin = ~ninf
+    assert np.isfinite(got_lse[fin]).all(), f"{tag}: non-finite lse"
+    lerr = float(np.abs(got_lse[fin] - exp_lse[fin]).max()) if fin.any() else 0.0
+    log(f"[parity] {tag}: max|out err|={emax:.3e} at {tuple(int(x) for x in i)} "
+        f"nmse={nmse:.3e} max|lse err|={lerr:.3e}")
+    assert emax <= TOL, f"{tag}: out error {emax} > {TOL} at {i}"
+    assert lerr <= TOL, f"{tag}: lse error {lerr} > {TOL}"
+    if strict:
+        assert emax <= REG_ABS, f"{tag}: out error {emax} above the regression gate {REG_ABS}"
+        assert lerr <= REG_ABS, f"{tag}: lse error {lerr} above the regression gate {REG_ABS}"
+        assert nmse <= REG_NMSE, f"{tag}: nmse {nmse}"
+    return dict(max_abs=emax, nmse=nmse, lse_max_abs=lerr)
+
+
+def sample_pairs(wl, n: int, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    B, Hq = wl.num_seqs, wl.num_q_heads
+    pairs = {(int(np.argmax(wl.seq_lens)), 0), (int(np.argmin(wl.seq_lens)), Hq - 1)}
+    while len(pairs) < min(n, B * Hq):
+        pairs.add((int(rng.integers(B)), int(rng.integers(Hq))))
+    return sorted(pairs)
+
+
+def cus() -> int:
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def bench_partition(wl) -> int:
+    """Partition size the bench uses for this workload."""
+    if wl.partition_size:
+        return wl.partition_size
+    return pa.suggest_partition_size(wl.num_seqs, wl.num_kv_heads, max_len(wl), wl.block_size,
+                                     cus())
+
+
+def finite_rows(x):
+    return np.isfinite(x).all(axis=-1)
+

@@ -1,0 +1,173 @@
+"""C-ABI tests that need no GPU: the library loads, exports every declared symbol, and rejects
+bad descriptors on the host before any launch (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_attention_attn_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    names = set()
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(paged_attn_\w+)\s*\(", text))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "paged_attn_decode" in names and "paged_attn_reduce" in names
+    lib = ctypes.CDLL(pa.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert set(pa.EXPORTED) == names
+
+
+def test_abi_version_and_status_strings():
+    assert pa.abi_version() == 1
+    for code, name in pa.STATUS_NAMES.items():
+        s = pa.status_string(code)
+        assert s and s != "unknown status", name
+    assert pa.status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("L,P,n", [(0, 0, 1), (5, 0, 1), (0, 512, 1), (1, 512, 1), (512, 512, 1),
+                                   (513, 512, 2), (131072, 512, 256), (-1, 16, -1), (3, -16, -1)])
+def test_num_partitions(L, P, n):
+    assert pa.num_partitions(L, P) == n
+
+
+def shape(**kw):
+    d = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, num_blocks=32, block_table_stride=8,
+             partition_size=0, max_partitions=0)
+    d.update(kw)
+    return pa.make_shape(**d)
+
+
+def test_variant_names():
+    assert pa.variant_name(shape(), 128, 16) == "pa_decode_d128_g4_w4"
+    assert pa.variant_name(shape(partition_size=512, max_partitions=4), 64, 64) == \
+        "pa_decode_d64_g4_w4_split"
+    assert pa.variant_name(shape(num_q_heads=6, num_kv_heads=2), 128, 16) is None   # g = 3
+    assert pa.variant_name(shape(), 96, 16) is None
+    assert pa.variant_name(shape(), 128, 8) is None
+
+
+def call_decode(s, *, head_dim=128, block_size=16, window=0, scale=0.1, q=FAKE, out=FAKE,
+                lse=None, sinks=None, shape_ptr=True):
+    sp = ctypes.byref(s) if shape_ptr else None
+    return pa.lib().paged_attn_decode(sp, q, FAKE, FAKE, FAKE, FAKE, scale, head_dim, block_size,
+                                      window, sinks, out, lse, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(shape_ptr=False), -1),
+    (dict(head_dim=96), -3), (dict(head_dim=512), -3),
+    (dict(block_size=8), -3), (dict(block_size=48), -3), (dict(block_size=512), -3),
+    (dict(window=-1), -2), (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2),
+    (dict(q=None), -1), (dict(out=None), -1),
+])
+def test_decode_rejects(kw, expect):
+    assert call_decode(shape(), **kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(num_q_heads=6, num_kv_heads=4), -2),          # Hq % Hkv != 0
+    (dict(num_q_heads=6, num_kv_heads=2), -3),          # g = 3 not compiled
+    (dict(num_q_heads=32, num_kv_heads=2), -3),         # g = 16 not compiled
+    (dict(num_seqs=-1), -2), (dict(num_q_heads=0), -2), (dict(num_kv_heads=0), -2),
+    (dict(num_blocks=0), -2), (dict(block_table_stride=0), -2),
+    (dict(partition_size=-16), -2),
+    (dict(partition_size=40, max_partitions=4), -2),    # not a multiple of 16
+    (dict(partition_size=512, max_partitions=0), -2),
+    (dict(partition_size=512, max_partitions=4), -4),   # split without lse
+    (dict(num_seqs=70000), -2),                         # grid limit
+])
+def test_decode_rejects_shape(kw, expect):
+    assert call_decode(shape(**kw)) == expect
+
+
+def test_empty_batch_is_ok_without_launch():
+    assert call_decode(shape(num_seqs=0), q=None, out=None) == 0
+
+
+def test_reduce_rejects():
+    r = pa.lib().paged_attn_reduce
+    s = shape(partition_size=512, max_partitions=4)
+    assert r(None, 128, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert r(ctypes.byref(shape()), 128, FAKE, FAKE, FAKE, FAKE, None, None) == -2   # unsplit
+    assert r(ctypes.byref(s), 96, FAKE, FAKE, FAKE, FAKE, None, None) == -3
+    assert r(ctypes.byref(s), 128, None, FAKE, FAKE, FAKE, None, None) == -1
+    assert r(ctypes.byref(s), 128, FAKE, FAKE, FAKE, None, None, None) == -1
+    assert r(ctypes.byref(shape(num_seqs=0, partition_size=512, max_partitions=4)), 128,
+             None, None, None, None, None, None) == 0
+
+
+def test_debug_entry_points_reject():
+    lib = pa.lib()
+    assert lib.paged_attn_stream_read(None, 1024, 4, FAKE, None) == -1
+    assert lib.paged_attn_stream_read(FAKE, 1000, 4, FAKE, None) == -2
+    assert lib.paged_attn_stream_read(FAKE, 1024, 0, FAKE, None) == -2
+    assert lib.paged_attn_copy(FAKE, None, 16, None) == -1
+    assert lib.paged_attn_copy(FAKE, FAKE, 15, None) == -2
+    s = shape()
+    w = lib.paged_attn_gather_witness
+    assert w(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 96, 16, 0, 8, FAKE, FAKE, None) == -3
+    assert w(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 128, 16, 0, 0, FAKE, FAKE, None) == -2
+    assert w(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 128, 16, 0, 8, None, FAKE, None) == -1
+
+
+# ---------------------------------------------------------------------------------------------
+# host table check
+# ---------------------------------------------------------------------------------------------
+def test_check_tables():
+    bt = np.array([[3, 1, 7, -1], [0, 2, 31, 5]], np.int32)
+    L = np.array([40, 64], np.int32)
+    s = shape(block_table_stride=4)
+    assert pa.check_tables(s, 16, 0, bt, L) == 0                     # entry 3 of row 0 unread
+    assert pa.check_tables(s, 16, 0, bt, np.array([49, 64], np.int32)) == -6   # reads -1
+    bad = bt.copy()
+    bad[1, 3] = 32
+    assert pa.check_tables(s, 16, 0, bad, L) == -6                   # id == num_blocks
+    assert pa.check_tables(s, 16, 0, bt, np.array([40, 65], np.int32)) == -6   # L > stride*bs
+    assert pa.check_tables(s, 16, 0, bt, np.array([-1, 3], np.int32)) == -6
+    # the window skips blocks before its start: a bad entry there is never read
+    pre = bt.copy()
+    pre[1, 0] = -5
+    assert pa.check_tables(s, 16, 0, pre, L) == -6
+    assert pa.check_tables(s, 16, 40, pre, L) == 0
+    sp = shape(block_table_stride=4, partition_size=32, max_partitions=1)
+    assert pa.check_tables(sp, 16, 0, bt, L) == -6                   # needs 2 partitions
+    assert pa.check_tables(shape(block_table_stride=4, partition_size=32, max_partitions=2),
+                           16, 0, bt, L) == 0
+
+
+def test_suggest_partition_size():
+    for B, hkv, L, bs in [(64, 8, 4096, 16), (4, 8, 131072, 64), (32, 8, 8192, 16),
+                          (1, 4, 2048, 16), (128, 8, 32768, 16)]:
+        P = pa.suggest_partition_size(B, hkv, L, bs, 256)
+        assert P == 0 or (P % bs == 0 and P % 16 == 0 and 256 <= P <= 2048), (B, L, P)
+    assert pa.suggest_partition_size(512, 8, 512, 16, 256) == 0
+    assert pa.suggest_partition_size(0, 8, 512, 16, 256) == 0
+
+
+# ---------------------------------------------------------------------------------------------
+# the Python binding refuses what the library cannot take, before calling it
+# ---------------------------------------------------------------------------------------------
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(32, 2, 16, 128, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 8, dtype=torch.int32)
+    L = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pa.decode(q, k, k, bt, L, 0.1)
