@@ -70,6 +70,28 @@ def cpu_baseline(wl) -> dict:
                       f"workload, NumPy float64, 1 BLAS thread"}
 
 
+def copy_mode(args, torch, debug, dev) -> int:
+    """Plain device copy of --bytes, --steps times: a kernel of known traffic (reads --bytes,
+    writes --bytes) for scaling the hardware byte counters."""
+    src = torch.ones(args.bytes // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        debug.copy(dst, src)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(args.steps):
+        debug.copy(dst, src)
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / args.steps
+    print(json.dumps({"mode": "copy", "bytes": args.bytes, "steps": args.steps,
+                      "us_per_copy": round(ms * 1e3, 2),
+                      "GBps_read_plus_write": round(2 * args.bytes / (ms / 1e3) / 1e9, 1)}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +104,9 @@ def main() -> int:
                     help="partition size (0 = unsplit); default: the library's suggestion")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=None)
+    ap.add_argument("--mode", choices=["decode", "copy"], default="decode",
+                    help="copy: run only the plain copy kernel on --bytes (counter calibration)")
+    ap.add_argument("--bytes", type=int, default=1 << 30)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -101,6 +126,9 @@ def main() -> int:
     props = torch.cuda.get_device_properties(0)
     print(f"[bench] device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}",
           file=sys.stderr, flush=True)
+
+    if args.mode == "copy":
+        return copy_mode(args, torch, debug, dev)
 
     kw = {}
     if args.config == 3:

@@ -128,7 +128,8 @@ pa_status paged_attn_reduce(const pa_shape* shape, int32_t head_dim, const float
 int32_t paged_attn_num_partitions(int32_t seq_len, int32_t partition_size);
 
 /* Name of the kernel variant paged_attn_decode would launch for these sizes, or NULL if the
- * combination is unsupported.  The string is static. */
+ * combination is unsupported.  The string stays valid until the next call of this function on
+ * the same thread. */
 const char* paged_attn_variant_name(const pa_shape* shape, int32_t head_dim, int32_t block_size);
 
 /* Static text for a status code. */

@@ -14,6 +14,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstdio>
+#include <cstring>
 
 #include "../../include/paged_attn.h"
 #include "../../include/paged_attn_debug.h"
@@ -45,6 +46,34 @@ pa_status check_shape(const pa_shape* s) {
   if (s->partition_size > 0 && (s->partition_size % 16 != 0 || s->max_partitions < 1))
     return PA_ERR_SHAPE;
   return PA_OK;
+}
+
+// Waves per decode workgroup: the library's choice, or PA_DECODE_WAVES (exactly "1", "2", "4"
+// or "8") for tuning runs.  Any other value of the variable is rejected, not ignored.
+int decode_waves(int head_dim, int group, int psize) {
+  const char* v = std::getenv("PA_DECODE_WAVES");
+  if (v == nullptr) return pa::decode_default_waves(head_dim, group, psize);
+  if (v[0] != '\0' && v[1] == '\0' && pa::decode_waves_supported(v[0] - '0')) return v[0] - '0';
+  return -1;
+}
+
+// QK^T path: the library's choice, or PA_DECODE_PATH (exactly "valu" or "mfma") for tuning
+// and for testing both paths.  Any other value is rejected.
+int decode_path(int head_dim, int group, pa::QkPath* out) {
+  const char* v = std::getenv("PA_DECODE_PATH");
+  if (v == nullptr) {
+    *out = pa::decode_default_path(head_dim, group);
+    return 0;
+  }
+  if (std::strcmp(v, "valu") == 0) {
+    *out = pa::QkPath::kValu;
+    return 0;
+  }
+  if (std::strcmp(v, "mfma") == 0) {
+    *out = pa::QkPath::kMfma;
+    return 0;
+  }
+  return -1;
 }
 
 bool debug_log() {
@@ -85,7 +114,10 @@ const char* paged_attn_variant_name(const pa_shape* shape, int32_t head_dim, int
     return nullptr;
   const int group = shape->num_q_heads / shape->num_kv_heads;
   if (!pa::decode_supported(head_dim, group)) return nullptr;
-  return pa::decode_variant_name(head_dim, group, shape->partition_size > 0);
+  const int waves = decode_waves(head_dim, group, shape->partition_size);
+  pa::QkPath path;
+  if (waves < 0 || decode_path(head_dim, group, &path) != 0) return nullptr;
+  return pa::decode_variant_name(head_dim, group, waves, shape->partition_size > 0, path);
 }
 
 pa_status paged_attn_decode(const pa_shape* shape, const void* q, const void* k_cache,
@@ -101,6 +133,9 @@ pa_status paged_attn_decode(const pa_shape* shape, const void* q, const void* k_
   if (window < 0 || !std::isfinite(scale)) return PA_ERR_SHAPE;
   const bool split = shape->partition_size > 0;
   if (split && lse == nullptr) return PA_ERR_LSE_REQUIRED;
+  const int waves = decode_waves(head_dim, group, shape->partition_size);
+  pa::QkPath path;
+  if (waves < 0 || decode_path(head_dim, group, &path) != 0) return PA_ERR_UNSUPPORTED;
   if (shape->num_seqs == 0) return PA_OK;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
       seq_lens == nullptr || out == nullptr)
@@ -126,11 +161,13 @@ pa_status paged_attn_decode(const pa_shape* shape, const void* q, const void* k_
   p.max_parts = split ? shape->max_partitions : 1;
   if (debug_log())
     std::fprintf(stderr, "[paged_attn] decode %s B=%d Hq=%d Hkv=%d bs=%d P=%d Pmax=%d W=%d\n",
-                 pa::decode_variant_name(head_dim, group, split), shape->num_seqs,
+                 pa::decode_variant_name(head_dim, group, waves, split, path), shape->num_seqs,
                  shape->num_q_heads, shape->num_kv_heads, block_size, p.psize, p.max_parts,
                  window);
-  const hipError_t e = pa::launch_decode(p, head_dim, group, shape->num_seqs,
-                                         static_cast<hipStream_t>(stream));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e = path == pa::QkPath::kMfma
+                           ? pa::launch_decode_mfma(p, head_dim, group, waves, shape->num_seqs, hs)
+                           : pa::launch_decode(p, head_dim, group, waves, shape->num_seqs, hs);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

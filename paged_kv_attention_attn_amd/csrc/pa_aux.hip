@@ -23,13 +23,13 @@ __global__ __launch_bounds__(kWave) void witness_kernel(const WitnessParams p) {
   const int L = p.seq_lens[b];
   if (L <= 0 || (int64_t)L > ((int64_t)p.stride << p.bs_log2)) return;
   const PartRange pr = part_range(L, p.window, 0, 0);
-  const TileAddr ta{p.block_table + (size_t)b * p.stride, p.num_blocks, p.num_kv_heads, kvh,
-                    p.bs_log2, RG::kRowBytes};
+  const TileAddr ta{p.num_blocks, p.num_kv_heads, kvh, p.bs_log2, RG::kRowBytes};
+  const int32_t* bt_row = p.block_table + (size_t)b * p.stride;
   const size_t base = ((size_t)b * p.num_kv_heads + kvh) * p.max_rows;
   const int t0 = pr.lo / kTileTokens;
   const int t1 = (pr.hi + kTileTokens - 1) / kTileTokens;
   for (int t = t0; t < t1; ++t) {
-    const int64_t off = ta.offset(t);
+    const int64_t off = ta.offset(__builtin_amdgcn_readfirstlane(bt_row[ta.logical_block(t)]), t);
 #pragma unroll
     for (int j = 0; j < kTileSteps; ++j) {
       const int tk = t * kTileTokens + kRows * j + r;

@@ -17,17 +17,133 @@
 // 8-byte vector loads per head size, same page, "The gap it specs"; wave64 reductions must cross
 // all four 16-lane rows, vllm.cpp PR #506 review, finding 2; sliding window with out-of-window
 // blocks skipped and attention sinks, randomvariable/vllm issue #23, table "Current state".
+#include <cstdio>
+
 #include "pa_device.hpp"
 #include "pa_kernels.hpp"
 
 namespace pa {
 
-template <int D, int G, int NW>
+// Rescale threshold of the online softmax, in log2 units.  The running max m of a row group is
+// only raised when a tile's max exceeds it by more than this, so between raises
+// p = 2^(s - m) <= 2^kRescaleSlack: no overflow risk in fp32, and most tiles skip the rescale
+// multiplies entirely.  The final result does not depend on when rescales happen: every
+// (m, l, acc) triple stays consistent and the merges use the exact log-sum-exp rule.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, int G>
+struct WaveState {
+  static constexpr int E = RowGeom<D>::kElems;
+  float m[G];       // running max of the row group's scores (log2 units), per head
+  float l[G];       // running sum of 2^(s - m)
+  float acc[G][E];  // running sum of 2^(s - m) v, this lane's slice of the head dim
+};
+
+// One tile (16 tokens) of K/V in registers: token 4j + r of the tile is row j of row group r.
+template <int D>
+struct TileRegs {
+  static constexpr int W = RowGeom<D>::kWords;
+  uint32_t k[kTileSteps][W];
+  uint32_t v[kTileSteps][W];
+};
+
+template <int D>
+__device__ __forceinline__ void issue_tile(TileRegs<D>& t, const char* kb, const char* vb, int r,
+                                           int c) {
+  constexpr int RB = RowGeom<D>::kRowBytes;
+#pragma unroll
+  for (int j = 0; j < kTileSteps; ++j) load_row<D>(kb + (kRows * j + r) * RB, c, t.k[j]);
+#pragma unroll
+  for (int j = 0; j < kTileSteps; ++j) load_row<D>(vb + (kRows * j + r) * RB, c, t.v[j]);
+}
+
+// Fold one tile into the row group's online-softmax state.  MASKED: some tokens of the tile
+// fall outside [lo, hi); they get score -inf and a zero value row by select, so whatever their
+// slots hold (NaN included) cannot reach the sums.
+template <int D, int G, bool MASKED>
+__device__ __forceinline__ void consume_tile(WaveState<D, G>& st, TileRegs<D>& t,
+                                             const uint32_t (&qw)[G][RowGeom<D>::kWords],
+                                             float c2, int tok0, int lo, int hi, int r) {
+  constexpr int W = RowGeom<D>::kWords;
+  constexpr int E = RowGeom<D>::kElems;
+  constexpr int J = kTileSteps;
+
+  // raw scores q.k of the row group's 4 tokens, complete in every lane of the row
+  float s[J][G];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float a = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) a = dot2_bf16(qw[h][w], t.k[j][w], a);
+      s[j][h] = row_sum16(a);
+    }
+  }
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int tk = tok0 + kRows * j + r;
+      const bool ok = tk >= lo && tk < hi;
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[j][h] = ok ? s[j][h] * c2 : -INFINITY;
+#pragma unroll
+      for (int w = 0; w < W; ++w) t.v[j][w] = ok ? t.v[j][w] : 0u;
+    }
+  }
+
+  // raise the running max only when a tile's max is well above it (wave-uniform decision)
+  float mx[G];
+  bool need = false;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mx[h] = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
+    if constexpr (!MASKED) mx[h] *= c2;    // c2 >= 0: the max commutes with the scale
+    need |= mx[h] > st.m[h] + kRescaleSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mn = fmaxf(st.m[h], mx[h]);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      const float alpha = fast_exp2(st.m[h] - mu);
+      st.l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < E; ++e) st.acc[h][e] *= alpha;
+      st.m[h] = mn;
+    }
+  }
+
+  // probabilities (overwriting the scores), then P.V one token row at a time
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float mu = st.m[h] == -INFINITY ? 0.f : st.m[h];
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      s[j][h] = MASKED ? fast_exp2(s[j][h] - mu) : fast_exp2(fmaf(s[j][h], c2, -mu));
+    st.l[h] += (s[0][h] + s[1][h]) + (s[2][h] + s[3][h]);
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    float vf[E];
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      vf[2 * w] = bf16_lo(t.v[j][w]);
+      vf[2 * w + 1] = bf16_hi(t.v[j][w]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) st.acc[h][e] = fmaf(s[j][h], vf[e], st.acc[h][e]);
+    }
+  }
+}
+
+template <int D, int G, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p) {
   using RG = RowGeom<D>;
   constexpr int W = RG::kWords;
   constexpr int E = RG::kElems;
-  constexpr int J = kTileSteps;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -47,114 +163,120 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
   if (split && part == p.max_parts - 1 && n_parts > p.max_parts) bad = true;
   const PartRange pr = part_range(bad ? 0 : L, p.window, part, p.psize);
 
-  // q for the G heads of this KV head, bf16 pairs in the lane's slice of the head dim
+  // q for the G heads of this KV head, bf16 pairs of the lane's slice of the head dim.  A
+  // negative scale is applied as |scale| on -q (a sign flip, exact), so the score scale c2 is
+  // never negative and commutes with max.
+  float c2 = p.qk_scale_log2;
+  const uint32_t qflip = c2 < 0.f ? 0x80008000u : 0u;
+  c2 = fabsf(c2);
   const int h0 = kvh * G;
   uint32_t qw[G][W];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const char* qrow = reinterpret_cast<const char*>(
-        p.q + ((size_t)b * p.num_q_heads + h0 + h) * D);
-    load_row<D>(qrow, c, qw[h]);
+    load_row_cached<D>(
+        reinterpret_cast<const char*>(p.q + ((size_t)b * p.num_q_heads + h0 + h) * D), c,
+        qw[h]);
+#pragma unroll
+    for (int w = 0; w < W; ++w) qw[h][w] ^= qflip;
   }
 
-  float m[G], l[G], acc[G][E];
+  WaveState<D, G> st;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
+    st.m[h] = -INFINITY;
+    st.l[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < E; ++e) st.acc[h][e] = 0.f;
   }
 
-  const TileAddr ta{p.block_table + (size_t)b * p.stride, p.num_blocks, p.num_kv_heads, kvh,
-                    p.bs_log2, RG::kRowBytes};
-  const int t0 = pr.lo / kTileTokens;
-  const int t1 = pr.hi > pr.lo ? (pr.hi + kTileTokens - 1) / kTileTokens : t0;
+  // Full tiles [f0, f1) are dealt round-robin to the waves: wave w takes f0 + w + NW*i,
+  // i in [0, n_w).  Their block-table entries are loaded 64 at a time into one VGPR (lane i holds
+  // tile i's physical block) and read back with readlane, so no scalar table load sits on a
+  // tile's critical path.  The at most two partial tiles at the range ends (masked) follow.
+  const TileAddr ta{p.num_blocks, p.num_kv_heads, kvh, p.bs_log2, RG::kRowBytes};
+  const int32_t* bt_row = p.block_table + (size_t)b * p.stride;
+  const int f0 = (pr.lo + kTileTokens - 1) / kTileTokens;
+  const int f1 = pr.hi / kTileTokens;
+  const int first = f0 + wave;
+  const int n_w = first < f1 ? (f1 - first + NW - 1) / NW : 0;
+  int phys_v = 0;
+  int chunk = -1;
   bool bad_table = false;
 
-  for (int t = t0 + wave; t < t1; t += NW) {
-    const int64_t off = ta.offset(t);
+  auto phys_of = [&](int i) -> int {
+    const int ch = i >> 6;
+    if (ch != chunk) {   // uniform: refill the lane table for tiles [64ch, 64ch+64)
+      chunk = ch;
+      const int li = (ch << 6) + lane;
+      phys_v = li < n_w ? bt_row[ta.logical_block(first + NW * li)] : 0;
+    }
+    return __builtin_amdgcn_readlane(phys_v, i & 63);
+  };
+  auto issue = [&](int i, TileRegs<D>& regs) -> bool {
+    const int64_t off = ta.offset(phys_of(i), first + NW * i);
     if (off < 0) {
       bad_table = true;
-      continue;
+      return false;
     }
-    const char* kb = p.k_cache + off;
-    const char* vb = p.v_cache + off;
-    uint32_t kw[J][W], vw[J][W];
-#pragma unroll
-    for (int j = 0; j < J; ++j) load_row<D>(kb + (kRows * j + r) * RG::kRowBytes, c, kw[j]);
-#pragma unroll
-    for (int j = 0; j < J; ++j) load_row<D>(vb + (kRows * j + r) * RG::kRowBytes, c, vw[j]);
+    issue_tile<D>(regs, p.k_cache + off, p.v_cache + off, r, c);
+    return true;
+  };
+  auto consume = [&](int i, TileRegs<D>& regs) {
+    consume_tile<D, G, false>(st, regs, qw, c2, 0, 0, 0, r);
+  };
 
-    // scores of the row group's 4 tokens for the G heads (log2 domain)
-    float s[J][G];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float a = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) a = dot2_bf16(qw[h][w], kw[j][w], a);
-        s[j][h] = row_sum16(a) * p.qk_scale_log2;
-      }
+  if constexpr (DEPTH == 2) {
+    // two tiles in flight: the loads of tile i+1 are issued before tile i is consumed
+    TileRegs<D> ra, rb;
+    bool oka = n_w > 0 ? issue(0, ra) : false;
+    bool okb = false;
+    for (int i = 0; i < n_w; i += 2) {
+      if (i + 1 < n_w) okb = issue(i + 1, rb);
+      if (oka) consume(i, ra);
+      if (i + 2 < n_w) oka = issue(i + 2, ra);
+      if (i + 1 < n_w && okb) consume(i + 1, rb);
     }
+  } else {
+    TileRegs<D> ra;
+    for (int i = 0; i < n_w; ++i)
+      if (issue(i, ra)) consume(i, ra);
+  }
 
-    const int tok0 = t * kTileTokens;
-    if (tok0 < pr.lo || tok0 + kTileTokens > pr.hi) {
-      // boundary tile: tokens outside [lo, hi) get score -inf and a zero value row, by select,
-      // so whatever those slots hold (NaN included) cannot reach the sums
+  // partial tiles at the ends of [lo, hi), on the last wave
+  if (wave == NW - 1 && pr.hi > pr.lo) {
+    const int head = pr.lo / kTileTokens;          // partial if lo is not tile-aligned
+    const int tail = pr.hi / kTileTokens;          // partial if hi is not tile-aligned
+    const bool has_head = head < f0;
+    // the tail tile is partial whenever hi is not aligned; it is only skipped when it is the
+    // head tile and the head pass (masked to [lo, hi)) already covers it
+    const bool has_tail = (pr.hi % kTileTokens) != 0 && !(has_head && tail == head);
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int tk = tok0 + kRows * j + r;
-        const bool ok = tk >= pr.lo && tk < pr.hi;
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[j][h] = ok ? s[j][h] : -INFINITY;
-#pragma unroll
-        for (int w = 0; w < W; ++w) vw[j][w] = ok ? vw[j][w] : 0u;
+    for (int k = 0; k < 2; ++k) {
+      const bool on = k == 0 ? has_head : has_tail;
+      if (!on) continue;
+      const int tile = k == 0 ? head : tail;
+      const int64_t off = ta.offset(__builtin_amdgcn_readfirstlane(bt_row[ta.logical_block(tile)]),
+                                    tile);
+      if (off < 0) {
+        bad_table = true;
+        continue;
       }
-    }
-
-    float vf[J][E];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        vf[j][2 * w] = bf16_lo(vw[j][w]);
-        vf[j][2 * w + 1] = bf16_hi(vw[j][w]);
-      }
-    }
-
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mx = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
-      const float mn = fmaxf(m[h], mx);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      const float alpha = fast_exp2(m[h] - mu);
-      float pj[J];
-#pragma unroll
-      for (int j = 0; j < J; ++j) pj[j] = fast_exp2(s[j][h] - mu);
-      l[h] = fmaf(l[h], alpha, (pj[0] + pj[1]) + (pj[2] + pj[3]));
-      m[h] = mn;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float a = acc[h][e] * alpha;
-#pragma unroll
-        for (int j = 0; j < J; ++j) a = fmaf(pj[j], vf[j][e], a);
-        acc[h][e] = a;
-      }
+      TileRegs<D> rt;
+      issue_tile<D>(rt, p.k_cache + off, p.v_cache + off, r, c);
+      consume_tile<D, G, true>(st, rt, qw, c2, tile * kTileTokens, pr.lo, pr.hi, r);
     }
   }
 
   // merge the 4 row groups of the wave (log-sum-exp rule); every row ends with the wave total
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float M = rows_max(m[h]);
+    const float M = rows_max(st.m[h]);
     const float Mu = M == -INFINITY ? 0.f : M;
-    const float f = fast_exp2(m[h] - Mu);
-    l[h] = rows_sum(l[h] * f);
+    const float f = fast_exp2(st.m[h] - Mu);
+    st.l[h] = rows_sum(st.l[h] * f);
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[h][e] = rows_sum(acc[h][e] * f);
-    m[h] = M;
+    for (int e = 0; e < E; ++e) st.acc[h][e] = rows_sum(st.acc[h][e] * f);
+    st.m[h] = M;
   }
 
   // merge the waves through LDS
@@ -166,14 +288,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) s_acc[wave][h][RG::dim(c, e)] = acc[h][e];
+      for (int e = 0; e < E; ++e) s_acc[wave][h][RG::dim(c, e)] = st.acc[h][e];
     }
   }
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      s_m[wave][h] = m[h];
-      s_l[wave][h] = l[h];
+      s_m[wave][h] = st.m[h];
+      s_l[wave][h] = st.l[h];
     }
     s_bad[wave] = bad_table ? 1 : 0;
   }
@@ -231,23 +353,39 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
 // ---------------------------------------------------------------------------------------------
 namespace {
 
-constexpr int kWavesPerWg = 4;
-
+// tiles in flight per wave: two where the registers allow it
 template <int D, int G>
-hipError_t launch_dg(const DecodeParams& p, int num_seqs, hipStream_t stream) {
+constexpr int pipeline_depth() {
+  return (D * G <= 512) ? 2 : 1;
+}
+
+template <int D, int G, int NW>
+hipError_t launch_dgw(const DecodeParams& p, int num_seqs, hipStream_t stream) {
   const dim3 grid(p.psize > 0 ? p.max_parts : 1, p.num_kv_heads, num_seqs);
-  hipLaunchKernelGGL((decode_kernel<D, G, kWavesPerWg>), grid, dim3(kWavesPerWg * kWave), 0,
-                     stream, p);
+  hipLaunchKernelGGL((decode_kernel<D, G, NW, pipeline_depth<D, G>()>), grid, dim3(NW * kWave),
+                     0, stream, p);
   return hipGetLastError();
 }
 
+template <int D, int G>
+hipError_t launch_dg(const DecodeParams& p, int waves, int num_seqs, hipStream_t stream) {
+  switch (waves) {
+    case 1: return launch_dgw<D, G, 1>(p, num_seqs, stream);
+    case 2: return launch_dgw<D, G, 2>(p, num_seqs, stream);
+    case 4: return launch_dgw<D, G, 4>(p, num_seqs, stream);
+    case 8: return launch_dgw<D, G, 8>(p, num_seqs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int D>
-hipError_t launch_d(const DecodeParams& p, int group, int num_seqs, hipStream_t stream) {
+hipError_t launch_d(const DecodeParams& p, int group, int waves, int num_seqs,
+                    hipStream_t stream) {
   switch (group) {
-    case 1: return launch_dg<D, 1>(p, num_seqs, stream);
-    case 2: return launch_dg<D, 2>(p, num_seqs, stream);
-    case 4: return launch_dg<D, 4>(p, num_seqs, stream);
-    case 8: return launch_dg<D, 8>(p, num_seqs, stream);
+    case 1: return launch_dg<D, 1>(p, waves, num_seqs, stream);
+    case 2: return launch_dg<D, 2>(p, waves, num_seqs, stream);
+    case 4: return launch_dg<D, 4>(p, waves, num_seqs, stream);
+    case 8: return launch_dg<D, 8>(p, waves, num_seqs, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -260,23 +398,37 @@ bool decode_supported(int head_dim, int group) {
   return d_ok && g_ok;
 }
 
-const char* decode_variant_name(int head_dim, int group, bool split) {
-#define PA_NAME(D, G)                                                                 \
-  if (head_dim == D && group == G)                                                  \
-    return split ? "pa_decode_d" #D "_g" #G "_w4_split" : "pa_decode_d" #D "_g" #G "_w4";
-  PA_NAME(64, 1) PA_NAME(64, 2) PA_NAME(64, 4) PA_NAME(64, 8)
-  PA_NAME(128, 1) PA_NAME(128, 2) PA_NAME(128, 4) PA_NAME(128, 8)
-  PA_NAME(256, 1) PA_NAME(256, 2) PA_NAME(256, 4) PA_NAME(256, 8)
-#undef PA_NAME
-  return nullptr;
+bool decode_waves_supported(int waves) {
+  return waves == 1 || waves == 2 || waves == 4 || waves == 8;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int num_seqs,
+int decode_default_waves(int head_dim, int group, int psize) {
+  (void)head_dim;
+  (void)group;
+  (void)psize;
+  return 4;
+}
+
+QkPath decode_default_path(int head_dim, int group) {
+  (void)head_dim;
+  (void)group;
+  return QkPath::kMfma;
+}
+
+const char* decode_variant_name(int head_dim, int group, int waves, bool split, QkPath path) {
+  static thread_local char buf[64];
+  std::snprintf(buf, sizeof(buf), "pa_decode_%s_d%d_g%d_w%d%s",
+                path == QkPath::kMfma ? "mfma" : "valu", head_dim, group, waves,
+                split ? "_split" : "");
+  return buf;
+}
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int waves, int num_seqs,
                          hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_d<64>(p, group, num_seqs, stream);
-    case 128: return launch_d<128>(p, group, num_seqs, stream);
-    case 256: return launch_d<256>(p, group, num_seqs, stream);
+    case 64: return launch_d<64>(p, group, waves, num_seqs, stream);
+    case 128: return launch_d<128>(p, group, waves, num_seqs, stream);
+    case 256: return launch_d<256>(p, group, waves, num_seqs, stream);
     default: return hipErrorInvalidValue;
   }
 }

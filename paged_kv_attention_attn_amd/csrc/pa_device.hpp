@@ -40,10 +40,34 @@ struct RowGeom {
   }
 };
 
-// Load the kWords words lane c holds of the row starting at byte address `row`.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Load the kWords words lane c holds of the row starting at byte address `row`.  KV rows are
+// read exactly once per step, so the loads carry the non-temporal hint: on gfx950 streaming
+// reads with it reach a markedly higher HBM rate than plain loads.
 template <int D>
 __device__ __forceinline__ void load_row(const char* __restrict__ row, int c,
                                          uint32_t (&w)[RowGeom<D>::kWords]) {
+  if constexpr (D == 64) {
+    const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(row + c * 8));
+    w[0] = x.x; w[1] = x.y;
+  } else if constexpr (D == 128) {
+    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + c * 16));
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+  } else {
+    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + c * 16));
+    const u32x4_t y =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 256 + c * 16));
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+    w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
+  }
+}
+
+// q rows are small and reused: plain loads
+template <int D>
+__device__ __forceinline__ void load_row_cached(const char* __restrict__ row, int c,
+                                                uint32_t (&w)[RowGeom<D>::kWords]) {
   if constexpr (D == 64) {
     const uint2 x = *reinterpret_cast<const uint2*>(row + c * 8);
     w[0] = x.x; w[1] = x.y;
@@ -157,23 +181,24 @@ constexpr float kLn2 = 0.6931471805599453f;
 // logical block 16t / block_size; its physical block comes from the sequence's block-table row.
 // Byte offset of the tile's first row in a pool [num_blocks][Hkv][block_size][D]:
 //   ((phys * Hkv + kvh) * block_size + slot) * D * 2, computed in 64 bits.
-// Returns -1 when the table entry is outside [0, num_blocks): the caller must not read.
-// All operands are wave-uniform, so this is scalar code.
+// A table entry outside [0, num_blocks) yields -1: the caller must not read.  All operands are
+// wave-uniform, so this is scalar code.
 // ---------------------------------------------------------------------------------------------
 struct TileAddr {
-  const int32_t* __restrict__ bt_row;   // this sequence's block-table row
   int32_t num_blocks;
   int32_t num_kv_heads;
   int32_t kvh;
   int32_t bs_log2;
   int32_t row_bytes;
 
-  __device__ __forceinline__ int64_t offset(int tile) const {
-    const int tok = tile * kTileTokens;
-    const int lb = tok >> bs_log2;
-    const int slot = tok & ((1 << bs_log2) - 1);
-    const int phys = __builtin_amdgcn_readfirstlane(bt_row[lb]);
+  // index into the sequence's block-table row of the block holding tile t
+  __device__ __forceinline__ int logical_block(int tile) const {
+    return (tile * kTileTokens) >> bs_log2;
+  }
+  // byte offset of tile t's first row given its physical block, -1 if phys is out of range
+  __device__ __forceinline__ int64_t offset(int phys, int tile) const {
     if (phys < 0 || phys >= num_blocks) return -1;
+    const int slot = (tile * kTileTokens) & ((1 << bs_log2) - 1);
     return ((((int64_t)phys * num_kv_heads + kvh) << bs_log2) + slot) * (int64_t)row_bytes;
   }
 };

@@ -54,10 +54,19 @@ struct WitnessParams {
 
 // Launchers return hipSuccess or the launch error.  Grid and variant choice is theirs; the
 // caller has validated the parameters.
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int num_seqs,
+// Decode kernels: QK^T on the vector ALUs (dot2 + DPP) or on the matrix cores (MFMA); P.V is
+// on the vector ALUs in fp32 in both.
+enum class QkPath { kValu = 0, kMfma = 1 };
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int waves, int num_seqs,
                          hipStream_t stream);
-const char* decode_variant_name(int head_dim, int group, bool split);
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, int group, int waves,
+                              int num_seqs, hipStream_t stream);
+// Variant name; the string lives in thread-local storage until the next call on this thread.
+const char* decode_variant_name(int head_dim, int group, int waves, bool split, QkPath path);
+QkPath decode_default_path(int head_dim, int group);
 bool decode_supported(int head_dim, int group);
+bool decode_waves_supported(int waves);
+int decode_default_waves(int head_dim, int group, int psize);
 
 hipError_t launch_reduce(const ReduceParams& p, int head_dim, int num_seqs, hipStream_t stream);
 

@@ -53,10 +53,15 @@ def shape(**kw):
     return pa.make_shape(**d)
 
 
-def test_variant_names():
-    assert pa.variant_name(shape(), 128, 16) == "pa_decode_d128_g4_w4"
+def test_variant_names(monkeypatch):
+    monkeypatch.setenv("PA_DECODE_PATH", "mfma")
+    monkeypatch.setenv("PA_DECODE_WAVES", "4")
+    assert pa.variant_name(shape(), 128, 16) == "pa_decode_mfma_d128_g4_w4"
     assert pa.variant_name(shape(partition_size=512, max_partitions=4), 64, 64) == \
-        "pa_decode_d64_g4_w4_split"
+        "pa_decode_mfma_d64_g4_w4_split"
+    monkeypatch.setenv("PA_DECODE_PATH", "valu")
+    monkeypatch.setenv("PA_DECODE_WAVES", "2")
+    assert pa.variant_name(shape(), 256, 16) == "pa_decode_valu_d256_g4_w2"
     assert pa.variant_name(shape(num_q_heads=6, num_kv_heads=2), 128, 16) is None   # g = 3
     assert pa.variant_name(shape(), 96, 16) is None
     assert pa.variant_name(shape(), 128, 8) is None
@@ -94,6 +99,15 @@ def test_decode_rejects(kw, expect):
 ])
 def test_decode_rejects_shape(kw, expect):
     assert call_decode(shape(**kw)) == expect
+
+
+@pytest.mark.parametrize("var,val", [("PA_DECODE_PATH", "VALU"), ("PA_DECODE_PATH", "auto"),
+                                     ("PA_DECODE_WAVES", "3"), ("PA_DECODE_WAVES", "4 "),
+                                     ("PA_DECODE_WAVES", "")])
+def test_tuning_variables_are_parsed_strictly(var, val, monkeypatch):
+    monkeypatch.setenv(var, val)
+    assert call_decode(shape()) == -3
+    assert pa.variant_name(shape(), 128, 16) is None
 
 
 def test_empty_batch_is_ok_without_launch():

@@ -25,6 +25,13 @@ def gpu_present():
     assert name.startswith("gfx950"), name
 
 
+@pytest.fixture(params=["mfma", "valu"])
+def qk_path(request, monkeypatch):
+    """Run the test on both QK^T paths (matrix cores / vector ALUs)."""
+    monkeypatch.setenv("PA_DECODE_PATH", request.param)
+    return request.param
+
+
 def f32_of_bf16(bits):
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
@@ -32,24 +39,25 @@ def f32_of_bf16(bits):
 # ---------------------------------------------------------------------------------------------
 # the five workloads
 # ---------------------------------------------------------------------------------------------
-def test_config1_unsplit():
+def test_config1_unsplit(qk_path):
     wl = make_config(1)
     t = to_dev(wl)
-    compare(*run_gpu(wl, t), *oracle_full(wl), "cfg1 unsplit")
+    compare(*run_gpu(wl, t), *oracle_full(wl), f"cfg1 unsplit {qk_path}")
 
 
 @pytest.mark.parametrize("P", [16, 32, 48, 64, 112])
-def test_config1_split(P):
+def test_config1_split(P, qk_path):
     wl = make_config(1)
     t = to_dev(wl)
-    compare(*run_gpu(wl, t, partition_size=P), *oracle_full(wl), f"cfg1 split P={P}")
+    compare(*run_gpu(wl, t, partition_size=P), *oracle_full(wl), f"cfg1 split P={P} {qk_path}")
 
 
 @pytest.mark.parametrize("P", [0, 32])
-def test_config1_poisoned(P):
+def test_config1_poisoned(P, qk_path):
     wl = make_config(1, poison=True)
     t = to_dev(wl)
-    compare(*run_gpu(wl, t, partition_size=P), *oracle_full(wl), f"cfg1 poisoned P={P}")
+    compare(*run_gpu(wl, t, partition_size=P), *oracle_full(wl),
+            f"cfg1 poisoned P={P} {qk_path}")
 
 
 def test_config2_bench_launch():
@@ -59,6 +67,18 @@ def test_config2_bench_launch():
     exp = oracle_full(wl)
     compare(*run_gpu(wl, t, partition_size=P), *exp, f"cfg2 split P={P}")
     compare(*run_gpu(wl, t), *exp, "cfg2 unsplit")
+
+
+def test_config2_both_paths_and_wave_counts(monkeypatch):
+    wl = make_config(2)
+    t = to_dev(wl)
+    exp = oracle_full(wl)
+    for path in ("valu", "mfma"):
+        for waves in ("1", "2", "4", "8"):
+            monkeypatch.setenv("PA_DECODE_PATH", path)
+            monkeypatch.setenv("PA_DECODE_WAVES", waves)
+            compare(*run_gpu(wl, t, partition_size=1024), *exp,
+                    f"cfg2 {path} waves={waves} P=1024")
 
 
 def test_config2_poisoned():
@@ -116,18 +136,18 @@ EDGE_COMBOS = [  # (block_size, window, sinks, partition)
 
 @pytest.mark.parametrize("combo", range(len(EDGE_COMBOS)))
 @pytest.mark.parametrize("D,g", [(D, g) for D in (64, 128, 256) for g in (1, 2, 4, 8)])
-def test_edges(D, g, combo):
+def test_edges(D, g, combo, qk_path):
     bs, W, sinks, P = EDGE_COMBOS[combo]
     wl = make_workload(name="edge", seq_lens=EDGE_LENS, num_q_heads=2 * g, num_kv_heads=2,
                        head_dim=D, block_size=bs, seed=[D, g, combo], window=W,
                        with_sinks=sinks, poison=True)
     t = to_dev(wl)
     compare(*run_gpu(wl, t, partition_size=P), *oracle_full(wl),
-            f"edge D={D} g={g} bs={bs} W={W} sinks={sinks} P={P}")
+            f"edge {qk_path} D={D} g={g} bs={bs} W={W} sinks={sinks} P={P}")
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
-def test_seq_len_one_is_v_row_bit_exact(D):
+def test_seq_len_one_is_v_row_bit_exact(D, qk_path):
     wl = make_workload(name="L1", seq_lens=[1, 1, 1, 1], num_q_heads=8, num_kv_heads=2,
                        head_dim=D, block_size=16, seed=[1, D], poison=True)
     t = to_dev(wl)
@@ -180,7 +200,7 @@ def test_lse_null_leaves_neighbours_untouched():
     assert np.abs(out.cpu().numpy() - eo).max() < 1e-3
 
 
-def test_unused_table_entries_may_hold_anything():
+def test_unused_table_entries_may_hold_anything(qk_path):
     wl = make_workload(name="inv", seq_lens=[3, 40, 17, 0, 64], num_q_heads=8, num_kv_heads=2,
                        head_dim=128, block_size=16, seed=[4], stride=12, unused_entry="invalid",
                        poison=True)
@@ -190,7 +210,7 @@ def test_unused_table_entries_may_hold_anything():
         compare(*run_gpu(wl, t, partition_size=P), *oracle_full(wl), f"-1 unused entries P={P}")
 
 
-def test_bad_table_entry_poisons_only_its_sequence():
+def test_bad_table_entry_poisons_only_its_sequence(qk_path):
     wl = make_workload(name="bad", seq_lens=[40, 40, 40], num_q_heads=8, num_kv_heads=2,
                        head_dim=128, block_size=16, seed=[5])
     exp = oracle_full(wl)
@@ -203,7 +223,7 @@ def test_bad_table_entry_poisons_only_its_sequence():
         assert np.abs(out[0] - exp[0][0]).max() < 1e-3
 
 
-def test_length_beyond_table_or_partitions_is_nan():
+def test_length_beyond_table_or_partitions_is_nan(qk_path):
     wl = make_workload(name="len", seq_lens=[40, 40], num_q_heads=4, num_kv_heads=2,
                        head_dim=64, block_size=16, seed=[6])
     exp = oracle_full(wl)
@@ -264,7 +284,7 @@ def test_witness_config2_and_5():
 # split partials and the reduce kernel on their own
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("P,W,sinks", [(32, 0, True), (64, 45, True), (16, 0, False)])
-def test_partials_match_oracle_partitions(P, W, sinks):
+def test_partials_match_oracle_partitions(P, W, sinks, qk_path):
     wl = make_workload(name="part", seq_lens=EDGE_LENS, num_q_heads=8, num_kv_heads=2,
                        head_dim=128, block_size=16, seed=[P, W], window=W, with_sinks=sinks,
                        poison=True)
