@@ -27,6 +27,8 @@ METRIC = "KV-read GB/s (% of HBM peak) + µs/decode step, bf16 d=128 GQA paged d
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = ["paged_kv_attention_attn_amd/csrc/pa_decode.hip",
+                  "paged_kv_attention_attn_amd/csrc/pa_balanced.hip",
+                  "paged_kv_attention_attn_amd/csrc/pa_qk.hpp",
                   "paged_kv_attention_attn_amd/csrc/pa_device.hpp"]
 
 
@@ -38,7 +40,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, partition: int):
+def measured_traffic(workload: str, schedule: str):
     """HBM bytes per decode launch from the committed rocprofv3 counter runs, if they were taken
     on the current kernel source for this workload; else None."""
     try:
@@ -48,7 +50,7 @@ def measured_traffic(workload: str, partition: int):
         return None
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    if rec.get("workload") != workload or rec.get("partition_size") != partition:
+    if rec.get("workload") != workload or rec.get("schedule") != schedule:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -100,8 +102,14 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--head-dim", type=int, default=128)
     ap.add_argument("--q-heads", type=int, default=None)
+    ap.add_argument("--schedule", choices=["balanced", "partitioned", "unsplit"],
+                    default="balanced",
+                    help="balanced: persistent workers + fix-up (default); partitioned: fixed "
+                         "partitions + reduce; unsplit: one workgroup per (sequence, KV head)")
     ap.add_argument("--partition", type=int, default=None,
-                    help="partition size (0 = unsplit); default: the library's suggestion")
+                    help="partitioned schedule: partition size (default: library suggestion)")
+    ap.add_argument("--workers", type=int, default=0,
+                    help="balanced schedule: persistent workers (0 = device default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--mode", choices=["decode", "copy"], default="decode",
@@ -136,11 +144,16 @@ def main() -> int:
     wl = make_config(args.config, **kw)
     B, Hq, D = wl.q.shape
     maxL = int(wl.seq_lens.max())
-    P = args.partition
-    if P is None:
-        P = wl.partition_size or pa.suggest_partition_size(B, wl.num_kv_heads, maxL,
-                                                           wl.block_size,
-                                                           props.multi_processor_count)
+    if args.schedule == "unsplit":
+        P = 0
+    elif args.schedule == "partitioned":
+        P = args.partition
+        if P is None:
+            P = wl.partition_size or pa.suggest_partition_size(B, wl.num_kv_heads, maxL,
+                                                               wl.block_size,
+                                                               props.multi_processor_count)
+    else:
+        P = -1
     pmax = pa.num_partitions(maxL, P) if P > 0 else 0
     kv_bytes = wl.kv_bytes()
     pool_bytes = 2 * wl.k_cache.nbytes
@@ -163,18 +176,41 @@ def main() -> int:
         part = torch.empty((B, Hq, pmax, D), dtype=torch.float32, device=dev)
         plse = torch.empty((B, Hq, pmax), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    shape = pa.make_shape(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, P, pmax)
-    variant = pa.variant_name(shape, D, wl.block_size)
+    shape = pa.make_shape(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, max(P, 0), pmax)
+    workers = args.workers
+    if P < 0:
+        workers = workers or pa.balanced_default_workers(D, Hq // wl.num_kv_heads)
+        ws = torch.empty(pa.balanced_workspace_size(shape, D, workers), dtype=torch.uint8,
+                         device=dev)
+        variant = f"pa_balanced_{'valu' if os.environ.get('PA_DECODE_PATH') == 'valu' else 'mfma'}" \
+                  f"_d{D}_g{Hq // wl.num_kv_heads}_workers{workers}"
+    else:
+        variant = pa.variant_name(shape, D, wl.block_size)
 
-    def step(i):
+    # one decode step = the decode kernel launch, then its merge launch (if any); events mark the
+    # end of the decode launch so its own duration can be read
+    def step(i, ev=None):
         c = i % copies
+        if ev is not None:
+            ev[0].record(stream)
         if P > 0:
             pa.decode(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window, sinks=sinks,
                       partition_size=P, max_partitions=pmax, out=part, lse=plse, stream=stream)
-            pa.reduce(part, plse, L, partition_size=P, out=out, lse=lse, stream=stream)
-        else:
+        elif P == 0:
             pa.decode(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window, sinks=sinks,
                       out=out, lse=lse, stream=stream)
+        else:
+            pa.decode_balanced(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window,
+                               sinks=sinks, out=out, lse=lse, workspace=ws, num_workers=workers,
+                               merge=False, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if P > 0:
+            pa.reduce(part, plse, L, partition_size=P, out=out, lse=lse, stream=stream)
+        elif P < 0:
+            pa.reduce_balanced(L, out, lse, shape=shape, head_dim=D, block_size=wl.block_size,
+                               window=wl.window, sinks=sinks, workspace=ws,
+                               num_workers=workers, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -186,17 +222,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        c = i % copies
-        ev[i][0].record(stream)
-        if P > 0:
-            pa.decode(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window, sinks=sinks,
-                      partition_size=P, max_partitions=pmax, out=part, lse=plse, stream=stream)
-            ev[i][1].record(stream)
-            pa.reduce(part, plse, L, partition_size=P, out=out, lse=lse, stream=stream)
-        else:
-            pa.decode(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window, sinks=sinks,
-                      out=out, lse=lse, stream=stream)
-            ev[i][1].record(stream)
+        step(i, ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dec_ms = [a.elapsed_time(b) for a, b in ev]
@@ -220,7 +246,7 @@ def main() -> int:
     del probe
 
     workload = f"config{args.config}" + (f"_d{D}_hq{Hq}" if args.config == 3 else "")
-    traffic = measured_traffic(workload, P)
+    traffic = measured_traffic(workload, args.schedule)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -241,7 +267,9 @@ def main() -> int:
             "batch": B, "q_heads": Hq, "kv_heads": wl.num_kv_heads, "head_dim": D,
             "block_size": wl.block_size, "window": wl.window,
             "sinks": wl.sinks is not None, "seq_len_sum": int(wl.seq_lens.sum()),
-            "max_seq_len": maxL, "partition_size": P, "kv_bytes_per_step": kv_bytes,
+            "max_seq_len": maxL, "schedule": args.schedule,
+            "partition_size": P if P > 0 else None,
+            "workers": workers if P < 0 else None, "kv_bytes_per_step": kv_bytes,
             "variant": variant, "kv_pool_copies": copies, "parallelism": "none (1 GPU)",
         },
         "roofline": {

@@ -123,6 +123,55 @@ pa_status paged_attn_reduce(const pa_shape* shape, int32_t head_dim, const float
                             const float* lse_partials, const int32_t* seq_lens, float* out,
                             float* lse_out, void* stream);
 
+/*
+ * Balanced split-KV decode: the same operation as paged_attn_decode + paged_attn_reduce, with the
+ * split placed where the work balances.  Every (sequence, KV head) is a unit of 16-token tiles
+ * over its attended range; units are laid end to end and num_workers persistent one-wave workers
+ * each take an equal contiguous share of all tiles, so a long sequence is split across several
+ * workers and several short ones may share one.  paged_attn_decode_balanced writes every unit
+ * that lies inside one worker's share to out/lse directly, and leaves partial outputs plus
+ * log-sum-exps in the workspace for units cut by share boundaries; paged_attn_reduce_balanced
+ * (same stream, same arguments) merges those with the log-sum-exp rule and handles empty
+ * sequences.  out/lse are complete only after both calls.  Sources as for paged_attn_decode /
+ * paged_attn_reduce (split-KV partitions with partial output + LSE merged by a reducer that
+ * takes the output, the sequence lengths and the LSE buffer).
+ *
+ *   shape->partition_size and max_partitions are not used.
+ *   out          fp32 [B][Hq][head_dim]      device, written
+ *   lse          fp32 [B][Hq] or NULL        device, written
+ *   workspace    device memory of at least paged_attn_balanced_workspace_size(...) bytes,
+ *                16-byte aligned, owned by the caller; no initialisation needed.  It carries
+ *                the partials from the decode call to the reduce call; calls that overlap in
+ *                time must use different workspaces.
+ *   num_workers  persistent workers (waves); 0 = paged_attn_balanced_default_workers(...).
+ *                Both calls must resolve to the same count.
+ *
+ * Errors and NaN reporting as for paged_attn_decode; a workspace that is too small or misaligned
+ * is PA_ERR_SHAPE.
+ */
+pa_status paged_attn_decode_balanced(const pa_shape* shape, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_table,
+                                     const int32_t* seq_lens, float scale, int32_t head_dim,
+                                     int32_t block_size, int32_t window, const float* sinks,
+                                     float* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, int32_t num_workers, void* stream);
+
+pa_status paged_attn_reduce_balanced(const pa_shape* shape, const int32_t* seq_lens,
+                                     int32_t head_dim, int32_t block_size, int32_t window,
+                                     const float* sinks, float* out, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     int32_t num_workers, void* stream);
+
+/* Workspace bytes paged_attn_decode_balanced needs for this shape and worker count (0 = the
+ * default count on the current device), or a negative pa_status. */
+int64_t paged_attn_balanced_workspace_size(const pa_shape* shape, int32_t head_dim,
+                                           int32_t num_workers);
+
+/* Workers that run at once on the current device for this head_dim and Hq/Hkv (compute units
+ * times resident one-wave workers per unit), or a negative pa_status.  Queries the device; does
+ * not launch anything. */
+int32_t paged_attn_balanced_default_workers(int32_t head_dim, int32_t group);
+
 /* Partitions a sequence of length seq_len occupies: max(1, ceil(seq_len / partition_size));
  * 1 when partition_size == 0; -1 for a negative length or partition size. */
 int32_t paged_attn_num_partitions(int32_t seq_len, int32_t partition_size);

@@ -47,7 +47,7 @@ class PaShape(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it first "
-                          "(python -m paged_kv_attention_attn_amd.build)")
+                          "(python paged_kv_attention_attn_amd/build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     sp = ctypes.POINTER(PaShape)
@@ -60,6 +60,12 @@ def _load() -> ctypes.CDLL:
         "paged_attn_check_tables": (i32, [sp, i32, i32, vp, vp]),
         "paged_attn_suggest_partition_size": (i32, [i32, i32, i32, i32, i32]),
         "paged_attn_abi_version": (i32, []),
+        "paged_attn_decode_balanced": (i32, [sp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp,
+                                             vp, vp, ctypes.c_size_t, i32, vp]),
+        "paged_attn_reduce_balanced": (i32, [sp, vp, i32, i32, i32, vp, vp, vp, vp,
+                                             ctypes.c_size_t, i32, vp]),
+        "paged_attn_balanced_workspace_size": (ctypes.c_int64, [sp, i32, i32]),
+        "paged_attn_balanced_default_workers": (i32, [i32, i32]),
         "paged_attn_gather_witness": (i32, [sp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]),
         "paged_attn_stream_read": (i32, [vp, ctypes.c_size_t, i32, vp, vp]),
         "paged_attn_copy": (i32, [vp, vp, ctypes.c_size_t, vp]),
@@ -73,7 +79,10 @@ def _load() -> ctypes.CDLL:
 
 _lib = _load()
 
-EXPORTED = ("paged_attn_decode", "paged_attn_reduce", "paged_attn_num_partitions",
+EXPORTED = ("paged_attn_decode", "paged_attn_reduce", "paged_attn_decode_balanced",
+            "paged_attn_reduce_balanced",
+            "paged_attn_balanced_workspace_size", "paged_attn_balanced_default_workers",
+            "paged_attn_num_partitions",
             "paged_attn_variant_name", "paged_attn_status_string", "paged_attn_check_tables",
             "paged_attn_suggest_partition_size", "paged_attn_abi_version",
             "paged_attn_gather_witness", "paged_attn_stream_read", "paged_attn_copy")
@@ -231,12 +240,99 @@ def reduce(partials: torch.Tensor, lse_partials: torch.Tensor, seq_lens: torch.T
     return out, lse
 
 
+def balanced_default_workers(head_dim: int, group: int) -> int:
+    n = int(_lib.paged_attn_balanced_default_workers(int(head_dim), int(group)))
+    if n <= 0:
+        raise PagedAttnError(n, "paged_attn_balanced_default_workers")
+    return n
+
+
+def balanced_workspace_size(shape: PaShape, head_dim: int, num_workers: int = 0) -> int:
+    n = int(_lib.paged_attn_balanced_workspace_size(ctypes.byref(shape), int(head_dim),
+                                                    int(num_workers)))
+    if n < 0:
+        raise PagedAttnError(n, "paged_attn_balanced_workspace_size")
+    return n
+
+
+def decode_balanced(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float, *,
+                    window: int = 0, sinks: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    want_lse: bool = True, workspace: Optional[torch.Tensor] = None,
+                    num_workers: int = 0, merge: bool = True, stream=None):
+    """paged_attn_decode_balanced (+ paged_attn_reduce_balanced when ``merge``) on torch tensors:
+    the final (out [B][Hq][D], lse [B][Hq] or None).  ``workspace`` (a device tensor of at least
+    balanced_workspace_size bytes) is allocated here when not given; with merge=False the caller
+    runs reduce_balanced with the same arguments and workspace."""
+    _dev(q, "q", _BF16_LIKE)
+    _dev(k_cache, "k_cache", _BF16_LIKE)
+    _dev(v_cache, "v_cache", _BF16_LIKE)
+    _dev(block_table, "block_table", (torch.int32,))
+    _dev(seq_lens, "seq_lens", (torch.int32,))
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B][Hq][D]; k_cache/v_cache [num_blocks][Hkv][bs][D], equal")
+    B, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("inconsistent q / cache / block_table / seq_lens shapes")
+    if sinks is not None:
+        _dev(sinks, "sinks", (torch.float32,))
+        if sinks.shape != (Hq,):
+            raise ValueError("sinks must be fp32 [Hq]")
+    shape = make_shape(B, Hq, Hkv, NB, block_table.shape[1])
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    else:
+        _dev(out, "out", (torch.float32,))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", (torch.float32,))
+    need = balanced_workspace_size(shape, D, num_workers)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.paged_attn_decode_balanced(ctypes.byref(shape), _ptr(q), _ptr(k_cache),
+                                         _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                         float(scale), int(D), int(bs), int(window),
+                                         _ptr(sinks), _ptr(out), _ptr(lse), _ptr(workspace),
+                                         nbytes, int(num_workers), _stream(q.device, stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "paged_attn_decode_balanced")
+    if merge:
+        reduce_balanced(seq_lens, out, lse, shape=shape, head_dim=D, block_size=bs,
+                        window=window, sinks=sinks, workspace=workspace, num_workers=num_workers,
+                        stream=stream)
+    return out, lse
+
+
+def reduce_balanced(seq_lens: torch.Tensor, out: torch.Tensor, lse: Optional[torch.Tensor], *,
+                    shape: PaShape, head_dim: int, block_size: int, window: int = 0,
+                    sinks: Optional[torch.Tensor] = None, workspace: torch.Tensor,
+                    num_workers: int = 0, stream=None) -> None:
+    """paged_attn_reduce_balanced: merge the partials decode_balanced left in ``workspace``."""
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.paged_attn_reduce_balanced(ctypes.byref(shape), _ptr(seq_lens), int(head_dim),
+                                         int(block_size), int(window), _ptr(sinks), _ptr(out),
+                                         _ptr(lse), _ptr(workspace), nbytes, int(num_workers),
+                                         _stream(out.device, stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "paged_attn_reduce_balanced")
+
+
 def paged_attention(q, k_cache, v_cache, block_table, seq_lens, scale, *, window: int = 0,
                     sinks=None, partition_size: int = 0, max_seq_len: Optional[int] = None,
                     want_lse: bool = True, stream=None):
     """One decode step end to end: decode (+ reduce when partition_size > 0).  In split mode
-    ``max_seq_len`` (a host-side bound on seq_lens) sizes the partial buffers."""
-    if partition_size <= 0:
+    ``max_seq_len`` (a host-side bound on seq_lens) sizes the partial buffers.
+    partition_size = -1 selects the balanced schedule (decode_balanced)."""
+    if partition_size < 0:
+        return decode_balanced(q, k_cache, v_cache, block_table, seq_lens, scale, window=window,
+                               sinks=sinks, want_lse=want_lse, stream=stream)
+    if partition_size == 0:
         return decode(q, k_cache, v_cache, block_table, seq_lens, scale, window=window,
                       sinks=sinks, want_lse=want_lse, stream=stream)
     if max_seq_len is None:

@@ -1,6 +1,8 @@
 """Build libpaged_attn.so (gfx950) in-tree with hipcc.
 
-    python -m paged_kv_attention_attn_amd.build [--verbose]
+    python paged_kv_attention_attn_amd/build.py [--verbose]
+
+(Run by path, not as a package module: importing the package loads the library it builds.)
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction selection turned off
 (-Xclang -target-feature -Xclang -packed-fp32-ops), and linked into one shared library next to
@@ -22,8 +24,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpaged_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_decode_mfma.hip", "pa_reduce.hip", "pa_aux.hip"]
-HEADERS = ["pa_device.hpp", "pa_kernels.hpp"]
+SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_balanced.hip", "pa_reduce.hip", "pa_aux.hip"]
+HEADERS = ["pa_device.hpp", "pa_kernels.hpp", "pa_qk.hpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

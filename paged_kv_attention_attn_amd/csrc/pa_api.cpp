@@ -45,6 +45,9 @@ pa_status check_shape(const pa_shape* s) {
   if (s->num_seqs > kMaxGridYZ || s->num_kv_heads > kMaxGridYZ) return PA_ERR_SHAPE;
   if (s->partition_size > 0 && (s->partition_size % 16 != 0 || s->max_partitions < 1))
     return PA_ERR_SHAPE;
+  // decode grid: (partition slots) x Hkv x B workgroups in one dimension
+  const int64_t slots = s->partition_size > 0 ? s->max_partitions : 1;
+  if (slots * s->num_kv_heads * (int64_t)s->num_seqs > 0x7FFFFFFF) return PA_ERR_SHAPE;
   return PA_OK;
 }
 
@@ -151,6 +154,7 @@ pa_status paged_attn_decode(const pa_shape* shape, const void* q, const void* k_
   p.out = out;
   p.lse = lse;
   p.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.num_seqs = shape->num_seqs;
   p.num_q_heads = shape->num_q_heads;
   p.num_kv_heads = shape->num_kv_heads;
   p.num_blocks = shape->num_blocks;
@@ -164,10 +168,151 @@ pa_status paged_attn_decode(const pa_shape* shape, const void* q, const void* k_
                  pa::decode_variant_name(head_dim, group, waves, split, path), shape->num_seqs,
                  shape->num_q_heads, shape->num_kv_heads, block_size, p.psize, p.max_parts,
                  window);
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
-  const hipError_t e = path == pa::QkPath::kMfma
-                           ? pa::launch_decode_mfma(p, head_dim, group, waves, shape->num_seqs, hs)
-                           : pa::launch_decode(p, head_dim, group, waves, shape->num_seqs, hs);
+  const hipError_t e =
+      pa::launch_decode(p, head_dim, group, waves, path, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+namespace {
+
+constexpr int32_t kMaxWorkers = 1 << 20;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// workspace layout: prefix int64 [B+1] | lse fp32 [N][2][G] | o fp32 [N][2][G][D]
+struct WsLayout {
+  size_t prefix, lse, o, total;
+};
+
+WsLayout ws_layout(int32_t num_seqs, int32_t group, int32_t head_dim, int32_t workers) {
+  WsLayout l;
+  l.prefix = 0;
+  l.lse = align256(((size_t)num_seqs + 1) * sizeof(int64_t));
+  l.o = l.lse + align256((size_t)workers * 2 * group * sizeof(float));
+  l.total = l.o + align256((size_t)workers * 2 * group * head_dim * sizeof(float));
+  return l;
+}
+
+}  // namespace
+
+int32_t paged_attn_balanced_default_workers(int32_t head_dim, int32_t group) {
+  if (!head_dim_ok(head_dim) || !pa::decode_supported(head_dim, group)) return PA_ERR_UNSUPPORTED;
+  pa::QkPath path;
+  if (decode_path(head_dim, group, &path) != 0) return PA_ERR_UNSUPPORTED;
+  const int n = pa::balanced_default_workers(head_dim, group, path);
+  return n > 0 ? n : PA_ERR_LAUNCH;
+}
+
+int64_t paged_attn_balanced_workspace_size(const pa_shape* shape, int32_t head_dim,
+                                           int32_t num_workers) {
+  const pa_status st = check_shape(shape);
+  if (st != PA_OK) return st;
+  const int group = shape->num_q_heads / shape->num_kv_heads;
+  if (!head_dim_ok(head_dim) || !pa::decode_supported(head_dim, group)) return PA_ERR_UNSUPPORTED;
+  if (num_workers < 0 || num_workers > kMaxWorkers) return PA_ERR_SHAPE;
+  if (num_workers == 0) {
+    num_workers = paged_attn_balanced_default_workers(head_dim, group);
+    if (num_workers < 0) return num_workers;
+  }
+  return (int64_t)ws_layout(shape->num_seqs, group, head_dim, num_workers).total;
+}
+
+// Validation and parameter block shared by the two balanced calls; returns PA_OK and fills bp,
+// or the status to return.  q/k/v/table may be null for the reduce call (not used there).
+pa_status balanced_setup(const pa_shape* shape, int32_t head_dim, int32_t block_size,
+                         int32_t window, const int32_t* seq_lens, const float* sinks, float* out,
+                         float* lse, void* workspace, size_t workspace_bytes,
+                         int32_t num_workers, pa::BalancedParams* bp, pa::QkPath* path,
+                         int* group_out) {
+  const pa_status st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  const int group = shape->num_q_heads / shape->num_kv_heads;
+  if (!pa::decode_supported(head_dim, group)) return PA_ERR_UNSUPPORTED;
+  if (window < 0) return PA_ERR_SHAPE;
+  if (num_workers < 0 || num_workers > kMaxWorkers) return PA_ERR_SHAPE;
+  if ((int64_t)shape->num_seqs * shape->num_q_heads > 0x7FFFFFFF) return PA_ERR_SHAPE;
+  if (decode_path(head_dim, group, path) != 0) return PA_ERR_UNSUPPORTED;
+  *group_out = group;
+  if (shape->num_seqs == 0) return PA_OK;
+  if (seq_lens == nullptr || out == nullptr || workspace == nullptr) return PA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return PA_ERR_SHAPE;
+  if (num_workers == 0) {
+    num_workers = pa::balanced_default_workers(head_dim, group, *path);
+    if (num_workers <= 0) return PA_ERR_LAUNCH;
+  }
+  const WsLayout wl = ws_layout(shape->num_seqs, group, head_dim, num_workers);
+  if (workspace_bytes < wl.total) return PA_ERR_SHAPE;
+  pa::DecodeParams& p = bp->d;
+  p.seq_lens = seq_lens;
+  p.sinks = sinks;
+  p.out = out;
+  p.lse = lse;
+  p.num_seqs = shape->num_seqs;
+  p.num_q_heads = shape->num_q_heads;
+  p.num_kv_heads = shape->num_kv_heads;
+  p.num_blocks = shape->num_blocks;
+  p.stride = shape->block_table_stride;
+  p.bs_log2 = log2_exact(block_size);
+  p.window = window;
+  p.psize = 0;
+  p.max_parts = 1;
+  char* ws = static_cast<char*>(workspace);
+  bp->prefix = reinterpret_cast<int64_t*>(ws + wl.prefix);
+  bp->ws_lse = reinterpret_cast<float*>(ws + wl.lse);
+  bp->ws_o = reinterpret_cast<float*>(ws + wl.o);
+  bp->num_workers = num_workers;
+  return PA_OK;
+}
+
+pa_status paged_attn_decode_balanced(const pa_shape* shape, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_table,
+                                     const int32_t* seq_lens, float scale, int32_t head_dim,
+                                     int32_t block_size, int32_t window, const float* sinks,
+                                     float* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, int32_t num_workers, void* stream) {
+  if (!std::isfinite(scale)) {
+    const pa_status st = check_shape(shape);
+    return st != PA_OK ? st : PA_ERR_SHAPE;
+  }
+  pa::BalancedParams bp{};
+  pa::QkPath path;
+  int group = 0;
+  const pa_status st = balanced_setup(shape, head_dim, block_size, window, seq_lens, sinks, out,
+                                      lse, workspace, workspace_bytes, num_workers, &bp, &path,
+                                      &group);
+  if (st != PA_OK || shape->num_seqs == 0) return st;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr)
+    return PA_ERR_NULL;
+  pa::DecodeParams& p = bp.d;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const char*>(k_cache);
+  p.v_cache = static_cast<const char*>(v_cache);
+  p.block_table = block_table;
+  p.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
+  if (debug_log())
+    std::fprintf(stderr, "[paged_attn] balanced %s B=%d Hq=%d Hkv=%d bs=%d W=%d workers=%d\n",
+                 path == pa::QkPath::kMfma ? "mfma" : "valu", shape->num_seqs,
+                 shape->num_q_heads, shape->num_kv_heads, block_size, window, bp.num_workers);
+  const hipError_t e =
+      pa::launch_balanced(bp, head_dim, group, path, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status paged_attn_reduce_balanced(const pa_shape* shape, const int32_t* seq_lens,
+                                     int32_t head_dim, int32_t block_size, int32_t window,
+                                     const float* sinks, float* out, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     int32_t num_workers, void* stream) {
+  pa::BalancedParams bp{};
+  pa::QkPath path;
+  int group = 0;
+  const pa_status st = balanced_setup(shape, head_dim, block_size, window, seq_lens, sinks, out,
+                                      lse, workspace, workspace_bytes, num_workers, &bp, &path,
+                                      &group);
+  if (st != PA_OK || shape->num_seqs == 0) return st;
+  const hipError_t e =
+      pa::launch_balanced_fixup(bp, head_dim, group, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -1,0 +1,523 @@
+// Balanced split-KV decode for gfx950: persistent one-wave workers over the flattened tile
+// sequence, then a fix-up merge.
+//
+// The split-KV method (partitions of a sequence's KV each emit a partial output plus a
+// log-sum-exp; a second kernel merges them) with the partition boundaries placed where the work
+// balances instead of at fixed token offsets.  Every (sequence b, KV head kvh) is a unit of
+// T_b 16-token tiles (its attended range); units are laid end to end in (b, kvh) order, and
+// worker w of N takes the contiguous tiles [A(w), A(w+1)), A(w) = floor(w * T_total / N).  A
+// worker streams its tiles with the loads of the next tile in flight, and at every unit boundary
+// inside its range flushes the unit's piece: a unit that starts and ends inside one worker is
+// final and written to the output directly (sink folded, normalised); a unit cut by a range
+// boundary leaves one partial per worker that holds part of it (at most two per worker: the
+// first and the last unit it touches), and the fix-up kernel merges them with the
+// log-sum-exp rule.
+//
+// All workers finish within about one tile of each other, no workgroup is launched per unit, and
+// the partial traffic is at most 2 * N * G * (D + 1) floats.  Measured on MI355X for a
+// 64-sequence, 512..4096-token Llama-8B-shaped step: fixed-partition grids left a quarter of the
+// workgroup slots idle and a long tail; persistent workers over the same tiles stream at the
+// rate of a plain gather.
+//
+// Sources: one-token split-KV decode with partial outputs + LSE merged by a reduce step,
+// ROCm/rocm-libraries PR #13700 "prepare saved paged decode bindings once", Summary and review
+// finding N1 (the reducer takes the output, the sequence lengths and the LSE buffer); the tile
+// math as in pa_qk.hpp; sliding window and attention sinks, randomvariable/vllm issue #23, table
+// "Current state".
+#include <cstdio>
+#include <type_traits>
+
+#include "pa_device.hpp"
+#include "pa_kernels.hpp"
+#include "pa_qk.hpp"
+
+namespace pa {
+
+// A worker gets at least this many tiles (fewer workers for tiny batches).
+constexpr int kMinTilesPerWorker = 4;
+
+// One sequence's attended range [start, L) in 16-token tiles: tiles [t0, t0 + T).  T = 0 for an
+// empty sequence or one whose length the block table cannot hold (bad).
+struct SeqSpan {
+  int L, start, t0, T;
+  bool bad;
+};
+
+__device__ __forceinline__ SeqSpan seq_span(int L, int window, int64_t cap) {
+  SeqSpan s;
+  s.L = L;
+  s.bad = L < 0 || (int64_t)L > cap;
+  const int Lc = s.bad ? 0 : L;
+  s.start = (window > 0 && Lc > window) ? Lc - window : 0;
+  s.t0 = s.start / kTileTokens;
+  s.T = Lc > 0 ? (Lc + kTileTokens - 1) / kTileTokens - s.t0 : 0;
+  return s;
+}
+
+// Workers actually used for T_total tiles, out of at most n.
+__device__ __forceinline__ int effective_workers(int64_t total, int n) {
+  const int64_t want = (total + kMinTilesPerWorker - 1) / kMinTilesPerWorker;
+  return (int)(want < 1 ? 1 : (want < n ? want : n));
+}
+
+// First tile of worker w: floor(w * total / n), evaluated as w*q + (w*r)/n with
+// total = q*n + r so that no product overflows (w < n <= 2^20).
+__device__ __forceinline__ int64_t worker_begin(int64_t total, int n, int w) {
+  const int64_t q = total / n, r = total - q * n;
+  return (int64_t)w * q + ((int64_t)w * r) / n;
+}
+
+// The worker whose range holds tile x (0 <= x < total): the largest w with
+// floor(w * total / n) <= x, i.e. ceil((x + 1) * n / total) - 1.  Exact in 64 bits while
+// total * n < 2^63 (2^43 tiles at the 2^20-worker limit).
+__device__ __forceinline__ int worker_of(int64_t total, int n, int64_t x) {
+  return (int)(((x + 1) * n + total - 1) / total) - 1;
+}
+
+__device__ __forceinline__ int64_t shfl_up64(int64_t x, int off, int lane) {
+  const int src = (lane >= off ? lane - off : lane) << 2;
+  const int lo = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)x);
+  const int hi = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)((uint64_t)x >> 32));
+  const int64_t y = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+  return lane >= off ? y : 0;
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan64(int64_t x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x += shfl_up64(x, off, lane);
+  return x;
+}
+
+__device__ __forceinline__ int64_t readlane64(int64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Position in the flattened tile sequence: unit (b, kvh), tile ti of the unit, and the span of
+// sequence b.  All fields are wave-uniform.
+struct Cursor {
+  int b, kvh, ti;
+  SeqSpan s;
+};
+
+struct BalancedCtx {
+  const DecodeParams* p;
+  int64_t cap;
+  __device__ __forceinline__ SeqSpan span(int b) const {
+    return seq_span(__builtin_amdgcn_readfirstlane(p->seq_lens[b]), p->window, cap);
+  }
+  // next tile; skips sequences without tiles (callers never step past the last tile)
+  __device__ __forceinline__ void advance(Cursor& c) const {
+    if (++c.ti < c.s.T) return;
+    c.ti = 0;
+    if (++c.kvh < p->num_kv_heads) return;
+    c.kvh = 0;
+    do {
+      ++c.b;
+      c.s = span(c.b);
+    } while (c.s.T == 0 && c.b + 1 < p->num_seqs);
+  }
+  // physical block of the cursor's tile
+  __device__ __forceinline__ int phys(const Cursor& c) const {
+    const int tile = c.s.t0 + c.ti;
+    return __builtin_amdgcn_readfirstlane(
+        p->block_table[(size_t)c.b * p->stride + ((tile * kTileTokens) >> p->bs_log2)]);
+  }
+};
+
+template <int D, int G, int DEPTH, class QK>
+__global__ __launch_bounds__(kWave) void balanced_decode_kernel(const BalancedParams bp) {
+  using RG = RowGeom<D>;
+  constexpr int E = RG::kElems;
+  const DecodeParams& p = bp.d;
+  const int lane = threadIdx.x;
+  const int c = lane & (kRowLanes - 1);
+  const int w = blockIdx.x;
+  const BalancedCtx ctx{&p, (int64_t)p.stride << p.bs_log2};
+
+  // pass 1: total tiles (worker 0 also records the per-sequence prefix for the fix-up)
+  int64_t carry = 0;
+  for (int base = 0; base < p.num_seqs; base += kWave) {
+    const int j = base + lane;
+    const int64_t T = j < p.num_seqs ? seq_span(p.seq_lens[j], p.window, ctx.cap).T : 0;
+    const int64_t incl = wave_incl_scan64(T, lane) + carry;
+    if (w == 0 && j < p.num_seqs) bp.prefix[j] = incl - T;
+    carry = readlane64(incl, kWave - 1);
+  }
+  if (w == 0 && lane == 0) bp.prefix[p.num_seqs] = carry;
+  const int64_t total = carry * p.num_kv_heads;
+  const int n_eff = effective_workers(total, bp.num_workers);
+  if (w >= n_eff) return;
+  const int64_t A = worker_begin(total, n_eff, w);
+  const int n = (int)(worker_begin(total, n_eff, w + 1) - A);
+  if (n <= 0) return;
+
+  // pass 2: the unit holding tile A
+  Cursor cur{0, 0, 0, {}};
+  carry = 0;
+  for (int base = 0; base < p.num_seqs; base += kWave) {
+    const int j = base + lane;
+    const int64_t T = j < p.num_seqs ? seq_span(p.seq_lens[j], p.window, ctx.cap).T : 0;
+    const int64_t incl = wave_incl_scan64(T, lane) + carry;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(j < p.num_seqs &&
+                                                     incl * p.num_kv_heads > A);
+    if (hit != 0) {
+      const int f = __builtin_ctzll(hit);
+      const int64_t P = readlane64(incl, f) - readlane64(T, f);
+      const int64_t Tb = readlane64(T, f);
+      const int64_t off = A - P * p.num_kv_heads;   // tiles into sequence base + f
+      cur.b = base + f;
+      cur.s = ctx.span(cur.b);
+      cur.kvh = (int)(off / Tb);
+      cur.ti = (int)(off - (int64_t)cur.kvh * Tb);
+      break;
+    }
+    carry = readlane64(incl, kWave - 1);
+  }
+
+  const float c2 = fabsf(p.qk_scale_log2);
+  const uint32_t qflip = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
+  QK qk;
+  qk.init(p, cur.b, cur.kvh * G, lane, qflip, c2);
+
+  // the issue cursor, with the block-table entry of the next tile fetched one issue ahead; it
+  // only advances while another tile of this worker follows, so it never walks past the last
+  // sequence that has tiles
+  Cursor iss = cur;
+  int phys_next = ctx.phys(iss);
+  struct Slot {
+    Cursor at;
+    bool ok;
+  };
+  auto issue = [&](int k, typename QK::Tile& t, Slot& s) {
+    s.at = iss;
+    const int phys = phys_next;
+    if (k + 1 < n) {
+      ctx.advance(iss);
+      phys_next = ctx.phys(iss);
+    }
+    const TileAddr ta{p.num_blocks, p.num_kv_heads, s.at.kvh, p.bs_log2, RG::kRowBytes};
+    const int64_t off = ta.offset(phys, s.at.s.t0 + s.at.ti);
+    s.ok = off >= 0;
+    if (s.ok) qk.issue(t, p.k_cache + off, p.v_cache + off, lane);
+  };
+
+  int piece_start = cur.ti;
+  bool first_piece = true;
+  bool piece_bad = false;
+
+  // flush the current piece of unit (at.b, at.kvh), which ends at tile at.ti
+  auto flush = [&](const Cursor& at) {
+    float Mh[G], lh[G];
+    qk.merge_rows(Mh, lh);
+    const bool whole = piece_start == 0 && at.ti == at.s.T - 1;
+    const int h0 = at.kvh * G;
+    if (lane < kRowLanes) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float M = Mh[h], lt = lh[h];
+        float scale_o = 1.f;
+        if (whole && p.sinks != nullptr) {
+          // the sink logit joins the max and the denominator with a zero value row
+          const float s2 = p.sinks[h0 + h] * kLog2e;
+          const float M2 = fmaxf(M, s2);
+          const float M2u = M2 == -INFINITY ? 0.f : M2;
+          scale_o = fast_exp2(M - M2u);
+          lt = fmaf(lt, scale_o, fast_exp2(s2 - M2u));
+          M = M2;
+        }
+        const float inv = lt > 0.f ? scale_o / lt : 0.f;
+        float lv = lt > 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
+        if (piece_bad) lv = __builtin_nanf("");
+        float* dst;
+        if (whole) {
+          const size_t row = (size_t)at.b * p.num_q_heads + h0 + h;
+          dst = p.out + row * D;
+          if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
+        } else {
+          const size_t slot = ((size_t)w * 2 + (first_piece ? 0 : 1)) * G + h;
+          dst = bp.ws_o + slot * D;
+          if (c == 0) bp.ws_lse[slot] = lv;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          dst[RG::dim(c, e)] = piece_bad ? __builtin_nanf("") : qk.acc[h][e] * inv;
+      }
+    }
+    first_piece = false;
+    piece_bad = false;
+    piece_start = 0;
+  };
+
+  auto consume = [&](int k, typename QK::Tile& t, const Slot& s, const Slot* next) {
+    const Cursor& at = s.at;
+    if (s.ok) {
+      const int tok0 = (at.s.t0 + at.ti) * kTileTokens;
+      if (tok0 >= at.s.start && tok0 + kTileTokens <= at.s.L)
+        qk.template consume<false>(t, 0, 0, 0, lane);
+      else
+        qk.template consume<true>(t, tok0, at.s.start, at.s.L, lane);
+    } else {
+      piece_bad = true;
+    }
+    if (at.ti == at.s.T - 1 || k == n - 1) {
+      flush(at);
+      if (k + 1 < n) {
+        // the next tile starts the next unit: its q, fresh state
+        qk.load_q(p, next->at.b, next->at.kvh * G, lane, qflip);
+        qk.reset();
+      }
+    }
+  };
+
+  if constexpr (DEPTH == 2) {
+    // two tiles in flight: the loads of tile k+1 are issued before tile k is consumed
+    typename QK::Tile t0_, t1_;
+    Slot s0, s1;
+    issue(0, t0_, s0);
+    for (int k = 0; k < n; k += 2) {
+      if (k + 1 < n) issue(k + 1, t1_, s1);
+      consume(k, t0_, s0, &s1);
+      if (k + 2 < n) issue(k + 2, t0_, s0);
+      if (k + 1 < n) consume(k + 1, t1_, s1, &s0);
+    }
+  } else {
+    typename QK::Tile t0_;
+    Slot s0, s1;
+    for (int k = 0; k < n; ++k) {
+      issue(k, t0_, s0);
+      // the next tile's unit, for the flush that may follow this tile
+      s1.at = iss;
+      consume(k, t0_, s0, &s1);
+    }
+  }
+}
+
+// Fix-up: one workgroup per (sequence b, query head h) of unit (b, h / G).  Units inside one
+// worker were written by the decode kernel; empty units get 0 (or the sink alone); a cut unit
+// merges its pieces: M = max lse_i, out = sum e^(lse_i - M) o_i / sum e^(lse_i - M),
+// lse = M + ln sum e^(lse_i - M).  Pass 1 takes M over the pieces; pass 2 reads the piece rows
+// with 16-byte loads, D/4 threads per row and 1024/D rows per step, the row-slot sums meeting
+// in LDS (as the partition reduce).
+constexpr int kFixupThreads = 256;
+
+template <int D, int G>
+__global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const BalancedParams bp) {
+  constexpr int TPR = D / 4;
+  constexpr int RPS = kFixupThreads / TPR;
+  const DecodeParams& p = bp.d;
+  const int bh = blockIdx.x;
+  const int b = bh / p.num_q_heads;
+  const int hq = bh - b * p.num_q_heads;
+  const int kvh = hq / G;
+  const int h = hq - kvh * G;
+  const int tid = threadIdx.x;
+  const SeqSpan s = seq_span(p.seq_lens[b], p.window, (int64_t)p.stride << p.bs_log2);
+  const int64_t total = bp.prefix[p.num_seqs] * p.num_kv_heads;
+  const int n_eff = effective_workers(total, bp.num_workers);
+
+  int wa = 0, np = 0, first_slot = 0;
+  if (s.T > 0) {
+    const int64_t S = bp.prefix[b] * p.num_kv_heads + (int64_t)kvh * s.T;
+    wa = worker_of(total, n_eff, S);
+    const int wb = worker_of(total, n_eff, S + s.T - 1);
+    if (wa == wb) return;   // written by the decode kernel
+    np = wb - wa + 1;
+    first_slot = worker_begin(total, n_eff, wa) < S ? 1 : 0;
+  }
+  // piece i of the unit: worker wa + i, slot first_slot for i == 0, else 0
+  auto slot_of = [&](int i) -> size_t {
+    return ((size_t)(wa + i) * 2 + (i == 0 ? first_slot : 0)) * G + h;
+  };
+
+  __shared__ float red[kFixupThreads / kWave];
+  __shared__ float s_acc[RPS][D];
+  __shared__ float s_sum[RPS];
+  __shared__ int s_nan;
+  if (tid == 0) s_nan = s.bad ? 1 : 0;
+  float mx = -INFINITY;
+  bool nan = false;
+  for (int i = tid; i < np; i += kFixupThreads) {
+    const float v = bp.ws_lse[slot_of(i)];
+    nan |= v != v;
+    mx = fmaxf(mx, v);
+  }
+  __syncthreads();
+  if (nan) s_nan = 1;
+  mx = wave_max(mx);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = mx;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < kFixupThreads / kWave; ++w) M = fmaxf(M, red[w]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+
+  const int pr = tid / TPR;
+  const int dq = tid - pr * TPR;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float z = 0.f;
+#pragma unroll 4
+  for (int i = pr; i < np; i += RPS) {
+    const size_t slot = slot_of(i);
+    const float li = bp.ws_lse[slot];
+    const float4 o = *reinterpret_cast<const float4*>(bp.ws_o + slot * D + 4 * dq);
+    const bool live = li != -INFINITY;
+    const float f = fast_exp2((li - Mu) * kLog2e);
+    a.x = live ? fmaf(f, o.x, a.x) : a.x;
+    a.y = live ? fmaf(f, o.y, a.y) : a.y;
+    a.z = live ? fmaf(f, o.z, a.z) : a.z;
+    a.w = live ? fmaf(f, o.w, a.w) : a.w;
+    z += live ? f : 0.f;
+  }
+  *reinterpret_cast<float4*>(&s_acc[pr][4 * dq]) = a;
+  if (dq == 0) s_sum[pr] = z;
+  __syncthreads();
+
+  if (tid < D) {
+    float o = 0.f, Z = 0.f;
+#pragma unroll
+    for (int k = 0; k < RPS; ++k) {
+      o += s_acc[k][tid];
+      Z += s_sum[k];
+    }
+    float Mo = M;
+    if (p.sinks != nullptr) {
+      // the sink logit joins the max and the denominator with a zero value row
+      const float sk = p.sinks[hq];
+      const float M2 = fmaxf(M, sk);
+      const float M2u = M2 == -INFINITY ? 0.f : M2;
+      const float f = fast_exp2((M - M2u) * kLog2e);
+      Z = fmaf(Z, f, fast_exp2((sk - M2u) * kLog2e));
+      o *= f;
+      Mo = M2;
+    }
+    float ov = Z > 0.f ? o / Z : 0.f;
+    float lv = Z > 0.f ? Mo + fast_log2(Z) * kLn2 : -INFINITY;
+    if (s_nan) {
+      ov = __builtin_nanf("");
+      lv = __builtin_nanf("");
+    }
+    const size_t row = (size_t)b * p.num_q_heads + hq;
+    p.out[row * D + tid] = ov;
+    if (tid == 0 && p.lse != nullptr) p.lse[row] = lv;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+template <int D, int G, QkPath PATH>
+using BQK = typename std::conditional<PATH == QkPath::kMfma, QkMfma<D, G>, QkValu<D, G>>::type;
+
+// tiles in flight per worker: two where the registers allow it
+template <int D, int G>
+constexpr int bal_depth() {
+  return D * G <= 512 ? 2 : 1;
+}
+
+template <int D, int G, QkPath PATH>
+const void* balanced_kernel_ptr() {
+  return reinterpret_cast<const void*>(
+      &balanced_decode_kernel<D, G, bal_depth<D, G>(), BQK<D, G, PATH>>);
+}
+
+template <int D, int G, QkPath PATH>
+hipError_t launch_bal(const BalancedParams& bp, hipStream_t stream) {
+  hipLaunchKernelGGL((balanced_decode_kernel<D, G, bal_depth<D, G>(), BQK<D, G, PATH>>),
+                     dim3(bp.num_workers), dim3(kWave), 0, stream, bp);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_fix(const BalancedParams& bp, hipStream_t stream) {
+  hipLaunchKernelGGL((balanced_fixup_kernel<D, G>),
+                     dim3((unsigned)bp.d.num_seqs * (unsigned)bp.d.num_q_heads),
+                     dim3(kFixupThreads), 0, stream, bp);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fix_g(const BalancedParams& bp, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_fix<D, 1>(bp, stream);
+    case 2: return launch_fix<D, 2>(bp, stream);
+    case 4: return launch_fix<D, 4>(bp, stream);
+    case 8: return launch_fix<D, 8>(bp, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D, QkPath PATH>
+hipError_t launch_bal_g(const BalancedParams& bp, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_bal<D, 1, PATH>(bp, stream);
+    case 2: return launch_bal<D, 2, PATH>(bp, stream);
+    case 4: return launch_bal<D, 4, PATH>(bp, stream);
+    case 8: return launch_bal<D, 8, PATH>(bp, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <QkPath PATH>
+hipError_t launch_bal_d(const BalancedParams& bp, int head_dim, int group, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_bal_g<64, PATH>(bp, group, stream);
+    case 128: return launch_bal_g<128, PATH>(bp, group, stream);
+    case 256: return launch_bal_g<256, PATH>(bp, group, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <QkPath PATH>
+const void* bal_ptr(int head_dim, int group) {
+#define PA_BP(D)                                                   \
+  if (head_dim == D) {                                             \
+    switch (group) {                                               \
+      case 1: return balanced_kernel_ptr<D, 1, PATH>();            \
+      case 2: return balanced_kernel_ptr<D, 2, PATH>();            \
+      case 4: return balanced_kernel_ptr<D, 4, PATH>();            \
+      case 8: return balanced_kernel_ptr<D, 8, PATH>();            \
+      default: return nullptr;                                     \
+    }                                                              \
+  }
+  PA_BP(64) PA_BP(128) PA_BP(256)
+#undef PA_BP
+  return nullptr;
+}
+
+}  // namespace
+
+hipError_t launch_balanced(const BalancedParams& bp, int head_dim, int group, QkPath path,
+                           hipStream_t stream) {
+  return path == QkPath::kMfma ? launch_bal_d<QkPath::kMfma>(bp, head_dim, group, stream)
+                               : launch_bal_d<QkPath::kValu>(bp, head_dim, group, stream);
+}
+
+hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int group,
+                                 hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_fix_g<64>(bp, group, stream);
+    case 128: return launch_fix_g<128>(bp, group, stream);
+    case 256: return launch_fix_g<256>(bp, group, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int balanced_default_workers(int head_dim, int group, QkPath path) {
+  const void* k = path == QkPath::kMfma ? bal_ptr<QkPath::kMfma>(head_dim, group)
+                                        : bal_ptr<QkPath::kValu>(head_dim, group);
+  if (k == nullptr) return -1;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kWave, 0) != hipSuccess)
+    return -1;
+  const long long n = (long long)cus * (per_cu > 0 ? per_cu : 1);
+  return (int)(n < (1 << 20) ? n : (1 << 20));
+}
+
+}  // namespace pa

@@ -1,253 +1,136 @@
 // Single-token paged-attention decode for gfx950 (CDNA4), unsplit and split-KV.
 //
 // One workgroup per (partition, KV head, sequence).  It walks the sequence's block table tile by
-// tile (16 tokens), loads each tile's K and V rows once with 16-byte coalesced loads (8 B at
-// head_dim 64), and serves all G query heads that share the KV head from the same registers, so
-// every K/V byte is read once per KV head.  QK^T uses bf16 dot2 with fp32 accumulation and a
-// DPP reduction across the 16 lanes that hold one row; softmax is online (running max and sum);
-// P.V accumulates in fp32.  Each of the 4 row groups of a wave runs its own online softmax over
-// tokens 4j + r of every tile (a strided subset); the row groups, then the waves, are merged
-// with the log-sum-exp rule at the end.  The epilogue folds the sink logit, normalises, and
-// writes the final output and LSE (unsplit) or the partition's partial output and LSE (split).
+// tile (16 tokens), loads each tile's K and V rows once with coalesced non-temporal loads, and
+// serves all G query heads that share the KV head from the same registers, so every K/V byte is
+// read once per KV head.  Softmax is online (running max and sum) in the log2 domain; P.V
+// accumulates in fp32.  Each of the 4 row groups (16-lane DPP rows) of a wave runs its own
+// online softmax over tokens 4j + r of every tile (a strided subset); the row groups, then the
+// waves, are merged with the log-sum-exp rule.  The epilogue folds the sink logit, normalises,
+// and writes the final output and LSE (unsplit) or the partition's partial output and LSE.
+//
+// Two ways to form the scores q.k, selected per variant (QkValu / QkMfma in pa_qk.hpp):
+//   - vector ALUs: one KV row per 16-lane row, bf16 dot2 with fp32 accumulation, DPP sum;
+//   - matrix cores: per tile the G query heads form a dense [16 x D] . [D x G] contraction,
+//     D/32 v_mfma_f32_16x16x32_bf16 (bf16 products, fp32 accumulation, heads padded to 16).
+// P.V is on the vector ALUs in fp32 in both: probabilities never round to bf16.
 //
 // Sources: one-token split-KV decode with partial outputs + LSE and a reduce step,
 // ROCm/rocm-libraries PR #13700 "prepare saved paged decode bindings once", Summary; online
 // softmax reaching the same function in another order, vllm.cpp PR #564 "spec(BACKEND-ROCM): the
-// ROCm head_dim=128 decode arm", "It is a mirror of merged work, not new design"; 16-byte vs
-// 8-byte vector loads per head size, same page, "The gap it specs"; wave64 reductions must cross
-// all four 16-lane rows, vllm.cpp PR #506 review, finding 2; sliding window with out-of-window
-// blocks skipped and attention sinks, randomvariable/vllm issue #23, table "Current state".
+// ROCm head_dim=128 decode arm", "It is a mirror of merged work, not new design"; GQA groups,
+// same page, "What is deliberately not here"; 16-byte vs 8-byte vector loads per head size, same
+// page, "The gap it specs"; a separate matrix-core arm for d=128, same page, "One deviation from
+// the original commit"; wave64 reductions must cross all four 16-lane rows, vllm.cpp PR #506
+// review, finding 2; sliding window with out-of-window blocks skipped and attention sinks,
+// randomvariable/vllm issue #23, table "Current state".
 #include <cstdio>
+#include <type_traits>
 
 #include "pa_device.hpp"
 #include "pa_kernels.hpp"
+#include "pa_qk.hpp"
 
 namespace pa {
 
-// Rescale threshold of the online softmax, in log2 units.  The running max m of a row group is
-// only raised when a tile's max exceeds it by more than this, so between raises
-// p = 2^(s - m) <= 2^kRescaleSlack: no overflow risk in fp32, and most tiles skip the rescale
-// multiplies entirely.  The final result does not depend on when rescales happen: every
-// (m, l, acc) triple stays consistent and the merges use the exact log-sum-exp rule.
-constexpr float kRescaleSlack = 8.0f;
-
-template <int D, int G>
-struct WaveState {
-  static constexpr int E = RowGeom<D>::kElems;
-  float m[G];       // running max of the row group's scores (log2 units), per head
-  float l[G];       // running sum of 2^(s - m)
-  float acc[G][E];  // running sum of 2^(s - m) v, this lane's slice of the head dim
-};
-
-// One tile (16 tokens) of K/V in registers: token 4j + r of the tile is row j of row group r.
-template <int D>
-struct TileRegs {
-  static constexpr int W = RowGeom<D>::kWords;
-  uint32_t k[kTileSteps][W];
-  uint32_t v[kTileSteps][W];
-};
-
-template <int D>
-__device__ __forceinline__ void issue_tile(TileRegs<D>& t, const char* kb, const char* vb, int r,
-                                           int c) {
-  constexpr int RB = RowGeom<D>::kRowBytes;
-#pragma unroll
-  for (int j = 0; j < kTileSteps; ++j) load_row<D>(kb + (kRows * j + r) * RB, c, t.k[j]);
-#pragma unroll
-  for (int j = 0; j < kTileSteps; ++j) load_row<D>(vb + (kRows * j + r) * RB, c, t.v[j]);
-}
-
-// Fold one tile into the row group's online-softmax state.  MASKED: some tokens of the tile
-// fall outside [lo, hi); they get score -inf and a zero value row by select, so whatever their
-// slots hold (NaN included) cannot reach the sums.
-template <int D, int G, bool MASKED>
-__device__ __forceinline__ void consume_tile(WaveState<D, G>& st, TileRegs<D>& t,
-                                             const uint32_t (&qw)[G][RowGeom<D>::kWords],
-                                             float c2, int tok0, int lo, int hi, int r) {
-  constexpr int W = RowGeom<D>::kWords;
-  constexpr int E = RowGeom<D>::kElems;
-  constexpr int J = kTileSteps;
-
-  // raw scores q.k of the row group's 4 tokens, complete in every lane of the row
-  float s[J][G];
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float a = 0.f;
-#pragma unroll
-      for (int w = 0; w < W; ++w) a = dot2_bf16(qw[h][w], t.k[j][w], a);
-      s[j][h] = row_sum16(a);
-    }
-  }
-  if constexpr (MASKED) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int tk = tok0 + kRows * j + r;
-      const bool ok = tk >= lo && tk < hi;
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[j][h] = ok ? s[j][h] * c2 : -INFINITY;
-#pragma unroll
-      for (int w = 0; w < W; ++w) t.v[j][w] = ok ? t.v[j][w] : 0u;
-    }
-  }
-
-  // raise the running max only when a tile's max is well above it (wave-uniform decision)
-  float mx[G];
-  bool need = false;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    mx[h] = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
-    if constexpr (!MASKED) mx[h] *= c2;    // c2 >= 0: the max commutes with the scale
-    need |= mx[h] > st.m[h] + kRescaleSlack;
-  }
-  if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mn = fmaxf(st.m[h], mx[h]);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      const float alpha = fast_exp2(st.m[h] - mu);
-      st.l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < E; ++e) st.acc[h][e] *= alpha;
-      st.m[h] = mn;
-    }
-  }
-
-  // probabilities (overwriting the scores), then P.V one token row at a time
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float mu = st.m[h] == -INFINITY ? 0.f : st.m[h];
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-      s[j][h] = MASKED ? fast_exp2(s[j][h] - mu) : fast_exp2(fmaf(s[j][h], c2, -mu));
-    st.l[h] += (s[0][h] + s[1][h]) + (s[2][h] + s[3][h]);
-  }
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    float vf[E];
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      vf[2 * w] = bf16_lo(t.v[j][w]);
-      vf[2 * w + 1] = bf16_hi(t.v[j][w]);
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) st.acc[h][e] = fmaf(s[j][h], vf[e], st.acc[h][e]);
-    }
-  }
-}
-
-template <int D, int G, int NW, int DEPTH>
+// ---------------------------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------------------------
+template <int D, int G, int NW, int DEPTH, class QK>
 __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p) {
   using RG = RowGeom<D>;
-  constexpr int W = RG::kWords;
   constexpr int E = RG::kElems;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane >> 4;
   const int c = lane & (kRowLanes - 1);
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
-
-  const int L = p.seq_lens[b];
+  const WorkItem it = decode_work_item(p.num_kv_heads, p.num_seqs);
+  const int h0 = it.kvh * G;
   const bool split = p.psize > 0;
-  const int n_parts = split ? (L > 0 ? (int)(((int64_t)L + p.psize - 1) / p.psize) : 1) : 1;
-  if (part >= n_parts) return;
 
+  // A negative scale is applied as |scale| on -q (a sign flip, exact), so the score scale c2 is
+  // never negative and commutes with max.
+  const float c2 = fabsf(p.qk_scale_log2);
+  const uint32_t qflip = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
+  QK qk;
+  qk.init(p, it.b, h0, lane, qflip, c2);
+
+  // Block-table entries of this wave's tiles, 64 at a time in one VGPR (lane i: tile i).  The
+  // first batch is requested before the sequence length arrives, for the range a partition has
+  // without a window (indices clamped into the row, so always in bounds); a window start that
+  // moves the range triggers a reload below.
+  const TileAddr ta{p.num_blocks, p.num_kv_heads, it.kvh, p.bs_log2, RG::kRowBytes};
+  const int32_t* bt_row = p.block_table + (size_t)it.b * p.stride;
+  const int lo_guess =
+      split ? (int)((int64_t)it.part * p.psize < 0x7FFFFFF0 ? (int64_t)it.part * p.psize
+                                                              : 0x7FFFFFF0)
+            : 0;
+  const int first_guess = (lo_guess + kTileTokens - 1) / kTileTokens + wave;
+  const int row_cap = p.stride - 1;
+  auto table_batch = [&](int first, int ch) -> int {
+    const int li = (ch << 6) + lane;
+    const int lb = ta.logical_block(first + NW * li);
+    return bt_row[lb < row_cap ? lb : row_cap];
+  };
+  int phys_v = table_batch(first_guess, 0);
+
+  const int L = p.seq_lens[it.b];
+  const int n_parts = split ? (L > 0 ? (int)(((int64_t)L + p.psize - 1) / p.psize) : 1) : 1;
+  if (it.part >= n_parts) return;   // uniform over the workgroup
   // Lengths the table cannot hold, or more partitions than slots: write NaN, read nothing.
   bool bad = L < 0 || (int64_t)L > ((int64_t)p.stride << p.bs_log2);
-  if (split && part == p.max_parts - 1 && n_parts > p.max_parts) bad = true;
-  const PartRange pr = part_range(bad ? 0 : L, p.window, part, p.psize);
+  if (split && it.part == p.max_parts - 1 && n_parts > p.max_parts) bad = true;
+  const PartRange pr = part_range(bad ? 0 : L, p.window, it.part, p.psize);
 
-  // q for the G heads of this KV head, bf16 pairs of the lane's slice of the head dim.  A
-  // negative scale is applied as |scale| on -q (a sign flip, exact), so the score scale c2 is
-  // never negative and commutes with max.
-  float c2 = p.qk_scale_log2;
-  const uint32_t qflip = c2 < 0.f ? 0x80008000u : 0u;
-  c2 = fabsf(c2);
-  const int h0 = kvh * G;
-  uint32_t qw[G][W];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    load_row_cached<D>(
-        reinterpret_cast<const char*>(p.q + ((size_t)b * p.num_q_heads + h0 + h) * D), c,
-        qw[h]);
-#pragma unroll
-    for (int w = 0; w < W; ++w) qw[h][w] ^= qflip;
-  }
-
-  WaveState<D, G> st;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    st.m[h] = -INFINITY;
-    st.l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) st.acc[h][e] = 0.f;
-  }
-
-  // Full tiles [f0, f1) are dealt round-robin to the waves: wave w takes f0 + w + NW*i,
-  // i in [0, n_w).  Their block-table entries are loaded 64 at a time into one VGPR (lane i holds
-  // tile i's physical block) and read back with readlane, so no scalar table load sits on a
-  // tile's critical path.  The at most two partial tiles at the range ends (masked) follow.
-  const TileAddr ta{p.num_blocks, p.num_kv_heads, kvh, p.bs_log2, RG::kRowBytes};
-  const int32_t* bt_row = p.block_table + (size_t)b * p.stride;
+  // full tiles [f0, f1) round-robin over the waves: wave w takes f0 + w + NW*i, i < n_w
   const int f0 = (pr.lo + kTileTokens - 1) / kTileTokens;
   const int f1 = pr.hi / kTileTokens;
   const int first = f0 + wave;
   const int n_w = first < f1 ? (f1 - first + NW - 1) / NW : 0;
-  int phys_v = 0;
-  int chunk = -1;
+  int chunk = first == first_guess ? 0 : -1;
   bool bad_table = false;
 
   auto phys_of = [&](int i) -> int {
     const int ch = i >> 6;
-    if (ch != chunk) {   // uniform: refill the lane table for tiles [64ch, 64ch+64)
+    if (ch != chunk) {   // uniform
       chunk = ch;
-      const int li = (ch << 6) + lane;
-      phys_v = li < n_w ? bt_row[ta.logical_block(first + NW * li)] : 0;
+      phys_v = table_batch(first, ch);
     }
     return __builtin_amdgcn_readlane(phys_v, i & 63);
   };
-  auto issue = [&](int i, TileRegs<D>& regs) -> bool {
+  auto issue = [&](int i, typename QK::Tile& t) -> bool {
     const int64_t off = ta.offset(phys_of(i), first + NW * i);
     if (off < 0) {
       bad_table = true;
       return false;
     }
-    issue_tile<D>(regs, p.k_cache + off, p.v_cache + off, r, c);
+    qk.issue(t, p.k_cache + off, p.v_cache + off, lane);
     return true;
-  };
-  auto consume = [&](int i, TileRegs<D>& regs) {
-    consume_tile<D, G, false>(st, regs, qw, c2, 0, 0, 0, r);
   };
 
   if constexpr (DEPTH == 2) {
     // two tiles in flight: the loads of tile i+1 are issued before tile i is consumed
-    TileRegs<D> ra, rb;
-    bool oka = n_w > 0 ? issue(0, ra) : false;
-    bool okb = false;
+    typename QK::Tile t0_, t1_;
+    bool ok0 = n_w > 0 ? issue(0, t0_) : false;
+    bool ok1 = false;
     for (int i = 0; i < n_w; i += 2) {
-      if (i + 1 < n_w) okb = issue(i + 1, rb);
-      if (oka) consume(i, ra);
-      if (i + 2 < n_w) oka = issue(i + 2, ra);
-      if (i + 1 < n_w && okb) consume(i + 1, rb);
+      if (i + 1 < n_w) ok1 = issue(i + 1, t1_);
+      if (ok0) qk.template consume<false>(t0_, 0, 0, 0, lane);
+      if (i + 2 < n_w) ok0 = issue(i + 2, t0_);
+      if (i + 1 < n_w && ok1) qk.template consume<false>(t1_, 0, 0, 0, lane);
     }
   } else {
-    TileRegs<D> ra;
+    typename QK::Tile t0_;
     for (int i = 0; i < n_w; ++i)
-      if (issue(i, ra)) consume(i, ra);
+      if (issue(i, t0_)) qk.template consume<false>(t0_, 0, 0, 0, lane);
   }
 
-  // partial tiles at the ends of [lo, hi), on the last wave
+  // the at most two partial tiles at the ends of [lo, hi), masked, on the last wave
   if (wave == NW - 1 && pr.hi > pr.lo) {
-    const int head = pr.lo / kTileTokens;          // partial if lo is not tile-aligned
-    const int tail = pr.hi / kTileTokens;          // partial if hi is not tile-aligned
+    const int head = pr.lo / kTileTokens;
+    const int tail = pr.hi / kTileTokens;
     const bool has_head = head < f0;
-    // the tail tile is partial whenever hi is not aligned; it is only skipped when it is the
+    // the tail tile is partial whenever hi is not aligned; it is skipped only when it is the
     // head tile and the head pass (masked to [lo, hi)) already covers it
     const bool has_tail = (pr.hi % kTileTokens) != 0 && !(has_head && tail == head);
 #pragma unroll
@@ -255,47 +138,37 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
       const bool on = k == 0 ? has_head : has_tail;
       if (!on) continue;
       const int tile = k == 0 ? head : tail;
-      const int64_t off = ta.offset(__builtin_amdgcn_readfirstlane(bt_row[ta.logical_block(tile)]),
-                                    tile);
+      const int64_t off =
+          ta.offset(__builtin_amdgcn_readfirstlane(bt_row[ta.logical_block(tile)]), tile);
       if (off < 0) {
         bad_table = true;
         continue;
       }
-      TileRegs<D> rt;
-      issue_tile<D>(rt, p.k_cache + off, p.v_cache + off, r, c);
-      consume_tile<D, G, true>(st, rt, qw, c2, tile * kTileTokens, pr.lo, pr.hi, r);
+      typename QK::Tile t;
+      qk.issue(t, p.k_cache + off, p.v_cache + off, lane);
+      qk.template consume<true>(t, tile * kTileTokens, pr.lo, pr.hi, lane);
     }
   }
 
-  // merge the 4 row groups of the wave (log-sum-exp rule); every row ends with the wave total
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float M = rows_max(st.m[h]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    const float f = fast_exp2(st.m[h] - Mu);
-    st.l[h] = rows_sum(st.l[h] * f);
-#pragma unroll
-    for (int e = 0; e < E; ++e) st.acc[h][e] = rows_sum(st.acc[h][e] * f);
-    st.m[h] = M;
-  }
-
-  // merge the waves through LDS
+  // merge rows within the wave, then waves through LDS
+  float Mh[G], lh[G];
+  qk.merge_rows(Mh, lh);
   __shared__ float s_acc[NW][G][D];
   __shared__ float s_m[NW][G];
   __shared__ float s_l[NW][G];
   __shared__ int s_bad[NW];
-  if (r == 0) {
+  if (lane < kRowLanes) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) s_acc[wave][h][RG::dim(c, e)] = st.acc[h][e];
+      for (int e = 0; e < E; ++e) s_acc[wave][h][RG::dim(c, e)] = qk.acc[h][e];
     }
   }
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      s_m[wave][h] = st.m[h];
-      s_l[wave][h] = st.l[h];
+      s_m[wave][h] = Mh[h];
+      s_l[wave][h] = lh[h];
     }
     s_bad[wave] = bad_table ? 1 : 0;
   }
@@ -305,7 +178,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
 #pragma unroll
   for (int w = 0; w < NW; ++w) any_bad |= s_bad[w] != 0;
 
-  const bool fold_sink = p.sinks != nullptr && part == pr.first_part;
+  const bool fold_sink = p.sinks != nullptr && it.part == pr.first_part;
   for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
     const int h = i / D;
     const int d = i - h * D;
@@ -337,10 +210,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
       ov = __builtin_nanf("");
       lv = __builtin_nanf("");
     }
-    const size_t row = (size_t)b * p.num_q_heads + hq;
+    const size_t row = (size_t)it.b * p.num_q_heads + hq;
     if (split) {
-      p.out[(row * p.max_parts + part) * D + d] = ov;
-      if (d == 0) p.lse[row * p.max_parts + part] = lv;
+      p.out[(row * p.max_parts + it.part) * D + d] = ov;
+      if (d == 0) p.lse[row * p.max_parts + it.part] = lv;
     } else {
       p.out[row * D + d] = ov;
       if (d == 0 && p.lse != nullptr) p.lse[row] = lv;
@@ -356,36 +229,48 @@ namespace {
 // tiles in flight per wave: two where the registers allow it
 template <int D, int G>
 constexpr int pipeline_depth() {
-  return (D * G <= 512) ? 2 : 1;
+  return D * G <= 512 ? 2 : 1;
 }
 
-template <int D, int G, int NW>
-hipError_t launch_dgw(const DecodeParams& p, int num_seqs, hipStream_t stream) {
-  const dim3 grid(p.psize > 0 ? p.max_parts : 1, p.num_kv_heads, num_seqs);
-  hipLaunchKernelGGL((decode_kernel<D, G, NW, pipeline_depth<D, G>()>), grid, dim3(NW * kWave),
-                     0, stream, p);
+template <int D, int G, int NW, QkPath PATH>
+hipError_t launch_v(const DecodeParams& p, hipStream_t stream) {
+  using QK = typename std::conditional<PATH == QkPath::kMfma, QkMfma<D, G>, QkValu<D, G>>::type;
+  const unsigned grid = (unsigned)((p.psize > 0 ? p.max_parts : 1) *
+                                   (int64_t)p.num_kv_heads * p.num_seqs);
+  hipLaunchKernelGGL((decode_kernel<D, G, NW, pipeline_depth<D, G>(), QK>), dim3(grid),
+                     dim3(NW * kWave), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int G>
-hipError_t launch_dg(const DecodeParams& p, int waves, int num_seqs, hipStream_t stream) {
+template <int D, int G, QkPath PATH>
+hipError_t launch_w(const DecodeParams& p, int waves, hipStream_t stream) {
   switch (waves) {
-    case 1: return launch_dgw<D, G, 1>(p, num_seqs, stream);
-    case 2: return launch_dgw<D, G, 2>(p, num_seqs, stream);
-    case 4: return launch_dgw<D, G, 4>(p, num_seqs, stream);
-    case 8: return launch_dgw<D, G, 8>(p, num_seqs, stream);
+    case 1: return launch_v<D, G, 1, PATH>(p, stream);
+    case 2: return launch_v<D, G, 2, PATH>(p, stream);
+    case 4: return launch_v<D, G, 4, PATH>(p, stream);
+    case 8: return launch_v<D, G, 8, PATH>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int D>
-hipError_t launch_d(const DecodeParams& p, int group, int waves, int num_seqs,
-                    hipStream_t stream) {
+template <int D, QkPath PATH>
+hipError_t launch_g(const DecodeParams& p, int group, int waves, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_dg<D, 1>(p, waves, num_seqs, stream);
-    case 2: return launch_dg<D, 2>(p, waves, num_seqs, stream);
-    case 4: return launch_dg<D, 4>(p, waves, num_seqs, stream);
-    case 8: return launch_dg<D, 8>(p, waves, num_seqs, stream);
+    case 1: return launch_w<D, 1, PATH>(p, waves, stream);
+    case 2: return launch_w<D, 2, PATH>(p, waves, stream);
+    case 4: return launch_w<D, 4, PATH>(p, waves, stream);
+    case 8: return launch_w<D, 8, PATH>(p, waves, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <QkPath PATH>
+hipError_t launch_d(const DecodeParams& p, int head_dim, int group, int waves,
+                    hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_g<64, PATH>(p, group, waves, stream);
+    case 128: return launch_g<128, PATH>(p, group, waves, stream);
+    case 256: return launch_g<256, PATH>(p, group, waves, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -423,14 +308,10 @@ const char* decode_variant_name(int head_dim, int group, int waves, bool split, 
   return buf;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int waves, int num_seqs,
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int waves, QkPath path,
                          hipStream_t stream) {
-  switch (head_dim) {
-    case 64: return launch_d<64>(p, group, waves, num_seqs, stream);
-    case 128: return launch_d<128>(p, group, waves, num_seqs, stream);
-    case 256: return launch_d<256>(p, group, waves, num_seqs, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return path == QkPath::kMfma ? launch_d<QkPath::kMfma>(p, head_dim, group, waves, stream)
+                               : launch_d<QkPath::kValu>(p, head_dim, group, waves, stream);
 }
 
 }  // namespace pa

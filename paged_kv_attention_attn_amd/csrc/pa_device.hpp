@@ -203,6 +203,27 @@ struct TileAddr {
   }
 };
 
+// Workgroup -> (partition, KV head, sequence).  The chip deals workgroups to its 8 XCDs
+// round-robin by linear id, so the KV head varies fastest, then the sequence, then the
+// partition: every XCD gets an even share of full and partial partitions, and the empty
+// partitions of short sequences (high partition index) come last.  (With the partition index
+// fastest, XCD k would receive only partition k mod 8 of every sequence: measured 12x more
+// work on one XCD than on another for 512-token partitions of a 512..4096-token batch.)
+struct WorkItem {
+  int part, kvh, b;
+};
+
+__device__ __forceinline__ WorkItem decode_work_item(int num_kv_heads, int num_seqs) {
+  const unsigned id = blockIdx.x;
+  const unsigned per_part = (unsigned)num_kv_heads * (unsigned)num_seqs;
+  WorkItem w;
+  w.part = (int)(id / per_part);
+  const unsigned rem = id - (unsigned)w.part * per_part;
+  w.b = (int)(rem / (unsigned)num_kv_heads);
+  w.kvh = (int)(rem - (unsigned)w.b * (unsigned)num_kv_heads);
+  return w;
+}
+
 // Attended token range of partition `part` of a sequence of length L, and the validity of L.
 struct PartRange {
   int lo, hi;        // tokens [lo, hi)

@@ -16,6 +16,7 @@ struct DecodeParams {
   float* out;                 // unsplit [B][Hq][D]; split [B][Hq][Pmax][D]
   float* lse;                 // unsplit [B][Hq] or null; split [B][Hq][Pmax]
   float qk_scale_log2;        // scale * log2(e)
+  int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t num_blocks;
@@ -24,6 +25,15 @@ struct DecodeParams {
   int32_t window;
   int32_t psize;              // 0 = unsplit
   int32_t max_parts;          // split: partition slots; unsplit: 1
+};
+
+// Balanced decode: persistent workers over the flattened tiles, partials in a workspace.
+struct BalancedParams {
+  DecodeParams d;             // out/lse are the final outputs; psize/max_parts unused
+  int64_t* prefix;            // [B + 1] tiles per KV head before sequence b (written by worker 0)
+  float* ws_lse;              // [N][2][G] partial LSEs (natural log)
+  float* ws_o;                // [N][2][G][D] partial outputs (normalised)
+  int32_t num_workers;        // N, one wave each
 };
 
 struct ReduceParams {
@@ -57,10 +67,9 @@ struct WitnessParams {
 // Decode kernels: QK^T on the vector ALUs (dot2 + DPP) or on the matrix cores (MFMA); P.V is
 // on the vector ALUs in fp32 in both.
 enum class QkPath { kValu = 0, kMfma = 1 };
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int waves, int num_seqs,
+// Grid: one workgroup per (partition slot, KV head, sequence), 1-D.
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int waves, QkPath path,
                          hipStream_t stream);
-hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, int group, int waves,
-                              int num_seqs, hipStream_t stream);
 // Variant name; the string lives in thread-local storage until the next call on this thread.
 const char* decode_variant_name(int head_dim, int group, int waves, bool split, QkPath path);
 QkPath decode_default_path(int head_dim, int group);
@@ -69,6 +78,15 @@ bool decode_waves_supported(int waves);
 int decode_default_waves(int head_dim, int group, int psize);
 
 hipError_t launch_reduce(const ReduceParams& p, int head_dim, int num_seqs, hipStream_t stream);
+
+// Balanced decode: the worker kernel, and the fix-up merge, each on `stream`.
+hipError_t launch_balanced(const BalancedParams& bp, int head_dim, int group, QkPath path,
+                           hipStream_t stream);
+hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int group,
+                                 hipStream_t stream);
+// Workers that fit on the current device at once (CUs x resident one-wave workgroups per CU),
+// or -1 if the query fails.
+int balanced_default_workers(int head_dim, int group, QkPath path);
 
 hipError_t launch_witness(const WitnessParams& p, int head_dim, int num_seqs, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int num_wg, uint32_t* sink,

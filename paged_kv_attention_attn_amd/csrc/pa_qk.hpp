@@ -1,0 +1,347 @@
+// Score / softmax / P.V machinery shared by the decode kernels (fixed-partition grid and
+// balanced persistent workers): the two ways to form q.k on gfx950 (vector ALUs or matrix cores)
+// and the per-row-group online softmax with fp32 P.V on the vector ALUs.
+//
+// Each policy holds the q operand and a wave's online-softmax state, and provides
+//   init(p, b, h0, lane, qflip, c2)   load q for query heads [h0, h0+G) of sequence b, reset state
+//   issue(tile, kb, vb, lane)         start the loads of one 16-token tile of K and V
+//   consume<MASKED>(tile, ...)        fold the tile into the state (MASKED: select tokens in
+//                                     [lo, hi), NaN-safe)
+//   merge_rows(M, l)                  merge the 4 row groups; row-0 lanes end with the wave's
+//                                     (max, sum, acc) of every head
+// Online softmax reaching the plain softmax in another order: vllm.cpp PR #564
+// "spec(BACKEND-ROCM): the ROCm head_dim=128 decode arm", "It is a mirror of merged work, not new
+// design"; a separate matrix-core arm for d=128: same page, "One deviation from the original
+// commit"; wave64 reductions crossing all four 16-lane rows: vllm.cpp PR #506 review, finding 2.
+#pragma once
+
+#include "pa_device.hpp"
+#include "pa_kernels.hpp"
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Rescale threshold of the online softmax, in log2 units.  A row group's running max m is only
+// raised when a tile's max exceeds it by more than this, so between raises
+// p = 2^(s - m) <= 2^kRescaleSlack (no overflow risk in fp32) and most tiles skip the rescale
+// multiplies.  The result does not depend on when rescales happen: every (m, l, acc) triple
+// stays consistent and the merges use the exact log-sum-exp rule.
+constexpr float kRescaleSlack = 8.0f;
+
+// value of x in lane H of this lane's 16-lane row (DPP row_newbcast)
+template <int H>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), 0x150 + H, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_bcast_dyn(float x, int h) {
+  switch (h) {   // h is a compile-time constant after unrolling
+    case 0: return row_bcast<0>(x);
+    case 1: return row_bcast<1>(x);
+    case 2: return row_bcast<2>(x);
+    case 3: return row_bcast<3>(x);
+    case 4: return row_bcast<4>(x);
+    case 5: return row_bcast<5>(x);
+    case 6: return row_bcast<6>(x);
+    default: return row_bcast<7>(x);
+  }
+}
+
+// V rows of a tile in the P.V layout: row group r (lane / 16) holds tokens 4j + r, lane c of the
+// row holds slice c of the head dim.
+template <int D>
+__device__ __forceinline__ void load_v_rows(uint32_t (&v)[kTileSteps][RowGeom<D>::kWords],
+                                            const char* vb, int lane) {
+  const int r = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int j = 0; j < kTileSteps; ++j)
+    load_row<D>(vb + (kRows * j + r) * RowGeom<D>::kRowBytes, c, v[j]);
+}
+
+template <int D>
+__device__ __forceinline__ void mask_v_rows(uint32_t (&v)[kTileSteps][RowGeom<D>::kWords],
+                                            int tok0, int lo, int hi, int lane) {
+#pragma unroll
+  for (int j = 0; j < kTileSteps; ++j) {
+    const int tk = tok0 + kRows * j + (lane >> 4);
+    const bool ok = tk >= lo && tk < hi;
+#pragma unroll
+    for (int w = 0; w < RowGeom<D>::kWords; ++w) v[j][w] = ok ? v[j][w] : 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// QK^T on the vector ALUs.  State per lane: (m, l) for each of the G heads of its row group,
+// acc[G][E] for its head-dim slice.
+// ---------------------------------------------------------------------------------------------
+template <int D, int G>
+struct QkValu {
+  static constexpr int W = RowGeom<D>::kWords;
+  static constexpr int E = RowGeom<D>::kElems;
+  struct Tile {
+    uint32_t k[kTileSteps][W];
+    uint32_t v[kTileSteps][W];
+  };
+  uint32_t qw[G][W];
+  float c2;
+  float m[G], l[G], acc[G][E];
+
+  __device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int lane,
+                                         uint32_t qflip) {
+    const int c = lane & 15;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      load_row_cached<D>(
+          reinterpret_cast<const char*>(p.q + ((size_t)b * p.num_q_heads + h0 + h) * D), c,
+          qw[h]);
+#pragma unroll
+      for (int w = 0; w < W; ++w) qw[h][w] ^= qflip;
+    }
+  }
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+    }
+  }
+  __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
+                                       uint32_t qflip, float c2_) {
+    c2 = c2_;
+    load_q(p, b, h0, lane, qflip);
+    reset();
+  }
+
+  __device__ __forceinline__ void issue(Tile& t, const char* kb, const char* vb, int lane) const {
+    const int r = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int j = 0; j < kTileSteps; ++j)
+      load_row<D>(kb + (kRows * j + r) * RowGeom<D>::kRowBytes, c, t.k[j]);
+    load_v_rows<D>(t.v, vb, lane);
+  }
+
+  template <bool MASKED>
+  __device__ __forceinline__ void consume(Tile& t, int tok0, int lo, int hi, int lane) {
+    constexpr int J = kTileSteps;
+    const int r = lane >> 4;
+    float s[J][G];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) a = dot2_bf16(qw[h][w], t.k[j][w], a);
+        s[j][h] = row_sum16(a);
+      }
+    }
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int tk = tok0 + kRows * j + r;
+        const bool ok = tk >= lo && tk < hi;
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[j][h] = ok ? s[j][h] * c2 : -INFINITY;
+      }
+      mask_v_rows<D>(t.v, tok0, lo, hi, lane);
+    }
+    float mx[G];
+    bool need = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mx[h] = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
+      if constexpr (!MASKED) mx[h] *= c2;    // c2 >= 0 commutes with max
+      need |= mx[h] > m[h] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(m[h], mx[h]);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        const float alpha = fast_exp2(m[h] - mu);
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+        m[h] = mn;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mu = m[h] == -INFINITY ? 0.f : m[h];
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        s[j][h] = MASKED ? fast_exp2(s[j][h] - mu) : fast_exp2(fmaf(s[j][h], c2, -mu));
+      l[h] += (s[0][h] + s[1][h]) + (s[2][h] + s[3][h]);
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      float vf[E];
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        vf[2 * w] = bf16_lo(t.v[j][w]);
+        vf[2 * w + 1] = bf16_hi(t.v[j][w]);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(s[j][h], vf[e], acc[h][e]);
+      }
+    }
+  }
+
+  // Merge the 4 row groups; lanes of row 0 end with the wave's (M, l, acc) of every head.
+  __device__ __forceinline__ void merge_rows(float (&Mh)[G], float (&lh)[G]) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float M = rows_max(m[h]);
+      const float f = fast_exp2(m[h] - (M == -INFINITY ? 0.f : M));
+      lh[h] = rows_sum(l[h] * f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] = rows_sum(acc[h][e] * f);
+      Mh[h] = M;
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------------------------
+// QK^T on the matrix cores.  For the 16x16x32 bf16 MFMA, lane l holds A[l%16][8(l/16)+i],
+// B[8(l/16)+i][l%16] and C[4(l/16)+i][l%16] (checked on gfx950).  MFMA row m of a tile is token
+// 4(m%4) + m/4, so the four scores a lane gets back (C rows 4g+i, g = l/16) are tokens 4i+g: the
+// tokens its row group handles in the P.V layout.  The k order inside the contraction is free
+// (A and B share it): chunk 4kk + l/16 of the head dim for MFMA kk, so each lane reads whole
+// 16-byte pieces of K rows and q.  State per lane: (m, l) of head l%16 for row group l/16, and
+// acc[G][E] in the P.V layout; probabilities reach the P.V layout by row_newbcast.
+// ---------------------------------------------------------------------------------------------
+template <int D, int G>
+struct QkMfma {
+  static constexpr int KK = D / 32;
+  static constexpr int W = RowGeom<D>::kWords;
+  static constexpr int E = RowGeom<D>::kElems;
+  struct Tile {
+    u32x4_t k[KK];
+    uint32_t v[kTileSteps][W];
+  };
+  u32x4_t qb[KK];
+  float c2;
+  bool head_lane;
+  float m, l, acc[G][E];
+
+  __device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int lane,
+                                         uint32_t qflip) {
+    const int n = lane & 15;
+    head_lane = n < G;
+    const char* qrow = reinterpret_cast<const char*>(
+        p.q + ((size_t)b * p.num_q_heads + h0 + (head_lane ? n : 0)) * D);
+    const uint32_t keep = head_lane ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + 64 * kk + 16 * (lane >> 4));
+      x.x = (x.x ^ qflip) & keep;
+      x.y = (x.y ^ qflip) & keep;
+      x.z = (x.z ^ qflip) & keep;
+      x.w = (x.w ^ qflip) & keep;
+      qb[kk] = x;
+    }
+  }
+  __device__ __forceinline__ void reset() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+    }
+  }
+  __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
+                                       uint32_t qflip, float c2_) {
+    c2 = c2_;
+    load_q(p, b, h0, lane, qflip);
+    reset();
+  }
+
+  __device__ __forceinline__ void issue(Tile& t, const char* kb, const char* vb, int lane) const {
+    const int mrow = lane & 15;
+    const int tok = 4 * (mrow & 3) + (mrow >> 2);
+    const char* krow = kb + tok * RowGeom<D>::kRowBytes + 16 * (lane >> 4);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      t.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + 64 * kk));
+    load_v_rows<D>(t.v, vb, lane);
+  }
+
+  template <bool MASKED>
+  __device__ __forceinline__ void consume(Tile& t, int tok0, int lo, int hi, int lane) {
+    const int g = lane >> 4;
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[kk]),
+                                                   __builtin_bit_cast(bf16x8_t, qb[kk]), sc, 0,
+                                                   0, 0);
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tk = tok0 + 4 * i + g;
+        sc[i] = (tk >= lo && tk < hi) ? sc[i] * c2 : -INFINITY;
+      }
+      mask_v_rows<D>(t.v, tok0, lo, hi, lane);
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    if constexpr (!MASKED) mx *= c2;
+    const bool need = head_lane && mx > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
+      l *= alpha;
+      m = mn;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float a_h = row_bcast_dyn(alpha, h);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] *= a_h;
+      }
+    }
+    const float mu = m == -INFINITY ? 0.f : m;
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pr[i] = MASKED ? fast_exp2(sc[i] - mu) : fast_exp2(fmaf(sc[i], c2, -mu));
+    l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+#pragma unroll
+    for (int j = 0; j < kTileSteps; ++j) {
+      float vf[E];
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        vf[2 * w] = bf16_lo(t.v[j][w]);
+        vf[2 * w + 1] = bf16_hi(t.v[j][w]);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float pb = row_bcast_dyn(pr[j], h);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pb, vf[e], acc[h][e]);
+      }
+    }
+  }
+
+  // Merge the 4 row groups; lanes of row 0 end with the wave's (M, l, acc) of every head.
+  __device__ __forceinline__ void merge_rows(float (&Mh)[G], float (&lh)[G]) {
+    const float M = rows_max(m);
+    const float f = fast_exp2(m - (M == -INFINITY ? 0.f : M));
+    const float lt = rows_sum(l * f);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float f_h = row_bcast_dyn(f, h);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] = rows_sum(acc[h][e] * f_h);
+      Mh[h] = row_bcast_dyn(M, h);
+      lh[h] = row_bcast_dyn(lt, h);
+    }
+  }
+};
+
+}  // namespace pa

@@ -40,12 +40,25 @@ def max_len(wl) -> int:
     return int(wl.seq_lens.max()) if wl.num_seqs else 0
 
 
-def run_gpu(wl, t, partition_size: int = 0, max_partitions=None, poison_outputs=True):
-    """One decode step through the ABI; returns (out, lse) as NumPy float64.  Output buffers are
-    NaN-poisoned first so an unwritten element cannot pass."""
+BALANCED = -1   # partition_size value that selects the balanced schedule in run_gpu
+
+
+def run_gpu(wl, t, partition_size: int = 0, max_partitions=None, num_workers: int = 0):
+    """One decode step through the ABI; returns (out, lse) as NumPy float64.  Output buffers (and
+    the balanced workspace) are NaN-poisoned first so an unwritten element cannot pass.
+    partition_size: 0 unsplit, > 0 fixed partitions + reduce, BALANCED the balanced schedule."""
     B, Hq, D = wl.q.shape
     dev = t["q"].device
-    if partition_size <= 0:
+    if partition_size == BALANCED:
+        out = torch.full((B, Hq, D), float("nan"), device=dev)
+        lse = torch.full((B, Hq), float("nan"), device=dev)
+        shape = pa.make_shape(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride)
+        nbytes = pa.balanced_workspace_size(shape, D, num_workers)
+        ws = torch.full((nbytes // 4 + 1,), float("nan"), device=dev)
+        pa.decode_balanced(t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale),
+                           window=wl.window, sinks=t["sinks"], out=out, lse=lse, workspace=ws,
+                           num_workers=num_workers)
+    elif partition_size == 0:
         out = torch.full((B, Hq, D), float("nan"), device=dev)
         lse = torch.full((B, Hq), float("nan"), device=dev)
         pa.decode(t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale), window=wl.window,

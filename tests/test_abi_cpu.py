@@ -185,3 +185,40 @@ def test_binding_refuses_host_tensors():
     L = torch.ones(2, dtype=torch.int32)
     with pytest.raises(ValueError):
         pa.decode(q, k, k, bt, L, 0.1)
+
+
+# ---------------------------------------------------------------------------------------------
+# balanced schedule: host-side validation
+# ---------------------------------------------------------------------------------------------
+def call_balanced(s, *, head_dim=128, block_size=16, window=0, ws=FAKE, ws_bytes=1 << 30,
+                  workers=64, out=FAKE):
+    return pa.lib().paged_attn_decode_balanced(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                               0.1, head_dim, block_size, window, None, out,
+                                               None, ws, ws_bytes, workers, None)
+
+
+def test_balanced_workspace_size_formula():
+    s = shape(num_seqs=5, num_q_heads=8, num_kv_heads=2)
+    n = pa.balanced_workspace_size(s, 128, 100)
+    # prefix int64[B+1] | lse f32[N][2][G] | o f32[N][2][G][D], each 256-byte aligned
+    a = lambda x: (x + 255) // 256 * 256
+    assert n == a(6 * 8) + a(100 * 2 * 4 * 4) + a(100 * 2 * 4 * 128 * 4)
+    with pytest.raises(pa.PagedAttnError):
+        pa.balanced_workspace_size(s, 96, 100)
+    with pytest.raises(pa.PagedAttnError):
+        pa.balanced_workspace_size(s, 128, -1)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(head_dim=96), -3), (dict(block_size=8), -3), (dict(window=-2), -2),
+    (dict(workers=-1), -2), (dict(workers=(1 << 20) + 1), -2),
+    (dict(ws=None), -1), (dict(out=None), -1),
+    (dict(ws=ctypes.c_void_p(0x1004)), -2),          # misaligned
+    (dict(ws_bytes=1024), -2),                        # too small for 64 workers
+])
+def test_balanced_rejects(kw, expect):
+    assert call_balanced(shape(), **kw) == expect
+
+
+def test_balanced_empty_batch_is_ok_without_launch():
+    assert call_balanced(shape(num_seqs=0), ws=None, out=None) == 0

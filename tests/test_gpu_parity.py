@@ -11,8 +11,8 @@ from paged_kv_attention_attn_amd import debug
 from oracle import ref
 from workloads import SWEEP_POINTS, config_seq_lens, make_config, make_workload
 
-from gpu_helpers import (bench_partition, compare, log, max_len, oracle_full, oracle_pairs,
-                         run_gpu, sample_pairs, to_dev)
+from gpu_helpers import (BALANCED, bench_partition, compare, log, max_len, oracle_full,
+                         oracle_pairs, run_gpu, sample_pairs, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -324,3 +324,100 @@ def test_reduce_kernel_on_oracle_partials():
     torch.cuda.synchronize()
     compare(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), eo, el,
             "reduce on oracle partials")
+
+
+# ---------------------------------------------------------------------------------------------
+# balanced schedule (persistent workers, fix-up merge)
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("workers", [0, 1, 2, 3, 5, 64])
+def test_config1_balanced(workers, qk_path):
+    wl = make_config(1, poison=True)
+    t = to_dev(wl)
+    compare(*run_gpu(wl, t, partition_size=BALANCED, num_workers=workers), *oracle_full(wl),
+            f"cfg1 balanced workers={workers} {qk_path}")
+
+
+@pytest.mark.parametrize("workers", [0, 7, 1000])
+def test_config2_balanced(workers):
+    wl = make_config(2)
+    t = to_dev(wl)
+    compare(*run_gpu(wl, t, partition_size=BALANCED, num_workers=workers), *oracle_full(wl),
+            f"cfg2 balanced workers={workers}")
+
+
+def test_config2_balanced_valu_and_poisoned(monkeypatch):
+    wl = make_config(2, poison=True)
+    t = to_dev(wl)
+    exp = oracle_full(wl)
+    compare(*run_gpu(wl, t, partition_size=BALANCED), *exp, "cfg2 balanced poisoned mfma")
+    monkeypatch.setenv("PA_DECODE_PATH", "valu")
+    compare(*run_gpu(wl, t, partition_size=BALANCED), *exp, "cfg2 balanced poisoned valu")
+
+
+@pytest.mark.parametrize("D,hq", SWEEP_POINTS)
+def test_config3_point_balanced(D, hq):
+    wl = make_config(3, head_dim=D, num_q_heads=hq)
+    t = to_dev(wl)
+    out, lse = run_gpu(wl, t, partition_size=BALANCED)
+    pairs = sample_pairs(wl, 24, seed=D * hq)
+    eo, el = oracle_pairs(wl, pairs)
+    idx = tuple(np.array(pairs).T)
+    compare(out[idx], lse[idx], eo, el, f"cfg3 balanced D={D} Hq={hq} ({len(pairs)} sampled)")
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_config4_balanced():
+    wl = make_config(4)
+    t = to_dev(wl)
+    compare(*run_gpu(wl, t, partition_size=BALANCED), *oracle_full(wl), "cfg4 balanced")
+
+
+def test_config5_balanced():
+    wl = make_config(5, poison=True)
+    t = to_dev(wl)
+    exp = oracle_full(wl)
+    for workers in (0, 333):
+        compare(*run_gpu(wl, t, partition_size=BALANCED, num_workers=workers), *exp,
+                f"cfg5 balanced poisoned workers={workers}")
+
+
+@pytest.mark.parametrize("workers", [0, 3, 17])
+@pytest.mark.parametrize("combo", range(len(EDGE_COMBOS)))
+@pytest.mark.parametrize("D,g", [(D, g) for D in (64, 128, 256) for g in (1, 2, 4, 8)])
+def test_edges_balanced(D, g, combo, workers):
+    bs, W, sinks, _ = EDGE_COMBOS[combo]
+    wl = make_workload(name="edge", seq_lens=EDGE_LENS, num_q_heads=2 * g, num_kv_heads=2,
+                       head_dim=D, block_size=bs, seed=[D, g, combo, 1], window=W,
+                       with_sinks=sinks, poison=True)
+    t = to_dev(wl)
+    compare(*run_gpu(wl, t, partition_size=BALANCED, num_workers=workers), *oracle_full(wl),
+            f"edge balanced workers={workers} D={D} g={g} bs={bs} W={W} sinks={sinks}")
+
+
+def test_balanced_bad_tables_and_lengths():
+    wl = make_workload(name="bad", seq_lens=[40, 40, 40, 33], num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, seed=[5])
+    exp = oracle_full(wl)
+    wl.block_table[1, 1] = wl.num_blocks
+    wl.block_table[2, 0] = -7
+    t = to_dev(wl)
+    t["L"] = torch.tensor([40, 40, 40, 49], dtype=torch.int32, device="cuda")   # 49 > 3 * 16
+    for workers in (0, 1, 5):
+        out, lse = run_gpu(wl, t, partition_size=BALANCED, num_workers=workers)
+        assert np.isnan(out[1:]).all() and np.isnan(lse[1:]).all(), workers
+        assert np.abs(out[0] - exp[0][0]).max() < 1e-3
+
+
+def test_balanced_repeat_bit_identical_and_lse_null():
+    wl = make_config(5, seq_lens=[5000, 17, 9000, 4096, 4097, 1, 300, 0])
+    t = to_dev(wl)
+    a = run_gpu(wl, t, partition_size=BALANCED, num_workers=50)
+    for _ in range(3):
+        b = run_gpu(wl, t, partition_size=BALANCED, num_workers=50)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    out, lse = pa.decode_balanced(t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale),
+                                  window=wl.window, sinks=t["sinks"], want_lse=False,
+                                  num_workers=50)
+    torch.cuda.synchronize()
+    assert lse is None
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), a[0])
