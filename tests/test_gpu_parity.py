@@ -421,3 +421,18 @@ def test_balanced_repeat_bit_identical_and_lse_null():
     torch.cuda.synchronize()
     assert lse is None
     assert np.array_equal(out.cpu().numpy().astype(np.float64), a[0])
+
+
+@pytest.mark.parametrize("hkv,g", [(1, 8), (2, 2), (4, 1)])
+@pytest.mark.parametrize("workers", [997, 4096])
+def test_balanced_many_pieces(hkv, g, workers):
+    """Units cut into hundreds of pieces (long chains for the fix-up merge), next to short and
+    empty sequences, with sinks."""
+    wl = make_workload(name="long", seq_lens=[32768, 100, 0, 16384, 4097], num_q_heads=hkv * g,
+                       num_kv_heads=hkv, head_dim=128, block_size=64, seed=[hkv, g, workers],
+                       with_sinks=True, poison=True)
+    t = to_dev(wl)
+    a = run_gpu(wl, t, partition_size=BALANCED, num_workers=workers)
+    compare(*a, *oracle_full(wl), f"many pieces Hkv={hkv} g={g} workers={workers}")
+    b = run_gpu(wl, t, partition_size=BALANCED, num_workers=workers)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
