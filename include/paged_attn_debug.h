@@ -43,7 +43,8 @@ pa_status paged_attn_gather_witness(const pa_shape* shape, const void* k_cache,
 
 /*
  * Streaming-read probe: reads `bytes` (a multiple of 16) from `buf` with 16-byte coalesced
- * loads, as many workgroups as `num_workgroups`, and writes one 32-bit checksum per workgroup to
+ * non-temporal loads (the load kind the decode kernels use for K/V), as many workgroups as
+ * `num_workgroups`, and writes one 32-bit checksum per workgroup to
  * `sink` (uint32 [num_workgroups]) so the loads cannot be elided.  Attainable HBM read
  * bandwidth next to the nominal figure.
  */

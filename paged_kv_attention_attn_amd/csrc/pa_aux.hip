@@ -69,13 +69,19 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4
                                                                     size_t n16, uint32_t* sink) {
   const size_t stride = (size_t)gridDim.x * kStreamThreads;
   size_t i = (size_t)blockIdx.x * kStreamThreads + threadIdx.x;
+  // non-temporal loads, as the decode kernels stream K/V
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(buf);
   uint32_t x = 0;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
-    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    const u32x4_t a = __builtin_nontemporal_load(src + i);
+    const u32x4_t b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4_t c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4_t d = __builtin_nontemporal_load(src + i + 3 * stride);
+    const u32x4_t e = a ^ b ^ c ^ d;
+    x ^= e.x ^ e.y ^ e.z ^ e.w;
   }
   for (; i < n16; i += stride) {
-    const uint4 a = buf[i];
+    const u32x4_t a = __builtin_nontemporal_load(src + i);
     x ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   __shared__ uint32_t red[kStreamThreads];
