@@ -271,16 +271,21 @@ __global__ __launch_bounds__(kWave) void balanced_decode_kernel(const BalancedPa
     }
   };
 
-  if constexpr (DEPTH == 2) {
-    // two tiles in flight: the loads of tile k+1 are issued before tile k is consumed
-    typename QK::Tile t0_, t1_;
-    Slot s0, s1;
-    issue(0, t0_, s0);
-    for (int k = 0; k < n; k += 2) {
-      if (k + 1 < n) issue(k + 1, t1_, s1);
-      consume(k, t0_, s0, &s1);
-      if (k + 2 < n) issue(k + 2, t0_, s0);
-      if (k + 1 < n) consume(k + 1, t1_, s1, &s0);
+  if constexpr (DEPTH > 1) {
+    // DEPTH tiles in flight: the loads of tiles k+1 .. k+DEPTH-1 are issued before tile k is
+    // consumed; the loop is unrolled DEPTH times so every buffer index is a constant
+    typename QK::Tile t[DEPTH];
+    Slot sl[DEPTH];
+#pragma unroll
+    for (int j = 0; j + 1 < DEPTH; ++j)
+      if (j < n) issue(j, t[j], sl[j]);
+    for (int k = 0; k < n; k += DEPTH) {
+#pragma unroll
+      for (int j = 0; j < DEPTH; ++j) {
+        if (k + j + DEPTH - 1 < n)
+          issue(k + j + DEPTH - 1, t[(j + DEPTH - 1) % DEPTH], sl[(j + DEPTH - 1) % DEPTH]);
+        if (k + j < n) consume(k + j, t[j], sl[j], &sl[(j + 1) % DEPTH]);
+      }
     }
   } else {
     typename QK::Tile t0_;
@@ -294,113 +299,116 @@ __global__ __launch_bounds__(kWave) void balanced_decode_kernel(const BalancedPa
   }
 }
 
-// Fix-up: one workgroup per (sequence b, query head h) of unit (b, h / G).  Units inside one
-// worker were written by the decode kernel; empty units get 0 (or the sink alone); a cut unit
-// merges its pieces: M = max lse_i, out = sum e^(lse_i - M) o_i / sum e^(lse_i - M),
-// lse = M + ln sum e^(lse_i - M).  Pass 1 takes M over the pieces; pass 2 reads the piece rows
-// with 16-byte loads, D/4 threads per row and 1024/D rows per step, the row-slot sums meeting
-// in LDS (as the partition reduce).
+// Fix-up: one workgroup per (sequence b, KV head kvh, group of H of its G query heads), with
+// H = min(G, 256 / D) so that a workgroup reads 1 KiB of every piece.  Units inside one worker
+// were written by the decode kernel; empty units get 0 (or the sink alone); a cut unit merges
+// its pieces head by head: M = max lse_i, out = sum e^(lse_i - M) o_i / sum e^(lse_i - M),
+// lse = M + ln sum e^(lse_i - M).  The H heads of a piece are H*D contiguous floats; each
+// thread takes a 16-byte slice of every RPS-th piece (one pass, a running max per slice, the
+// piece's lse loaded with its slice), and the row slots then meet in LDS with the same rule.
+// The kernel is latency-bound: its chain of dependent memory accesses is kept to two,
+// (lengths, prefix, sinks) then (piece LSEs and rows).
 constexpr int kFixupThreads = 256;
 
 template <int D, int G>
+constexpr int fixup_heads() {
+  return G < 256 / D ? G : (256 / D < 1 ? 1 : 256 / D);
+}
+
+template <int D, int G>
 __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const BalancedParams bp) {
-  constexpr int TPR = D / 4;
-  constexpr int RPS = kFixupThreads / TPR;
+  constexpr int H = fixup_heads<D, G>();
+  constexpr int F = H * D / 4;                          // float4 slices per piece row
+  constexpr int RPS = kFixupThreads / F;                // piece rows per step
+  static_assert(G % H == 0 && kFixupThreads % F == 0, "fix-up tiling");
   const DecodeParams& p = bp.d;
-  const int bh = blockIdx.x;
-  const int b = bh / p.num_q_heads;
-  const int hq = bh - b * p.num_q_heads;
-  const int kvh = hq / G;
-  const int h = hq - kvh * G;
+  const int ug = blockIdx.x;
+  const int u = ug / (G / H);
+  const int h0 = (ug - u * (G / H)) * H;                // first head of this group, within G
+  const int b = u / p.num_kv_heads;
+  const int kvh = u - b * p.num_kv_heads;
   const int tid = threadIdx.x;
-  const SeqSpan s = seq_span(p.seq_lens[b], p.window, (int64_t)p.stride << p.bs_log2);
-  const int64_t total = bp.prefix[p.num_seqs] * p.num_kv_heads;
+  const int Lb = p.seq_lens[b];
+  const int64_t pre_b = bp.prefix[b];
+  const int64_t pre_B = bp.prefix[p.num_seqs];
+  const SeqSpan s = seq_span(Lb, p.window, (int64_t)p.stride << p.bs_log2);
+  const int64_t total = pre_B * p.num_kv_heads;
   const int n_eff = effective_workers(total, bp.num_workers);
 
   int wa = 0, np = 0, first_slot = 0;
   if (s.T > 0) {
-    const int64_t S = bp.prefix[b] * p.num_kv_heads + (int64_t)kvh * s.T;
+    const int64_t S = pre_b * p.num_kv_heads + (int64_t)kvh * s.T;
     wa = worker_of(total, n_eff, S);
     const int wb = worker_of(total, n_eff, S + s.T - 1);
     if (wa == wb) return;   // written by the decode kernel
     np = wb - wa + 1;
     first_slot = worker_begin(total, n_eff, wa) < S ? 1 : 0;
   }
+
   // piece i of the unit: worker wa + i, slot first_slot for i == 0, else 0
-  auto slot_of = [&](int i) -> size_t {
-    return ((size_t)(wa + i) * 2 + (i == 0 ? first_slot : 0)) * G + h;
-  };
-
-  __shared__ float red[kFixupThreads / kWave];
-  __shared__ float s_acc[RPS][D];
-  __shared__ float s_sum[RPS];
-  __shared__ int s_nan;
-  if (tid == 0) s_nan = s.bad ? 1 : 0;
-  float mx = -INFINITY;
-  bool nan = false;
-  for (int i = tid; i < np; i += kFixupThreads) {
-    const float v = bp.ws_lse[slot_of(i)];
-    nan |= v != v;
-    mx = fmaxf(mx, v);
-  }
-  __syncthreads();
-  if (nan) s_nan = 1;
-  mx = wave_max(mx);
-  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = mx;
-  __syncthreads();
-  float M = red[0];
-#pragma unroll
-  for (int w = 1; w < kFixupThreads / kWave; ++w) M = fmaxf(M, red[w]);
-  const float Mu = M == -INFINITY ? 0.f : M;
-
-  const int pr = tid / TPR;
-  const int dq = tid - pr * TPR;
+  const int pr = tid / F;
+  const int f = tid - pr * F;                           // slice f covers head h0 + 4f / D
+  const int hl = (4 * f) / D;
+  float m = -INFINITY, z = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  float z = 0.f;
+  bool nan = s.bad;
 #pragma unroll 4
   for (int i = pr; i < np; i += RPS) {
-    const size_t slot = slot_of(i);
-    const float li = bp.ws_lse[slot];
-    const float4 o = *reinterpret_cast<const float4*>(bp.ws_o + slot * D + 4 * dq);
-    const bool live = li != -INFINITY;
-    const float f = fast_exp2((li - Mu) * kLog2e);
-    a.x = live ? fmaf(f, o.x, a.x) : a.x;
-    a.y = live ? fmaf(f, o.y, a.y) : a.y;
-    a.z = live ? fmaf(f, o.z, a.z) : a.z;
-    a.w = live ? fmaf(f, o.w, a.w) : a.w;
-    z += live ? f : 0.f;
+    const size_t slot = (size_t)(wa + i) * 2 + (i == 0 ? first_slot : 0);
+    const float li = bp.ws_lse[slot * G + h0 + hl];
+    const float4 o = *reinterpret_cast<const float4*>(bp.ws_o + (slot * G + h0) * D + 4 * f);
+    nan |= li != li;
+    // a piece with lse = -inf has no weight; selects instead of a branch keep the loads of
+    // several pieces in flight
+    const float mn = fmaxf(m, li);
+    const float e0 = m == mn ? 1.f : fast_exp2((m - mn) * kLog2e);
+    const float e1 = li > -INFINITY ? fast_exp2((li - mn) * kLog2e) : 0.f;
+    a.x = fmaf(a.x, e0, e1 * o.x);
+    a.y = fmaf(a.y, e0, e1 * o.y);
+    a.z = fmaf(a.z, e0, e1 * o.z);
+    a.w = fmaf(a.w, e0, e1 * o.w);
+    z = fmaf(z, e0, e1);
+    m = mn;
   }
-  *reinterpret_cast<float4*>(&s_acc[pr][4 * dq]) = a;
-  if (dq == 0) s_sum[pr] = z;
+
+  __shared__ float s_acc[RPS][H * D];
+  __shared__ float s_m[RPS][H], s_z[RPS][H];
+  __shared__ int s_nan;
+  if (tid == 0) s_nan = 0;
+  __syncthreads();
+  if (nan) s_nan = 1;
+  *reinterpret_cast<float4*>(&s_acc[pr][4 * f]) = a;
+  if ((4 * f) % D == 0) {   // the first slice of a head carries the head's (max, sum)
+    s_m[pr][hl] = m;
+    s_z[pr][hl] = z;
+  }
   __syncthreads();
 
-  if (tid < D) {
-    float o = 0.f, Z = 0.f;
+  for (int e = tid; e < H * D; e += kFixupThreads) {
+    const int h = e / D;
+    const int hq = kvh * G + h0 + h;
+    // the sink logit joins the max and the denominator with a zero value row
+    const float sink = p.sinks != nullptr ? p.sinks[hq] : -INFINITY;
+    float M = sink;
+#pragma unroll
+    for (int k = 0; k < RPS; ++k) M = fmaxf(M, s_m[k][h]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float o = 0.f, Z = sink > -INFINITY ? fast_exp2((sink - Mu) * kLog2e) : 0.f;
 #pragma unroll
     for (int k = 0; k < RPS; ++k) {
-      o += s_acc[k][tid];
-      Z += s_sum[k];
-    }
-    float Mo = M;
-    if (p.sinks != nullptr) {
-      // the sink logit joins the max and the denominator with a zero value row
-      const float sk = p.sinks[hq];
-      const float M2 = fmaxf(M, sk);
-      const float M2u = M2 == -INFINITY ? 0.f : M2;
-      const float f = fast_exp2((M - M2u) * kLog2e);
-      Z = fmaf(Z, f, fast_exp2((sk - M2u) * kLog2e));
-      o *= f;
-      Mo = M2;
+      const float w = fast_exp2((s_m[k][h] - Mu) * kLog2e);   // 0 for an empty row slot
+      o = fmaf(s_acc[k][e], w, o);
+      Z = fmaf(s_z[k][h], w, Z);
     }
     float ov = Z > 0.f ? o / Z : 0.f;
-    float lv = Z > 0.f ? Mo + fast_log2(Z) * kLn2 : -INFINITY;
+    float lv = Z > 0.f ? M + fast_log2(Z) * kLn2 : -INFINITY;
     if (s_nan) {
       ov = __builtin_nanf("");
       lv = __builtin_nanf("");
     }
     const size_t row = (size_t)b * p.num_q_heads + hq;
-    p.out[row * D + tid] = ov;
-    if (tid == 0 && p.lse != nullptr) p.lse[row] = lv;
+    p.out[row * D + (e - h * D)] = ov;
+    if (e == h * D && p.lse != nullptr) p.lse[row] = lv;
   }
 }
 
@@ -413,7 +421,7 @@ template <int D, int G, QkPath PATH>
 using BQK = typename std::conditional<PATH == QkPath::kMfma, QkMfma<D, G>, QkValu<D, G>>::type;
 
 // tiles in flight per worker: two where the registers allow it
-template <int D, int G>
+template <int D, int G, QkPath PATH>
 constexpr int bal_depth() {
   return D * G <= 512 ? 2 : 1;
 }
@@ -421,12 +429,12 @@ constexpr int bal_depth() {
 template <int D, int G, QkPath PATH>
 const void* balanced_kernel_ptr() {
   return reinterpret_cast<const void*>(
-      &balanced_decode_kernel<D, G, bal_depth<D, G>(), BQK<D, G, PATH>>);
+      &balanced_decode_kernel<D, G, bal_depth<D, G, PATH>(), BQK<D, G, PATH>>);
 }
 
 template <int D, int G, QkPath PATH>
 hipError_t launch_bal(const BalancedParams& bp, hipStream_t stream) {
-  hipLaunchKernelGGL((balanced_decode_kernel<D, G, bal_depth<D, G>(), BQK<D, G, PATH>>),
+  hipLaunchKernelGGL((balanced_decode_kernel<D, G, bal_depth<D, G, PATH>(), BQK<D, G, PATH>>),
                      dim3(bp.num_workers), dim3(kWave), 0, stream, bp);
   return hipGetLastError();
 }
@@ -434,7 +442,8 @@ hipError_t launch_bal(const BalancedParams& bp, hipStream_t stream) {
 template <int D, int G>
 hipError_t launch_fix(const BalancedParams& bp, hipStream_t stream) {
   hipLaunchKernelGGL((balanced_fixup_kernel<D, G>),
-                     dim3((unsigned)bp.d.num_seqs * (unsigned)bp.d.num_q_heads),
+                     dim3((unsigned)bp.d.num_seqs * (unsigned)bp.d.num_kv_heads *
+                          (unsigned)(G / fixup_heads<D, G>())),
                      dim3(kFixupThreads), 0, stream, bp);
   return hipGetLastError();
 }
