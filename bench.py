@@ -186,7 +186,8 @@ def main() -> int:
         workers = workers or pa.balanced_default_workers(D, Hq // wl.num_kv_heads)
         ws = torch.empty(pa.balanced_workspace_size(shape, D, workers), dtype=torch.uint8,
                          device=dev)
-        variant = f"pa_balanced_{'valu' if os.environ.get('PA_DECODE_PATH') == 'valu' else 'mfma'}" \
+        path = (pa.variant_name(shape, D, wl.block_size) or "pa_decode_?").split("_")[2]
+        variant = f"pa_balanced_{path}" \
                   f"_d{D}_g{Hq // wl.num_kv_heads}_workers{workers}"
     else:
         variant = pa.variant_name(shape, D, wl.block_size)

@@ -60,8 +60,8 @@ int decode_waves(int head_dim, int group, int psize) {
   return -1;
 }
 
-// QK^T path: the library's choice, or PA_DECODE_PATH (exactly "valu" or "mfma") for tuning
-// and for testing both paths.  Any other value is rejected.
+// Score path: the library's choice, or PA_DECODE_PATH (exactly "valu", "mfma" or "mfma_pv")
+// for tuning and for testing every path.  Any other value is rejected.
 int decode_path(int head_dim, int group, pa::QkPath* out) {
   const char* v = std::getenv("PA_DECODE_PATH");
   if (v == nullptr) {
@@ -74,6 +74,10 @@ int decode_path(int head_dim, int group, pa::QkPath* out) {
   }
   if (std::strcmp(v, "mfma") == 0) {
     *out = pa::QkPath::kMfma;
+    return 0;
+  }
+  if (std::strcmp(v, "mfma_pv") == 0) {
+    *out = pa::QkPath::kMfmaPv;
     return 0;
   }
   return -1;
@@ -292,7 +296,7 @@ pa_status paged_attn_decode_balanced(const pa_shape* shape, const void* q, const
   p.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
   if (debug_log())
     std::fprintf(stderr, "[paged_attn] balanced %s B=%d Hq=%d Hkv=%d bs=%d W=%d workers=%d\n",
-                 path == pa::QkPath::kMfma ? "mfma" : "valu", shape->num_seqs,
+                 pa::qk_path_name(path), shape->num_seqs,
                  shape->num_q_heads, shape->num_kv_heads, block_size, window, bp.num_workers);
   const hipError_t e =
       pa::launch_balanced(bp, head_dim, group, path, static_cast<hipStream_t>(stream));

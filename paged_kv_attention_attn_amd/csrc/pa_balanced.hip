@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kWave) void balanced_decode_kernel(const BalancedPa
         }
 #pragma unroll
         for (int e = 0; e < E; ++e)
-          dst[RG::dim(c, e)] = piece_bad ? __builtin_nanf("") : qk.acc[h][e] * inv;
+          dst[RG::dim(c, e)] = piece_bad ? __builtin_nanf("") : qk.out(h, e) * inv;
       }
     }
     first_piece = false;
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
 namespace {
 
 template <int D, int G, QkPath PATH>
-using BQK = typename std::conditional<PATH == QkPath::kMfma, QkMfma<D, G>, QkValu<D, G>>::type;
+using BQK = QkPolicy<D, G, PATH>;
 
 // tiles in flight per worker: two where the registers allow it
 template <int D, int G, QkPath PATH>
@@ -501,8 +501,11 @@ const void* bal_ptr(int head_dim, int group) {
 
 hipError_t launch_balanced(const BalancedParams& bp, int head_dim, int group, QkPath path,
                            hipStream_t stream) {
-  return path == QkPath::kMfma ? launch_bal_d<QkPath::kMfma>(bp, head_dim, group, stream)
-                               : launch_bal_d<QkPath::kValu>(bp, head_dim, group, stream);
+  switch (path) {
+    case QkPath::kValu: return launch_bal_d<QkPath::kValu>(bp, head_dim, group, stream);
+    case QkPath::kMfma: return launch_bal_d<QkPath::kMfma>(bp, head_dim, group, stream);
+    default: return launch_bal_d<QkPath::kMfmaPv>(bp, head_dim, group, stream);
+  }
 }
 
 hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int group,
@@ -516,8 +519,9 @@ hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int gro
 }
 
 int balanced_default_workers(int head_dim, int group, QkPath path) {
-  const void* k = path == QkPath::kMfma ? bal_ptr<QkPath::kMfma>(head_dim, group)
-                                        : bal_ptr<QkPath::kValu>(head_dim, group);
+  const void* k = path == QkPath::kValu   ? bal_ptr<QkPath::kValu>(head_dim, group)
+                  : path == QkPath::kMfma ? bal_ptr<QkPath::kMfma>(head_dim, group)
+                                          : bal_ptr<QkPath::kMfmaPv>(head_dim, group);
   if (k == nullptr) return -1;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;

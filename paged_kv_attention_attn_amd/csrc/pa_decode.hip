@@ -161,7 +161,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) s_acc[wave][h][RG::dim(c, e)] = qk.acc[h][e];
+      for (int e = 0; e < E; ++e) s_acc[wave][h][RG::dim(c, e)] = qk.out(h, e);
     }
   }
   if (lane == 0) {
@@ -234,7 +234,7 @@ constexpr int pipeline_depth() {
 
 template <int D, int G, int NW, QkPath PATH>
 hipError_t launch_v(const DecodeParams& p, hipStream_t stream) {
-  using QK = typename std::conditional<PATH == QkPath::kMfma, QkMfma<D, G>, QkValu<D, G>>::type;
+  using QK = QkPolicy<D, G, PATH>;
   const unsigned grid = (unsigned)((p.psize > 0 ? p.max_parts : 1) *
                                    (int64_t)p.num_kv_heads * p.num_seqs);
   hipLaunchKernelGGL((decode_kernel<D, G, NW, pipeline_depth<D, G>(), QK>), dim3(grid),
@@ -295,23 +295,35 @@ int decode_default_waves(int head_dim, int group, int psize) {
 }
 
 QkPath decode_default_path(int head_dim, int group) {
+  // P.V on the matrix cores pays once a KV head serves two or more query heads; a single head
+  // would use one row of sixteen.
   (void)head_dim;
-  (void)group;
-  return QkPath::kMfma;
+  return group >= 2 ? QkPath::kMfmaPv : QkPath::kMfma;
+}
+
+const char* qk_path_name(QkPath path) {
+  switch (path) {
+    case QkPath::kValu: return "valu";
+    case QkPath::kMfma: return "mfma";
+    default: return "mfmapv";
+  }
 }
 
 const char* decode_variant_name(int head_dim, int group, int waves, bool split, QkPath path) {
   static thread_local char buf[64];
   std::snprintf(buf, sizeof(buf), "pa_decode_%s_d%d_g%d_w%d%s",
-                path == QkPath::kMfma ? "mfma" : "valu", head_dim, group, waves,
+                qk_path_name(path), head_dim, group, waves,
                 split ? "_split" : "");
   return buf;
 }
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int waves, QkPath path,
                          hipStream_t stream) {
-  return path == QkPath::kMfma ? launch_d<QkPath::kMfma>(p, head_dim, group, waves, stream)
-                               : launch_d<QkPath::kValu>(p, head_dim, group, waves, stream);
+  switch (path) {
+    case QkPath::kValu: return launch_d<QkPath::kValu>(p, head_dim, group, waves, stream);
+    case QkPath::kMfma: return launch_d<QkPath::kMfma>(p, head_dim, group, waves, stream);
+    default: return launch_d<QkPath::kMfmaPv>(p, head_dim, group, waves, stream);
+  }
 }
 
 }  // namespace pa

@@ -64,9 +64,12 @@ struct WitnessParams {
 
 // Launchers return hipSuccess or the launch error.  Grid and variant choice is theirs; the
 // caller has validated the parameters.
-// Decode kernels: QK^T on the vector ALUs (dot2 + DPP) or on the matrix cores (MFMA); P.V is
-// on the vector ALUs in fp32 in both.
-enum class QkPath { kValu = 0, kMfma = 1 };
+// Decode kernels: q.k on the vector ALUs (dot2 + DPP) with P.V in fp32 on the vector ALUs
+// (kValu); q.k on the matrix cores with P.V on the vector ALUs (kMfma); or both on the matrix
+// cores, P carried as two bf16 terms (kMfmaPv).
+enum class QkPath { kValu = 0, kMfma = 1, kMfmaPv = 2 };
+// Short name of a path ("valu", "mfma", "mfmapv").
+const char* qk_path_name(QkPath path);
 // Grid: one workgroup per (partition slot, KV head, sequence), 1-D.
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int waves, QkPath path,
                          hipStream_t stream);

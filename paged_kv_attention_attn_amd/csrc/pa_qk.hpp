@@ -15,6 +15,8 @@
 // commit"; wave64 reductions crossing all four 16-lane rows: vllm.cpp PR #506 review, finding 2.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_device.hpp"
 #include "pa_kernels.hpp"
 
@@ -205,6 +207,8 @@ struct QkValu {
       Mh[h] = M;
     }
   }
+  // After merge_rows, on the row-0 lanes: the accumulated P.V of head h at dim(lane, e).
+  __device__ __forceinline__ float out(int h, int e) const { return acc[h][e]; }
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -342,6 +346,176 @@ struct QkMfma {
       lh[h] = row_bcast_dyn(lt, h);
     }
   }
+  // After merge_rows, on the row-0 lanes: the accumulated P.V of head h at dim(lane, e).
+  __device__ __forceinline__ float out(int h, int e) const { return acc[h][e]; }
 };
+
+// ---------------------------------------------------------------------------------------------
+// q.k and P.V both on the matrix cores.  q.k as in QkMfma.  P.V uses the 16x16x16 bf16 MFMA
+// (lane l holds A[l%16][4(l/16)+j], B[4(l/16)+j][l%16], C[4(l/16)+i][l%16]; checked on gfx950)
+// with the probabilities as A (row = query head l%16, k = 4(l/16)+j = token 4j+l/16: exactly the
+// scores the lane holds after q.k) and V as B (column c of MFMA e = head-dim index dim(c, e);
+// k = 4g+j is token 4j+g, the rows row group g loads).  P is split into two bf16 terms,
+// p = hi + lo, each multiplied exactly and accumulated in fp32, so the product keeps about
+// 16 bits of p (relative error below 2^-16) instead of bf16's 8.  All row groups feed the same
+// accumulator, so they share one running max per head (raised, lazily, from the wave-wide tile
+// max); each keeps its own partial sum of p.  State per lane: m and l of head l%16, and
+// cacc[e] = C rows 4(l/16)+i (heads), column l%16 (dim(l%16, e)).
+// ---------------------------------------------------------------------------------------------
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int D, int G>
+struct QkMfmaPv {
+  static constexpr int KK = D / 32;
+  static constexpr int W = RowGeom<D>::kWords;
+  static constexpr int E = RowGeom<D>::kElems;
+  struct Tile {
+    u32x4_t k[KK];
+    uint32_t v[kTileSteps][W];
+  };
+  u32x4_t qb[KK];
+  float c2;
+  bool head_lane;
+  float m, l;
+  f32x4_t cacc[E];
+  float up[G > 4 ? 4 : 1][E];   // G = 8: heads 4..7 brought up from row 1 by merge_rows
+
+  __device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int lane,
+                                         uint32_t qflip) {
+    const int n = lane & 15;
+    head_lane = n < G;
+    const char* qrow = reinterpret_cast<const char*>(
+        p.q + ((size_t)b * p.num_q_heads + h0 + (head_lane ? n : 0)) * D);
+    const uint32_t keep = head_lane ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + 64 * kk + 16 * (lane >> 4));
+      x.x = (x.x ^ qflip) & keep;
+      x.y = (x.y ^ qflip) & keep;
+      x.z = (x.z ^ qflip) & keep;
+      x.w = (x.w ^ qflip) & keep;
+      qb[kk] = x;
+    }
+  }
+  __device__ __forceinline__ void reset() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
+                                       uint32_t qflip, float c2_) {
+    c2 = c2_;
+    load_q(p, b, h0, lane, qflip);
+    reset();
+  }
+
+  __device__ __forceinline__ void issue(Tile& t, const char* kb, const char* vb, int lane) const {
+    const int mrow = lane & 15;
+    const int tok = 4 * (mrow & 3) + (mrow >> 2);
+    const char* krow = kb + tok * RowGeom<D>::kRowBytes + 16 * (lane >> 4);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      t.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + 64 * kk));
+    load_v_rows<D>(t.v, vb, lane);
+  }
+
+  template <bool MASKED>
+  __device__ __forceinline__ void consume(Tile& t, int tok0, int lo, int hi, int lane) {
+    const int g = lane >> 4;
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[kk]),
+                                                   __builtin_bit_cast(bf16x8_t, qb[kk]), sc, 0,
+                                                   0, 0);
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tk = tok0 + 4 * i + g;
+        sc[i] = (tk >= lo && tk < hi) ? sc[i] * c2 : -INFINITY;
+      }
+      mask_v_rows<D>(t.v, tok0, lo, hi, lane);
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    if constexpr (!MASKED) mx *= c2;
+    const bool need = head_lane && mx > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      // one running max per head for the whole wave: raise it to the wave's tile max
+      const float mn = fmaxf(m, rows_max(mx));
+      const float alpha = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
+      l *= alpha;
+      m = mn;
+      // C row 4g+i is head 4g+i, whose factor sits in lane 4g+i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a_i = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute((4 * g + i) << 2, __builtin_bit_cast(int, alpha)));
+#pragma unroll
+        for (int e = 0; e < E; ++e) cacc[e][i] *= a_i;
+      }
+    }
+    const float mu = m == -INFINITY ? 0.f : m;
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = MASKED ? fast_exp2(sc[i] - mu) : fast_exp2(fmaf(sc[i], c2, -mu));
+      pr[i] = head_lane ? pr[i] : 0.f;
+    }
+    l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    // p = hi + lo in bf16
+    const bf16x2_t h01 = {(__bf16)pr[0], (__bf16)pr[1]};
+    const bf16x2_t h23 = {(__bf16)pr[2], (__bf16)pr[3]};
+    const uint32_t uh01 = __builtin_bit_cast(uint32_t, h01);
+    const uint32_t uh23 = __builtin_bit_cast(uint32_t, h23);
+    const bf16x2_t l01 = {(__bf16)(pr[0] - __builtin_bit_cast(float, uh01 << 16)),
+                          (__bf16)(pr[1] - __builtin_bit_cast(float, uh01 & 0xFFFF0000u))};
+    const bf16x2_t l23 = {(__bf16)(pr[2] - __builtin_bit_cast(float, uh23 << 16)),
+                          (__bf16)(pr[3] - __builtin_bit_cast(float, uh23 & 0xFFFF0000u))};
+    const s16x4_t a_hi = __builtin_bit_cast(s16x4_t, u32x2_t{uh01, uh23});
+    const s16x4_t a_lo = __builtin_bit_cast(
+        s16x4_t, u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      // B: element e of the slice of tokens 4j+g, j = 0..3 (bf16 halves gathered by v_perm)
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t b01 = __builtin_amdgcn_perm(t.v[1][e / 2], t.v[0][e / 2], sel);
+      const uint32_t b23 = __builtin_amdgcn_perm(t.v[3][e / 2], t.v[2][e / 2], sel);
+      const s16x4_t bv = __builtin_bit_cast(s16x4_t, u32x2_t{b01, b23});
+      cacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, bv, cacc[e], 0, 0, 0);
+      cacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, bv, cacc[e], 0, 0, 0);
+    }
+  }
+
+  // Sum the row groups' partial sums: every lane ends with the wave's (M, l) of every head.
+  // With G = 8, heads 4..7 live in row 1 and are brought up here, where every lane is active
+  // (a lane permute reads nothing from inactive lanes).
+  __device__ __forceinline__ void merge_rows(float (&Mh)[G], float (&lh)[G]) {
+    const float lt = rows_sum(l);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      Mh[h] = row_bcast_dyn(m, h);
+      lh[h] = row_bcast_dyn(lt, h);
+    }
+    if constexpr (G > 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) up[i][e] = xor_lane(cacc[e][i], 16);
+      }
+    }
+  }
+  // After merge_rows, on the row-0 lanes: the accumulated P.V of head h at dim(lane, e).
+  __device__ __forceinline__ float out(int h, int e) const {
+    return h < 4 ? cacc[e][h & 3] : up[(h - 4) & 3][e];
+  }
+};
+
+// The policy of a path.
+template <int D, int G, QkPath PATH>
+using QkPolicy = typename std::conditional<
+    PATH == QkPath::kValu, QkValu<D, G>,
+    typename std::conditional<PATH == QkPath::kMfma, QkMfma<D, G>, QkMfmaPv<D, G>>::type>::type;
 
 }  // namespace pa

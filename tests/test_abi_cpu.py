@@ -54,6 +54,13 @@ def shape(**kw):
 
 
 def test_variant_names(monkeypatch):
+    monkeypatch.delenv("PA_DECODE_PATH", raising=False)
+    monkeypatch.delenv("PA_DECODE_WAVES", raising=False)
+    # default score path: P.V on the matrix cores from two query heads per KV head up
+    assert pa.variant_name(shape(), 128, 16) == "pa_decode_mfmapv_d128_g4_w4"
+    assert pa.variant_name(shape(num_q_heads=2), 128, 16) == "pa_decode_mfma_d128_g1_w4"
+    monkeypatch.setenv("PA_DECODE_PATH", "mfma_pv")
+    assert pa.variant_name(shape(num_q_heads=2), 64, 16) == "pa_decode_mfmapv_d64_g1_w4"
     monkeypatch.setenv("PA_DECODE_PATH", "mfma")
     monkeypatch.setenv("PA_DECODE_WAVES", "4")
     assert pa.variant_name(shape(), 128, 16) == "pa_decode_mfma_d128_g4_w4"
@@ -102,6 +109,7 @@ def test_decode_rejects_shape(kw, expect):
 
 
 @pytest.mark.parametrize("var,val", [("PA_DECODE_PATH", "VALU"), ("PA_DECODE_PATH", "auto"),
+                                     ("PA_DECODE_PATH", "mfmapv"), ("PA_DECODE_PATH", "mfma_pv "),
                                      ("PA_DECODE_WAVES", "3"), ("PA_DECODE_WAVES", "4 "),
                                      ("PA_DECODE_WAVES", "")])
 def test_tuning_variables_are_parsed_strictly(var, val, monkeypatch):

@@ -25,9 +25,10 @@ def gpu_present():
     assert name.startswith("gfx950"), name
 
 
-@pytest.fixture(params=["mfma", "valu"])
+@pytest.fixture(params=["mfma_pv", "mfma", "valu"])
 def qk_path(request, monkeypatch):
-    """Run the test on both QK^T paths (matrix cores / vector ALUs)."""
+    """Run the test on every score path: q.k and P.V on the matrix cores, q.k on the matrix
+    cores with P.V on the vector ALUs, both on the vector ALUs."""
     monkeypatch.setenv("PA_DECODE_PATH", request.param)
     return request.param
 
@@ -73,7 +74,7 @@ def test_config2_both_paths_and_wave_counts(monkeypatch):
     wl = make_config(2)
     t = to_dev(wl)
     exp = oracle_full(wl)
-    for path in ("valu", "mfma"):
+    for path in ("valu", "mfma", "mfma_pv"):
         for waves in ("1", "2", "4", "8"):
             monkeypatch.setenv("PA_DECODE_PATH", path)
             monkeypatch.setenv("PA_DECODE_WAVES", waves)
@@ -349,9 +350,10 @@ def test_config2_balanced_valu_and_poisoned(monkeypatch):
     wl = make_config(2, poison=True)
     t = to_dev(wl)
     exp = oracle_full(wl)
-    compare(*run_gpu(wl, t, partition_size=BALANCED), *exp, "cfg2 balanced poisoned mfma")
-    monkeypatch.setenv("PA_DECODE_PATH", "valu")
-    compare(*run_gpu(wl, t, partition_size=BALANCED), *exp, "cfg2 balanced poisoned valu")
+    compare(*run_gpu(wl, t, partition_size=BALANCED), *exp, "cfg2 balanced poisoned default")
+    for path in ("mfma", "valu"):
+        monkeypatch.setenv("PA_DECODE_PATH", path)
+        compare(*run_gpu(wl, t, partition_size=BALANCED), *exp, f"cfg2 balanced poisoned {path}")
 
 
 @pytest.mark.parametrize("D,hq", SWEEP_POINTS)
