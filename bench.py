@@ -98,6 +98,100 @@ def copy_mode(args, torch, debug, dev) -> int:
     return 0
 
 
+def latency_mode(args, torch, pa, dev) -> int:
+    """Small-batch latency rows (not the headline): the tiny workload and the two context shapes
+    (32 q / 4 KV heads, D 128, bs 16, B1 L2048 and B4 L4096), each schedule run three ways:
+    the eager binding (checks + launches per call), a prepared plan, and a HIP graph replaying
+    the plan's launches.  Prints one JSON line with a row per (shape, schedule)."""
+    import numpy as np
+
+    from workloads import make_config, make_workload
+
+    shapes = [("tiny B2 L{37,100} 4q/2kv", make_config(1))]
+    for B, L in ((1, 2048), (4, 4096)):
+        shapes.append((f"context B{B} L{L} 32q/4kv D128 bs16",
+                       make_workload(name="context", seq_lens=[L] * B, num_q_heads=32,
+                                     num_kv_heads=4, head_dim=128, block_size=16,
+                                     seed=[11, B, L])))
+    K = args.steps
+    rows = []
+    for label, wl in shapes:
+        def up(a):
+            a = np.ascontiguousarray(a)
+            return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+        q, k, v, bt, L = up(wl.q), up(wl.k_cache), up(wl.v_cache), up(wl.block_table), \
+            up(wl.seq_lens)
+        B, Hq, D = wl.q.shape
+        maxL = int(wl.seq_lens.max())
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        for sched in ("unsplit", "partitioned", "balanced"):
+            P = 256 if sched == "partitioned" else 0
+            plan = pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
+                           schedule=sched, partition_size=P, max_seq_len=maxL)
+            ws = plan.workspace(dev)
+            if ws is not None:
+                ws.zero_()
+            pmax = pa.num_partitions(maxL, P) if P else 0
+            if P:
+                part = torch.empty((B, Hq, pmax, D), dtype=torch.float32, device=dev)
+                plse = torch.empty((B, Hq, pmax), dtype=torch.float32, device=dev)
+            bws = torch.zeros(plan.workspace_size if sched == "balanced" else 1,
+                              dtype=torch.uint8, device=dev)
+
+            def eager():
+                if sched == "unsplit":
+                    pa.decode(q, k, v, bt, L, float(wl.scale), out=out, lse=lse)
+                elif sched == "partitioned":
+                    pa.decode(q, k, v, bt, L, float(wl.scale), partition_size=P,
+                              max_partitions=pmax, out=part, lse=plse)
+                    pa.reduce(part, plse, L, partition_size=P, out=out, lse=lse)
+                else:
+                    pa.decode_balanced(q, k, v, bt, L, float(wl.scale), out=out, lse=lse,
+                                       workspace=bws)
+
+            def planned():
+                plan.run(q, k, v, bt, L, float(wl.scale), out=out, lse=lse, workspace=ws)
+
+            res = {"shape": label, "schedule": sched, "variant": plan.name}
+            for name, fn in (("eager", eager), ("plan", planned)):
+                for _ in range(10):
+                    fn()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(K):
+                    fn()
+                t1 = time.perf_counter()
+                torch.cuda.synchronize()
+                t2 = time.perf_counter()
+                res[f"{name}_host_us_per_call"] = round((t1 - t0) / K * 1e6, 2)
+                res[f"{name}_us_per_step"] = round((t2 - t0) / K * 1e6, 2)
+            # a graph of 20 consecutive steps, replayed
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                planned()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(20):
+                    planned()
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, K // 20)
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            res["graph_us_per_step"] = round((time.perf_counter() - t0) / (reps * 20) * 1e6, 2)
+            res["kv_bytes_per_step"] = wl.kv_bytes()
+            rows.append(res)
+            print(f"[latency] {res}", file=sys.stderr, flush=True)
+    print(json.dumps({"mode": "latency", "steps": K, "rows": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,8 +210,9 @@ def main() -> int:
                     help="balanced schedule: persistent workers (0 = device default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=None)
-    ap.add_argument("--mode", choices=["decode", "copy"], default="decode",
-                    help="copy: run only the plain copy kernel on --bytes (counter calibration)")
+    ap.add_argument("--mode", choices=["decode", "copy", "latency"], default="decode",
+                    help="copy: run only the plain copy kernel on --bytes (counter calibration); "
+                         "latency: small-batch rows, eager vs prepared plan vs graph replay")
     ap.add_argument("--bytes", type=int, default=1 << 30)
     args = ap.parse_args()
 
@@ -141,6 +236,8 @@ def main() -> int:
 
     if args.mode == "copy":
         return copy_mode(args, torch, debug, dev)
+    if args.mode == "latency":
+        return latency_mode(args, torch, pa, dev)
 
     kw = {}
     if args.config == 3:

@@ -205,6 +205,72 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
                                           int32_t max_seq_len, int32_t block_size,
                                           int32_t num_cus);
 
+/*
+ * Prepared decode (a "plan"): every check, the variant choice and the launch geometry are done
+ * once by paged_attn_plan_create; paged_attn_plan_run then only fills the pointers and launches
+ * the kernels of one whole step (decode, plus the merge for a split schedule), so a step costs
+ * one call with no validation, no environment lookups and no device queries.  This is the
+ * small-batch latency path: at one to four sequences the device work is a few microseconds and
+ * host preparation dominates, the problem ROCm/rocm-libraries PR #13700 "prepare saved paged
+ * decode bindings once" (Summary, and its host-overhead measurements at B = 1 and 4) prepares
+ * paged-decode bindings once for.  A run records nothing but kernel launches on `stream`, so it
+ * can be captured into a HIP graph and replayed.
+ *
+ *   schedule       PA_SCHEDULE_UNSPLIT (one workgroup per sequence and KV head; requires
+ *                  shape->partition_size == 0), PA_SCHEDULE_PARTITIONED (fixed partitions of
+ *                  shape->partition_size tokens, shape->max_partitions slots, then the reduce),
+ *                  or PA_SCHEDULE_BALANCED (persistent workers, then the fix-up merge).
+ *   max_seq_len    host-side upper bound on the lengths the plan will see, or 0 if unknown.
+ *                  Balanced plans launch no more workers than that many tiles can keep busy
+ *                  (a small batch then does not pay for thousands of idle workers); a length
+ *                  above the bound still gives correct results, only fewer workers.
+ *   num_workers    balanced only: 0 = paged_attn_balanced_default_workers (queries the current
+ *                  device at creation), else 1 .. 2^20.
+ *   plan           receives a host-memory object owned by the caller until
+ *                  paged_attn_plan_destroy.  A plan is immutable: several threads may run it at
+ *                  once, each with its own workspace and outputs.
+ *
+ * Errors at creation are those of paged_attn_decode / paged_attn_decode_balanced for the same
+ * arguments (PA_ERR_SHAPE for a schedule that does not match the shape, PA_ERR_NULL for a NULL
+ * plan pointer).
+ */
+typedef struct pa_plan pa_plan;
+
+enum {
+  PA_SCHEDULE_UNSPLIT = 0,
+  PA_SCHEDULE_PARTITIONED = 1,
+  PA_SCHEDULE_BALANCED = 2
+};
+
+pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,
+                                 int32_t window, int32_t schedule, int32_t max_seq_len,
+                                 int32_t num_workers, pa_plan** plan);
+
+/* Device workspace bytes a run needs (0 for the unsplit schedule): the partition partials and
+ * their LSEs, or the balanced workspace.  Caller-owned, 256-byte aligned, contents need no
+ * initialisation; runs that overlap in time need separate workspaces. */
+int64_t paged_attn_plan_workspace_size(const pa_plan* plan);
+
+/*
+ * One decode step with a plan: the operation of paged_attn_decode (+ paged_attn_reduce) on the
+ * sizes fixed at creation.  Pointers, layouts and the scale / sinks / lse conventions are those
+ * of paged_attn_decode; out is always the final fp32 [B][Hq][head_dim] and lse the final
+ * [B][Hq] (or NULL).  Returns PA_ERR_NULL for a missing pointer (workspace included when the
+ * plan needs one), PA_ERR_SHAPE for a non-finite scale or a misaligned workspace, and
+ * PA_ERR_LAUNCH when HIP rejects a launch.  Bad tables and lengths are reported as NaN, as for
+ * paged_attn_decode.
+ */
+pa_status paged_attn_plan_run(const pa_plan* plan, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, float scale, const float* sinks,
+                              float* out, float* lse, void* workspace, void* stream);
+
+/* Kernel variants a run launches (static storage owned by the plan). */
+const char* paged_attn_plan_name(const pa_plan* plan);
+
+/* Frees a plan (NULL is a no-op).  No run may be in progress on the host. */
+void paged_attn_plan_destroy(pa_plan* plan);
+
 /* ABI version, bumped on any incompatible change. */
 int32_t paged_attn_abi_version(void);
 

@@ -66,6 +66,12 @@ def _load() -> ctypes.CDLL:
                                              ctypes.c_size_t, i32, vp]),
         "paged_attn_balanced_workspace_size": (ctypes.c_int64, [sp, i32, i32]),
         "paged_attn_balanced_default_workers": (i32, [i32, i32]),
+        "paged_attn_plan_create": (i32, [sp, i32, i32, i32, i32, i32, i32,
+                                         ctypes.POINTER(vp)]),
+        "paged_attn_plan_workspace_size": (ctypes.c_int64, [vp]),
+        "paged_attn_plan_run": (i32, [vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp]),
+        "paged_attn_plan_name": (ctypes.c_char_p, [vp]),
+        "paged_attn_plan_destroy": (None, [vp]),
         "paged_attn_gather_witness": (i32, [sp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]),
         "paged_attn_stream_read": (i32, [vp, ctypes.c_size_t, i32, vp, vp]),
         "paged_attn_copy": (i32, [vp, vp, ctypes.c_size_t, vp]),
@@ -85,7 +91,9 @@ EXPORTED = ("paged_attn_decode", "paged_attn_reduce", "paged_attn_decode_balance
             "paged_attn_num_partitions",
             "paged_attn_variant_name", "paged_attn_status_string", "paged_attn_check_tables",
             "paged_attn_suggest_partition_size", "paged_attn_abi_version",
-            "paged_attn_gather_witness", "paged_attn_stream_read", "paged_attn_copy")
+            "paged_attn_gather_witness", "paged_attn_stream_read", "paged_attn_copy",
+            "paged_attn_plan_create", "paged_attn_plan_workspace_size", "paged_attn_plan_run",
+            "paged_attn_plan_name", "paged_attn_plan_destroy")
 
 
 def lib() -> ctypes.CDLL:
@@ -343,3 +351,70 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, scale, *, window
                         stream=stream)
     return reduce(part, plse, seq_lens, partition_size=partition_size, want_lse=want_lse,
                   stream=stream)
+
+
+SCHEDULES = {"unsplit": 0, "partitioned": 1, "balanced": 2}
+
+
+class Plan:
+    """A prepared decode step (paged_attn_plan_*): checks, variant choice and launch geometry
+    done once; run() fills pointers and launches decode (+ merge).  ``schedule`` is "unsplit",
+    "partitioned" (``partition_size`` tokens, partition slots for ``max_seq_len``) or
+    "balanced" (``num_workers``, 0 = the device default; ``max_seq_len``, a bound on the
+    lengths, caps the workers of a small batch).  run() records only kernel launches on the
+    stream, so it can be captured in a CUDA/HIP graph."""
+
+    def __init__(self, num_seqs: int, num_q_heads: int, num_kv_heads: int, num_blocks: int,
+                 block_table_stride: int, head_dim: int, block_size: int, *, window: int = 0,
+                 schedule: str = "balanced", partition_size: int = 0,
+                 max_seq_len: Optional[int] = None, num_workers: int = 0):
+        if schedule not in SCHEDULES:
+            raise ValueError(f"schedule must be one of {sorted(SCHEDULES)}")
+        pmax = 0
+        if schedule == "partitioned":
+            if partition_size <= 0 or max_seq_len is None:
+                raise ValueError("the partitioned schedule needs partition_size and max_seq_len")
+            pmax = num_partitions(int(max_seq_len), int(partition_size))
+        else:
+            partition_size = 0
+        self.shape = make_shape(num_seqs, num_q_heads, num_kv_heads, num_blocks,
+                                block_table_stride, partition_size, pmax)
+        self.dims = (num_seqs, num_q_heads, head_dim)
+        self._h = ctypes.c_void_p()
+        st = _lib.paged_attn_plan_create(ctypes.byref(self.shape), int(head_dim), int(block_size),
+                                         int(window), SCHEDULES[schedule],
+                                         int(max_seq_len or 0), int(num_workers),
+                                         ctypes.byref(self._h))
+        if st != PA_OK:
+            raise PagedAttnError(st, "paged_attn_plan_create")
+        self.workspace_size = int(_lib.paged_attn_plan_workspace_size(self._h))
+        self.name = _lib.paged_attn_plan_name(self._h).decode()
+
+    def workspace(self, device) -> Optional[torch.Tensor]:
+        """A workspace tensor of the size the plan needs (None when it needs none)."""
+        if self.workspace_size == 0:
+            return None
+        return torch.empty(self.workspace_size, dtype=torch.uint8, device=device)
+
+    def run(self, q, k_cache, v_cache, block_table, seq_lens, scale: float, *, out, lse=None,
+            sinks=None, workspace=None, stream=None) -> None:
+        """One step into the caller's ``out`` (fp32 [B][Hq][D]) and ``lse`` (fp32 [B][Hq] or
+        None).  Pointers only: the tensors must match the sizes the plan was made for (only
+        their being on the GPU is checked here)."""
+        for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                        ("block_table", block_table), ("seq_lens", seq_lens), ("out", out),
+                        ("lse", lse), ("sinks", sinks), ("workspace", workspace)):
+            if t is not None and not t.is_cuda:
+                raise ValueError(f"{name} must be a GPU tensor")
+        st = _lib.paged_attn_plan_run(self._h, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(block_table), _ptr(seq_lens), float(scale),
+                                      _ptr(sinks), _ptr(out), _ptr(lse), _ptr(workspace),
+                                      _stream(out.device, stream))
+        if st != PA_OK:
+            raise PagedAttnError(st, "paged_attn_plan_run")
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.paged_attn_plan_destroy(h)
+            self._h = ctypes.c_void_p()

@@ -15,6 +15,7 @@
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
+#include <new>
 
 #include "../../include/paged_attn.h"
 #include "../../include/paged_attn_debug.h"
@@ -22,7 +23,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 constexpr int32_t kMaxGridYZ = 65535;
 
 int log2_exact(int32_t v) {
@@ -434,6 +435,192 @@ pa_status paged_attn_copy(void* dst, const void* src, size_t bytes, void* stream
   if (dst == nullptr || src == nullptr) return PA_ERR_NULL;
   if (bytes % 16 != 0) return PA_ERR_SHAPE;
   const hipError_t e = pa::launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// Prepared decode (plans)
+// ---------------------------------------------------------------------------------------------
+struct pa_plan {
+  int32_t schedule;
+  int32_t head_dim, group, waves, num_workers;
+  pa::QkPath path;
+  pa::DecodeParams dec;   // sizes; pointers are filled per run
+  pa::ReduceParams red;   // partitioned schedule: sizes
+  size_t part_bytes;      // partitioned: partials, then their LSEs
+  WsLayout bal;           // balanced workspace layout
+  int64_t workspace_bytes;
+  char name[128];
+};
+
+namespace {
+
+pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size, int32_t window,
+                     int32_t schedule, int32_t max_seq_len, int32_t num_workers, pa_plan* pl) {
+  const pa_status st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  const int group = shape->num_q_heads / shape->num_kv_heads;
+  if (!pa::decode_supported(head_dim, group)) return PA_ERR_UNSUPPORTED;
+  if (window < 0 || max_seq_len < 0) return PA_ERR_SHAPE;
+  if (schedule == PA_SCHEDULE_UNSPLIT && shape->partition_size != 0) return PA_ERR_SHAPE;
+  if (schedule == PA_SCHEDULE_PARTITIONED && shape->partition_size <= 0) return PA_ERR_SHAPE;
+  if (schedule != PA_SCHEDULE_UNSPLIT && schedule != PA_SCHEDULE_PARTITIONED &&
+      schedule != PA_SCHEDULE_BALANCED)
+    return PA_ERR_SHAPE;
+  if (schedule == PA_SCHEDULE_PARTITIONED && shape->num_q_heads > kMaxGridYZ * 32)
+    return PA_ERR_SHAPE;
+  if (schedule == PA_SCHEDULE_BALANCED &&
+      ((int64_t)shape->num_seqs * shape->num_q_heads > 0x7FFFFFFF || num_workers < 0 ||
+       num_workers > kMaxWorkers))
+    return PA_ERR_SHAPE;
+  pa::QkPath path;
+  if (decode_path(head_dim, group, &path) != 0) return PA_ERR_UNSUPPORTED;
+  const int waves = decode_waves(head_dim, group,
+                                 schedule == PA_SCHEDULE_PARTITIONED ? shape->partition_size : 0);
+  if (waves < 0) return PA_ERR_UNSUPPORTED;
+
+  pl->schedule = schedule;
+  pl->head_dim = head_dim;
+  pl->group = group;
+  pl->waves = waves;
+  pl->path = path;
+  pl->num_workers = 0;
+  pl->part_bytes = 0;
+  pl->workspace_bytes = 0;
+  pa::DecodeParams& p = pl->dec;
+  p = pa::DecodeParams{};
+  p.num_seqs = shape->num_seqs;
+  p.num_q_heads = shape->num_q_heads;
+  p.num_kv_heads = shape->num_kv_heads;
+  p.num_blocks = shape->num_blocks;
+  p.stride = shape->block_table_stride;
+  p.bs_log2 = log2_exact(block_size);
+  p.window = window;
+  p.psize = schedule == PA_SCHEDULE_PARTITIONED ? shape->partition_size : 0;
+  p.max_parts = schedule == PA_SCHEDULE_PARTITIONED ? shape->max_partitions : 1;
+  pl->red = pa::ReduceParams{};
+  const char* dname = pa::decode_variant_name(head_dim, group, waves,
+                                              schedule == PA_SCHEDULE_PARTITIONED, path);
+  if (schedule == PA_SCHEDULE_UNSPLIT) {
+    std::snprintf(pl->name, sizeof(pl->name), "%s", dname);
+  } else if (schedule == PA_SCHEDULE_PARTITIONED) {
+    const size_t rows = (size_t)shape->num_seqs * shape->num_q_heads * shape->max_partitions;
+    pl->part_bytes = align256(rows * head_dim * sizeof(float));
+    pl->workspace_bytes = (int64_t)(pl->part_bytes + align256(rows * sizeof(float)));
+    pl->red.num_q_heads = shape->num_q_heads;
+    pl->red.psize = shape->partition_size;
+    pl->red.max_parts = shape->max_partitions;
+    std::snprintf(pl->name, sizeof(pl->name), "%s + pa_reduce_d%d", dname, head_dim);
+  } else {
+    if (num_workers == 0) {
+      num_workers = pa::balanced_default_workers(head_dim, group, path);
+      if (num_workers <= 0) return PA_ERR_LAUNCH;
+    }
+    if (max_seq_len > 0) {
+      // at most this many 16-token tiles (a window start may add one), four per worker
+      const int64_t span = window > 0 && window < max_seq_len ? window : max_seq_len;
+      const int64_t tiles = (int64_t)shape->num_seqs * shape->num_kv_heads * ((span + 15) / 16 + 1);
+      const int64_t cap = (tiles + 3) / 4;
+      if (cap < num_workers) num_workers = (int32_t)(cap < 1 ? 1 : cap);
+    }
+    pl->num_workers = num_workers;
+    pl->bal = ws_layout(shape->num_seqs, group, head_dim, num_workers);
+    pl->workspace_bytes = (int64_t)pl->bal.total;
+    std::snprintf(pl->name, sizeof(pl->name), "pa_balanced_%s_d%d_g%d_workers%d + fixup",
+                  pa::qk_path_name(path), head_dim, group, num_workers);
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,
+                                 int32_t window, int32_t schedule, int32_t max_seq_len,
+                                 int32_t num_workers, pa_plan** plan) {
+  if (plan == nullptr) return PA_ERR_NULL;
+  *plan = nullptr;
+  pa_plan* pl = new (std::nothrow) pa_plan;
+  if (pl == nullptr) return PA_ERR_LAUNCH;
+  const pa_status st =
+      plan_build(shape, head_dim, block_size, window, schedule, max_seq_len, num_workers, pl);
+  if (st != PA_OK) {
+    delete pl;
+    return st;
+  }
+  *plan = pl;
+  return PA_OK;
+}
+
+int64_t paged_attn_plan_workspace_size(const pa_plan* plan) {
+  return plan == nullptr ? PA_ERR_NULL : plan->workspace_bytes;
+}
+
+const char* paged_attn_plan_name(const pa_plan* plan) {
+  return plan == nullptr ? nullptr : plan->name;
+}
+
+void paged_attn_plan_destroy(pa_plan* plan) { delete plan; }
+
+pa_status paged_attn_plan_run(const pa_plan* plan, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, float scale, const float* sinks,
+                              float* out, float* lse, void* workspace, void* stream) {
+  if (plan == nullptr) return PA_ERR_NULL;
+  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (plan->dec.num_seqs == 0) return PA_OK;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+      seq_lens == nullptr || out == nullptr)
+    return PA_ERR_NULL;
+  if (plan->workspace_bytes > 0) {
+    if (workspace == nullptr) return PA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PA_ERR_SHAPE;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  pa::DecodeParams p = plan->dec;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const char*>(k_cache);
+  p.v_cache = static_cast<const char*>(v_cache);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.sinks = sinks;
+  p.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
+  hipError_t e = hipSuccess;
+  if (plan->schedule == PA_SCHEDULE_UNSPLIT) {
+    p.out = out;
+    p.lse = lse;
+    e = pa::launch_decode(p, plan->head_dim, plan->group, plan->waves, plan->path, s);
+  } else if (plan->schedule == PA_SCHEDULE_PARTITIONED) {
+    char* ws = static_cast<char*>(workspace);
+    p.out = reinterpret_cast<float*>(ws);
+    p.lse = reinterpret_cast<float*>(ws + plan->part_bytes);
+    e = pa::launch_decode(p, plan->head_dim, plan->group, plan->waves, plan->path, s);
+    if (e == hipSuccess) {
+      pa::ReduceParams r = plan->red;
+      r.partials = p.out;
+      r.lse_partials = p.lse;
+      r.seq_lens = seq_lens;
+      r.out = out;
+      r.lse = lse;
+      e = pa::launch_reduce(r, plan->head_dim, plan->dec.num_seqs, s);
+    }
+  } else {
+    char* ws = static_cast<char*>(workspace);
+    pa::BalancedParams bp{};
+    bp.d = p;
+    bp.d.out = out;
+    bp.d.lse = lse;
+    bp.prefix = reinterpret_cast<int64_t*>(ws + plan->bal.prefix);
+    bp.ws_lse = reinterpret_cast<float*>(ws + plan->bal.lse);
+    bp.ws_o = reinterpret_cast<float*>(ws + plan->bal.o);
+    bp.num_workers = plan->num_workers;
+    e = pa::launch_balanced(bp, plan->head_dim, plan->group, plan->path, s);
+    if (e == hipSuccess) e = pa::launch_balanced_fixup(bp, plan->head_dim, plan->group, s);
+  }
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

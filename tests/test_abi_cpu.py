@@ -6,6 +6,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import paged_kv_attention_attn_amd as pa
 
@@ -33,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert pa.abi_version() == 1
+    assert pa.abi_version() == 2
     for code, name in pa.STATUS_NAMES.items():
         s = pa.status_string(code)
         assert s and s != "unknown status", name
@@ -230,3 +231,92 @@ def test_balanced_rejects(kw, expect):
 
 def test_balanced_empty_batch_is_ok_without_launch():
     assert call_balanced(shape(num_seqs=0), ws=None, out=None) == 0
+
+
+# ---------------------------------------------------------------------------------------------
+# prepared decode (plans): creation-time checks, workspace sizes, run-time argument checks
+# ---------------------------------------------------------------------------------------------
+def plan_create(s, *, head_dim=128, block_size=16, window=0, schedule=0, workers=0, max_len=0):
+    h = ctypes.c_void_p()
+    st = pa.lib().paged_attn_plan_create(ctypes.byref(s), head_dim, block_size, window, schedule,
+                                         max_len, workers, ctypes.byref(h))
+    return st, h
+
+
+def test_plan_create_and_workspace_sizes():
+    a = lambda x: (x + 255) // 256 * 256
+    st, h = plan_create(shape())
+    assert st == 0 and h.value
+    assert pa.lib().paged_attn_plan_workspace_size(h) == 0
+    assert pa.lib().paged_attn_plan_name(h).decode().startswith("pa_decode_")
+    pa.lib().paged_attn_plan_destroy(h)
+    s = shape(partition_size=512, max_partitions=4)
+    st, h = plan_create(s, schedule=1)
+    assert st == 0
+    rows = 2 * 8 * 4
+    assert pa.lib().paged_attn_plan_workspace_size(h) == a(rows * 128 * 4) + a(rows * 4)
+    assert b"pa_reduce" in pa.lib().paged_attn_plan_name(h)
+    pa.lib().paged_attn_plan_destroy(h)
+    st, h = plan_create(shape(), schedule=2, workers=100)
+    assert st == 0
+    assert pa.lib().paged_attn_plan_workspace_size(h) == pa.balanced_workspace_size(shape(), 128,
+                                                                                     100)
+    assert b"workers100" in pa.lib().paged_attn_plan_name(h)
+    pa.lib().paged_attn_plan_destroy(h)
+    # a length bound caps the workers: 2 seqs x 2 KV heads x (7 + 1) tiles / 4 = 8
+    st, h = plan_create(shape(), schedule=2, workers=100, max_len=100)
+    assert st == 0 and b"workers8 " in pa.lib().paged_attn_plan_name(h)
+    pa.lib().paged_attn_plan_destroy(h)
+    pa.lib().paged_attn_plan_destroy(None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(schedule=1), -2),                      # partitioned without a partition size
+    (dict(schedule=3), -2), (dict(schedule=-1), -2),
+    (dict(head_dim=96), -3), (dict(block_size=8), -3), (dict(window=-1), -2),
+    (dict(schedule=2, workers=-1), -2), (dict(schedule=2, workers=(1 << 20) + 1), -2),
+    (dict(max_len=-1), -2),
+])
+def test_plan_create_rejects(kw, expect):
+    st, h = plan_create(shape(), **kw)
+    assert st == expect and not h.value
+
+
+def test_plan_unsplit_rejects_a_partitioned_shape_and_null_out_pointer():
+    st, h = plan_create(shape(partition_size=512, max_partitions=4), schedule=0)
+    assert st == -2
+    s = shape()
+    assert pa.lib().paged_attn_plan_create(ctypes.byref(s), 128, 16, 0, 0, 0, 0, None) == -1
+
+
+def test_plan_run_argument_checks_without_launch():
+    lib = pa.lib()
+    st, h = plan_create(shape(), schedule=2, workers=64)
+    assert st == 0
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, None, FAKE, None, FAKE, None]
+    assert lib.paged_attn_plan_run(None, *args) == -1
+    bad = list(args); bad[5] = float("inf")
+    assert lib.paged_attn_plan_run(h, *bad) == -2
+    for i in (0, 1, 2, 3, 4, 7):
+        bad = list(args); bad[i] = None
+        assert lib.paged_attn_plan_run(h, *bad) == -1, i
+    bad = list(args); bad[9] = None          # balanced plans need a workspace
+    assert lib.paged_attn_plan_run(h, *bad) == -1
+    bad = list(args); bad[9] = ctypes.c_void_p(0x1010)   # not 256-byte aligned
+    assert lib.paged_attn_plan_run(h, *bad) == -2
+    lib.paged_attn_plan_destroy(h)
+    st, h = plan_create(shape(num_seqs=0), schedule=2, workers=64)
+    assert st == 0 and lib.paged_attn_plan_run(h, *([None] * 5 + [0.1] + [None] * 5)) == 0
+    lib.paged_attn_plan_destroy(h)
+
+
+def test_plan_binding_refuses_host_tensors():
+    plan = pa.Plan(2, 8, 2, 32, 8, 128, 16, schedule="unsplit")
+    assert plan.workspace_size == 0 and plan.workspace("cpu") is None
+    x = torch.zeros(4)
+    with pytest.raises(ValueError):
+        plan.run(x, x, x, x, x, 0.1, out=x)
+    with pytest.raises(ValueError):
+        pa.Plan(2, 8, 2, 32, 8, 128, 16, schedule="partitioned")
+    with pytest.raises(ValueError):
+        pa.Plan(2, 8, 2, 32, 8, 128, 16, schedule="fast")

@@ -1,0 +1,136 @@
+"""GPU tests of prepared decode steps (plans): parity with the fp64 oracle through
+paged_attn_plan_run for every schedule, and HIP-graph capture and replay of a run."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_attn_amd as pa
+from workloads import make_config, make_workload
+
+from gpu_helpers import compare, log, oracle_full, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SCHEDULES = ["unsplit", "partitioned", "balanced"]
+
+
+def make_plan(wl, schedule, partition_size=256, num_workers=0):
+    B, Hq, D = wl.q.shape
+    return pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
+                   window=wl.window, schedule=schedule, partition_size=partition_size,
+                   max_seq_len=int(wl.seq_lens.max()) if wl.num_seqs else 0,
+                   num_workers=num_workers)
+
+
+def run_plan(plan, wl, t, workspace=None):
+    B, Hq, D = wl.q.shape
+    out = torch.full((B, Hq, D), float("nan"), device="cuda")
+    lse = torch.full((B, Hq), float("nan"), device="cuda")
+    ws = workspace if workspace is not None else plan.workspace("cuda")
+    if ws is not None and workspace is None:
+        ws.fill_(0xFF)   # stale workspace contents must not matter
+    plan.run(t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale), out=out, lse=lse,
+             sinks=t["sinks"], workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def context_workload(B, L):
+    """The small-batch context shapes: 32 q / 4 KV heads, D 128, block size 16."""
+    return make_workload(name=f"context B{B} L{L}", seq_lens=[L] * B, num_q_heads=32,
+                         num_kv_heads=4, head_dim=128, block_size=16, seed=[11, B, L],
+                         poison=True)
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_plan_config1(schedule):
+    wl = make_config(1, poison=True)
+    plan = make_plan(wl, schedule, partition_size=32)
+    log(f"[plan] {plan.name}")
+    compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl), f"plan cfg1 {schedule}")
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_plan_config5_window_sinks(schedule):
+    wl = make_config(5, poison=True)
+    plan = make_plan(wl, schedule, partition_size=1024)
+    compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl), f"plan cfg5 {schedule}")
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("B,L", [(1, 2048), (4, 4096)])
+def test_plan_context_shapes(B, L, schedule):
+    wl = context_workload(B, L)
+    plan = make_plan(wl, schedule, partition_size=256)
+    compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl),
+            f"plan context B{B} L{L} {schedule}")
+
+
+def test_plan_empty_batch_is_a_no_op():
+    wl = make_config(1)
+    plan = pa.Plan(0, 4, 2, wl.num_blocks, wl.stride, 128, 16, schedule="balanced")
+    x = torch.zeros(1, device="cuda")
+    plan.run(x, x, x, x, x, 0.1, out=x, workspace=plan.workspace("cuda"))
+    torch.cuda.synchronize()
+    assert float(x.item()) == 0.0
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_plan_graph_replay(schedule):
+    """A run captured in a graph and replayed five times, with the inputs changed in place and
+    eager runs and synchronisations between replays: every replay equals the eager run bit for
+    bit, and one of them the oracle."""
+    wl = context_workload(4, 4096)
+    t = to_dev(wl)
+    plan = make_plan(wl, schedule, partition_size=256)
+    B, Hq, D = wl.q.shape
+    ws = plan.workspace("cuda")
+    out = torch.zeros((B, Hq, D), device="cuda")
+    lse = torch.zeros((B, Hq), device="cuda")
+    args = (t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.run(*args, out=out, lse=lse, workspace=ws)     # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.run(*args, out=out, lse=lse, workspace=ws)
+    q0 = t["q"].clone()
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    for r in range(5):
+        # new query values (bf16 bit patterns of N(0,1) draws), written in place
+        t["q"].copy_(torch.randn(q0.shape, device="cuda", generator=gen)
+                     .to(torch.bfloat16).view(torch.int16))
+        g.replay()
+        torch.cuda.synchronize()
+        got = (out.clone(), lse.clone())
+        ref_out = torch.full_like(out, float("nan"))
+        ref_lse = torch.full_like(lse, float("nan"))
+        ws_ref = plan.workspace("cuda")
+        plan.run(*args, out=ref_out, lse=ref_lse, workspace=ws_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ref_out) and torch.equal(got[1], ref_lse), f"replay {r}"
+        if r == 4:
+            wl.q[...] = t["q"].cpu().numpy().view(np.uint16)
+            compare(got[0].cpu().numpy().astype(np.float64),
+                    got[1].cpu().numpy().astype(np.float64), *oracle_full(wl),
+                    f"graph replay {schedule}")
+    t["q"].copy_(q0)
+
+
+def test_plan_length_bound_caps_workers_and_a_violated_bound_stays_correct():
+    wl = make_config(1, poison=True)
+    B, Hq, D = wl.q.shape
+    capped = pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
+                     schedule="balanced", max_seq_len=100)
+    assert "workers" in capped.name and int(capped.name.split("workers")[1].split()[0]) <= 8
+    low = pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
+                  schedule="balanced", max_seq_len=16)    # below the real lengths (37, 100)
+    t = to_dev(wl)
+    exp = oracle_full(wl)
+    compare(*run_plan(capped, wl, t), *exp, f"plan {capped.name}")
+    compare(*run_plan(low, wl, t), *exp, f"plan {low.name} (bound below the lengths)")
