@@ -125,8 +125,8 @@ def latency_mode(args, torch, pa, dev) -> int:
         maxL = int(wl.seq_lens.max())
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-        for sched in ("unsplit", "partitioned", "balanced"):
-            P = 256 if sched == "partitioned" else 0
+        for sched in ("unsplit", "partitioned", "fused", "balanced"):
+            P = 256 if sched in ("partitioned", "fused") else 0
             plan = pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
                            schedule=sched, partition_size=P, max_seq_len=maxL)
             ws = plan.workspace(dev)
@@ -136,13 +136,14 @@ def latency_mode(args, torch, pa, dev) -> int:
             if P:
                 part = torch.empty((B, Hq, pmax, D), dtype=torch.float32, device=dev)
                 plse = torch.empty((B, Hq, pmax), dtype=torch.float32, device=dev)
-            bws = torch.zeros(plan.workspace_size if sched == "balanced" else 1,
-                              dtype=torch.uint8, device=dev)
+            bws = torch.zeros(pa.balanced_workspace_size(
+                pa.make_shape(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride), D)
+                if sched == "balanced" else 1, dtype=torch.uint8, device=dev)
 
             def eager():
                 if sched == "unsplit":
                     pa.decode(q, k, v, bt, L, float(wl.scale), out=out, lse=lse)
-                elif sched == "partitioned":
+                elif sched in ("partitioned", "fused"):   # eager: decode + reduce
                     pa.decode(q, k, v, bt, L, float(wl.scale), partition_size=P,
                               max_partitions=pmax, out=part, lse=plse)
                     pa.reduce(part, plse, L, partition_size=P, out=out, lse=lse)

@@ -219,7 +219,11 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  *   schedule       PA_SCHEDULE_UNSPLIT (one workgroup per sequence and KV head; requires
  *                  shape->partition_size == 0), PA_SCHEDULE_PARTITIONED (fixed partitions of
  *                  shape->partition_size tokens, shape->max_partitions slots, then the reduce),
- *                  or PA_SCHEDULE_BALANCED (persistent workers, then the fix-up merge).
+ *                  PA_SCHEDULE_BALANCED (persistent workers, then the fix-up merge), or
+ *                  PA_SCHEDULE_PARTITIONED_FUSED (fixed partitions as PARTITIONED, merged in
+ *                  the same launch by whichever partition of a (sequence, KV head) finishes
+ *                  last: one kernel per step, for small batches; its device-scope release per
+ *                  partition makes it slow for large ones).
  *   max_seq_len    host-side upper bound on the lengths the plan will see, or 0 if unknown.
  *                  Balanced plans launch no more workers than that many tiles can keep busy
  *                  (a small batch then does not pay for thousands of idle workers); a length
@@ -239,7 +243,8 @@ typedef struct pa_plan pa_plan;
 enum {
   PA_SCHEDULE_UNSPLIT = 0,
   PA_SCHEDULE_PARTITIONED = 1,
-  PA_SCHEDULE_BALANCED = 2
+  PA_SCHEDULE_BALANCED = 2,
+  PA_SCHEDULE_PARTITIONED_FUSED = 3
 };
 
 pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,
@@ -247,8 +252,10 @@ pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_
                                  int32_t num_workers, pa_plan** plan);
 
 /* Device workspace bytes a run needs (0 for the unsplit schedule): the partition partials and
- * their LSEs, or the balanced workspace.  Caller-owned, 256-byte aligned, contents need no
- * initialisation; runs that overlap in time need separate workspaces. */
+ * their LSEs (plus one merge counter per (sequence, KV head) for the fused schedule), or the
+ * balanced workspace.  Caller-owned and 256-byte aligned.  A fused plan's workspace must be
+ * zero-filled before its first run; every run leaves its counters at zero again.  Other plans
+ * need no initialisation.  Runs that overlap in time need separate workspaces. */
 int64_t paged_attn_plan_workspace_size(const pa_plan* plan);
 
 /*

@@ -353,13 +353,14 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, scale, *, window
                   stream=stream)
 
 
-SCHEDULES = {"unsplit": 0, "partitioned": 1, "balanced": 2}
+SCHEDULES = {"unsplit": 0, "partitioned": 1, "balanced": 2, "fused": 3}
 
 
 class Plan:
     """A prepared decode step (paged_attn_plan_*): checks, variant choice and launch geometry
     done once; run() fills pointers and launches decode (+ merge).  ``schedule`` is "unsplit",
-    "partitioned" (``partition_size`` tokens, partition slots for ``max_seq_len``) or
+    "partitioned" (``partition_size`` tokens, partition slots for ``max_seq_len``), "fused"
+    (partitioned, merged in the same launch by the last partition to finish) or
     "balanced" (``num_workers``, 0 = the device default; ``max_seq_len``, a bound on the
     lengths, caps the workers of a small batch).  run() records only kernel launches on the
     stream, so it can be captured in a CUDA/HIP graph."""
@@ -371,9 +372,10 @@ class Plan:
         if schedule not in SCHEDULES:
             raise ValueError(f"schedule must be one of {sorted(SCHEDULES)}")
         pmax = 0
-        if schedule == "partitioned":
+        if schedule in ("partitioned", "fused"):
             if partition_size <= 0 or max_seq_len is None:
-                raise ValueError("the partitioned schedule needs partition_size and max_seq_len")
+                raise ValueError(f"the {schedule} schedule needs partition_size and "
+                                 "max_seq_len")
             pmax = num_partitions(int(max_seq_len), int(partition_size))
         else:
             partition_size = 0
@@ -391,10 +393,11 @@ class Plan:
         self.name = _lib.paged_attn_plan_name(self._h).decode()
 
     def workspace(self, device) -> Optional[torch.Tensor]:
-        """A workspace tensor of the size the plan needs (None when it needs none)."""
+        """A zero-filled workspace tensor of the size the plan needs (None when it needs
+        none)."""
         if self.workspace_size == 0:
             return None
-        return torch.empty(self.workspace_size, dtype=torch.uint8, device=device)
+        return torch.zeros(self.workspace_size, dtype=torch.uint8, device=device)
 
     def run(self, q, k_cache, v_cache, block_table, seq_lens, scale: float, *, out, lse=None,
             sinks=None, workspace=None, stream=None) -> None:

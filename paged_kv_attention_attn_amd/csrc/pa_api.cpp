@@ -450,6 +450,7 @@ struct pa_plan {
   pa::DecodeParams dec;   // sizes; pointers are filled per run
   pa::ReduceParams red;   // partitioned schedule: sizes
   size_t part_bytes;      // partitioned: partials, then their LSEs
+  size_t counter_off;     // fused: merge counters [B][Hkv] after the LSEs
   WsLayout bal;           // balanced workspace layout
   int64_t workspace_bytes;
   char name[128];
@@ -466,20 +467,19 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   if (!pa::decode_supported(head_dim, group)) return PA_ERR_UNSUPPORTED;
   if (window < 0 || max_seq_len < 0) return PA_ERR_SHAPE;
   if (schedule == PA_SCHEDULE_UNSPLIT && shape->partition_size != 0) return PA_ERR_SHAPE;
-  if (schedule == PA_SCHEDULE_PARTITIONED && shape->partition_size <= 0) return PA_ERR_SHAPE;
-  if (schedule != PA_SCHEDULE_UNSPLIT && schedule != PA_SCHEDULE_PARTITIONED &&
-      schedule != PA_SCHEDULE_BALANCED)
+  const bool parted =
+      schedule == PA_SCHEDULE_PARTITIONED || schedule == PA_SCHEDULE_PARTITIONED_FUSED;
+  if (parted && shape->partition_size <= 0) return PA_ERR_SHAPE;
+  if (!parted && schedule != PA_SCHEDULE_UNSPLIT && schedule != PA_SCHEDULE_BALANCED)
     return PA_ERR_SHAPE;
-  if (schedule == PA_SCHEDULE_PARTITIONED && shape->num_q_heads > kMaxGridYZ * 32)
-    return PA_ERR_SHAPE;
+  if (parted && shape->num_q_heads > kMaxGridYZ * 32) return PA_ERR_SHAPE;
   if (schedule == PA_SCHEDULE_BALANCED &&
       ((int64_t)shape->num_seqs * shape->num_q_heads > 0x7FFFFFFF || num_workers < 0 ||
        num_workers > kMaxWorkers))
     return PA_ERR_SHAPE;
   pa::QkPath path;
   if (decode_path(head_dim, group, &path) != 0) return PA_ERR_UNSUPPORTED;
-  const int waves = decode_waves(head_dim, group,
-                                 schedule == PA_SCHEDULE_PARTITIONED ? shape->partition_size : 0);
+  const int waves = decode_waves(head_dim, group, parted ? shape->partition_size : 0);
   if (waves < 0) return PA_ERR_UNSUPPORTED;
 
   pl->schedule = schedule;
@@ -489,6 +489,7 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   pl->path = path;
   pl->num_workers = 0;
   pl->part_bytes = 0;
+  pl->counter_off = 0;
   pl->workspace_bytes = 0;
   pa::DecodeParams& p = pl->dec;
   p = pa::DecodeParams{};
@@ -499,11 +500,10 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   p.stride = shape->block_table_stride;
   p.bs_log2 = log2_exact(block_size);
   p.window = window;
-  p.psize = schedule == PA_SCHEDULE_PARTITIONED ? shape->partition_size : 0;
-  p.max_parts = schedule == PA_SCHEDULE_PARTITIONED ? shape->max_partitions : 1;
+  p.psize = parted ? shape->partition_size : 0;
+  p.max_parts = parted ? shape->max_partitions : 1;
   pl->red = pa::ReduceParams{};
-  const char* dname = pa::decode_variant_name(head_dim, group, waves,
-                                              schedule == PA_SCHEDULE_PARTITIONED, path);
+  const char* dname = pa::decode_variant_name(head_dim, group, waves, parted, path);
   if (schedule == PA_SCHEDULE_UNSPLIT) {
     std::snprintf(pl->name, sizeof(pl->name), "%s", dname);
   } else if (schedule == PA_SCHEDULE_PARTITIONED) {
@@ -514,6 +514,13 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
     pl->red.psize = shape->partition_size;
     pl->red.max_parts = shape->max_partitions;
     std::snprintf(pl->name, sizeof(pl->name), "%s + pa_reduce_d%d", dname, head_dim);
+  } else if (schedule == PA_SCHEDULE_PARTITIONED_FUSED) {
+    const size_t rows = (size_t)shape->num_seqs * shape->num_q_heads * shape->max_partitions;
+    pl->part_bytes = align256(rows * head_dim * sizeof(float));
+    pl->counter_off = pl->part_bytes + align256(rows * sizeof(float));
+    pl->workspace_bytes = (int64_t)(pl->counter_off +
+                                    align256((size_t)shape->num_seqs * shape->num_kv_heads * 4));
+    std::snprintf(pl->name, sizeof(pl->name), "%s + merge by the last partition", dname);
   } else {
     if (num_workers == 0) {
       num_workers = pa::balanced_default_workers(head_dim, group, path);
@@ -593,6 +600,14 @@ pa_status paged_attn_plan_run(const pa_plan* plan, const void* q, const void* k_
   if (plan->schedule == PA_SCHEDULE_UNSPLIT) {
     p.out = out;
     p.lse = lse;
+    e = pa::launch_decode(p, plan->head_dim, plan->group, plan->waves, plan->path, s);
+  } else if (plan->schedule == PA_SCHEDULE_PARTITIONED_FUSED) {
+    char* ws = static_cast<char*>(workspace);
+    p.out = reinterpret_cast<float*>(ws);
+    p.lse = reinterpret_cast<float*>(ws + plan->part_bytes);
+    p.merge_counters = reinterpret_cast<uint32_t*>(ws + plan->counter_off);
+    p.final_out = out;
+    p.final_lse = lse;
     e = pa::launch_decode(p, plan->head_dim, plan->group, plan->waves, plan->path, s);
   } else if (plan->schedule == PA_SCHEDULE_PARTITIONED) {
     char* ws = static_cast<char*>(workspace);

@@ -219,6 +219,60 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
       if (d == 0 && p.lse != nullptr) p.lse[row] = lv;
     }
   }
+
+  // Merge in the same launch: every partition of (b, kvh) bumps its counter after releasing its
+  // partials to the device; the one that brings it to the partition count merges them all with
+  // the log-sum-exp rule (as the reduce kernel does) and puts the counter back to zero.
+  if (split && p.merge_counters != nullptr) {
+    __shared__ int s_last;
+    const int target = n_parts < p.max_parts ? n_parts : p.max_parts;
+    __syncthreads();   // every thread's partial stores happen before thread 0's release
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      uint32_t* ctr = p.merge_counters + (size_t)it.b * p.num_kv_heads + it.kvh;
+      const uint32_t old =
+          __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == (uint32_t)(target - 1);
+      if (last) {
+        __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+      s_last = last ? 1 : 0;
+    }
+    __syncthreads();   // thread 0's acquire happens before every thread's loads below
+    if (s_last) {
+      for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
+        const int h = i / D;
+        const int d = i - h * D;
+        const size_t row = (size_t)it.b * p.num_q_heads + h0 + h;
+        const float* lr = p.lse + row * p.max_parts;
+        float M = -INFINITY;
+        bool nan = false;
+        for (int q = 0; q < target; ++q) {
+          const float v = lr[q];
+          nan |= v != v;
+          M = fmaxf(M, v);
+        }
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float z = 0.f, o = 0.f;
+        for (int q = 0; q < target; ++q) {
+          const float li = lr[q];
+          if (!(li > -INFINITY)) continue;   // an empty partition (or NaN, reported)
+          const float f = fast_exp2((li - Mu) * kLog2e);
+          z += f;
+          o = fmaf(f, p.out[(row * p.max_parts + q) * D + d], o);
+        }
+        float ov = z > 0.f ? o / z : 0.f;
+        float lv = z > 0.f ? M + fast_log2(z) * kLn2 : -INFINITY;
+        if (nan) {
+          ov = __builtin_nanf("");
+          lv = __builtin_nanf("");
+        }
+        p.final_out[row * D + d] = ov;
+        if (d == 0 && p.final_lse != nullptr) p.final_lse[row] = lv;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -25,6 +25,12 @@ struct DecodeParams {
   int32_t window;
   int32_t psize;              // 0 = unsplit
   int32_t max_parts;          // split: partition slots; unsplit: 1
+  // Split only, optional: the last partition of each (sequence, KV head) to finish merges them
+  // all into final_out [B][Hq][D] / final_lse [B][Hq] (or null).  merge_counters [B][Hkv] are
+  // zero on entry and left zero.
+  uint32_t* merge_counters;
+  float* final_out;
+  float* final_lse;
 };
 
 // Balanced decode: persistent workers over the flattened tiles, partials in a workspace.

@@ -257,6 +257,12 @@ def test_plan_create_and_workspace_sizes():
     assert pa.lib().paged_attn_plan_workspace_size(h) == a(rows * 128 * 4) + a(rows * 4)
     assert b"pa_reduce" in pa.lib().paged_attn_plan_name(h)
     pa.lib().paged_attn_plan_destroy(h)
+    st, h = plan_create(s, schedule=3)
+    assert st == 0
+    assert pa.lib().paged_attn_plan_workspace_size(h) == \
+        a(rows * 128 * 4) + a(rows * 4) + a(2 * 2 * 4)
+    assert b"last partition" in pa.lib().paged_attn_plan_name(h)
+    pa.lib().paged_attn_plan_destroy(h)
     st, h = plan_create(shape(), schedule=2, workers=100)
     assert st == 0
     assert pa.lib().paged_attn_plan_workspace_size(h) == pa.balanced_workspace_size(shape(), 128,
@@ -272,7 +278,7 @@ def test_plan_create_and_workspace_sizes():
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(schedule=1), -2),                      # partitioned without a partition size
-    (dict(schedule=3), -2), (dict(schedule=-1), -2),
+    (dict(schedule=3), -2), (dict(schedule=4), -2), (dict(schedule=-1), -2),
     (dict(head_dim=96), -3), (dict(block_size=8), -3), (dict(window=-1), -2),
     (dict(schedule=2, workers=-1), -2), (dict(schedule=2, workers=(1 << 20) + 1), -2),
     (dict(max_len=-1), -2),

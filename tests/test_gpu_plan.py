@@ -13,7 +13,7 @@ from gpu_helpers import compare, log, oracle_full, to_dev
 
 pytestmark = pytest.mark.gpu
 
-SCHEDULES = ["unsplit", "partitioned", "balanced"]
+SCHEDULES = ["unsplit", "partitioned", "balanced", "fused"]
 
 
 def make_plan(wl, schedule, partition_size=256, num_workers=0):
@@ -24,16 +24,26 @@ def make_plan(wl, schedule, partition_size=256, num_workers=0):
                    num_workers=num_workers)
 
 
+def counter_bytes(wl):
+    """The fused schedule's merge counters: the last 256-byte-aligned section of its workspace."""
+    return (4 * wl.num_seqs * wl.num_kv_heads + 255) // 256 * 256
+
+
 def run_plan(plan, wl, t, workspace=None):
     B, Hq, D = wl.q.shape
+    fused = "last partition" in plan.name
     out = torch.full((B, Hq, D), float("nan"), device="cuda")
     lse = torch.full((B, Hq), float("nan"), device="cuda")
     ws = workspace if workspace is not None else plan.workspace("cuda")
     if ws is not None and workspace is None:
-        ws.fill_(0xFF)   # stale workspace contents must not matter
+        # stale contents must not matter (except the fused counters, which start at zero)
+        ws[:ws.numel() - (counter_bytes(wl) if fused else 0)].fill_(0xFF)
     plan.run(t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale), out=out, lse=lse,
              sinks=t["sinks"], workspace=ws)
     torch.cuda.synchronize()
+    if fused:
+        assert int(torch.count_nonzero(ws[ws.numel() - counter_bytes(wl):])) == 0, \
+            "merge counters not back at zero"
     return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
