@@ -29,6 +29,11 @@ Readings where the pages are silent (each is listed with its reason in the desig
   the attended range, a sequence has max(1, ceil(L/P)) of them, the sink is folded into the first
   non-empty one (floor(start/P)), and an empty partition has lse = -inf and o = 0;
   L = 0 gives out = 0 and lse = -inf (lse = sink with a sink).
+
+An FP8 KV cache (the 8-bit sibling of the bf16 path, named but not specified by the PR #13700
+page above) is read as OCP FP8 E4M3 codes with one fp32 scale for K and one for V: the real
+value of a stored code is its E4M3 value times the scale.  Everything after dequantisation is
+the same definition.
 """
 from __future__ import annotations
 
@@ -44,6 +49,29 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns (uint16) -> float64, exactly: bf16 is the top half of an fp32."""
     u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return u32.view(np.float32).astype(np.float64)
+
+
+def fp8_e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) -> float64, exactly.  A code is sign | 4-bit exponent (bias 7)
+    | 3-bit mantissa: exponent 0 is subnormal, m/8 * 2^-6; S.1111.111 is NaN; there are no
+    infinities (the largest finite magnitude is 1.75 * 2^8 = 448)."""
+    c = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) == 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def kv_rows_to_f64(rows: np.ndarray, kv_format: str, scale: float) -> np.ndarray:
+    """Gathered cache rows -> float64 values: bf16 bit patterns as they are, FP8 E4M3 codes
+    times the tensor's fp32 scale."""
+    if kv_format == "bf16":
+        return bf16_bits_to_f64(rows)
+    if kv_format == "fp8_e4m3":
+        return fp8_e4m3_bits_to_f64(rows) * float(np.float32(scale))
+    raise ValueError(f"unknown KV format {kv_format!r}")
 
 
 def kv_head_of(h: int, num_q_heads: int, num_kv_heads: int) -> int:
@@ -89,14 +117,17 @@ def softmax_attention(qv: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float
 def decode_one(wl_q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                block_table: np.ndarray, seq_lens: np.ndarray, scale: float, block_size: int,
                b: int, h: int, window: int = 0, sinks: Optional[np.ndarray] = None,
-               num_kv_heads: Optional[int] = None) -> Tuple[np.ndarray, float]:
+               num_kv_heads: Optional[int] = None, kv_format: str = "bf16",
+               k_scale: float = 1.0, v_scale: float = 1.0) -> Tuple[np.ndarray, float]:
     """Output row and LSE of query head h of sequence b."""
     Hq = wl_q.shape[1]
     Hkv = k_cache.shape[1] if num_kv_heads is None else num_kv_heads
     kvh = kv_head_of(h, Hq, Hkv)
     start, stop = attended_range(int(seq_lens[b]), window)
-    K = bf16_bits_to_f64(gather_rows(k_cache, block_table, b, kvh, start, stop, block_size))
-    V = bf16_bits_to_f64(gather_rows(v_cache, block_table, b, kvh, start, stop, block_size))
+    K = kv_rows_to_f64(gather_rows(k_cache, block_table, b, kvh, start, stop, block_size),
+                       kv_format, k_scale)
+    V = kv_rows_to_f64(gather_rows(v_cache, block_table, b, kvh, start, stop, block_size),
+                       kv_format, v_scale)
     qv = bf16_bits_to_f64(wl_q[b, h])
     sink = None if sinks is None else float(np.float32(sinks[h]))
     return softmax_attention(qv, K, V, float(np.float32(scale)), sink)
@@ -104,8 +135,10 @@ def decode_one(wl_q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
 
 def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
            seq_lens: np.ndarray, scale: float, block_size: int, window: int = 0,
-           sinks: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """Whole batch: out float64 [B][Hq][D], lse float64 [B][Hq]."""
+           sinks: Optional[np.ndarray] = None, kv_format: str = "bf16", k_scale: float = 1.0,
+           v_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+    """Whole batch: out float64 [B][Hq][D], lse float64 [B][Hq].  kv_format "bf16" (bit
+    patterns) or "fp8_e4m3" (codes, with k_scale / v_scale)."""
     B, Hq, D = q.shape
     Hkv = k_cache.shape[1]
     g = Hq // Hkv
@@ -119,10 +152,10 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table:
             kvh = kv_head_of(h, Hq, Hkv)
             if kvh not in rows:
                 rows[kvh] = (
-                    bf16_bits_to_f64(gather_rows(k_cache, block_table, b, kvh, start, stop,
-                                                 block_size)),
-                    bf16_bits_to_f64(gather_rows(v_cache, block_table, b, kvh, start, stop,
-                                                 block_size)))
+                    kv_rows_to_f64(gather_rows(k_cache, block_table, b, kvh, start, stop,
+                                               block_size), kv_format, k_scale),
+                    kv_rows_to_f64(gather_rows(v_cache, block_table, b, kvh, start, stop,
+                                               block_size), kv_format, v_scale))
             K, V = rows[kvh]
             sink = None if sinks is None else float(np.float32(sinks[h]))
             out[b, h], lse[b, h] = softmax_attention(bf16_bits_to_f64(q[b, h]), K, V, sc, sink)

@@ -75,9 +75,34 @@ MUTATIONS = {
 }
 
 
+_orig_rows = ref.kv_rows_to_f64
+
+
+def _fp8_bias_off_by_one(bits):
+    c = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 8))
+    return np.where((c >> 7) == 1, -1.0, 1.0) * np.where((e == 15) & (m == 7), np.nan, mag)
+
+
+def _fp8_scale_ignored(rows, kv_format, scale):
+    return _orig_rows(rows, kv_format, 1.0)
+
+
+MUTATIONS.update({
+    "fp8 exponent bias off by one": ("fp8_e4m3_bits_to_f64", _fp8_bias_off_by_one,
+                                     [(pins.test_fp8_e4m3_decoding_matches_torch,)]),
+    "fp8 scale ignored": ("kv_rows_to_f64", _fp8_scale_ignored,
+                          [(pins.test_fp8_scales_act_as_closed_forms,),
+                           (pins.test_fp8_attention_equals_bf16_attention_on_dequantized_values,)]),
+})
+
+
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     attr, bad, checks = MUTATIONS[name]
     monkeypatch.setattr(ref, attr, bad)
     caught = [_fails(c[0], *c[1:]) for c in checks]
     assert all(caught), f"mutation '{name}' escaped: {caught}"
+

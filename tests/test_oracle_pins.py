@@ -386,3 +386,62 @@ def test_config5_lengths():
     L = config_seq_lens(5)
     assert L.shape == (128,) and L.min() >= 1 and L.max() <= 32768
     assert 1200 < np.median(L) < 3500
+
+
+# ---------------------------------------------------------------------------------------------
+# FP8 E4M3 KV cache
+# ---------------------------------------------------------------------------------------------
+def test_fp8_e4m3_decoding_matches_torch():
+    """All 256 codes against torch's float8_e4m3fn (a library decoding of the OCP format)."""
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    mine = ref.fp8_e4m3_bits_to_f64(codes)
+    lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(lib))
+    ok = ~np.isnan(lib)
+    assert np.array_equal(mine[ok], lib[ok])
+    assert np.isnan(mine).sum() == 2 and mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9
+
+
+def _fp8_workload(scales, **kw):
+    d = dict(name="fp8", seq_lens=[37, 100, 1, 0], num_q_heads=8, num_kv_heads=2, head_dim=64,
+             block_size=16, seed=[41], kv_format="fp8_e4m3", kv_scales=scales)
+    d.update(kw)
+    return make_workload(**d)
+
+
+def _decode(wl, scale=None, **over):
+    kw = dict(window=wl.window, sinks=wl.sinks, kv_format=wl.kv_format, k_scale=wl.k_scale,
+              v_scale=wl.v_scale)
+    kw.update(over)
+    return ref.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens,
+                      wl.scale if scale is None else scale, wl.block_size, **kw)
+
+
+def test_fp8_attention_equals_bf16_attention_on_dequantized_values():
+    """With power-of-two scales every dequantised value is exact in bf16, so the FP8 path must
+    equal the bf16 definition applied to those values."""
+    wl = _fp8_workload((0.0625, 0.125), window=64, with_sinks=True)
+    o8, l8 = _decode(wl)
+    kb = f32_to_bf16_bits((ref.fp8_e4m3_bits_to_f64(wl.k_cache) * 0.0625).astype(np.float32))
+    vb = f32_to_bf16_bits((ref.fp8_e4m3_bits_to_f64(wl.v_cache) * 0.125).astype(np.float32))
+    assert np.array_equal(ref.bf16_bits_to_f64(kb), ref.fp8_e4m3_bits_to_f64(wl.k_cache) * 0.0625)
+    ob, lb = ref.decode(wl.q, kb, vb, wl.block_table, wl.seq_lens, wl.scale, wl.block_size,
+                        window=wl.window, sinks=wl.sinks)
+    np.testing.assert_allclose(o8, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l8, lb, rtol=0, atol=1e-12)
+
+
+def test_fp8_scales_act_as_closed_forms():
+    """v_scale multiplies the output and leaves the LSE alone; k_scale multiplies every logit,
+    which is the same as multiplying the attention scale."""
+    wl = _fp8_workload((1.0, 1.0))
+    o1, l1 = _decode(wl)
+    o2, l2 = _decode(wl, v_scale=0.5)
+    assert np.abs(o2 - 0.5 * o1).max() <= 1e-12
+    assert np.array_equal(l1, l2)
+    o3, l3 = _decode(wl, k_scale=0.25)
+    o4, l4 = _decode(wl, scale=np.float32(wl.scale) * np.float32(0.25))
+    np.testing.assert_allclose(o3, o4, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l3, l4, rtol=0, atol=1e-12)   # -inf for the empty sequence

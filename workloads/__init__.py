@@ -79,6 +79,34 @@ def normal_bf16(root: np.random.SeedSequence, stream: int, n: int, mult: float =
     return out
 
 
+FP8_E4M3_MAX = 448.0
+FP8_QNAN = np.uint8(0x7F)
+
+
+def normal_fp8_e4m3(root: np.random.SeedSequence, stream: int, n: int, mult: float,
+                    scale: float) -> np.ndarray:
+    """n OCP FP8 E4M3 codes of N(0,1)*mult / scale: the same fp32 draws as normal_bf16, divided
+    by the tensor scale, clipped to the format's range and rounded to nearest even by torch's
+    float8_e4m3fn conversion."""
+    import torch
+
+    out = np.empty(n, dtype=np.uint8)
+    nchunks = (n + CHUNK - 1) // CHUNK
+
+    def fill(c: int) -> None:
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        g = np.random.Generator(np.random.PCG64(_chunk_seed(root, stream, c)))
+        x = g.standard_normal(hi - lo, dtype=np.float32)
+        if mult != 1.0:
+            x *= np.float32(mult)
+        x = np.clip(x / np.float32(scale), -FP8_E4M3_MAX, FP8_E4M3_MAX)
+        out[lo:hi] = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    for c in range(nchunks):
+        fill(c)
+    return out
+
+
 def _rng(root: np.random.SeedSequence, stream: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(_chunk_seed(root, stream, 1 << 30)))
 
@@ -95,13 +123,16 @@ class Workload:
     block_table: np.ndarray         # int32 [B][stride]
     num_blocks: int
     q: np.ndarray                   # uint16 [B][Hq][D]
-    k_cache: np.ndarray             # uint16 [NB][Hkv][bs][D]
-    v_cache: np.ndarray             # uint16 [NB][Hkv][bs][D]
+    k_cache: np.ndarray             # [NB][Hkv][bs][D]: uint16 bf16 bits, or uint8 FP8 E4M3 codes
+    v_cache: np.ndarray
     scale: np.float32
     window: int = 0
     sinks: Optional[np.ndarray] = None   # float32 [Hq]
     partition_size: int = 0
     meta: dict = field(default_factory=dict)
+    kv_format: str = "bf16"         # "bf16" or "fp8_e4m3"
+    k_scale: float = 1.0            # FP8: value = code value * scale
+    v_scale: float = 1.0
 
     @property
     def group(self) -> int:
@@ -117,8 +148,9 @@ class Workload:
 
     def kv_bytes(self) -> int:
         """Algorithmic K+V bytes one decode step must read: every attended token's K and V row,
-        once per KV head, bf16."""
-        return int(self.attended_tokens().sum()) * self.num_kv_heads * self.head_dim * 2 * 2
+        once per KV head (2 bytes per value in bf16, 1 in FP8)."""
+        elem = 1 if self.kv_format == "fp8_e4m3" else 2
+        return int(self.attended_tokens().sum()) * self.num_kv_heads * self.head_dim * 2 * elem
 
 
 def pool_blocks(seq_lens: Sequence[int], block_size: int, extra: float = 0.10) -> int:
@@ -130,7 +162,8 @@ def make_workload(*, name: str, seq_lens: Sequence[int], num_q_heads: int, num_k
                   head_dim: int, block_size: int, seed, num_blocks: Optional[int] = None,
                   window: int = 0, with_sinks: bool = False, k_mult: float = 1.0,
                   partition_size: int = 0, poison: bool = False, stride: Optional[int] = None,
-                  scale: Optional[float] = None, unused_entry: str = "spare") -> Workload:
+                  scale: Optional[float] = None, unused_entry: str = "spare",
+                  kv_format: str = "bf16", kv_scales=(1.0, 1.0)) -> Workload:
     """Build one seeded workload.
 
     Physical blocks are a seeded permutation of the pool; sequences take consecutive slices of it
@@ -163,38 +196,49 @@ def make_workload(*, name: str, seq_lens: Sequence[int], num_q_heads: int, num_k
 
     Hq, Hkv, D = int(num_q_heads), int(num_kv_heads), int(head_dim)
     q = normal_bf16(root, S_Q, B * Hq * D).reshape(B, Hq, D)
-    k = normal_bf16(root, S_K, num_blocks * Hkv * bs * D, k_mult).reshape(num_blocks, Hkv, bs, D)
-    v = normal_bf16(root, S_V, num_blocks * Hkv * bs * D).reshape(num_blocks, Hkv, bs, D)
+    nkv = num_blocks * Hkv * bs * D
+    if kv_format == "bf16":
+        k = normal_bf16(root, S_K, nkv, k_mult).reshape(num_blocks, Hkv, bs, D)
+        v = normal_bf16(root, S_V, nkv).reshape(num_blocks, Hkv, bs, D)
+        nan = BF16_QNAN
+    elif kv_format == "fp8_e4m3":
+        k = normal_fp8_e4m3(root, S_K, nkv, k_mult, kv_scales[0]).reshape(num_blocks, Hkv, bs, D)
+        v = normal_fp8_e4m3(root, S_V, nkv, 1.0, kv_scales[1]).reshape(num_blocks, Hkv, bs, D)
+        nan = FP8_QNAN
+    else:
+        raise ValueError(f"unknown KV format {kv_format!r}")
     sinks = None
     if with_sinks:
         sinks = _rng(root, S_SINKS).standard_normal(Hq, dtype=np.float32)
     if poison:
-        _poison(k, v, bt, L, bs, window, perm[used:])
+        _poison(k, v, bt, L, bs, window, perm[used:], nan)
     sc = np.float32(1.0 / math.sqrt(D)) if scale is None else np.float32(scale)
     return Workload(name=name, num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                     block_size=bs, seq_lens=L, block_table=bt, num_blocks=int(num_blocks),
                     q=q, k_cache=k, v_cache=v, scale=sc, window=int(window), sinks=sinks,
-                    partition_size=int(partition_size), meta={"seed": str(seed)})
+                    partition_size=int(partition_size), meta={"seed": str(seed)},
+                    kv_format=kv_format, k_scale=float(np.float32(kv_scales[0])),
+                    v_scale=float(np.float32(kv_scales[1])))
 
 
-def _poison(k, v, bt, L, bs, window, spare_blocks) -> None:
-    k[spare_blocks] = BF16_QNAN
-    v[spare_blocks] = BF16_QNAN
+def _poison(k, v, bt, L, bs, window, spare_blocks, nan=BF16_QNAN) -> None:
+    k[spare_blocks] = nan
+    v[spare_blocks] = nan
     for b in range(bt.shape[0]):
         Lb = int(L[b])
         if Lb == 0:
             continue
         last = (Lb - 1) // bs
         tail = Lb - last * bs
-        k[bt[b, last], :, tail:, :] = BF16_QNAN
-        v[bt[b, last], :, tail:, :] = BF16_QNAN
+        k[bt[b, last], :, tail:, :] = nan
+        v[bt[b, last], :, tail:, :] = nan
         if window > 0 and Lb > window:
             start = Lb - window
             for i in range(start // bs + 1):
                 lo = i * bs
                 hi = min(start, lo + bs)
-                k[bt[b, i], :, : hi - lo, :] = BF16_QNAN
-                v[bt[b, i], :, : hi - lo, :] = BF16_QNAN
+                k[bt[b, i], :, : hi - lo, :] = nan
+                v[bt[b, i], :, : hi - lo, :] = nan
 
 
 # ---------------------------------------------------------------------------------------------
@@ -228,29 +272,40 @@ def config_seq_lens(idx: int) -> np.ndarray:
     raise ValueError(f"no workload {idx}")
 
 
+# FP8 KV variants: one fp32 scale per tensor (K, V); N(0,1) values divided by them stay well
+# inside E4M3's +-448 range, and 0.05 is deliberately not a power of two
+FP8_SCALES = (0.0625, 0.05)
+
+
 def make_config(idx: int, *, head_dim: int = 128, num_q_heads: Optional[int] = None,
-                poison: bool = False, seq_lens: Optional[Sequence[int]] = None) -> Workload:
+                poison: bool = False, seq_lens: Optional[Sequence[int]] = None,
+                kv_format: str = "bf16") -> Workload:
     """Workload ``idx`` in 1..5.  Workload 3 is a sweep: pick the point with ``head_dim`` in
-    {64,128,256} and ``num_q_heads`` in {8,32,64} (8 KV heads)."""
+    {64,128,256} and ``num_q_heads`` in {8,32,64} (8 KV heads).  ``kv_format="fp8_e4m3"`` gives
+    the same workload with an FP8 E4M3 KV cache (scales FP8_SCALES)."""
     L = config_seq_lens(idx) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
     name = CONFIG_NAMES[idx]
+    kw = dict(poison=poison, kv_format=kv_format,
+              kv_scales=FP8_SCALES if kv_format == "fp8_e4m3" else (1.0, 1.0))
+    if kv_format != "bf16":
+        name = f"{name} kv={kv_format}"
     if idx == 1:
         return make_workload(name=name, seq_lens=L, num_q_heads=4, num_kv_heads=2, head_dim=128,
-                             block_size=16, num_blocks=32, seed=[BASE_SEED, 1], poison=poison)
+                             block_size=16, num_blocks=32, seed=[BASE_SEED, 1], **kw)
     if idx == 2:
         return make_workload(name=name, seq_lens=L, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                             block_size=16, seed=[BASE_SEED, 2], poison=poison)
+                             block_size=16, seed=[BASE_SEED, 2], **kw)
     if idx == 3:
         hq = 32 if num_q_heads is None else int(num_q_heads)
         return make_workload(name=f"{name} D{head_dim} {hq}q", seq_lens=L, num_q_heads=hq,
                              num_kv_heads=8, head_dim=head_dim, block_size=16,
-                             seed=[BASE_SEED, 3, head_dim, hq], poison=poison)
+                             seed=[BASE_SEED, 3, head_dim, hq], **kw)
     if idx == 4:
         return make_workload(name=name, seq_lens=L, num_q_heads=64, num_kv_heads=8, head_dim=128,
                              block_size=64, seed=[BASE_SEED, 4], k_mult=0.5, partition_size=512,
-                             poison=poison)
+                             **kw)
     if idx == 5:
         return make_workload(name=name, seq_lens=L, num_q_heads=32, num_kv_heads=8, head_dim=128,
                              block_size=16, seed=[BASE_SEED, 5], window=4096, with_sinks=True,
-                             poison=poison)
+                             **kw)
     raise ValueError(f"no workload {idx}")
