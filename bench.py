@@ -67,7 +67,8 @@ def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
         while dt < min_seconds:
             t0 = time.perf_counter()
             ref.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
-                       wl.block_size, window=wl.window, sinks=wl.sinks)
+                       wl.block_size, window=wl.window, sinks=wl.sinks, kv_format=wl.kv_format,
+                       k_scale=wl.k_scale, v_scale=wl.v_scale)
             dt += time.perf_counter() - t0
             reps += 1
     return {"value": round(wl.kv_bytes() * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
@@ -215,6 +216,9 @@ def main() -> int:
                     help="copy: run only the plain copy kernel on --bytes (counter calibration); "
                          "latency: small-batch rows, eager vs prepared plan vs graph replay")
     ap.add_argument("--bytes", type=int, default=1 << 30)
+    ap.add_argument("--kv", choices=["bf16", "fp8_e4m3"], default="bf16",
+                    help="KV cache format; fp8_e4m3 runs through a prepared plan (the timed "
+                         "kernel interval then spans the decode and merge launches)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -243,7 +247,8 @@ def main() -> int:
     kw = {}
     if args.config == 3:
         kw = dict(head_dim=args.head_dim, num_q_heads=args.q_heads or 32)
-    wl = make_config(args.config, **kw)
+    wl = make_config(args.config, kv_format=args.kv, **kw)
+    fp8 = args.kv != "bf16"
     B, Hq, D = wl.q.shape
     maxL = int(wl.seq_lens.max())
     if args.schedule == "unsplit":
@@ -280,7 +285,16 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     shape = pa.make_shape(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, max(P, 0), pmax)
     workers = args.workers
-    if P < 0:
+    plan = None
+    if fp8:
+        plan = pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
+                       window=wl.window, schedule=args.schedule, partition_size=max(P, 0),
+                       max_seq_len=maxL, num_workers=workers, kv_dtype=args.kv)
+        plan_ws = plan.workspace(dev)
+        variant = plan.name
+        if P < 0:
+            workers = int(variant.split("workers")[1].split()[0])
+    elif P < 0:
         workers = workers or pa.balanced_default_workers(D, Hq // wl.num_kv_heads)
         ws = torch.empty(pa.balanced_workspace_size(shape, D, workers), dtype=torch.uint8,
                          device=dev)
@@ -296,7 +310,10 @@ def main() -> int:
         c = i % copies
         if ev is not None:
             ev[0].record(stream)
-        if P > 0:
+        if plan is not None:
+            plan.run(q, ks[c], vs[c], bt, L, float(wl.scale), out=out, lse=lse, sinks=sinks,
+                     workspace=plan_ws, k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream)
+        elif P > 0:
             pa.decode(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window, sinks=sinks,
                       partition_size=P, max_partitions=pmax, out=part, lse=plse, stream=stream)
         elif P == 0:
@@ -308,7 +325,9 @@ def main() -> int:
                                merge=False, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        if P > 0:
+        if plan is not None:
+            pass
+        elif P > 0:
             pa.reduce(part, plse, L, partition_size=P, out=out, lse=lse, stream=stream)
         elif P < 0:
             pa.reduce_balanced(L, out, lse, shape=shape, head_dim=D, block_size=wl.block_size,
@@ -348,10 +367,11 @@ def main() -> int:
     attainable = probe.numel() * 10 / (s0.elapsed_time(s1) / 1e3) / 1e9
     del probe
 
-    workload = f"config{args.config}" + (f"_d{D}_hq{Hq}" if args.config == 3 else "")
+    workload = f"config{args.config}" + (f"_d{D}_hq{Hq}" if args.config == 3 else "") + \
+        ("_fp8" if fp8 else "")
     traffic = measured_traffic(workload, args.schedule)
     res = {
-        "metric": METRIC,
+        "metric": METRIC if not fp8 else METRIC.replace("bf16 d=128", "FP8 E4M3 KV d=128"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -370,7 +390,7 @@ def main() -> int:
             "batch": B, "q_heads": Hq, "kv_heads": wl.num_kv_heads, "head_dim": D,
             "block_size": wl.block_size, "window": wl.window,
             "sinks": wl.sinks is not None, "seq_len_sum": int(wl.seq_lens.sum()),
-            "max_seq_len": maxL, "schedule": args.schedule,
+            "max_seq_len": maxL, "schedule": args.schedule, "kv_dtype": args.kv,
             "partition_size": P if P > 0 else None,
             "workers": workers if P < 0 else None, "kv_bytes_per_step": kv_bytes,
             "variant": variant, "kv_pool_copies": copies, "parallelism": "none (1 GPU)",
@@ -384,6 +404,7 @@ def main() -> int:
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "decode_us_avg": round(dec_avg_s * 1e6, 3),
+            "interval": "decode and merge launches" if fp8 else "decode launch",
             "algorithmic_bytes_per_launch": kv_bytes,
             "attainable_stream_read_GBps": round(attainable, 1),
         },

@@ -47,6 +47,10 @@
  * (sequence, head): a physical block id outside [0, num_blocks), a length L < 0 or
  * L > block_table_stride * block_size, or (split mode) a sequence needing more than
  * max_partitions partitions.  paged_attn_check_tables() runs the same checks on host copies.
+ * NaN inputs propagate as in the definition: a NaN in an attended key row makes the outputs and
+ * LSEs of that KV head's query heads NaN; a NaN in an attended value row makes that one output
+ * dimension NaN; NaNs outside the attended range (unused slots, masked tokens) are never read
+ * into a result.
  */
 #ifndef PAGED_ATTN_H
 #define PAGED_ATTN_H
@@ -224,6 +228,13 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  *                  the same launch by whichever partition of a (sequence, KV head) finishes
  *                  last: one kernel per step, for small batches; its device-scope release per
  *                  partition makes it slow for large ones).
+ *   kv_dtype       PA_KV_BF16, or PA_KV_FP8_E4M3: k_cache and v_cache then hold one byte per
+ *                  value, [num_blocks][Hkv][block_size][head_dim] uint8, each code standing for
+ *                  its E4M3 value times the tensor's scale (given per run).  The FP8 KV cache is
+ *                  the sibling the one-token decode work sets aside (ROCm/rocm-libraries PR
+ *                  #13700, Summary: the prepared path is the non-FP8 one); the format and the
+ *                  per-tensor scales are this library's reading, the pages give none.  Every
+ *                  schedule supports it; other values give PA_ERR_UNSUPPORTED.
  *   max_seq_len    host-side upper bound on the lengths the plan will see, or 0 if unknown.
  *                  Balanced plans launch no more workers than that many tiles can keep busy
  *                  (a small batch then does not pay for thousands of idle workers); a length
@@ -240,6 +251,13 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  */
 typedef struct pa_plan pa_plan;
 
+/* KV cache element formats a plan reads. */
+enum {
+  PA_KV_BF16 = 0,       /* bf16 rows of head_dim values (2 * head_dim bytes)                 */
+  PA_KV_FP8_E4M3 = 1    /* OCP FP8 E4M3 codes, one byte per value (head_dim bytes per row),
+                           with one fp32 scale for all of K and one for all of V             */
+};
+
 enum {
   PA_SCHEDULE_UNSPLIT = 0,
   PA_SCHEDULE_PARTITIONED = 1,
@@ -248,8 +266,8 @@ enum {
 };
 
 pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,
-                                 int32_t window, int32_t schedule, int32_t max_seq_len,
-                                 int32_t num_workers, pa_plan** plan);
+                                 int32_t window, int32_t schedule, int32_t kv_dtype,
+                                 int32_t max_seq_len, int32_t num_workers, pa_plan** plan);
 
 /* Device workspace bytes a run needs (0 for the unsplit schedule): the partition partials and
  * their LSEs (plus one merge counter per (sequence, KV head) for the fused schedule), or the
@@ -262,15 +280,19 @@ int64_t paged_attn_plan_workspace_size(const pa_plan* plan);
  * One decode step with a plan: the operation of paged_attn_decode (+ paged_attn_reduce) on the
  * sizes fixed at creation.  Pointers, layouts and the scale / sinks / lse conventions are those
  * of paged_attn_decode; out is always the final fp32 [B][Hq][head_dim] and lse the final
- * [B][Hq] (or NULL).  Returns PA_ERR_NULL for a missing pointer (workspace included when the
- * plan needs one), PA_ERR_SHAPE for a non-finite scale or a misaligned workspace, and
- * PA_ERR_LAUNCH when HIP rejects a launch.  Bad tables and lengths are reported as NaN, as for
- * paged_attn_decode.
+ * [B][Hq] (or NULL).  k_scale and v_scale are the FP8 cache's per-tensor scales (a key is
+ * k_scale times its decoded code, a value v_scale times its code); a bf16 plan requires both to
+ * be 1.  Returns PA_ERR_NULL for a missing pointer (workspace included when the plan needs
+ * one), PA_ERR_SHAPE for a non-finite scale, a bf16 plan given scales other than 1, or a
+ * misaligned workspace, and PA_ERR_LAUNCH when HIP rejects a launch.  Bad tables and lengths are
+ * reported as NaN, as for paged_attn_decode; a NaN code in an attended FP8 row gives NaN outputs
+ * for that (sequence, KV head), as a NaN bf16 value does.
  */
 pa_status paged_attn_plan_run(const pa_plan* plan, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* block_table,
-                              const int32_t* seq_lens, float scale, const float* sinks,
-                              float* out, float* lse, void* workspace, void* stream);
+                              const int32_t* seq_lens, float scale, float k_scale, float v_scale,
+                              const float* sinks, float* out, float* lse, void* workspace,
+                              void* stream);
 
 /* Kernel variants a run launches (static storage owned by the plan). */
 const char* paged_attn_plan_name(const pa_plan* plan);

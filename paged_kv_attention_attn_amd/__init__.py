@@ -66,10 +66,11 @@ def _load() -> ctypes.CDLL:
                                              ctypes.c_size_t, i32, vp]),
         "paged_attn_balanced_workspace_size": (ctypes.c_int64, [sp, i32, i32]),
         "paged_attn_balanced_default_workers": (i32, [i32, i32]),
-        "paged_attn_plan_create": (i32, [sp, i32, i32, i32, i32, i32, i32,
+        "paged_attn_plan_create": (i32, [sp, i32, i32, i32, i32, i32, i32, i32,
                                          ctypes.POINTER(vp)]),
         "paged_attn_plan_workspace_size": (ctypes.c_int64, [vp]),
-        "paged_attn_plan_run": (i32, [vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp]),
+        "paged_attn_plan_run": (i32, [vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp, vp,
+                                      vp]),
         "paged_attn_plan_name": (ctypes.c_char_p, [vp]),
         "paged_attn_plan_destroy": (None, [vp]),
         "paged_attn_gather_witness": (i32, [sp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]),
@@ -354,6 +355,7 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, scale, *, window
 
 
 SCHEDULES = {"unsplit": 0, "partitioned": 1, "balanced": 2, "fused": 3}
+KV_DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
 
 class Plan:
@@ -362,15 +364,20 @@ class Plan:
     "partitioned" (``partition_size`` tokens, partition slots for ``max_seq_len``), "fused"
     (partitioned, merged in the same launch by the last partition to finish) or
     "balanced" (``num_workers``, 0 = the device default; ``max_seq_len``, a bound on the
-    lengths, caps the workers of a small batch).  run() records only kernel launches on the
-    stream, so it can be captured in a CUDA/HIP graph."""
+    lengths, caps the workers of a small batch).  ``kv_dtype`` is "bf16" or "fp8_e4m3" (KV
+    pools of one byte per value, uint8 tensors, with per-tensor scales given to run()).  run()
+    records only kernel launches on the stream, so it can be captured in a CUDA/HIP graph."""
 
     def __init__(self, num_seqs: int, num_q_heads: int, num_kv_heads: int, num_blocks: int,
                  block_table_stride: int, head_dim: int, block_size: int, *, window: int = 0,
                  schedule: str = "balanced", partition_size: int = 0,
-                 max_seq_len: Optional[int] = None, num_workers: int = 0):
+                 max_seq_len: Optional[int] = None, num_workers: int = 0,
+                 kv_dtype: str = "bf16"):
         if schedule not in SCHEDULES:
             raise ValueError(f"schedule must be one of {sorted(SCHEDULES)}")
+        if kv_dtype not in KV_DTYPES:
+            raise ValueError(f"kv_dtype must be one of {sorted(KV_DTYPES)}")
+        self.kv_dtype = kv_dtype
         pmax = 0
         if schedule in ("partitioned", "fused"):
             if partition_size <= 0 or max_seq_len is None:
@@ -384,7 +391,7 @@ class Plan:
         self.dims = (num_seqs, num_q_heads, head_dim)
         self._h = ctypes.c_void_p()
         st = _lib.paged_attn_plan_create(ctypes.byref(self.shape), int(head_dim), int(block_size),
-                                         int(window), SCHEDULES[schedule],
+                                         int(window), SCHEDULES[schedule], KV_DTYPES[kv_dtype],
                                          int(max_seq_len or 0), int(num_workers),
                                          ctypes.byref(self._h))
         if st != PA_OK:
@@ -400,10 +407,12 @@ class Plan:
         return torch.zeros(self.workspace_size, dtype=torch.uint8, device=device)
 
     def run(self, q, k_cache, v_cache, block_table, seq_lens, scale: float, *, out, lse=None,
-            sinks=None, workspace=None, stream=None) -> None:
+            sinks=None, workspace=None, stream=None, k_scale: float = 1.0,
+            v_scale: float = 1.0) -> None:
         """One step into the caller's ``out`` (fp32 [B][Hq][D]) and ``lse`` (fp32 [B][Hq] or
-        None).  Pointers only: the tensors must match the sizes the plan was made for (only
-        their being on the GPU is checked here)."""
+        None).  ``k_scale`` / ``v_scale``: an FP8 cache's per-tensor scales (1 for bf16).
+        Pointers only: the tensors must match the sizes the plan was made for (only their being
+        on the GPU is checked here)."""
         for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                         ("block_table", block_table), ("seq_lens", seq_lens), ("out", out),
                         ("lse", lse), ("sinks", sinks), ("workspace", workspace)):
@@ -411,6 +420,7 @@ class Plan:
                 raise ValueError(f"{name} must be a GPU tensor")
         st = _lib.paged_attn_plan_run(self._h, _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                       _ptr(block_table), _ptr(seq_lens), float(scale),
+                                      float(k_scale), float(v_scale),
                                       _ptr(sinks), _ptr(out), _ptr(lse), _ptr(workspace),
                                       _stream(out.device, stream))
         if st != PA_OK:

@@ -23,7 +23,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 constexpr int32_t kMaxGridYZ = 65535;
 
 int log2_exact(int32_t v) {
@@ -159,6 +159,7 @@ pa_status paged_attn_decode(const pa_shape* shape, const void* q, const void* k_
   p.out = out;
   p.lse = lse;
   p.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.v_scale = 1.f;
   p.num_seqs = shape->num_seqs;
   p.num_q_heads = shape->num_q_heads;
   p.num_kv_heads = shape->num_kv_heads;
@@ -295,6 +296,7 @@ pa_status paged_attn_decode_balanced(const pa_shape* shape, const void* q, const
   p.v_cache = static_cast<const char*>(v_cache);
   p.block_table = block_table;
   p.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.v_scale = 1.f;
   if (debug_log())
     std::fprintf(stderr, "[paged_attn] balanced %s B=%d Hq=%d Hkv=%d bs=%d W=%d workers=%d\n",
                  pa::qk_path_name(path), shape->num_seqs,
@@ -445,6 +447,7 @@ pa_status paged_attn_copy(void* dst, const void* src, size_t bytes, void* stream
 // ---------------------------------------------------------------------------------------------
 struct pa_plan {
   int32_t schedule;
+  int32_t kv_dtype;
   int32_t head_dim, group, waves, num_workers;
   pa::QkPath path;
   pa::DecodeParams dec;   // sizes; pointers are filled per run
@@ -459,7 +462,8 @@ struct pa_plan {
 namespace {
 
 pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size, int32_t window,
-                     int32_t schedule, int32_t max_seq_len, int32_t num_workers, pa_plan* pl) {
+                     int32_t schedule, int32_t kv_dtype, int32_t max_seq_len,
+                     int32_t num_workers, pa_plan* pl) {
   const pa_status st = check_shape(shape);
   if (st != PA_OK) return st;
   if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
@@ -477,12 +481,17 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
       ((int64_t)shape->num_seqs * shape->num_q_heads > 0x7FFFFFFF || num_workers < 0 ||
        num_workers > kMaxWorkers))
     return PA_ERR_SHAPE;
+  if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   pa::QkPath path;
-  if (decode_path(head_dim, group, &path) != 0) return PA_ERR_UNSUPPORTED;
+  if (kv_dtype == PA_KV_FP8_E4M3)
+    path = pa::QkPath::kMfmaPvFp8;   // the one path that reads FP8 rows
+  else if (decode_path(head_dim, group, &path) != 0)
+    return PA_ERR_UNSUPPORTED;
   const int waves = decode_waves(head_dim, group, parted ? shape->partition_size : 0);
   if (waves < 0) return PA_ERR_UNSUPPORTED;
 
   pl->schedule = schedule;
+  pl->kv_dtype = kv_dtype;
   pl->head_dim = head_dim;
   pl->group = group;
   pl->waves = waves;
@@ -547,14 +556,15 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
 extern "C" {
 
 pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,
-                                 int32_t window, int32_t schedule, int32_t max_seq_len,
-                                 int32_t num_workers, pa_plan** plan) {
+                                 int32_t window, int32_t schedule, int32_t kv_dtype,
+                                 int32_t max_seq_len, int32_t num_workers, pa_plan** plan) {
   if (plan == nullptr) return PA_ERR_NULL;
   *plan = nullptr;
   pa_plan* pl = new (std::nothrow) pa_plan;
   if (pl == nullptr) return PA_ERR_LAUNCH;
   const pa_status st =
-      plan_build(shape, head_dim, block_size, window, schedule, max_seq_len, num_workers, pl);
+      plan_build(shape, head_dim, block_size, window, schedule, kv_dtype, max_seq_len,
+                 num_workers, pl);
   if (st != PA_OK) {
     delete pl;
     return st;
@@ -575,10 +585,13 @@ void paged_attn_plan_destroy(pa_plan* plan) { delete plan; }
 
 pa_status paged_attn_plan_run(const pa_plan* plan, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* block_table,
-                              const int32_t* seq_lens, float scale, const float* sinks,
-                              float* out, float* lse, void* workspace, void* stream) {
+                              const int32_t* seq_lens, float scale, float k_scale,
+                              float v_scale, const float* sinks, float* out, float* lse,
+                              void* workspace, void* stream) {
   if (plan == nullptr) return PA_ERR_NULL;
-  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return PA_ERR_SHAPE;
+  if (plan->kv_dtype == PA_KV_BF16 && (k_scale != 1.f || v_scale != 1.f)) return PA_ERR_SHAPE;
   if (plan->dec.num_seqs == 0) return PA_OK;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
       seq_lens == nullptr || out == nullptr)
@@ -595,7 +608,9 @@ pa_status paged_attn_plan_run(const pa_plan* plan, const void* q, const void* k_
   p.block_table = block_table;
   p.seq_lens = seq_lens;
   p.sinks = sinks;
-  p.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
+  // an FP8 cache's K scale multiplies every score: folded into the score scale
+  p.qk_scale_log2 = (float)((double)scale * (double)k_scale * 1.4426950408889634);
+  p.v_scale = v_scale;
   hipError_t e = hipSuccess;
   if (plan->schedule == PA_SCHEDULE_UNSPLIT) {
     p.out = out;

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kWave) void balanced_decode_kernel(const BalancedPa
       ctx.advance(iss);
       phys_next = ctx.phys(iss);
     }
-    const TileAddr ta{p.num_blocks, p.num_kv_heads, s.at.kvh, p.bs_log2, RG::kRowBytes};
+    const TileAddr ta{p.num_blocks, p.num_kv_heads, s.at.kvh, p.bs_log2, QK::kRowBytes};
     const int64_t off = ta.offset(phys, s.at.s.t0 + s.at.ti);
     s.ok = off >= 0;
     if (s.ok) qk.issue(t, p.k_cache + off, p.v_cache + off, lane);
@@ -227,8 +227,9 @@ __global__ __launch_bounds__(kWave) void balanced_decode_kernel(const BalancedPa
           lt = fmaf(lt, scale_o, fast_exp2(s2 - M2u));
           M = M2;
         }
-        const float inv = lt > 0.f ? scale_o / lt : 0.f;
-        float lv = lt > 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
+        // lt is 0 only for an empty piece; a NaN input (lt = NaN) must reach the outputs
+        const float inv = lt != 0.f ? scale_o / lt : 0.f;
+        float lv = lt != 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
         if (piece_bad) lv = __builtin_nanf("");
         float* dst;
         if (whole) {
@@ -504,6 +505,7 @@ hipError_t launch_balanced(const BalancedParams& bp, int head_dim, int group, Qk
   switch (path) {
     case QkPath::kValu: return launch_bal_d<QkPath::kValu>(bp, head_dim, group, stream);
     case QkPath::kMfma: return launch_bal_d<QkPath::kMfma>(bp, head_dim, group, stream);
+    case QkPath::kMfmaPvFp8: return launch_bal_d<QkPath::kMfmaPvFp8>(bp, head_dim, group, stream);
     default: return launch_bal_d<QkPath::kMfmaPv>(bp, head_dim, group, stream);
   }
 }
@@ -519,9 +521,10 @@ hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int gro
 }
 
 int balanced_default_workers(int head_dim, int group, QkPath path) {
-  const void* k = path == QkPath::kValu   ? bal_ptr<QkPath::kValu>(head_dim, group)
-                  : path == QkPath::kMfma ? bal_ptr<QkPath::kMfma>(head_dim, group)
-                                          : bal_ptr<QkPath::kMfmaPv>(head_dim, group);
+  const void* k = path == QkPath::kValu         ? bal_ptr<QkPath::kValu>(head_dim, group)
+                  : path == QkPath::kMfma       ? bal_ptr<QkPath::kMfma>(head_dim, group)
+                  : path == QkPath::kMfmaPvFp8  ? bal_ptr<QkPath::kMfmaPvFp8>(head_dim, group)
+                                                : bal_ptr<QkPath::kMfmaPv>(head_dim, group);
   if (k == nullptr) return -1;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;

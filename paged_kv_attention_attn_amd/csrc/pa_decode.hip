@@ -59,7 +59,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
   // first batch is requested before the sequence length arrives, for the range a partition has
   // without a window (indices clamped into the row, so always in bounds); a window start that
   // moves the range triggers a reload below.
-  const TileAddr ta{p.num_blocks, p.num_kv_heads, it.kvh, p.bs_log2, RG::kRowBytes};
+  const TileAddr ta{p.num_blocks, p.num_kv_heads, it.kvh, p.bs_log2, QK::kRowBytes};
   const int32_t* bt_row = p.block_table + (size_t)it.b * p.stride;
   const int lo_guess =
       split ? (int)((int64_t)it.part * p.psize < 0x7FFFFFF0 ? (int64_t)it.part * p.psize
@@ -204,8 +204,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
       o *= f;
       M = M2;
     }
-    float ov = lt > 0.f ? o / lt : 0.f;
-    float lv = lt > 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
+    // lt is 0 only for an empty range; a NaN score (lt = NaN) must reach the outputs
+    float ov = lt != 0.f ? o / lt : 0.f;
+    float lv = lt != 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
     if (any_bad) {
       ov = __builtin_nanf("");
       lv = __builtin_nanf("");
@@ -359,6 +360,7 @@ const char* qk_path_name(QkPath path) {
   switch (path) {
     case QkPath::kValu: return "valu";
     case QkPath::kMfma: return "mfma";
+    case QkPath::kMfmaPvFp8: return "mfmapv_fp8";
     default: return "mfmapv";
   }
 }
@@ -376,6 +378,8 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int wav
   switch (path) {
     case QkPath::kValu: return launch_d<QkPath::kValu>(p, head_dim, group, waves, stream);
     case QkPath::kMfma: return launch_d<QkPath::kMfma>(p, head_dim, group, waves, stream);
+    case QkPath::kMfmaPvFp8:
+      return launch_d<QkPath::kMfmaPvFp8>(p, head_dim, group, waves, stream);
     default: return launch_d<QkPath::kMfmaPv>(p, head_dim, group, waves, stream);
   }
 }

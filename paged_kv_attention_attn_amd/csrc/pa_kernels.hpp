@@ -8,14 +8,15 @@ namespace pa {
 
 struct DecodeParams {
   const uint16_t* q;          // bf16 [B][Hq][D]
-  const char* k_cache;        // bf16 [NB][Hkv][bs][D]
+  const char* k_cache;        // bf16 [NB][Hkv][bs][D], or FP8 E4M3 bytes for the FP8 path
   const char* v_cache;
   const int32_t* block_table; // [B][stride]
   const int32_t* seq_lens;    // [B]
   const float* sinks;         // [Hq] or null
   float* out;                 // unsplit [B][Hq][D]; split [B][Hq][Pmax][D]
   float* lse;                 // unsplit [B][Hq] or null; split [B][Hq][Pmax]
-  float qk_scale_log2;        // scale * log2(e)
+  float qk_scale_log2;        // scale * log2(e) (FP8 path: times the K scale)
+  float v_scale;              // FP8 path: multiplier on the output; unused otherwise
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -72,8 +73,9 @@ struct WitnessParams {
 // caller has validated the parameters.
 // Decode kernels: q.k on the vector ALUs (dot2 + DPP) with P.V in fp32 on the vector ALUs
 // (kValu); q.k on the matrix cores with P.V on the vector ALUs (kMfma); or both on the matrix
-// cores, P carried as two bf16 terms (kMfmaPv).
-enum class QkPath { kValu = 0, kMfma = 1, kMfmaPv = 2 };
+// cores, P carried as two bf16 terms (kMfmaPv); the same for a KV cache of FP8 E4M3 codes with
+// per-tensor scales, converted to bf16 in registers (kMfmaPvFp8).
+enum class QkPath { kValu = 0, kMfma = 1, kMfmaPv = 2, kMfmaPvFp8 = 3 };
 // Short name of a path ("valu", "mfma", "mfmapv").
 const char* qk_path_name(QkPath path);
 // Grid: one workgroup per (partition slot, KV head, sequence), 1-D.

@@ -62,16 +62,22 @@ __device__ __forceinline__ void load_v_rows(uint32_t (&v)[kTileSteps][RowGeom<D>
     load_row<D>(vb + (kRows * j + r) * RowGeom<D>::kRowBytes, c, v[j]);
 }
 
-template <int D>
-__device__ __forceinline__ void mask_v_rows(uint32_t (&v)[kTileSteps][RowGeom<D>::kWords],
-                                            int tok0, int lo, int hi, int lane) {
+template <int NWORDS>
+__device__ __forceinline__ void mask_v_words(uint32_t (&v)[kTileSteps][NWORDS], int tok0, int lo,
+                                             int hi, int lane) {
 #pragma unroll
   for (int j = 0; j < kTileSteps; ++j) {
     const int tk = tok0 + kRows * j + (lane >> 4);
     const bool ok = tk >= lo && tk < hi;
 #pragma unroll
-    for (int w = 0; w < RowGeom<D>::kWords; ++w) v[j][w] = ok ? v[j][w] : 0u;
+    for (int w = 0; w < NWORDS; ++w) v[j][w] = ok ? v[j][w] : 0u;
   }
+}
+
+template <int D>
+__device__ __forceinline__ void mask_v_rows(uint32_t (&v)[kTileSteps][RowGeom<D>::kWords],
+                                            int tok0, int lo, int hi, int lane) {
+  mask_v_words<RowGeom<D>::kWords>(v, tok0, lo, hi, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -82,6 +88,7 @@ template <int D, int G>
 struct QkValu {
   static constexpr int W = RowGeom<D>::kWords;
   static constexpr int E = RowGeom<D>::kElems;
+  static constexpr int kRowBytes = RowGeom<D>::kRowBytes;
   struct Tile {
     uint32_t k[kTileSteps][W];
     uint32_t v[kTileSteps][W];
@@ -225,6 +232,7 @@ struct QkMfma {
   static constexpr int KK = D / 32;
   static constexpr int W = RowGeom<D>::kWords;
   static constexpr int E = RowGeom<D>::kElems;
+  static constexpr int kRowBytes = RowGeom<D>::kRowBytes;
   struct Tile {
     u32x4_t k[KK];
     uint32_t v[kTileSteps][W];
@@ -364,18 +372,44 @@ struct QkMfma {
 // ---------------------------------------------------------------------------------------------
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-template <int D, int G>
-struct QkMfmaPv {
+// Eight OCP FP8 E4M3 values (two words) -> eight bf16 (four words), exactly: the hardware
+// conversion gives their fp32 values, and an E4M3 value has at most four significant bits, so
+// packing them to bf16 (v_cvt_pk_bf16_f32) rounds nothing.  (A byte permute taking the upper
+// halves of the two floats was compiled, for gfx950, with the same source register for both
+// operands when both come from one conversion; the packing conversion has no such form.)
+__device__ __forceinline__ uint32_t f32_pair_to_bf16(f32x2_t f) {
+  const bf16x2_t h = {(__bf16)f.x, (__bf16)f.y};
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t x) {
+  u32x4_t r;
+  r.x = f32_pair_to_bf16(__builtin_amdgcn_cvt_pk_f32_fp8((int)x.x, false));
+  r.y = f32_pair_to_bf16(__builtin_amdgcn_cvt_pk_f32_fp8((int)x.x, true));
+  r.z = f32_pair_to_bf16(__builtin_amdgcn_cvt_pk_f32_fp8((int)x.y, false));
+  r.w = f32_pair_to_bf16(__builtin_amdgcn_cvt_pk_f32_fp8((int)x.y, true));
+  return r;
+}
+
+// FP8 = true: the KV cache holds OCP FP8 E4M3 codes (one byte per value, rows of D bytes) with
+// one fp32 scale per tensor.  K and V are converted to bf16 in registers (exactly) and go
+// through the same MFMAs; the K scale is folded into the score scale by the host and the V
+// scale multiplies the output.
+template <int D, int G, bool FP8>
+struct QkMfmaPvT {
   static constexpr int KK = D / 32;
   static constexpr int W = RowGeom<D>::kWords;
   static constexpr int E = RowGeom<D>::kElems;
+  static constexpr int kRowBytes = FP8 ? D : 2 * D;
+  static constexpr int VW = FP8 ? (E + 3) / 4 : W;   // words a lane holds of one V row
   struct Tile {
-    u32x4_t k[KK];
-    uint32_t v[kTileSteps][W];
+    typename std::conditional<FP8, u32x2_t, u32x4_t>::type k[KK];
+    uint32_t v[kTileSteps][VW];
   };
   u32x4_t qb[KK];
   float c2;
+  float vs;   // FP8: V scale
   bool head_lane;
   float m, l;
   f32x4_t cacc[E];
@@ -407,6 +441,7 @@ struct QkMfmaPv {
   __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
                                        uint32_t qflip, float c2_) {
     c2 = c2_;
+    vs = p.v_scale;
     load_q(p, b, h0, lane, qflip);
     reset();
   }
@@ -414,11 +449,39 @@ struct QkMfmaPv {
   __device__ __forceinline__ void issue(Tile& t, const char* kb, const char* vb, int lane) const {
     const int mrow = lane & 15;
     const int tok = 4 * (mrow & 3) + (mrow >> 2);
-    const char* krow = kb + tok * RowGeom<D>::kRowBytes + 16 * (lane >> 4);
+    if constexpr (FP8) {
+      // K: bytes 32kk + 8(lane/16) .. +8 of the token's row (the same dims as the bf16 path);
+      // V: the lane's slice of each of its four rows, E bytes (two 8-byte pieces at D = 256)
+      const char* krow = kb + tok * kRowBytes + 8 * (lane >> 4);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      t.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + 64 * kk));
-    load_v_rows<D>(t.v, vb, lane);
+      for (int kk = 0; kk < KK; ++kk)
+        t.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(krow + 32 * kk));
+      const int r = lane >> 4, c = lane & 15;
+#pragma unroll
+      for (int j = 0; j < kTileSteps; ++j) {
+        const char* row = vb + (kRows * j + r) * kRowBytes;
+        if constexpr (D == 64) {
+          t.v[j][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row + 4 * c));
+        } else {
+          const u32x2_t x =
+              __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(row + 8 * c));
+          t.v[j][0] = x.x;
+          t.v[j][1] = x.y;
+          if constexpr (D == 256) {
+            const u32x2_t y =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(row + 128 + 8 * c));
+            t.v[j][2] = y.x;
+            t.v[j][3] = y.y;
+          }
+        }
+      }
+    } else {
+      const char* krow = kb + tok * kRowBytes + 16 * (lane >> 4);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        t.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + 64 * kk));
+      load_v_rows<D>(t.v, vb, lane);
+    }
   }
 
   template <bool MASKED>
@@ -426,17 +489,23 @@ struct QkMfmaPv {
     const int g = lane >> 4;
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[kk]),
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4_t kw;
+      if constexpr (FP8)
+        kw = fp8x8_to_bf16x8(t.k[kk]);
+      else
+        kw = t.k[kk];
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw),
                                                    __builtin_bit_cast(bf16x8_t, qb[kk]), sc, 0,
                                                    0, 0);
+    }
     if constexpr (MASKED) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tk = tok0 + 4 * i + g;
         sc[i] = (tk >= lo && tk < hi) ? sc[i] * c2 : -INFINITY;
       }
-      mask_v_rows<D>(t.v, tok0, lo, hi, lane);
+      mask_v_words<VW>(t.v, tok0, lo, hi, lane);
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     if constexpr (!MASKED) mx *= c2;
@@ -476,12 +545,31 @@ struct QkMfmaPv {
     const s16x4_t a_hi = __builtin_bit_cast(s16x4_t, u32x2_t{uh01, uh23});
     const s16x4_t a_lo = __builtin_bit_cast(
         s16x4_t, u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
+    // FP8: the fp32 values of the four rows' elements (exact), two per conversion
+    f32x2_t vf[FP8 ? kTileSteps : 1][FP8 ? 2 * VW : 1];
+    if constexpr (FP8) {
+#pragma unroll
+      for (int j = 0; j < kTileSteps; ++j) {
+#pragma unroll
+        for (int w = 0; w < VW; ++w) {
+          vf[j][2 * w] = __builtin_amdgcn_cvt_pk_f32_fp8((int)t.v[j][w], false);
+          vf[j][2 * w + 1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)t.v[j][w], true);
+        }
+      }
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       // B: element e of the slice of tokens 4j+g, j = 0..3 (bf16 halves gathered by v_perm)
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t b01 = __builtin_amdgcn_perm(t.v[1][e / 2], t.v[0][e / 2], sel);
-      const uint32_t b23 = __builtin_amdgcn_perm(t.v[3][e / 2], t.v[2][e / 2], sel);
+      uint32_t b01, b23;
+      if constexpr (FP8) {
+        const auto f = [&](int j) { return (e & 1) ? vf[j][e / 2].y : vf[j][e / 2].x; };
+        b01 = f32_pair_to_bf16(f32x2_t{f(0), f(1)});
+        b23 = f32_pair_to_bf16(f32x2_t{f(2), f(3)});
+      } else {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        b01 = __builtin_amdgcn_perm(t.v[1][e / 2], t.v[0][e / 2], sel);
+        b23 = __builtin_amdgcn_perm(t.v[3][e / 2], t.v[2][e / 2], sel);
+      }
       const s16x4_t bv = __builtin_bit_cast(s16x4_t, u32x2_t{b01, b23});
       cacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, bv, cacc[e], 0, 0, 0);
       cacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, bv, cacc[e], 0, 0, 0);
@@ -506,16 +594,26 @@ struct QkMfmaPv {
       }
     }
   }
-  // After merge_rows, on the row-0 lanes: the accumulated P.V of head h at dim(lane, e).
+  // After merge_rows, on the row-0 lanes: the accumulated P.V of head h at dim(lane, e)
+  // (times the V scale for an FP8 cache).
   __device__ __forceinline__ float out(int h, int e) const {
-    return h < 4 ? cacc[e][h & 3] : up[(h - 4) & 3][e];
+    const float x = h < 4 ? cacc[e][h & 3] : up[(h - 4) & 3][e];
+    return FP8 ? x * vs : x;
   }
 };
+
+template <int D, int G>
+using QkMfmaPv = QkMfmaPvT<D, G, false>;
+template <int D, int G>
+using QkMfmaPvFp8 = QkMfmaPvT<D, G, true>;
 
 // The policy of a path.
 template <int D, int G, QkPath PATH>
 using QkPolicy = typename std::conditional<
     PATH == QkPath::kValu, QkValu<D, G>,
-    typename std::conditional<PATH == QkPath::kMfma, QkMfma<D, G>, QkMfmaPv<D, G>>::type>::type;
+    typename std::conditional<
+        PATH == QkPath::kMfma, QkMfma<D, G>,
+        typename std::conditional<PATH == QkPath::kMfmaPv, QkMfmaPv<D, G>,
+                                  QkMfmaPvFp8<D, G>>::type>::type>::type;
 
 }  // namespace pa

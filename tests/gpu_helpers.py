@@ -24,10 +24,11 @@ def log(msg: str) -> None:
 
 def to_dev(wl):
     d = torch.device("cuda")
+    kv = np.uint8 if wl.kv_format == "fp8_e4m3" else np.int16   # raw codes / bf16 bits
     t = dict(
         q=torch.from_numpy(np.ascontiguousarray(wl.q).view(np.int16)).to(d),
-        k=torch.from_numpy(np.ascontiguousarray(wl.k_cache).view(np.int16)).to(d),
-        v=torch.from_numpy(np.ascontiguousarray(wl.v_cache).view(np.int16)).to(d),
+        k=torch.from_numpy(np.ascontiguousarray(wl.k_cache).view(kv)).to(d),
+        v=torch.from_numpy(np.ascontiguousarray(wl.v_cache).view(kv)).to(d),
         bt=torch.from_numpy(np.ascontiguousarray(wl.block_table)).to(d),
         L=torch.from_numpy(np.ascontiguousarray(wl.seq_lens)).to(d),
         sinks=None if wl.sinks is None else torch.from_numpy(wl.sinks).to(d),
@@ -79,14 +80,16 @@ def run_gpu(wl, t, partition_size: int = 0, max_partitions=None, num_workers: in
 
 def oracle_full(wl):
     return ref.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
-                      wl.block_size, window=wl.window, sinks=wl.sinks)
+                      wl.block_size, window=wl.window, sinks=wl.sinks, kv_format=wl.kv_format,
+                      k_scale=wl.k_scale, v_scale=wl.v_scale)
 
 
 def oracle_pairs(wl, pairs):
     outs, lses = [], []
     for b, h in pairs:
         o, l = ref.decode_one(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens,
-                              wl.scale, wl.block_size, b, h, window=wl.window, sinks=wl.sinks)
+                              wl.scale, wl.block_size, b, h, window=wl.window, sinks=wl.sinks,
+                              kv_format=wl.kv_format, k_scale=wl.k_scale, v_scale=wl.v_scale)
         outs.append(o)
         lses.append(l)
     return np.array(outs), np.array(lses)
@@ -143,3 +146,37 @@ def bench_partition(wl) -> int:
 def finite_rows(x):
     return np.isfinite(x).all(axis=-1)
 
+
+# ---------------------------------------------------------------------------------------------
+# prepared decode steps (plans)
+# ---------------------------------------------------------------------------------------------
+def make_plan(wl, schedule, partition_size=256, num_workers=0):
+    B, Hq, D = wl.q.shape
+    return pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
+                   window=wl.window, schedule=schedule, partition_size=partition_size,
+                   max_seq_len=max_len(wl), num_workers=num_workers, kv_dtype=wl.kv_format)
+
+
+def counter_bytes(wl):
+    """The fused schedule's merge counters: the last 256-byte-aligned section of its workspace."""
+    return (4 * wl.num_seqs * wl.num_kv_heads + 255) // 256 * 256
+
+
+def run_plan(plan, wl, t, workspace=None):
+    """One step through paged_attn_plan_run into NaN-filled outputs (and, unless a workspace is
+    given, a workspace whose non-counter bytes are 0xFF); returns (out, lse) as float64."""
+    B, Hq, D = wl.q.shape
+    fused = "last partition" in plan.name
+    out = torch.full((B, Hq, D), float("nan"), device="cuda")
+    lse = torch.full((B, Hq), float("nan"), device="cuda")
+    ws = workspace if workspace is not None else plan.workspace("cuda")
+    if ws is not None and workspace is None:
+        # stale contents must not matter (except the fused counters, which start at zero)
+        ws[:ws.numel() - (counter_bytes(wl) if fused else 0)].fill_(0xFF)
+    plan.run(t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale), out=out, lse=lse,
+             sinks=t["sinks"], workspace=ws, k_scale=wl.k_scale, v_scale=wl.v_scale)
+    torch.cuda.synchronize()
+    if fused:
+        assert int(torch.count_nonzero(ws[ws.numel() - counter_bytes(wl):])) == 0, \
+            "merge counters not back at zero"
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)

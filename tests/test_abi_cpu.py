@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert pa.abi_version() == 2
+    assert pa.abi_version() == 3
     for code, name in pa.STATUS_NAMES.items():
         s = pa.status_string(code)
         assert s and s != "unknown status", name
@@ -236,10 +236,11 @@ def test_balanced_empty_batch_is_ok_without_launch():
 # ---------------------------------------------------------------------------------------------
 # prepared decode (plans): creation-time checks, workspace sizes, run-time argument checks
 # ---------------------------------------------------------------------------------------------
-def plan_create(s, *, head_dim=128, block_size=16, window=0, schedule=0, workers=0, max_len=0):
+def plan_create(s, *, head_dim=128, block_size=16, window=0, schedule=0, workers=0, max_len=0,
+                kv_dtype=0):
     h = ctypes.c_void_p()
     st = pa.lib().paged_attn_plan_create(ctypes.byref(s), head_dim, block_size, window, schedule,
-                                         max_len, workers, ctypes.byref(h))
+                                         kv_dtype, max_len, workers, ctypes.byref(h))
     return st, h
 
 
@@ -273,6 +274,19 @@ def test_plan_create_and_workspace_sizes():
     st, h = plan_create(shape(), schedule=2, workers=100, max_len=100)
     assert st == 0 and b"workers8 " in pa.lib().paged_attn_plan_name(h)
     pa.lib().paged_attn_plan_destroy(h)
+    # an FP8 cache: the FP8 path under every schedule, the same workspace as bf16
+    for sched, sh in ((0, shape()), (1, s), (3, s)):
+        st, h = plan_create(sh, schedule=sched, kv_dtype=1)
+        st16, h16 = plan_create(sh, schedule=sched)
+        assert st == 0 and st16 == 0
+        assert b"mfmapv_fp8" in pa.lib().paged_attn_plan_name(h)
+        assert pa.lib().paged_attn_plan_workspace_size(h) == \
+            pa.lib().paged_attn_plan_workspace_size(h16)
+        pa.lib().paged_attn_plan_destroy(h)
+        pa.lib().paged_attn_plan_destroy(h16)
+    st, h = plan_create(shape(), schedule=2, workers=100, kv_dtype=1)
+    assert st == 0 and pa.lib().paged_attn_plan_name(h).startswith(b"pa_balanced_mfmapv_fp8_")
+    pa.lib().paged_attn_plan_destroy(h)
     pa.lib().paged_attn_plan_destroy(None)
 
 
@@ -281,7 +295,7 @@ def test_plan_create_and_workspace_sizes():
     (dict(schedule=3), -2), (dict(schedule=4), -2), (dict(schedule=-1), -2),
     (dict(head_dim=96), -3), (dict(block_size=8), -3), (dict(window=-1), -2),
     (dict(schedule=2, workers=-1), -2), (dict(schedule=2, workers=(1 << 20) + 1), -2),
-    (dict(max_len=-1), -2),
+    (dict(max_len=-1), -2), (dict(kv_dtype=2), -3), (dict(kv_dtype=-1), -3),
 ])
 def test_plan_create_rejects(kw, expect):
     st, h = plan_create(shape(), **kw)
@@ -292,27 +306,40 @@ def test_plan_unsplit_rejects_a_partitioned_shape_and_null_out_pointer():
     st, h = plan_create(shape(partition_size=512, max_partitions=4), schedule=0)
     assert st == -2
     s = shape()
-    assert pa.lib().paged_attn_plan_create(ctypes.byref(s), 128, 16, 0, 0, 0, 0, None) == -1
+    assert pa.lib().paged_attn_plan_create(ctypes.byref(s), 128, 16, 0, 0, 0, 0, 0, None) == -1
 
 
 def test_plan_run_argument_checks_without_launch():
     lib = pa.lib()
     st, h = plan_create(shape(), schedule=2, workers=64)
     assert st == 0
-    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, None, FAKE, None, FAKE, None]
+    # q k v table lens scale k_scale v_scale sinks out lse workspace stream
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 1.0, 1.0, None, FAKE, None, FAKE, None]
     assert lib.paged_attn_plan_run(None, *args) == -1
-    bad = list(args); bad[5] = float("inf")
-    assert lib.paged_attn_plan_run(h, *bad) == -2
-    for i in (0, 1, 2, 3, 4, 7):
+    for i in (5, 6, 7):
+        for v in (float("inf"), float("nan")):
+            bad = list(args); bad[i] = v
+            assert lib.paged_attn_plan_run(h, *bad) == -2, (i, v)
+    for i in (6, 7):                          # a bf16 plan takes no KV scales
+        bad = list(args); bad[i] = 0.5
+        assert lib.paged_attn_plan_run(h, *bad) == -2, i
+    for i in (0, 1, 2, 3, 4, 9):
         bad = list(args); bad[i] = None
         assert lib.paged_attn_plan_run(h, *bad) == -1, i
-    bad = list(args); bad[9] = None          # balanced plans need a workspace
+    bad = list(args); bad[11] = None          # balanced plans need a workspace
     assert lib.paged_attn_plan_run(h, *bad) == -1
-    bad = list(args); bad[9] = ctypes.c_void_p(0x1010)   # not 256-byte aligned
+    bad = list(args); bad[11] = ctypes.c_void_p(0x1010)   # not 256-byte aligned
     assert lib.paged_attn_plan_run(h, *bad) == -2
     lib.paged_attn_plan_destroy(h)
     st, h = plan_create(shape(num_seqs=0), schedule=2, workers=64)
-    assert st == 0 and lib.paged_attn_plan_run(h, *([None] * 5 + [0.1] + [None] * 5)) == 0
+    assert st == 0 and lib.paged_attn_plan_run(h, *([None] * 5 + [0.1, 1.0, 1.0] + [None] * 5)) == 0
+    lib.paged_attn_plan_destroy(h)
+    # an FP8 plan takes any finite scales; an empty batch returns before any launch
+    st, h = plan_create(shape(num_seqs=0), schedule=0, kv_dtype=1)
+    assert st == 0
+    assert lib.paged_attn_plan_run(h, *([None] * 5 + [0.1, 0.03, -2.0] + [None] * 5)) == 0
+    bad = [None] * 5 + [0.1, float("nan"), 1.0] + [None] * 5
+    assert lib.paged_attn_plan_run(h, *bad) == -2
     lib.paged_attn_plan_destroy(h)
 
 
@@ -326,3 +353,5 @@ def test_plan_binding_refuses_host_tensors():
         pa.Plan(2, 8, 2, 32, 8, 128, 16, schedule="partitioned")
     with pytest.raises(ValueError):
         pa.Plan(2, 8, 2, 32, 8, 128, 16, schedule="fast")
+    with pytest.raises(ValueError):
+        pa.Plan(2, 8, 2, 32, 8, 128, 16, schedule="unsplit", kv_dtype="fp8")

@@ -1,5 +1,6 @@
 """GPU tests of prepared decode steps (plans): parity with the fp64 oracle through
-paged_attn_plan_run for every schedule, and HIP-graph capture and replay of a run."""
+paged_attn_plan_run for every schedule, NaN inputs inside the attended range, and HIP-graph
+capture and replay of a run."""
 from __future__ import annotations
 
 import numpy as np
@@ -7,44 +8,13 @@ import pytest
 import torch
 
 import paged_kv_attention_attn_amd as pa
-from workloads import make_config, make_workload
+from workloads import FP8_QNAN, make_config, make_workload
 
-from gpu_helpers import compare, log, oracle_full, to_dev
+from gpu_helpers import compare, log, make_plan, oracle_full, run_plan, to_dev
 
 pytestmark = pytest.mark.gpu
 
 SCHEDULES = ["unsplit", "partitioned", "balanced", "fused"]
-
-
-def make_plan(wl, schedule, partition_size=256, num_workers=0):
-    B, Hq, D = wl.q.shape
-    return pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
-                   window=wl.window, schedule=schedule, partition_size=partition_size,
-                   max_seq_len=int(wl.seq_lens.max()) if wl.num_seqs else 0,
-                   num_workers=num_workers)
-
-
-def counter_bytes(wl):
-    """The fused schedule's merge counters: the last 256-byte-aligned section of its workspace."""
-    return (4 * wl.num_seqs * wl.num_kv_heads + 255) // 256 * 256
-
-
-def run_plan(plan, wl, t, workspace=None):
-    B, Hq, D = wl.q.shape
-    fused = "last partition" in plan.name
-    out = torch.full((B, Hq, D), float("nan"), device="cuda")
-    lse = torch.full((B, Hq), float("nan"), device="cuda")
-    ws = workspace if workspace is not None else plan.workspace("cuda")
-    if ws is not None and workspace is None:
-        # stale contents must not matter (except the fused counters, which start at zero)
-        ws[:ws.numel() - (counter_bytes(wl) if fused else 0)].fill_(0xFF)
-    plan.run(t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale), out=out, lse=lse,
-             sinks=t["sinks"], workspace=ws)
-    torch.cuda.synchronize()
-    if fused:
-        assert int(torch.count_nonzero(ws[ws.numel() - counter_bytes(wl):])) == 0, \
-            "merge counters not back at zero"
-    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
 def context_workload(B, L):
@@ -85,6 +55,40 @@ def test_plan_empty_batch_is_a_no_op():
     plan.run(x, x, x, x, x, 0.1, out=x, workspace=plan.workspace("cuda"))
     torch.cuda.synchronize()
     assert float(x.item()) == 0.0
+
+
+@pytest.mark.parametrize("which", ["k", "v"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_nan_in_attended_row(schedule, kv, which):
+    """A NaN (bf16 0x7FC0, or the FP8 code 0x7F) inside the attended range of one (sequence, KV
+    head): in K the oracle gives NaN outputs and LSEs for that KV head's query heads, in V NaN
+    in the one output dimension it sits in; the kernels must give NaN in exactly those places
+    and match everywhere else."""
+    wl = make_workload(name="nan", seq_lens=[200, 90, 333], num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, seed=[22], poison=True, kv_format=kv,
+                       kv_scales=(0.0625, 0.05) if kv != "bf16" else (1.0, 1.0))
+    cache = wl.k_cache if which == "k" else wl.v_cache
+    tok = 77                                     # sequence 1, KV head 1, inside its 90 tokens
+    cache[wl.block_table[1, tok // 16], 1, tok % 16, 5] = \
+        FP8_QNAN if kv != "bf16" else np.uint16(0x7FC0)
+    exp_o, exp_l = oracle_full(wl)
+    if which == "k":
+        assert np.isnan(exp_o[1, 4:8]).all() and np.isnan(exp_l[1, 4:8]).all()
+        assert np.isnan(exp_o).sum() == 4 * 128
+    else:
+        assert np.isnan(exp_o[1, 4:8, 5]).all() and np.isnan(exp_o).sum() == 4
+        assert not np.isnan(exp_l).any()
+    got_o, got_l = run_plan(make_plan(wl, schedule, partition_size=32), wl, to_dev(wl))
+    bad_o = np.argwhere(np.isnan(got_o) != np.isnan(exp_o))
+    bad_l = np.argwhere(np.isnan(got_l) != np.isnan(exp_l))
+    assert bad_o.size == 0, f"NaN pattern of out differs at {bad_o[:4].tolist()} " \
+        f"({len(bad_o)} places)"
+    assert bad_l.size == 0, f"NaN pattern of lse differs at {bad_l[:4].tolist()}"
+    ok = ~np.isnan(exp_o)
+    assert np.abs(got_o[ok] - exp_o[ok]).max() <= 1e-3
+    okl = ~np.isnan(exp_l)
+    assert np.abs(got_l[okl] - exp_l[okl]).max() <= 1e-3
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES)
