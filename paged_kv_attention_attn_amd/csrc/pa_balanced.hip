@@ -127,7 +127,8 @@ struct BalancedCtx {
 };
 
 template <int D, int G, int DEPTH, class QK>
-__global__ __launch_bounds__(kWave) void balanced_decode_kernel(const BalancedParams bp) {
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(QK::kMinWavesPerEu)))
+void balanced_decode_kernel(const BalancedParams bp) {
   using RG = RowGeom<D>;
   constexpr int E = RG::kElems;
   const DecodeParams& p = bp.d;
@@ -421,7 +422,8 @@ namespace {
 template <int D, int G, QkPath PATH>
 using BQK = QkPolicy<D, G, PATH>;
 
-// tiles in flight per worker: two where the registers allow it
+// tiles in flight per worker: two where the registers allow it (for FP8 tiles too: four,
+// for the same bytes in flight, measured slower)
 template <int D, int G, QkPath PATH>
 constexpr int bal_depth() {
   return D * G <= 512 ? 2 : 1;

@@ -37,7 +37,8 @@ namespace pa {
 // the kernel
 // ---------------------------------------------------------------------------------------------
 template <int D, int G, int NW, int DEPTH, class QK>
-__global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(QK::kMinWavesPerEu)))
+void decode_kernel(const DecodeParams p) {
   using RG = RowGeom<D>;
   constexpr int E = RG::kElems;
 

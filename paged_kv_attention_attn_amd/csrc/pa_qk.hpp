@@ -89,6 +89,7 @@ struct QkValu {
   static constexpr int W = RowGeom<D>::kWords;
   static constexpr int E = RowGeom<D>::kElems;
   static constexpr int kRowBytes = RowGeom<D>::kRowBytes;
+  static constexpr int kMinWavesPerEu = 1;
   struct Tile {
     uint32_t k[kTileSteps][W];
     uint32_t v[kTileSteps][W];
@@ -233,6 +234,7 @@ struct QkMfma {
   static constexpr int W = RowGeom<D>::kWords;
   static constexpr int E = RowGeom<D>::kElems;
   static constexpr int kRowBytes = RowGeom<D>::kRowBytes;
+  static constexpr int kMinWavesPerEu = 1;
   struct Tile {
     u32x4_t k[KK];
     uint32_t v[kTileSteps][W];
@@ -372,23 +374,22 @@ struct QkMfma {
 // ---------------------------------------------------------------------------------------------
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// Eight OCP FP8 E4M3 values (two words) -> eight bf16 (four words), exactly: the hardware
-// conversion gives their fp32 values, and an E4M3 value has at most four significant bits, so
-// packing them to bf16 (v_cvt_pk_bf16_f32) rounds nothing.  (A byte permute taking the upper
-// halves of the two floats was compiled, for gfx950, with the same source register for both
-// operands when both come from one conversion; the packing conversion has no such form.)
-__device__ __forceinline__ uint32_t f32_pair_to_bf16(f32x2_t f) {
-  const bf16x2_t h = {(__bf16)f.x, (__bf16)f.y};
-  return __builtin_bit_cast(uint32_t, h);
+// Two OCP FP8 E4M3 codes (the low or the high half of a word) -> a bf16 pair, exactly: an E4M3
+// value has at most four significant bits and an exponent inside bf16's range, and with a
+// scale of 1 gfx950's scaled conversion (v_cvt_scalef32_pk_bf16_fp8) is the plain decoding (a
+// NaN code gives a NaN).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
+// Eight codes (two words) -> eight bf16 (four words), in order.
 __device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t x) {
   u32x4_t r;
-  r.x = f32_pair_to_bf16(__builtin_amdgcn_cvt_pk_f32_fp8((int)x.x, false));
-  r.y = f32_pair_to_bf16(__builtin_amdgcn_cvt_pk_f32_fp8((int)x.x, true));
-  r.z = f32_pair_to_bf16(__builtin_amdgcn_cvt_pk_f32_fp8((int)x.y, false));
-  r.w = f32_pair_to_bf16(__builtin_amdgcn_cvt_pk_f32_fp8((int)x.y, true));
+  r.x = fp8x2_to_bf16x2<false>(x.x);
+  r.y = fp8x2_to_bf16x2<true>(x.x);
+  r.z = fp8x2_to_bf16x2<false>(x.y);
+  r.w = fp8x2_to_bf16x2<true>(x.y);
   return r;
 }
 
@@ -402,9 +403,18 @@ struct QkMfmaPvT {
   static constexpr int W = RowGeom<D>::kWords;
   static constexpr int E = RowGeom<D>::kElems;
   static constexpr int kRowBytes = FP8 ? D : 2 * D;
-  static constexpr int VW = FP8 ? (E + 3) / 4 : W;   // words a lane holds of one V row
+  // Occupancy floor handed to the compiler.  A floor of two caps a wave at 256 registers,
+  // which also makes it keep the MFMA accumulators in ordinary VGPRs instead of copying them
+  // to and from AGPRs around every branch of the tile loop.  For FP8 tiles (half the bytes per
+  // tile, so the per-tile instruction stream weighs twice as much) that pays; a floor of three
+  // (168 registers at D = 128, with two spilled) measured no better.
+  static constexpr int kMinWavesPerEu = FP8 && D <= 128 ? 2 : 1;
+  static constexpr int VW = FP8 ? E / 4 : W;   // words a lane holds of one V row
+  static_assert(!FP8 || E == 4 * VW, "an FP8 lane slice is whole words");
+  // K: bf16, one 16-byte piece per score MFMA; FP8, one 16-byte piece per two (halves)
+  static constexpr int KL = FP8 ? KK / 2 : KK;
   struct Tile {
-    typename std::conditional<FP8, u32x2_t, u32x4_t>::type k[KK];
+    u32x4_t k[KL];
     uint32_t v[kTileSteps][VW];
   };
   u32x4_t qb[KK];
@@ -424,7 +434,11 @@ struct QkMfmaPvT {
     const uint32_t keep = head_lane ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + 64 * kk + 16 * (lane >> 4));
+      // score MFMA kk, lane group g: dims 32kk + 8g .. +8 (bf16), or, matching the FP8 K
+      // pieces, 64(kk/2) + 16g + 8(kk%2) .. +8 (a permutation of the dot product's terms)
+      const int off = FP8 ? 128 * (kk >> 1) + 32 * (lane >> 4) + 16 * (kk & 1)
+                          : 64 * kk + 16 * (lane >> 4);
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + off);
       x.x = (x.x ^ qflip) & keep;
       x.y = (x.y ^ qflip) & keep;
       x.z = (x.z ^ qflip) & keep;
@@ -450,12 +464,13 @@ struct QkMfmaPvT {
     const int mrow = lane & 15;
     const int tok = 4 * (mrow & 3) + (mrow >> 2);
     if constexpr (FP8) {
-      // K: bytes 32kk + 8(lane/16) .. +8 of the token's row (the same dims as the bf16 path);
+      // K: bytes 64i + 16(lane/16) .. +16 of the token's row, i < KK/2 (16-byte pieces: 8-byte
+      // ones, one per score MFMA, halve the streaming rate); its halves feed MFMAs 2i, 2i+1.
       // V: the lane's slice of each of its four rows, E bytes (two 8-byte pieces at D = 256)
-      const char* krow = kb + tok * kRowBytes + 8 * (lane >> 4);
+      const char* krow = kb + tok * kRowBytes + 16 * (lane >> 4);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        t.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(krow + 32 * kk));
+      for (int i = 0; i < KL; ++i)
+        t.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + 64 * i));
       const int r = lane >> 4, c = lane & 15;
 #pragma unroll
       for (int j = 0; j < kTileSteps; ++j) {
@@ -491,10 +506,12 @@ struct QkMfmaPvT {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4_t kw;
-      if constexpr (FP8)
-        kw = fp8x8_to_bf16x8(t.k[kk]);
-      else
+      if constexpr (FP8) {
+        const u32x4_t x = t.k[kk >> 1];
+        kw = fp8x8_to_bf16x8((kk & 1) ? u32x2_t{x.z, x.w} : u32x2_t{x.x, x.y});
+      } else {
         kw = t.k[kk];
+      }
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw),
                                                    __builtin_bit_cast(bf16x8_t, qb[kk]), sc, 0,
                                                    0, 0);
@@ -545,34 +562,35 @@ struct QkMfmaPvT {
     const s16x4_t a_hi = __builtin_bit_cast(s16x4_t, u32x2_t{uh01, uh23});
     const s16x4_t a_lo = __builtin_bit_cast(
         s16x4_t, u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
-    // FP8: the fp32 values of the four rows' elements (exact), two per conversion
-    f32x2_t vf[FP8 ? kTileSteps : 1][FP8 ? 2 * VW : 1];
-    if constexpr (FP8) {
-#pragma unroll
-      for (int j = 0; j < kTileSteps; ++j) {
-#pragma unroll
-        for (int w = 0; w < VW; ++w) {
-          vf[j][2 * w] = __builtin_amdgcn_cvt_pk_f32_fp8((int)t.v[j][w], false);
-          vf[j][2 * w + 1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)t.v[j][w], true);
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      // B: element e of the slice of tokens 4j+g, j = 0..3 (bf16 halves gathered by v_perm)
-      uint32_t b01, b23;
-      if constexpr (FP8) {
-        const auto f = [&](int j) { return (e & 1) ? vf[j][e / 2].y : vf[j][e / 2].x; };
-        b01 = f32_pair_to_bf16(f32x2_t{f(0), f(1)});
-        b23 = f32_pair_to_bf16(f32x2_t{f(2), f(3)});
-      } else {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        b01 = __builtin_amdgcn_perm(t.v[1][e / 2], t.v[0][e / 2], sel);
-        b23 = __builtin_amdgcn_perm(t.v[3][e / 2], t.v[2][e / 2], sel);
-      }
+    // B: element e of the slice of tokens 4j+g, j = 0..3, as bf16 pairs {token 4j+g of rows
+    // j = 0, 1} and {j = 2, 3}
+    const auto pv = [&](int e, uint32_t b01, uint32_t b23) {
       const s16x4_t bv = __builtin_bit_cast(s16x4_t, u32x2_t{b01, b23});
       cacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, bv, cacc[e], 0, 0, 0);
       cacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, bv, cacc[e], 0, 0, 0);
+    };
+    if constexpr (FP8) {
+      // word w holds elements 4w..4w+3 of a row: interleave the bytes of rows (0, 1) and (2, 3)
+      // (x: elements 4w, 4w+1; y: 4w+2, 4w+3), then each half converts to one bf16 pair
+#pragma unroll
+      for (int w = 0; w < VW; ++w) {
+        const uint32_t x01 = __builtin_amdgcn_perm(t.v[1][w], t.v[0][w], 0x05010400u);
+        const uint32_t y01 = __builtin_amdgcn_perm(t.v[1][w], t.v[0][w], 0x07030602u);
+        const uint32_t x23 = __builtin_amdgcn_perm(t.v[3][w], t.v[2][w], 0x05010400u);
+        const uint32_t y23 = __builtin_amdgcn_perm(t.v[3][w], t.v[2][w], 0x07030602u);
+        pv(4 * w + 0, fp8x2_to_bf16x2<false>(x01), fp8x2_to_bf16x2<false>(x23));
+        pv(4 * w + 1, fp8x2_to_bf16x2<true>(x01), fp8x2_to_bf16x2<true>(x23));
+        pv(4 * w + 2, fp8x2_to_bf16x2<false>(y01), fp8x2_to_bf16x2<false>(y23));
+        pv(4 * w + 3, fp8x2_to_bf16x2<true>(y01), fp8x2_to_bf16x2<true>(y23));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        // bf16 halves gathered by v_perm
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        pv(e, __builtin_amdgcn_perm(t.v[1][e / 2], t.v[0][e / 2], sel),
+           __builtin_amdgcn_perm(t.v[3][e / 2], t.v[2][e / 2], sel));
+      }
     }
   }
 
