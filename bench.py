@@ -50,9 +50,10 @@ def measured_traffic(workload: str, schedule: str):
         return None
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    if rec.get("workload") != workload or rec.get("schedule") != schedule:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    for r in rec.get("records", []):
+        if r.get("workload") == workload and r.get("schedule") == schedule:
+            return r.get("hbm_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
