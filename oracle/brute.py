@@ -58,3 +58,38 @@ def decode_head(q, k_cache, v_cache, block_table, seq_lens, scale, block_size, b
         for d in range(D):
             out[d] += w * row[d]
     return [x / Z for x in out], math.log(Z)
+
+
+def decode_head_multi(q, k_cache, v_cache, block_table, seq_lens, scale, block_size, b, i, h,
+                      q_len, window=0, sinks=None):
+    """(out row, lse) for query token i (of q_len) and head h of sequence b, q[b][i][h][d].
+
+    The token sits at position L - q_len + i of the L tokens (new ones included) and sees the
+    keys at or before it, the last `window` of them when window > 0."""
+    Hq = len(q[b][i])
+    Hkv = len(k_cache[0])
+    kvh = h // (Hq // Hkv)
+    D = len(q[b][i][h])
+    pos = int(seq_lens[b]) - q_len + i
+    sc = f32(scale)
+    weights, rows = [], []
+    for t in range(0, pos + 1):
+        if window > 0 and t <= pos - window:
+            continue
+        blk = int(block_table[b][t // block_size])
+        slot = t % block_size
+        dot = 0.0
+        for d in range(D):
+            dot += bf16_to_float(q[b][i][h][d]) * bf16_to_float(k_cache[blk][kvh][slot][d])
+        weights.append(math.exp(sc * dot))
+        rows.append([bf16_to_float(v_cache[blk][kvh][slot][d]) for d in range(D)])
+    Z = sum(weights)
+    if sinks is not None:
+        Z += math.exp(f32(sinks[h]))
+    if Z == 0.0:
+        return [0.0] * D, -math.inf
+    out = [0.0] * D
+    for w, row in zip(weights, rows):
+        for d in range(D):
+            out[d] += w * row[d]
+    return [x / Z for x in out], math.log(Z)

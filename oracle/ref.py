@@ -34,6 +34,13 @@ An FP8 KV cache (the 8-bit sibling of the bf16 path, named but not specified by 
 page above) is read as OCP FP8 E4M3 codes with one fp32 scale for K and one for V: the real
 value of a stored code is its E4M3 value times the scale.  Everything after dequantisation is
 the same definition.
+
+Several new query tokens per sequence (decode_multi): the PR #13700 page's benchmark takes a
+query length (its decode runs use one), and vllm.cpp PR #564, "What is deliberately not here",
+leaves the longer-query case (prefill) out.  Reading: with q_len = Q new tokens and a sequence
+length L that counts them, query token i sits at position p = L - Q + i and attends causally,
+keys t <= p, within its own window [p + 1 - W, p] when W > 0; a position p < 0 attends nothing.
+One token (Q = 1) is the decode above.
 """
 from __future__ import annotations
 
@@ -159,6 +166,45 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table:
             K, V = rows[kvh]
             sink = None if sinks is None else float(np.float32(sinks[h]))
             out[b, h], lse[b, h] = softmax_attention(bf16_bits_to_f64(q[b, h]), K, V, sc, sink)
+    return out, lse
+
+
+def query_range(L: int, q_len: int, i: int, window: int) -> Tuple[int, int]:
+    """Keys [start, stop) that query token i of q_len attends in a sequence of length L (the new
+    tokens included): causal up to its own position p = L - q_len + i, windowed to the last W
+    keys up to p when W > 0.  Empty when p < 0."""
+    p = L - q_len + i
+    if p < 0:
+        return 0, 0
+    start = max(0, p + 1 - window) if window > 0 else 0
+    return start, p + 1
+
+
+def decode_multi(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                 block_table: np.ndarray, seq_lens: np.ndarray, scale: float, block_size: int,
+                 window: int = 0, sinks: Optional[np.ndarray] = None, kv_format: str = "bf16",
+                 k_scale: float = 1.0, v_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+    """q_len query tokens per sequence: q bf16 bits [B][Q][Hq][D] -> out float64 [B][Q][Hq][D],
+    lse float64 [B][Q][Hq].  Each (b, i, h) is the softmax attention of its query over the keys
+    query_range gives, with the head's sink."""
+    B, Q, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    out = np.zeros((B, Q, Hq, D))
+    lse = np.full((B, Q, Hq), NEG_INF)
+    sc = float(np.float32(scale))
+    for b in range(B):
+        L = int(seq_lens[b])
+        for i in range(Q):
+            start, stop = query_range(L, Q, i, window)
+            for h in range(Hq):
+                kvh = kv_head_of(h, Hq, Hkv)
+                K = kv_rows_to_f64(gather_rows(k_cache, block_table, b, kvh, start, stop,
+                                               block_size), kv_format, k_scale)
+                V = kv_rows_to_f64(gather_rows(v_cache, block_table, b, kvh, start, stop,
+                                               block_size), kv_format, v_scale)
+                sink = None if sinks is None else float(np.float32(sinks[h]))
+                out[b, i, h], lse[b, i, h] = softmax_attention(bf16_bits_to_f64(q[b, i, h]), K,
+                                                               V, sc, sink)
     return out, lse
 
 

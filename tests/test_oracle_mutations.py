@@ -54,6 +54,15 @@ def _merge_drops_last(o, lse, counts):
     return _orig_merge(o, lse, np.maximum(np.asarray(counts) - 1, 1))
 
 
+def _causal_off_by_one(L, q_len, i, window):
+    # the query's own key left out
+    p = L - q_len + i
+    if p < 0:
+        return 0, 0
+    start = max(0, p + 1 - window) if window > 0 else 0
+    return start, p
+
+
 MUTATIONS = {
     "gqa head map interleaved": ("kv_head_of", _wrong_kv_head,
                            [(pins.test_paged_equals_dense_unpaged, 0, False, 8, 2),
@@ -72,6 +81,10 @@ MUTATIONS = {
                        (pins.test_hand_worked_golden,)]),
     "merge drops last partition": ("merge_partitions", _merge_drops_last,
                                    [(pins.test_split_merge_equals_unsplit, 8, 0, True)]),
+    "multi-token causal bound off by one": ("query_range", _causal_off_by_one,
+                                            [(pins.test_multi_equals_dense_causal_masked_softmax,
+                                              3, 0, True),
+                                             (pins.test_multi_brute_force_tiny, 2, 0, True)]),
 }
 
 

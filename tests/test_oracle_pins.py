@@ -445,3 +445,110 @@ def test_fp8_scales_act_as_closed_forms():
     o4, l4 = _decode(wl, scale=np.float32(wl.scale) * np.float32(0.25))
     np.testing.assert_allclose(o3, o4, rtol=0, atol=1e-12)
     np.testing.assert_allclose(l3, l4, rtol=0, atol=1e-12)   # -inf for the empty sequence
+
+
+# ---------------------------------------------------------------------------------------------
+# several query tokens per sequence (decode_multi): causal, each token at position L - Q + i
+# ---------------------------------------------------------------------------------------------
+def run_multi(wl, **over):
+    args = dict(window=wl.window, sinks=wl.sinks)
+    args.update(over)
+    return ref.decode_multi(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
+                            wl.block_size, **args)
+
+
+def test_multi_with_one_token_is_decode():
+    wl = small([1, 4, 9, 23, 0, 17], window=5, with_sinks=True)
+    o1, l1 = run(wl)
+    om, lm = ref.decode_multi(wl.q[:, None], wl.k_cache, wl.v_cache, wl.block_table,
+                              wl.seq_lens, wl.scale, wl.block_size, window=wl.window,
+                              sinks=wl.sinks)
+    assert np.array_equal(om[:, 0], o1) and np.array_equal(lm[:, 0], l1)
+
+
+@pytest.mark.parametrize("Q,window,with_sinks", [(2, 0, False), (3, 0, True), (4, 5, False),
+                                                 (5, 3, True), (8, 1, False)])
+def test_multi_equals_dense_causal_masked_softmax(Q, window, with_sinks):
+    """Against the textbook masked form on unpaged tensors: S = scale Q K^T [Q x L], masked
+    where key t lies after the query's position or before its window, softmax by rows (scipy),
+    times V."""
+    lens = [Q + 6, 1, 23, Q, 17]
+    wl = small(lens, hq=4, hkv=2, d=8, bs=4, seed=29, q_len=Q, window=window,
+               with_sinks=with_sinks)
+    out, lse = run_multi(wl)
+    for b, L in enumerate(lens):
+        for kvh in range(2):
+            Kd = f64(ref.gather_rows(wl.k_cache, wl.block_table, b, kvh, 0, L, wl.block_size))
+            Vd = f64(ref.gather_rows(wl.v_cache, wl.block_table, b, kvh, 0, L, wl.block_size))
+            t = np.arange(L)
+            pos = L - Q + np.arange(Q)
+            allowed = t[None, :] <= pos[:, None]
+            if window > 0:
+                allowed &= t[None, :] > pos[:, None] - window
+            for h in range(2 * kvh, 2 * kvh + 2):
+                S = float(wl.scale) * (f64(wl.q[b, :, h]) @ Kd.T)
+                S = np.where(allowed, S, -np.inf)
+                if with_sinks:
+                    S = np.concatenate([S, np.full((Q, 1), float(wl.sinks[h]))], axis=1)
+                for i in range(Q):
+                    if not np.isfinite(S[i]).any():
+                        assert lse[b, i, h] == -np.inf and not out[b, i, h].any()
+                        continue
+                    p = softmax(S[i])
+                    assert np.abs(out[b, i, h] - p[:L] @ Vd).max() < 1e-12
+                    assert abs(lse[b, i, h] - logsumexp(S[i])) < 1e-12
+
+
+def test_multi_token_equals_decode_of_its_prefix():
+    """Query token i of Q sees exactly what a one-token decode of the first L - Q + i + 1
+    tokens sees (the causal rule)."""
+    Q = 4
+    lens = [9, 23, 4, 2]
+    wl = small(lens, hq=4, hkv=2, d=8, bs=4, seed=31, q_len=Q, window=6, with_sinks=True)
+    out, lse = run_multi(wl)
+    for i in range(Q):
+        prefix = np.maximum(wl.seq_lens - Q + i + 1, 0).astype(np.int32)
+        o1, l1 = ref.decode(wl.q[:, i], wl.k_cache, wl.v_cache, wl.block_table, prefix,
+                            wl.scale, wl.block_size, window=wl.window, sinks=wl.sinks)
+        assert np.array_equal(out[:, i], o1) and np.array_equal(lse[:, i], l1), i
+
+
+def test_multi_positions_before_the_sequence_attend_nothing():
+    Q = 4
+    wl = small([2, 0], hq=2, hkv=1, d=4, bs=4, seed=5, q_len=Q, with_sinks=True)
+    out, lse = run_multi(wl)
+    # sequence 0: tokens 0 and 1 sit at positions -2 and -1, tokens 2 and 3 at 0 and 1
+    for b, first_real in ((0, 2), (1, Q)):
+        for i in range(first_real):
+            assert not out[b, i].any()
+            assert np.array_equal(lse[b, i], wl.sinks.astype(np.float64))
+    assert np.isfinite(lse[0, 2:]).all() and out[0, 2:].any()
+
+
+@pytest.mark.parametrize("Q,window,with_sinks", [(2, 0, True), (3, 2, False), (4, 3, True)])
+def test_multi_brute_force_tiny(Q, window, with_sinks):
+    wl = small([Q + 5, 3, Q], hq=2, hkv=1, d=4, bs=2, seed=37, q_len=Q, window=window,
+               with_sinks=with_sinks)
+    out, lse = run_multi(wl)
+    q = wl.q.tolist()
+    k = wl.k_cache.tolist()
+    v = wl.v_cache.tolist()
+    bt = wl.block_table.tolist()
+    for b in range(wl.num_seqs):
+        for i in range(Q):
+            for h in range(wl.num_q_heads):
+                eo, el = brute.decode_head_multi(q, k, v, bt, wl.seq_lens.tolist(),
+                                                 float(wl.scale), wl.block_size, b, i, h, Q,
+                                                 window, None if wl.sinks is None
+                                                 else wl.sinks.tolist())
+                assert np.abs(out[b, i, h] - np.array(eo)).max() < 1e-12
+                assert (lse[b, i, h] == el == -math.inf) or abs(lse[b, i, h] - el) < 1e-12
+
+
+def test_multi_workload_poison_spares_every_query_window():
+    """The generator's poison must leave every key some query token attends finite."""
+    Q, W = 3, 5
+    wl = small([20, 9, 3], hq=2, hkv=1, d=4, bs=4, seed=41, q_len=Q, window=W, poison=True)
+    out, lse = run_multi(wl)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert wl.attended_tokens().tolist() == [min(20, W + Q - 1), min(9, W + Q - 1), 3]

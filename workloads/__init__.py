@@ -122,7 +122,7 @@ class Workload:
     seq_lens: np.ndarray            # int32 [B]
     block_table: np.ndarray         # int32 [B][stride]
     num_blocks: int
-    q: np.ndarray                   # uint16 [B][Hq][D]
+    q: np.ndarray                   # uint16 [B][Hq][D], or [B][q_len][Hq][D] when q_len > 1
     k_cache: np.ndarray             # [NB][Hkv][bs][D]: uint16 bf16 bits, or uint8 FP8 E4M3 codes
     v_cache: np.ndarray
     scale: np.float32
@@ -133,6 +133,7 @@ class Workload:
     kv_format: str = "bf16"         # "bf16" or "fp8_e4m3"
     k_scale: float = 1.0            # FP8: value = code value * scale
     v_scale: float = 1.0
+    q_len: int = 1                  # new query tokens per sequence (the last q_len positions)
 
     @property
     def group(self) -> int:
@@ -142,9 +143,16 @@ class Workload:
     def stride(self) -> int:
         return int(self.block_table.shape[1])
 
+    @property
+    def window_span(self) -> int:
+        """Keys before the last position that some query token can see: the union of the
+        q_len queries' windows is W + q_len - 1 keys (0 = no window)."""
+        return self.window + self.q_len - 1 if self.window > 0 else 0
+
     def attended_tokens(self) -> np.ndarray:
+        """Tokens of each sequence that at least one query attends (their union)."""
         L = self.seq_lens.astype(np.int64)
-        return np.minimum(L, self.window) if self.window > 0 else L
+        return np.minimum(L, self.window_span) if self.window > 0 else L
 
     def kv_bytes(self) -> int:
         """Algorithmic K+V bytes one decode step must read: every attended token's K and V row,
@@ -163,7 +171,7 @@ def make_workload(*, name: str, seq_lens: Sequence[int], num_q_heads: int, num_k
                   window: int = 0, with_sinks: bool = False, k_mult: float = 1.0,
                   partition_size: int = 0, poison: bool = False, stride: Optional[int] = None,
                   scale: Optional[float] = None, unused_entry: str = "spare",
-                  kv_format: str = "bf16", kv_scales=(1.0, 1.0)) -> Workload:
+                  kv_format: str = "bf16", kv_scales=(1.0, 1.0), q_len: int = 1) -> Workload:
     """Build one seeded workload.
 
     Physical blocks are a seeded permutation of the pool; sequences take consecutive slices of it
@@ -171,6 +179,8 @@ def make_workload(*, name: str, seq_lens: Sequence[int], num_q_heads: int, num_k
     (never attended) block, or hold -1 when ``unused_entry == "invalid"``.  With ``poison`` every
     K/V slot that no query attends (spare blocks, the tail slots of each last block, and the
     tokens before a sliding window) holds a bf16 NaN, so any stray read shows up in the output.
+    With ``q_len`` > 1 there are q_len query tokens per sequence (q is [B][q_len][Hq][D]); the
+    lengths count them, and the poison spares every key some query token attends.
     """
     root = np.random.SeedSequence(seed)
     L = np.asarray(seq_lens, dtype=np.int32)
@@ -195,7 +205,11 @@ def make_workload(*, name: str, seq_lens: Sequence[int], num_q_heads: int, num_k
         off += n
 
     Hq, Hkv, D = int(num_q_heads), int(num_kv_heads), int(head_dim)
-    q = normal_bf16(root, S_Q, B * Hq * D).reshape(B, Hq, D)
+    Q = int(q_len)
+    if Q < 1:
+        raise ValueError("q_len must be at least 1")
+    q = normal_bf16(root, S_Q, B * Q * Hq * D)
+    q = q.reshape(B, Hq, D) if Q == 1 else q.reshape(B, Q, Hq, D)
     nkv = num_blocks * Hkv * bs * D
     if kv_format == "bf16":
         k = normal_bf16(root, S_K, nkv, k_mult).reshape(num_blocks, Hkv, bs, D)
@@ -211,14 +225,14 @@ def make_workload(*, name: str, seq_lens: Sequence[int], num_q_heads: int, num_k
     if with_sinks:
         sinks = _rng(root, S_SINKS).standard_normal(Hq, dtype=np.float32)
     if poison:
-        _poison(k, v, bt, L, bs, window, perm[used:], nan)
+        _poison(k, v, bt, L, bs, window + Q - 1 if window > 0 else 0, perm[used:], nan)
     sc = np.float32(1.0 / math.sqrt(D)) if scale is None else np.float32(scale)
     return Workload(name=name, num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                     block_size=bs, seq_lens=L, block_table=bt, num_blocks=int(num_blocks),
                     q=q, k_cache=k, v_cache=v, scale=sc, window=int(window), sinks=sinks,
                     partition_size=int(partition_size), meta={"seed": str(seed)},
                     kv_format=kv_format, k_scale=float(np.float32(kv_scales[0])),
-                    v_scale=float(np.float32(kv_scales[1])))
+                    v_scale=float(np.float32(kv_scales[1])), q_len=Q)
 
 
 def _poison(k, v, bt, L, bs, window, spare_blocks, nan=BF16_QNAN) -> None:
@@ -279,16 +293,18 @@ FP8_SCALES = (0.0625, 0.05)
 
 def make_config(idx: int, *, head_dim: int = 128, num_q_heads: Optional[int] = None,
                 poison: bool = False, seq_lens: Optional[Sequence[int]] = None,
-                kv_format: str = "bf16") -> Workload:
+                kv_format: str = "bf16", q_len: int = 1) -> Workload:
     """Workload ``idx`` in 1..5.  Workload 3 is a sweep: pick the point with ``head_dim`` in
     {64,128,256} and ``num_q_heads`` in {8,32,64} (8 KV heads).  ``kv_format="fp8_e4m3"`` gives
     the same workload with an FP8 E4M3 KV cache (scales FP8_SCALES)."""
     L = config_seq_lens(idx) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
     name = CONFIG_NAMES[idx]
     kw = dict(poison=poison, kv_format=kv_format,
-              kv_scales=FP8_SCALES if kv_format == "fp8_e4m3" else (1.0, 1.0))
+              kv_scales=FP8_SCALES if kv_format == "fp8_e4m3" else (1.0, 1.0), q_len=q_len)
     if kv_format != "bf16":
         name = f"{name} kv={kv_format}"
+    if q_len > 1:
+        name = f"{name} q_len={q_len}"
     if idx == 1:
         return make_workload(name=name, seq_lens=L, num_q_heads=4, num_kv_heads=2, head_dim=128,
                              block_size=16, num_blocks=32, seed=[BASE_SEED, 1], **kw)
