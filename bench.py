@@ -67,9 +67,10 @@ def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
     with threadpool_limits(1):
         while dt < min_seconds:
             t0 = time.perf_counter()
-            ref.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
-                       wl.block_size, window=wl.window, sinks=wl.sinks, kv_format=wl.kv_format,
-                       k_scale=wl.k_scale, v_scale=wl.v_scale)
+            fn = ref.decode_multi if wl.q_len > 1 else ref.decode
+            fn(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
+               wl.block_size, window=wl.window, sinks=wl.sinks, kv_format=wl.kv_format,
+               k_scale=wl.k_scale, v_scale=wl.v_scale)
             dt += time.perf_counter() - t0
             reps += 1
     return {"value": round(wl.kv_bytes() * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
@@ -220,6 +221,9 @@ def main() -> int:
     ap.add_argument("--kv", choices=["bf16", "fp8_e4m3"], default="bf16",
                     help="KV cache format; fp8_e4m3 runs through a prepared plan (the timed "
                          "kernel interval then spans the decode and merge launches)")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per sequence (> 1: causal, balanced schedule, through a "
+                         "prepared plan like --kv fp8_e4m3)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -248,9 +252,10 @@ def main() -> int:
     kw = {}
     if args.config == 3:
         kw = dict(head_dim=args.head_dim, num_q_heads=args.q_heads or 32)
-    wl = make_config(args.config, kv_format=args.kv, **kw)
+    wl = make_config(args.config, kv_format=args.kv, q_len=args.q_len, **kw)
     fp8 = args.kv != "bf16"
-    B, Hq, D = wl.q.shape
+    planned = fp8 or args.q_len > 1
+    B, Hq, D = wl.num_seqs, wl.num_q_heads, wl.head_dim
     maxL = int(wl.seq_lens.max())
     if args.schedule == "unsplit":
         P = 0
@@ -278,8 +283,8 @@ def main() -> int:
     k0, v0 = up(wl.k_cache), up(wl.v_cache)
     ks = [k0] + [k0.clone() for _ in range(copies - 1)]
     vs = [v0] + [v0.clone() for _ in range(copies - 1)]
-    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    out = torch.empty(wl.q.shape, dtype=torch.float32, device=dev)      # [B]([Q])[Hq][D]
+    lse = torch.empty(wl.q.shape[:-1], dtype=torch.float32, device=dev)
     if P > 0:
         part = torch.empty((B, Hq, pmax, D), dtype=torch.float32, device=dev)
         plse = torch.empty((B, Hq, pmax), dtype=torch.float32, device=dev)
@@ -287,10 +292,11 @@ def main() -> int:
     shape = pa.make_shape(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, max(P, 0), pmax)
     workers = args.workers
     plan = None
-    if fp8:
+    if planned:
         plan = pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
                        window=wl.window, schedule=args.schedule, partition_size=max(P, 0),
-                       max_seq_len=maxL, num_workers=workers, kv_dtype=args.kv)
+                       max_seq_len=maxL, num_workers=workers, kv_dtype=args.kv,
+                       q_len=args.q_len)
         plan_ws = plan.workspace(dev)
         variant = plan.name
         if P < 0:
@@ -369,7 +375,7 @@ def main() -> int:
     del probe
 
     workload = f"config{args.config}" + (f"_d{D}_hq{Hq}" if args.config == 3 else "") + \
-        ("_fp8" if fp8 else "")
+        ("_fp8" if fp8 else "") + (f"_q{args.q_len}" if args.q_len > 1 else "")
     traffic = measured_traffic(workload, args.schedule)
     res = {
         "metric": METRIC if not fp8 else METRIC.replace("bf16 d=128", "FP8 E4M3 KV d=128"),
@@ -392,6 +398,7 @@ def main() -> int:
             "block_size": wl.block_size, "window": wl.window,
             "sinks": wl.sinks is not None, "seq_len_sum": int(wl.seq_lens.sum()),
             "max_seq_len": maxL, "schedule": args.schedule, "kv_dtype": args.kv,
+            "q_len": args.q_len,
             "partition_size": P if P > 0 else None,
             "workers": workers if P < 0 else None, "kv_bytes_per_step": kv_bytes,
             "variant": variant, "kv_pool_copies": copies, "parallelism": "none (1 GPU)",
@@ -405,7 +412,7 @@ def main() -> int:
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "decode_us_avg": round(dec_avg_s * 1e6, 3),
-            "interval": "decode and merge launches" if fp8 else "decode launch",
+            "interval": "decode and merge launches" if planned else "decode launch",
             "algorithmic_bytes_per_launch": kv_bytes,
             "attainable_stream_read_GBps": round(attainable, 1),
         },

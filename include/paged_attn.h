@@ -235,6 +235,18 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  *                  #13700, Summary: the prepared path is the non-FP8 one); the format and the
  *                  per-tensor scales are this library's reading, the pages give none.  Every
  *                  schedule supports it; other values give PA_ERR_UNSUPPORTED.
+ *   q_len          new query tokens per sequence, >= 1 (1 = one-token decode).  With q_len > 1
+ *                  the run takes q bf16 [B][q_len][Hq][head_dim] and writes out fp32
+ *                  [B][q_len][Hq][head_dim] and lse fp32 [B][q_len][Hq]; seq_lens count the new
+ *                  tokens, token i of sequence b sits at position seq_lens[b] - q_len + i and
+ *                  attends causally: keys t <= its position, the last `window` of them when
+ *                  window > 0 (a position below 0 attends nothing: out 0, lse -inf or the sink).
+ *                  This is the query length the one-token decode benchmark of ROCm/rocm-libraries
+ *                  PR #13700 fixes at 1, and the longer-query case vllm.cpp PR #564 ("What is
+ *                  deliberately not here") leaves out; the causal rule is this library's reading.
+ *                  Every K/V row is read once per KV head for all q_len tokens: the (token, head)
+ *                  pairs of a KV head share the tile.  Requires PA_SCHEDULE_BALANCED and
+ *                  q_len * Hq/Hkv <= 16 (else PA_ERR_UNSUPPORTED); bf16 and FP8 caches alike.
  *   max_seq_len    host-side upper bound on the lengths the plan will see, or 0 if unknown.
  *                  Balanced plans launch no more workers than that many tiles can keep busy
  *                  (a small batch then does not pay for thousands of idle workers); a length
@@ -267,7 +279,8 @@ enum {
 
 pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,
                                  int32_t window, int32_t schedule, int32_t kv_dtype,
-                                 int32_t max_seq_len, int32_t num_workers, pa_plan** plan);
+                                 int32_t q_len, int32_t max_seq_len, int32_t num_workers,
+                                 pa_plan** plan);
 
 /* Device workspace bytes a run needs (0 for the unsplit schedule): the partition partials and
  * their LSEs (plus one merge counter per (sequence, KV head) for the fused schedule), or the

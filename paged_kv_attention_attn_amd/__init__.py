@@ -66,7 +66,7 @@ def _load() -> ctypes.CDLL:
                                              ctypes.c_size_t, i32, vp]),
         "paged_attn_balanced_workspace_size": (ctypes.c_int64, [sp, i32, i32]),
         "paged_attn_balanced_default_workers": (i32, [i32, i32]),
-        "paged_attn_plan_create": (i32, [sp, i32, i32, i32, i32, i32, i32, i32,
+        "paged_attn_plan_create": (i32, [sp, i32, i32, i32, i32, i32, i32, i32, i32,
                                          ctypes.POINTER(vp)]),
         "paged_attn_plan_workspace_size": (ctypes.c_int64, [vp]),
         "paged_attn_plan_run": (i32, [vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp, vp,
@@ -365,14 +365,16 @@ class Plan:
     (partitioned, merged in the same launch by the last partition to finish) or
     "balanced" (``num_workers``, 0 = the device default; ``max_seq_len``, a bound on the
     lengths, caps the workers of a small batch).  ``kv_dtype`` is "bf16" or "fp8_e4m3" (KV
-    pools of one byte per value, uint8 tensors, with per-tensor scales given to run()).  run()
-    records only kernel launches on the stream, so it can be captured in a CUDA/HIP graph."""
+    pools of one byte per value, uint8 tensors, with per-tensor scales given to run()).
+    ``q_len`` > 1 (balanced schedule): q_len causal query tokens per sequence, q [B][q_len][Hq][D]
+    -> out [B][q_len][Hq][D], lse [B][q_len][Hq].  run() records only kernel launches on the
+    stream, so it can be captured in a CUDA/HIP graph."""
 
     def __init__(self, num_seqs: int, num_q_heads: int, num_kv_heads: int, num_blocks: int,
                  block_table_stride: int, head_dim: int, block_size: int, *, window: int = 0,
                  schedule: str = "balanced", partition_size: int = 0,
                  max_seq_len: Optional[int] = None, num_workers: int = 0,
-                 kv_dtype: str = "bf16"):
+                 kv_dtype: str = "bf16", q_len: int = 1):
         if schedule not in SCHEDULES:
             raise ValueError(f"schedule must be one of {sorted(SCHEDULES)}")
         if kv_dtype not in KV_DTYPES:
@@ -392,7 +394,7 @@ class Plan:
         self._h = ctypes.c_void_p()
         st = _lib.paged_attn_plan_create(ctypes.byref(self.shape), int(head_dim), int(block_size),
                                          int(window), SCHEDULES[schedule], KV_DTYPES[kv_dtype],
-                                         int(max_seq_len or 0), int(num_workers),
+                                         int(q_len), int(max_seq_len or 0), int(num_workers),
                                          ctypes.byref(self._h))
         if st != PA_OK:
             raise PagedAttnError(st, "paged_attn_plan_create")

@@ -23,7 +23,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 constexpr int32_t kMaxGridYZ = 65535;
 
 int log2_exact(int32_t v) {
@@ -169,6 +169,8 @@ pa_status paged_attn_decode(const pa_shape* shape, const void* q, const void* k_
   p.window = window;
   p.psize = shape->partition_size;
   p.max_parts = split ? shape->max_partitions : 1;
+  p.q_len = 1;
+  p.group = group;
   if (debug_log())
     std::fprintf(stderr, "[paged_attn] decode %s B=%d Hq=%d Hkv=%d bs=%d P=%d Pmax=%d W=%d\n",
                  pa::decode_variant_name(head_dim, group, waves, split, path), shape->num_seqs,
@@ -263,6 +265,8 @@ pa_status balanced_setup(const pa_shape* shape, int32_t head_dim, int32_t block_
   p.window = window;
   p.psize = 0;
   p.max_parts = 1;
+  p.q_len = 1;
+  p.group = group;
   char* ws = static_cast<char*>(workspace);
   bp->prefix = reinterpret_cast<int64_t*>(ws + wl.prefix);
   bp->ws_lse = reinterpret_cast<float*>(ws + wl.lse);
@@ -448,7 +452,9 @@ pa_status paged_attn_copy(void* dst, const void* src, size_t bytes, void* stream
 struct pa_plan {
   int32_t schedule;
   int32_t kv_dtype;
-  int32_t head_dim, group, waves, num_workers;
+  int32_t head_dim;
+  int32_t group;          // kernel columns: Hq/Hkv, or (q_len > 1) q_len*Hq/Hkv rounded up to 2^k
+  int32_t waves, num_workers;
   pa::QkPath path;
   pa::DecodeParams dec;   // sizes; pointers are filled per run
   pa::ReduceParams red;   // partitioned schedule: sizes
@@ -461,8 +467,10 @@ struct pa_plan {
 
 namespace {
 
+constexpr int32_t kMaxColumns = 16;   // (query token, head) pairs per KV head and kernel
+
 pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size, int32_t window,
-                     int32_t schedule, int32_t kv_dtype, int32_t max_seq_len,
+                     int32_t schedule, int32_t kv_dtype, int32_t q_len, int32_t max_seq_len,
                      int32_t num_workers, pa_plan* pl) {
   const pa_status st = check_shape(shape);
   if (st != PA_OK) return st;
@@ -482,9 +490,22 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
        num_workers > kMaxWorkers))
     return PA_ERR_SHAPE;
   if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+  if (q_len < 1) return PA_ERR_SHAPE;
+  int32_t columns = group;
+  if (q_len > 1) {
+    // several query tokens: the balanced schedule, (token, head) columns on the matrix cores
+    if (schedule != PA_SCHEDULE_BALANCED) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)q_len * group > kMaxColumns) return PA_ERR_UNSUPPORTED;
+    if (window > 0x7FFFFFFF - q_len) return PA_ERR_SHAPE;
+    if ((int64_t)shape->num_seqs * q_len * shape->num_q_heads > 0x7FFFFFFF) return PA_ERR_SHAPE;
+    columns = 1;
+    while (columns < q_len * group) columns *= 2;
+  }
   pa::QkPath path;
   if (kv_dtype == PA_KV_FP8_E4M3)
     path = pa::QkPath::kMfmaPvFp8;   // the one path that reads FP8 rows
+  else if (q_len > 1)
+    path = pa::QkPath::kMfmaPv;      // the one path with column-wise query tokens
   else if (decode_path(head_dim, group, &path) != 0)
     return PA_ERR_UNSUPPORTED;
   const int waves = decode_waves(head_dim, group, parted ? shape->partition_size : 0);
@@ -493,7 +514,7 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   pl->schedule = schedule;
   pl->kv_dtype = kv_dtype;
   pl->head_dim = head_dim;
-  pl->group = group;
+  pl->group = columns;
   pl->waves = waves;
   pl->path = path;
   pl->num_workers = 0;
@@ -511,6 +532,8 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   p.window = window;
   p.psize = parted ? shape->partition_size : 0;
   p.max_parts = parted ? shape->max_partitions : 1;
+  p.q_len = q_len;
+  p.group = group;
   pl->red = pa::ReduceParams{};
   const char* dname = pa::decode_variant_name(head_dim, group, waves, parted, path);
   if (schedule == PA_SCHEDULE_UNSPLIT) {
@@ -532,21 +555,25 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
     std::snprintf(pl->name, sizeof(pl->name), "%s + merge by the last partition", dname);
   } else {
     if (num_workers == 0) {
-      num_workers = pa::balanced_default_workers(head_dim, group, path);
+      num_workers = pa::balanced_default_workers(head_dim, columns, path);
       if (num_workers <= 0) return PA_ERR_LAUNCH;
     }
     if (max_seq_len > 0) {
-      // at most this many 16-token tiles (a window start may add one), four per worker
-      const int64_t span = window > 0 && window < max_seq_len ? window : max_seq_len;
+      // at most this many 16-token tiles (a window start may add one), four per worker; the
+      // query tokens' windows together span window + q_len - 1 keys
+      const int64_t wspan = window > 0 ? (int64_t)window + q_len - 1 : 0;
+      const int64_t span = wspan > 0 && wspan < max_seq_len ? wspan : max_seq_len;
       const int64_t tiles = (int64_t)shape->num_seqs * shape->num_kv_heads * ((span + 15) / 16 + 1);
       const int64_t cap = (tiles + 3) / 4;
       if (cap < num_workers) num_workers = (int32_t)(cap < 1 ? 1 : cap);
     }
     pl->num_workers = num_workers;
-    pl->bal = ws_layout(shape->num_seqs, group, head_dim, num_workers);
+    pl->bal = ws_layout(shape->num_seqs, columns, head_dim, num_workers);
     pl->workspace_bytes = (int64_t)pl->bal.total;
-    std::snprintf(pl->name, sizeof(pl->name), "pa_balanced_%s_d%d_g%d_workers%d + fixup",
-                  pa::qk_path_name(path), head_dim, group, num_workers);
+    char qtag[32] = "";
+    if (q_len > 1) std::snprintf(qtag, sizeof(qtag), "_q%d_c%d", q_len, columns);
+    std::snprintf(pl->name, sizeof(pl->name), "pa_balanced_%s_d%d_g%d%s_workers%d + fixup",
+                  pa::qk_path_name(path), head_dim, group, qtag, num_workers);
   }
   return PA_OK;
 }
@@ -557,13 +584,14 @@ extern "C" {
 
 pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,
                                  int32_t window, int32_t schedule, int32_t kv_dtype,
-                                 int32_t max_seq_len, int32_t num_workers, pa_plan** plan) {
+                                 int32_t q_len, int32_t max_seq_len, int32_t num_workers,
+                                 pa_plan** plan) {
   if (plan == nullptr) return PA_ERR_NULL;
   *plan = nullptr;
   pa_plan* pl = new (std::nothrow) pa_plan;
   if (pl == nullptr) return PA_ERR_LAUNCH;
   const pa_status st =
-      plan_build(shape, head_dim, block_size, window, schedule, kv_dtype, max_seq_len,
+      plan_build(shape, head_dim, block_size, window, schedule, kv_dtype, q_len, max_seq_len,
                  num_workers, pl);
   if (st != PA_OK) {
     delete pl;

@@ -54,6 +54,13 @@ __device__ __forceinline__ SeqSpan seq_span(int L, int window, int64_t cap) {
   return s;
 }
 
+// Window that decides a unit's tiles: with q_len query tokens the union of their windows is
+// window + q_len - 1 keys ending at the last position (0 = no window).  The host keeps the sum
+// in range.
+__device__ __forceinline__ int span_window(const DecodeParams& p) {
+  return p.window > 0 ? p.window + p.q_len - 1 : 0;
+}
+
 // Workers actually used for T_total tiles, out of at most n.
 __device__ __forceinline__ int effective_workers(int64_t total, int n) {
   const int64_t want = (total + kMinTilesPerWorker - 1) / kMinTilesPerWorker;
@@ -105,7 +112,7 @@ struct BalancedCtx {
   const DecodeParams* p;
   int64_t cap;
   __device__ __forceinline__ SeqSpan span(int b) const {
-    return seq_span(__builtin_amdgcn_readfirstlane(p->seq_lens[b]), p->window, cap);
+    return seq_span(__builtin_amdgcn_readfirstlane(p->seq_lens[b]), span_window(*p), cap);
   }
   // next tile; skips sequences without tiles (callers never step past the last tile)
   __device__ __forceinline__ void advance(Cursor& c) const {
@@ -141,7 +148,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
   int64_t carry = 0;
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int j = base + lane;
-    const int64_t T = j < p.num_seqs ? seq_span(p.seq_lens[j], p.window, ctx.cap).T : 0;
+    const int64_t T = j < p.num_seqs ? seq_span(p.seq_lens[j], span_window(p), ctx.cap).T : 0;
     const int64_t incl = wave_incl_scan64(T, lane) + carry;
     if (w == 0 && j < p.num_seqs) bp.prefix[j] = incl - T;
     carry = readlane64(incl, kWave - 1);
@@ -159,7 +166,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
   carry = 0;
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int j = base + lane;
-    const int64_t T = j < p.num_seqs ? seq_span(p.seq_lens[j], p.window, ctx.cap).T : 0;
+    const int64_t T = j < p.num_seqs ? seq_span(p.seq_lens[j], span_window(p), ctx.cap).T : 0;
     const int64_t incl = wave_incl_scan64(T, lane) + carry;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(j < p.num_seqs &&
                                                      incl * p.num_kv_heads > A);
@@ -180,7 +187,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
   const float c2 = fabsf(p.qk_scale_log2);
   const uint32_t qflip = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
   QK qk;
-  qk.init(p, cur.b, cur.kvh * G, lane, qflip, c2);
+  qk.init(p, cur.b, cur.kvh * p.group, lane, qflip, c2);
 
   // the issue cursor, with the block-table entry of the next tile fetched one issue ahead; it
   // only advances while another tile of this worker follows, so it never walks past the last
@@ -210,18 +217,69 @@ void balanced_decode_kernel(const BalancedParams bp) {
 
   // flush the current piece of unit (at.b, at.kvh), which ends at tile at.ti
   auto flush = [&](const Cursor& at) {
+    if constexpr (QK::kColumns) {
+      // by columns: lane (r, c) finishes columns 4r + i, i < 4, that exist
+      qk.merge_cols();
+      const bool whole = piece_start == 0 && at.ti == at.s.T - 1;
+      const int ncols = p.q_len * p.group;
+      const int sh = __builtin_ctz((unsigned)p.group);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 4 * (lane >> 4) + i;
+        float M = qk.col_m(n), lt = qk.col_l(n);   // every lane takes part in the reads
+        if (n < ncols) {
+          const int hq = at.kvh * p.group + (n & (p.group - 1));
+          float scale_o = 1.f;
+          if (whole && p.sinks != nullptr) {
+            // the sink logit joins the max and the denominator with a zero value row
+            const float s2 = p.sinks[hq] * kLog2e;
+            const float M2 = fmaxf(M, s2);
+            const float M2u = M2 == -INFINITY ? 0.f : M2;
+            scale_o = fast_exp2(M - M2u);
+            lt = fmaf(lt, scale_o, fast_exp2(s2 - M2u));
+            M = M2;
+          }
+          // lt is 0 only for an empty piece; a NaN input (lt = NaN) must reach the outputs
+          const float inv = lt != 0.f ? scale_o / lt : 0.f;
+          float lv = lt != 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
+          if (piece_bad) lv = __builtin_nanf("");
+          float* dst;
+          if (whole) {
+            const size_t row = ((size_t)at.b * p.q_len + (n >> sh)) * p.num_q_heads + hq;
+            dst = p.out + row * D;
+            if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
+          } else {
+            const size_t slot = ((size_t)w * 2 + (first_piece ? 0 : 1)) * G + n;
+            dst = bp.ws_o + slot * D;
+            if (c == 0) bp.ws_lse[slot] = lv;
+          }
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            dst[RG::dim(c, e)] = piece_bad ? __builtin_nanf("") : qk.acc(i, e) * inv;
+        }
+      }
+      first_piece = false;
+      piece_bad = false;
+      piece_start = 0;
+      return;
+    } else {
+    // by heads, on the lanes of row group 0: column h (query token h / group) for h < G
     float Mh[G], lh[G];
     qk.merge_rows(Mh, lh);
     const bool whole = piece_start == 0 && at.ti == at.s.T - 1;
-    const int h0 = at.kvh * G;
+    const int h0 = at.kvh * p.group;
+    const int ncols = p.q_len * p.group;
+    const int sh = __builtin_ctz((unsigned)p.group);
     if (lane < kRowLanes) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
+        if (h >= ncols) break;   // padding columns (uniform)
+        const int hq = h0 + (h & (p.group - 1));
         float M = Mh[h], lt = lh[h];
         float scale_o = 1.f;
         if (whole && p.sinks != nullptr) {
           // the sink logit joins the max and the denominator with a zero value row
-          const float s2 = p.sinks[h0 + h] * kLog2e;
+          const float s2 = p.sinks[hq] * kLog2e;
           const float M2 = fmaxf(M, s2);
           const float M2u = M2 == -INFINITY ? 0.f : M2;
           scale_o = fast_exp2(M - M2u);
@@ -234,7 +292,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
         if (piece_bad) lv = __builtin_nanf("");
         float* dst;
         if (whole) {
-          const size_t row = (size_t)at.b * p.num_q_heads + h0 + h;
+          const size_t row = ((size_t)at.b * p.q_len + (h >> sh)) * p.num_q_heads + hq;
           dst = p.out + row * D;
           if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
         } else {
@@ -250,16 +308,32 @@ void balanced_decode_kernel(const BalancedParams bp) {
     first_piece = false;
     piece_bad = false;
     piece_start = 0;
+    }
   };
 
   auto consume = [&](int k, typename QK::Tile& t, const Slot& s, const Slot* next) {
     const Cursor& at = s.at;
     if (s.ok) {
       const int tok0 = (at.s.t0 + at.ti) * kTileTokens;
-      if (tok0 >= at.s.start && tok0 + kTileTokens <= at.s.L)
-        qk.template consume<false>(t, 0, 0, 0, lane);
-      else
-        qk.template consume<true>(t, tok0, at.s.start, at.s.L, lane);
+      if constexpr (QK::kQueryTokens) {
+        // every column sees the keys inside [lo_all, hi_all): from the last query token's
+        // window start to the first query token's position (with one token: the attended range)
+        const int hi_all = at.s.L - p.q_len + 1;
+        const int lo_all = (p.window > 0 && at.s.L > p.window) ? at.s.L - p.window : 0;
+        if (tok0 >= lo_all && tok0 + kTileTokens <= hi_all) {
+          qk.template consume<false>(t, 0, 0, 0, lane);
+        } else {
+          // this lane's column: its query token's keys [lo, hi)
+          const int hi = at.s.L - p.q_len + qk.col_q + 1;
+          const int lo = p.window > 0 ? max(hi - p.window, 0) : 0;
+          qk.template consume<true>(t, tok0, lo, hi, at.s.start, at.s.L, lane);
+        }
+      } else {
+        if (tok0 >= at.s.start && tok0 + kTileTokens <= at.s.L)
+          qk.template consume<false>(t, 0, 0, 0, lane);
+        else
+          qk.template consume<true>(t, tok0, at.s.start, at.s.L, lane);
+      }
     } else {
       piece_bad = true;
     }
@@ -267,7 +341,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
       flush(at);
       if (k + 1 < n) {
         // the next tile starts the next unit: its q, fresh state
-        qk.load_q(p, next->at.b, next->at.kvh * G, lane, qflip);
+        qk.load_q(p, next->at.b, next->at.kvh * p.group, lane, qflip);
         qk.reset();
       }
     }
@@ -333,7 +407,7 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
   const int Lb = p.seq_lens[b];
   const int64_t pre_b = bp.prefix[b];
   const int64_t pre_B = bp.prefix[p.num_seqs];
-  const SeqSpan s = seq_span(Lb, p.window, (int64_t)p.stride << p.bs_log2);
+  const SeqSpan s = seq_span(Lb, span_window(p), (int64_t)p.stride << p.bs_log2);
   const int64_t total = pre_B * p.num_kv_heads;
   const int n_eff = effective_workers(total, bp.num_workers);
 
@@ -349,8 +423,10 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
 
   // piece i of the unit: worker wa + i, slot first_slot for i == 0, else 0
   const int pr = tid / F;
-  const int f = tid - pr * F;                           // slice f covers head h0 + 4f / D
+  const int f = tid - pr * F;                           // slice f covers column h0 + 4f / D
   const int hl = (4 * f) / D;
+  const int ncols = p.q_len * p.group;                  // columns past it are padding
+  const bool col_ok = h0 + hl < ncols;
   float m = -INFINITY, z = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   bool nan = s.bad;
@@ -359,7 +435,7 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
     const size_t slot = (size_t)(wa + i) * 2 + (i == 0 ? first_slot : 0);
     const float li = bp.ws_lse[slot * G + h0 + hl];
     const float4 o = *reinterpret_cast<const float4*>(bp.ws_o + (slot * G + h0) * D + 4 * f);
-    nan |= li != li;
+    nan |= col_ok && li != li;   // padding columns' slots are never written
     // a piece with lse = -inf has no weight; selects instead of a branch keep the loads of
     // several pieces in flight
     const float mn = fmaxf(m, li);
@@ -386,9 +462,12 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
   }
   __syncthreads();
 
+  const int sh = __builtin_ctz((unsigned)p.group);
   for (int e = tid; e < H * D; e += kFixupThreads) {
     const int h = e / D;
-    const int hq = kvh * G + h0 + h;
+    const int n = h0 + h;                               // column: query token n / group
+    if (n >= ncols) continue;
+    const int hq = kvh * p.group + (n & (p.group - 1));
     // the sink logit joins the max and the denominator with a zero value row
     const float sink = p.sinks != nullptr ? p.sinks[hq] : -INFINITY;
     float M = sink;
@@ -408,7 +487,7 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
       ov = __builtin_nanf("");
       lv = __builtin_nanf("");
     }
-    const size_t row = (size_t)b * p.num_q_heads + hq;
+    const size_t row = ((size_t)b * p.q_len + (n >> sh)) * p.num_q_heads + hq;
     p.out[row * D + (e - h * D)] = ov;
     if (e == h * D && p.lse != nullptr) p.lse[row] = lv;
   }
@@ -458,8 +537,15 @@ hipError_t launch_fix_g(const BalancedParams& bp, int group, hipStream_t stream)
     case 2: return launch_fix<D, 2>(bp, stream);
     case 4: return launch_fix<D, 4>(bp, stream);
     case 8: return launch_fix<D, 8>(bp, stream);
+    case 16: return launch_fix<D, 16>(bp, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Sixteen columns exist only for the matrix-core P.V policies (several query tokens).
+template <QkPath PATH>
+constexpr bool has_16_columns() {
+  return PATH == QkPath::kMfmaPv || PATH == QkPath::kMfmaPvFp8;
 }
 
 template <int D, QkPath PATH>
@@ -469,6 +555,9 @@ hipError_t launch_bal_g(const BalancedParams& bp, int group, hipStream_t stream)
     case 2: return launch_bal<D, 2, PATH>(bp, stream);
     case 4: return launch_bal<D, 4, PATH>(bp, stream);
     case 8: return launch_bal<D, 8, PATH>(bp, stream);
+    case 16:
+      if constexpr (has_16_columns<PATH>()) return launch_bal<D, 16, PATH>(bp, stream);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -492,6 +581,10 @@ const void* bal_ptr(int head_dim, int group) {
       case 2: return balanced_kernel_ptr<D, 2, PATH>();            \
       case 4: return balanced_kernel_ptr<D, 4, PATH>();            \
       case 8: return balanced_kernel_ptr<D, 8, PATH>();            \
+      case 16:                                                     \
+        if constexpr (has_16_columns<PATH>())                      \
+          return balanced_kernel_ptr<D, 16, PATH>();               \
+        return nullptr;                                            \
       default: return nullptr;                                     \
     }                                                              \
   }

@@ -26,6 +26,12 @@ struct DecodeParams {
   int32_t window;
   int32_t psize;              // 0 = unsplit
   int32_t max_parts;          // split: partition slots; unsplit: 1
+  // Query tokens per sequence (1 = one-token decode; more only on the balanced schedule):
+  // q [B][q_len][Hq][D], out [B][q_len][Hq][D], lse [B][q_len][Hq]; token i of sequence b sits
+  // at position seq_lens[b] - q_len + i and attends causally.  group = Hq / Hkv; a kernel's
+  // G template parameter counts columns (query token, head) per KV head, q_len * group <= G.
+  int32_t q_len;
+  int32_t group;
   // Split only, optional: the last partition of each (sequence, KV head) to finish merges them
   // all into final_out [B][Hq][D] / final_lse [B][Hq] (or null).  merge_counters [B][Hkv] are
   // zero on entry and left zero.

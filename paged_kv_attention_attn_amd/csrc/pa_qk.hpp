@@ -90,6 +90,8 @@ struct QkValu {
   static constexpr int E = RowGeom<D>::kElems;
   static constexpr int kRowBytes = RowGeom<D>::kRowBytes;
   static constexpr int kMinWavesPerEu = 1;
+  static constexpr bool kColumns = false;   // one query token, flush by heads (out)
+  static constexpr bool kQueryTokens = false;
   struct Tile {
     uint32_t k[kTileSteps][W];
     uint32_t v[kTileSteps][W];
@@ -235,6 +237,8 @@ struct QkMfma {
   static constexpr int E = RowGeom<D>::kElems;
   static constexpr int kRowBytes = RowGeom<D>::kRowBytes;
   static constexpr int kMinWavesPerEu = 1;
+  static constexpr bool kColumns = false;   // one query token, flush by heads (out)
+  static constexpr bool kQueryTokens = false;
   struct Tile {
     u32x4_t k[KK];
     uint32_t v[kTileSteps][W];
@@ -417,20 +421,36 @@ struct QkMfmaPvT {
     u32x4_t k[KL];
     uint32_t v[kTileSteps][VW];
   };
+  // Columns: the N side of both contractions is (query token, head) pairs, n = i * group + h,
+  // G of them at most (q_len * group <= G <= 16); with one query token a column is a head.
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "columns");
+  // Sixteen columns live in all four row groups: flush them column-wise (merge_cols, col_m,
+  // acc).  Up to eight, the head-wise flush (merge_rows, out) keeps the finishing values in
+  // scalar registers and costs about 28 fewer VGPRs.
+  static constexpr bool kColumns = G == 16;
+  static constexpr bool kQueryTokens = true;   // columns may be several query tokens
   u32x4_t qb[KK];
   float c2;
   float vs;   // FP8: V scale
   bool head_lane;
+  int col_q;  // query token of this lane's column
   float m, l;
+  float lsum;  // after merge_cols: the column's sum over the row groups
   f32x4_t cacc[E];
-  float up[G > 4 ? 4 : 1][E];   // G = 8: heads 4..7 brought up from row 1 by merge_rows
+  float up[(G > 4 && G <= 8) ? 4 : 1][E];   // G = 8: heads 4..7 brought up by merge_rows
 
+  // q rows of the unit whose first head is h0 (= KV head * group): lane column n reads query
+  // token n / group, head h0 + n % group.
   __device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int lane,
                                          uint32_t qflip) {
     const int n = lane & 15;
-    head_lane = n < G;
+    const int sh = __builtin_ctz((unsigned)p.group);   // group is a power of two
+    col_q = n >> sh;
+    head_lane = n < G && col_q < p.q_len;
+    const int hh = n & (p.group - 1);
     const char* qrow = reinterpret_cast<const char*>(
-        p.q + ((size_t)b * p.num_q_heads + h0 + (head_lane ? n : 0)) * D);
+        p.q + (((size_t)b * p.q_len + (head_lane ? col_q : 0)) * p.num_q_heads + h0 +
+               (head_lane ? hh : 0)) * D);
     const uint32_t keep = head_lane ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -501,6 +521,14 @@ struct QkMfmaPvT {
 
   template <bool MASKED>
   __device__ __forceinline__ void consume(Tile& t, int tok0, int lo, int hi, int lane) {
+    consume<MASKED>(t, tok0, lo, hi, lo, hi, lane);
+  }
+  // Masked form: scores of column (lane) keys outside [lo, hi) drop out (lo, hi may differ by
+  // lane: the column's query token); V rows outside [vlo, vhi), the union, are zeroed so that a
+  // stray NaN there cannot meet a zero probability.
+  template <bool MASKED>
+  __device__ __forceinline__ void consume(Tile& t, int tok0, int lo, int hi, int vlo, int vhi,
+                                          int lane) {
     const int g = lane >> 4;
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -522,7 +550,7 @@ struct QkMfmaPvT {
         const int tk = tok0 + 4 * i + g;
         sc[i] = (tk >= lo && tk < hi) ? sc[i] * c2 : -INFINITY;
       }
-      mask_v_words<VW>(t.v, tok0, lo, hi, lane);
+      mask_v_words<VW>(t.v, tok0, vlo, vhi, lane);
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     if constexpr (!MASKED) mx *= c2;
@@ -604,7 +632,7 @@ struct QkMfmaPvT {
       Mh[h] = row_bcast_dyn(m, h);
       lh[h] = row_bcast_dyn(lt, h);
     }
-    if constexpr (G > 4) {
+    if constexpr (G > 4 && G <= 8) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -615,8 +643,25 @@ struct QkMfmaPvT {
   // After merge_rows, on the row-0 lanes: the accumulated P.V of head h at dim(lane, e)
   // (times the V scale for an FP8 cache).
   __device__ __forceinline__ float out(int h, int e) const {
+    static_assert(G <= 8, "out() covers eight columns");
     const float x = h < 4 ? cacc[e][h & 3] : up[(h - 4) & 3][e];
     return FP8 ? x * vs : x;
+  }
+
+  // Column-wise finish, for any G: after merge_cols every lane can read column n's running max
+  // and sum (col_m / col_l, read from lane n; call them on every lane), and lane (r, c) holds
+  // the accumulated P.V of column 4r + i at dim(c, e) as acc(i, e).
+  __device__ __forceinline__ void merge_cols() { lsum = rows_sum(l); }
+  __device__ __forceinline__ float col_m(int n) const {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_ds_bpermute(n << 2, __builtin_bit_cast(int, m)));
+  }
+  __device__ __forceinline__ float col_l(int n) const {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_ds_bpermute(n << 2, __builtin_bit_cast(int, lsum)));
+  }
+  __device__ __forceinline__ float acc(int i, int e) const {
+    return FP8 ? cacc[e][i] * vs : cacc[e][i];
   }
 };
 

@@ -79,9 +79,31 @@ def run_gpu(wl, t, partition_size: int = 0, max_partitions=None, num_workers: in
 
 
 def oracle_full(wl):
+    if wl.q_len > 1:
+        return ref.decode_multi(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens,
+                                wl.scale, wl.block_size, window=wl.window, sinks=wl.sinks,
+                                kv_format=wl.kv_format, k_scale=wl.k_scale, v_scale=wl.v_scale)
     return ref.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
                       wl.block_size, window=wl.window, sinks=wl.sinks, kv_format=wl.kv_format,
                       k_scale=wl.k_scale, v_scale=wl.v_scale)
+
+
+def oracle_multi_triples(wl, triples):
+    """Oracle rows of (sequence, query token, head) triples, one by one (q_len > 1): each is the
+    one-token decode of the sequence's first L - q_len + i + 1 tokens (the causal rule, pinned
+    against decode_multi on the CPU)."""
+    outs, lses = [], []
+    Q = wl.q_len
+    for b, i, h in triples:
+        L = int(wl.seq_lens[b])
+        prefix = np.array([max(L - Q + i + 1, 0)], np.int32)
+        o, l = ref.decode_one(wl.q[b:b + 1, i], wl.k_cache, wl.v_cache, wl.block_table[b:b + 1],
+                              prefix, wl.scale, wl.block_size, 0, h, window=wl.window,
+                              sinks=wl.sinks, kv_format=wl.kv_format, k_scale=wl.k_scale,
+                              v_scale=wl.v_scale)
+        outs.append(o)
+        lses.append(l)
+    return np.array(outs), np.array(lses)
 
 
 def oracle_pairs(wl, pairs):
@@ -151,10 +173,10 @@ def finite_rows(x):
 # prepared decode steps (plans)
 # ---------------------------------------------------------------------------------------------
 def make_plan(wl, schedule, partition_size=256, num_workers=0):
-    B, Hq, D = wl.q.shape
-    return pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
-                   window=wl.window, schedule=schedule, partition_size=partition_size,
-                   max_seq_len=max_len(wl), num_workers=num_workers, kv_dtype=wl.kv_format)
+    return pa.Plan(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.stride,
+                   wl.head_dim, wl.block_size, window=wl.window, schedule=schedule,
+                   partition_size=partition_size, max_seq_len=max_len(wl),
+                   num_workers=num_workers, kv_dtype=wl.kv_format, q_len=wl.q_len)
 
 
 def counter_bytes(wl):
@@ -165,10 +187,9 @@ def counter_bytes(wl):
 def run_plan(plan, wl, t, workspace=None):
     """One step through paged_attn_plan_run into NaN-filled outputs (and, unless a workspace is
     given, a workspace whose non-counter bytes are 0xFF); returns (out, lse) as float64."""
-    B, Hq, D = wl.q.shape
     fused = "last partition" in plan.name
-    out = torch.full((B, Hq, D), float("nan"), device="cuda")
-    lse = torch.full((B, Hq), float("nan"), device="cuda")
+    out = torch.full(wl.q.shape, float("nan"), device="cuda")      # [B]([Q])[Hq][D]
+    lse = torch.full(wl.q.shape[:-1], float("nan"), device="cuda")
     ws = workspace if workspace is not None else plan.workspace("cuda")
     if ws is not None and workspace is None:
         # stale contents must not matter (except the fused counters, which start at zero)

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert pa.abi_version() == 3
+    assert pa.abi_version() == 4
     for code, name in pa.STATUS_NAMES.items():
         s = pa.status_string(code)
         assert s and s != "unknown status", name
@@ -237,10 +237,10 @@ def test_balanced_empty_batch_is_ok_without_launch():
 # prepared decode (plans): creation-time checks, workspace sizes, run-time argument checks
 # ---------------------------------------------------------------------------------------------
 def plan_create(s, *, head_dim=128, block_size=16, window=0, schedule=0, workers=0, max_len=0,
-                kv_dtype=0):
+                kv_dtype=0, q_len=1):
     h = ctypes.c_void_p()
     st = pa.lib().paged_attn_plan_create(ctypes.byref(s), head_dim, block_size, window, schedule,
-                                         kv_dtype, max_len, workers, ctypes.byref(h))
+                                         kv_dtype, q_len, max_len, workers, ctypes.byref(h))
     return st, h
 
 
@@ -287,6 +287,17 @@ def test_plan_create_and_workspace_sizes():
     st, h = plan_create(shape(), schedule=2, workers=100, kv_dtype=1)
     assert st == 0 and pa.lib().paged_attn_plan_name(h).startswith(b"pa_balanced_mfmapv_fp8_")
     pa.lib().paged_attn_plan_destroy(h)
+    # several query tokens: (token, head) columns rounded up to a power of two, the workspace
+    # sized for them; 3 tokens x 4 heads -> 16 columns
+    st, h = plan_create(shape(), schedule=2, workers=100, q_len=3)
+    assert st == 0 and b"_g4_q3_c16_workers100" in pa.lib().paged_attn_plan_name(h)
+    a = lambda x: (x + 255) // 256 * 256
+    ws = a(3 * 8) + a(100 * 2 * 16 * 4) + a(100 * 2 * 16 * 128 * 4)
+    assert pa.lib().paged_attn_plan_workspace_size(h) == ws
+    pa.lib().paged_attn_plan_destroy(h)
+    st, h = plan_create(shape(), schedule=2, workers=100, q_len=2, kv_dtype=1)
+    assert st == 0 and b"mfmapv_fp8_d128_g4_q2_c8" in pa.lib().paged_attn_plan_name(h)
+    pa.lib().paged_attn_plan_destroy(h)
     pa.lib().paged_attn_plan_destroy(None)
 
 
@@ -296,6 +307,10 @@ def test_plan_create_and_workspace_sizes():
     (dict(head_dim=96), -3), (dict(block_size=8), -3), (dict(window=-1), -2),
     (dict(schedule=2, workers=-1), -2), (dict(schedule=2, workers=(1 << 20) + 1), -2),
     (dict(max_len=-1), -2), (dict(kv_dtype=2), -3), (dict(kv_dtype=-1), -3),
+    (dict(q_len=0), -2), (dict(q_len=-3), -2),
+    (dict(q_len=2), -3),                         # several query tokens: balanced schedule only
+    (dict(q_len=5, schedule=2, workers=64), -3),  # 5 tokens x 4 heads > 16 columns
+    (dict(q_len=2, schedule=2, workers=64, window=0x7FFFFFFF), -2),
 ])
 def test_plan_create_rejects(kw, expect):
     st, h = plan_create(shape(), **kw)
@@ -306,7 +321,7 @@ def test_plan_unsplit_rejects_a_partitioned_shape_and_null_out_pointer():
     st, h = plan_create(shape(partition_size=512, max_partitions=4), schedule=0)
     assert st == -2
     s = shape()
-    assert pa.lib().paged_attn_plan_create(ctypes.byref(s), 128, 16, 0, 0, 0, 0, 0, None) == -1
+    assert pa.lib().paged_attn_plan_create(ctypes.byref(s), 128, 16, 0, 0, 0, 1, 0, 0, None) == -1
 
 
 def test_plan_run_argument_checks_without_launch():
