@@ -13,6 +13,10 @@
 // first and the last unit it touches), and the fix-up kernel merges them with the
 // log-sum-exp rule.
 //
+// With several query tokens per sequence (q_len > 1) a unit's tiles span the union of the
+// tokens' key ranges, G counts (token, head) columns, and every column keeps its own causal
+// range inside the shared tiles.
+//
 // All workers finish within about one tile of each other, no workgroup is launched per unit, and
 // the partial traffic is at most 2 * N * G * (D + 1) floats.  Measured on MI355X for a
 // 64-sequence, 512..4096-token Llama-8B-shaped step: fixed-partition grids left a quarter of the

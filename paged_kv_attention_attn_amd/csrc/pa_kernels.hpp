@@ -96,7 +96,9 @@ int decode_default_waves(int head_dim, int group, int psize);
 
 hipError_t launch_reduce(const ReduceParams& p, int head_dim, int num_seqs, hipStream_t stream);
 
-// Balanced decode: the worker kernel, and the fix-up merge, each on `stream`.
+// Balanced decode: the worker kernel, and the fix-up merge, each on `stream`.  `group` is the
+// kernels' column count: Hq/Hkv, or with q_len > 1 the (token, head) pairs rounded up to a power
+// of two (16 at most, matrix-core P.V paths only).
 hipError_t launch_balanced(const BalancedParams& bp, int head_dim, int group, QkPath path,
                            hipStream_t stream);
 hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int group,
