@@ -32,11 +32,35 @@ KERNEL_SOURCES = ["paged_kv_attention_attn_amd/csrc/pa_decode.hip",
                   "paged_kv_attention_attn_amd/csrc/pa_device.hpp"]
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments and blank space removed: comment-only edits leave the kernels,
+    and so the counters taken on them, unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif text[i] == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments and spacing excluded)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
