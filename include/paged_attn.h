@@ -235,6 +235,8 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  *                  #13700, Summary: the prepared path is the non-FP8 one); the format and the
  *                  per-tensor scales are this library's reading, the pages give none.  Every
  *                  schedule supports it; other values give PA_ERR_UNSUPPORTED.
+ *   kv_layout      NULL for the default pool [num_blocks][Hkv][block_size][head_dim], else the
+ *                  strides of pa_kv_layout (copied; the plan keeps no pointer to it).
  *   q_len          new query tokens per sequence, >= 1 (1 = one-token decode).  With q_len > 1
  *                  the run takes q bf16 [B][q_len][Hq][head_dim] and writes out fp32
  *                  [B][q_len][Hq][head_dim] and lse fp32 [B][q_len][Hq]; seq_lens count the new
@@ -263,6 +265,25 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  */
 typedef struct pa_plan pa_plan;
 
+/*
+ * KV pool layout for plans: where the row of (physical block, KV head, slot) starts, in elements
+ * of the cache's type, the same for k_cache and v_cache:
+ *     block * block_stride + kv_head * head_stride + slot * token_stride
+ * with the head_dim values of a row contiguous.  The default pool [num_blocks][Hkv][bs][D] is
+ * (Hkv*bs*D, bs*D, D); a token-major pool [num_blocks][bs][Hkv][D] is (bs*Hkv*D, D, Hkv*D); K and
+ * V interleaved per block, [num_blocks][2][Hkv][bs][D], is (2*Hkv*bs*D, bs*D, D) with v_cache
+ * pointing Hkv*bs*D elements past k_cache.  Strides must be positive, token_stride >= head_dim,
+ * every stride a multiple of 16 bytes, token_stride * element size <= 2^26 bytes, block and head
+ * strides <= 2^40 elements (else PA_ERR_SHAPE).  The pages name a strided-KV decode mode
+ * (ROCm/rocm-libraries PR #13700, its file list: a strided-KV decode document and numeric test)
+ * without its layout; this descriptor is this library's reading.
+ */
+typedef struct {
+  int64_t block_stride;
+  int64_t head_stride;
+  int64_t token_stride;
+} pa_kv_layout;
+
 /* KV cache element formats a plan reads. */
 enum {
   PA_KV_BF16 = 0,       /* bf16 rows of head_dim values (2 * head_dim bytes)                 */
@@ -279,8 +300,8 @@ enum {
 
 pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,
                                  int32_t window, int32_t schedule, int32_t kv_dtype,
-                                 int32_t q_len, int32_t max_seq_len, int32_t num_workers,
-                                 pa_plan** plan);
+                                 const pa_kv_layout* kv_layout, int32_t q_len,
+                                 int32_t max_seq_len, int32_t num_workers, pa_plan** plan);
 
 /* Device workspace bytes a run needs (0 for the unsplit schedule): the partition partials and
  * their LSEs (plus one merge counter per (sequence, KV head) for the fused schedule), or the

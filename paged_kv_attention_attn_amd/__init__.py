@@ -66,7 +66,7 @@ def _load() -> ctypes.CDLL:
                                              ctypes.c_size_t, i32, vp]),
         "paged_attn_balanced_workspace_size": (ctypes.c_int64, [sp, i32, i32]),
         "paged_attn_balanced_default_workers": (i32, [i32, i32]),
-        "paged_attn_plan_create": (i32, [sp, i32, i32, i32, i32, i32, i32, i32, i32,
+        "paged_attn_plan_create": (i32, [sp, i32, i32, i32, i32, i32, vp, i32, i32, i32,
                                          ctypes.POINTER(vp)]),
         "paged_attn_plan_workspace_size": (ctypes.c_int64, [vp]),
         "paged_attn_plan_run": (i32, [vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp, vp,
@@ -355,6 +355,19 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, scale, *, window
 
 
 SCHEDULES = {"unsplit": 0, "partitioned": 1, "balanced": 2, "fused": 3}
+
+
+class KvLayout(ctypes.Structure):
+    """pa_kv_layout: row (block, head, slot) at block*block_stride + head*head_stride +
+    slot*token_stride elements."""
+    _fields_ = [("block_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("token_stride", ctypes.c_int64)]
+
+
+def _layout_ptr(layout):
+    if layout is None:
+        return None
+    return ctypes.cast(ctypes.pointer(KvLayout(*[int(x) for x in layout])), ctypes.c_void_p)
 KV_DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
 
@@ -366,6 +379,8 @@ class Plan:
     "balanced" (``num_workers``, 0 = the device default; ``max_seq_len``, a bound on the
     lengths, caps the workers of a small batch).  ``kv_dtype`` is "bf16" or "fp8_e4m3" (KV
     pools of one byte per value, uint8 tensors, with per-tensor scales given to run()).
+    ``kv_layout``: None for the pool [num_blocks][Hkv][bs][D], else (block, head, token) strides
+    in elements of the cache type (pa_kv_layout).
     ``q_len`` > 1 (balanced schedule): q_len causal query tokens per sequence, q [B][q_len][Hq][D]
     -> out [B][q_len][Hq][D], lse [B][q_len][Hq].  run() records only kernel launches on the
     stream, so it can be captured in a CUDA/HIP graph."""
@@ -374,7 +389,8 @@ class Plan:
                  block_table_stride: int, head_dim: int, block_size: int, *, window: int = 0,
                  schedule: str = "balanced", partition_size: int = 0,
                  max_seq_len: Optional[int] = None, num_workers: int = 0,
-                 kv_dtype: str = "bf16", q_len: int = 1):
+                 kv_dtype: str = "bf16", q_len: int = 1,
+                 kv_layout: Optional[Tuple[int, int, int]] = None):
         if schedule not in SCHEDULES:
             raise ValueError(f"schedule must be one of {sorted(SCHEDULES)}")
         if kv_dtype not in KV_DTYPES:
@@ -394,6 +410,7 @@ class Plan:
         self._h = ctypes.c_void_p()
         st = _lib.paged_attn_plan_create(ctypes.byref(self.shape), int(head_dim), int(block_size),
                                          int(window), SCHEDULES[schedule], KV_DTYPES[kv_dtype],
+                                         _layout_ptr(kv_layout),
                                          int(q_len), int(max_seq_len or 0), int(num_workers),
                                          ctypes.byref(self._h))
         if st != PA_OK:

@@ -23,7 +23,19 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 4;
+// Default pool layout [num_blocks][Hkv][block_size][D]: the three byte strides.
+void set_default_layout(pa::DecodeParams& p, int32_t num_kv_heads, int32_t block_size,
+                        int64_t row_bytes) {
+  p.kv_row_stride = row_bytes;
+  p.kv_head_stride = row_bytes * block_size;
+  p.kv_block_stride = p.kv_head_stride * num_kv_heads;
+}
+
+}  // namespace
+
+namespace {
+
+constexpr int32_t kAbiVersion = 5;
 constexpr int32_t kMaxGridYZ = 65535;
 
 int log2_exact(int32_t v) {
@@ -171,6 +183,7 @@ pa_status paged_attn_decode(const pa_shape* shape, const void* q, const void* k_
   p.max_parts = split ? shape->max_partitions : 1;
   p.q_len = 1;
   p.group = group;
+  set_default_layout(p, shape->num_kv_heads, block_size, 2 * (int64_t)head_dim);
   if (debug_log())
     std::fprintf(stderr, "[paged_attn] decode %s B=%d Hq=%d Hkv=%d bs=%d P=%d Pmax=%d W=%d\n",
                  pa::decode_variant_name(head_dim, group, waves, split, path), shape->num_seqs,
@@ -267,6 +280,7 @@ pa_status balanced_setup(const pa_shape* shape, int32_t head_dim, int32_t block_
   p.max_parts = 1;
   p.q_len = 1;
   p.group = group;
+  set_default_layout(p, shape->num_kv_heads, block_size, 2 * (int64_t)head_dim);
   char* ws = static_cast<char*>(workspace);
   bp->prefix = reinterpret_cast<int64_t*>(ws + wl.prefix);
   bp->ws_lse = reinterpret_cast<float*>(ws + wl.lse);
@@ -469,9 +483,12 @@ namespace {
 
 constexpr int32_t kMaxColumns = 16;   // (query token, head) pairs per KV head and kernel
 
+// Largest row stride in bytes: 16 rows of a tile stay within 32-bit lane offsets.
+constexpr int64_t kMaxRowStrideBytes = int64_t(1) << 26;
+
 pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size, int32_t window,
-                     int32_t schedule, int32_t kv_dtype, int32_t q_len, int32_t max_seq_len,
-                     int32_t num_workers, pa_plan* pl) {
+                     int32_t schedule, int32_t kv_dtype, const pa_kv_layout* kv_layout,
+                     int32_t q_len, int32_t max_seq_len, int32_t num_workers, pa_plan* pl) {
   const pa_status st = check_shape(shape);
   if (st != PA_OK) return st;
   if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
@@ -534,6 +551,21 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   p.max_parts = parted ? shape->max_partitions : 1;
   p.q_len = q_len;
   p.group = group;
+  const int64_t elem = kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2;
+  set_default_layout(p, shape->num_kv_heads, block_size, elem * head_dim);
+  if (kv_layout != nullptr) {
+    // strides in elements; every row 16-byte aligned, rows of a block at least a row apart
+    const int64_t bsb = kv_layout->block_stride * elem, hsb = kv_layout->head_stride * elem,
+                  rsb = kv_layout->token_stride * elem;
+    if (kv_layout->block_stride <= 0 || kv_layout->head_stride <= 0 ||
+        kv_layout->token_stride < head_dim || rsb > kMaxRowStrideBytes ||
+        kv_layout->block_stride > (int64_t(1) << 40) || kv_layout->head_stride > (int64_t(1) << 40))
+      return PA_ERR_SHAPE;
+    if (bsb % 16 != 0 || hsb % 16 != 0 || rsb % 16 != 0) return PA_ERR_SHAPE;
+    p.kv_block_stride = bsb;
+    p.kv_head_stride = hsb;
+    p.kv_row_stride = rsb;
+  }
   pl->red = pa::ReduceParams{};
   const char* dname = pa::decode_variant_name(head_dim, group, waves, parted, path);
   if (schedule == PA_SCHEDULE_UNSPLIT) {
@@ -584,15 +616,15 @@ extern "C" {
 
 pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,
                                  int32_t window, int32_t schedule, int32_t kv_dtype,
-                                 int32_t q_len, int32_t max_seq_len, int32_t num_workers,
-                                 pa_plan** plan) {
+                                 const pa_kv_layout* kv_layout, int32_t q_len,
+                                 int32_t max_seq_len, int32_t num_workers, pa_plan** plan) {
   if (plan == nullptr) return PA_ERR_NULL;
   *plan = nullptr;
   pa_plan* pl = new (std::nothrow) pa_plan;
   if (pl == nullptr) return PA_ERR_LAUNCH;
   const pa_status st =
-      plan_build(shape, head_dim, block_size, window, schedule, kv_dtype, q_len, max_seq_len,
-                 num_workers, pl);
+      plan_build(shape, head_dim, block_size, window, schedule, kv_dtype, kv_layout, q_len,
+                 max_seq_len, num_workers, pl);
   if (st != PA_OK) {
     delete pl;
     return st;

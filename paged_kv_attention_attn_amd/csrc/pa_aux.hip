@@ -23,7 +23,10 @@ __global__ __launch_bounds__(kWave) void witness_kernel(const WitnessParams p) {
   const int L = p.seq_lens[b];
   if (L <= 0 || (int64_t)L > ((int64_t)p.stride << p.bs_log2)) return;
   const PartRange pr = part_range(L, p.window, 0, 0);
-  const TileAddr ta{p.num_blocks, p.num_kv_heads, kvh, p.bs_log2, RG::kRowBytes};
+  // the default pool layout [num_blocks][Hkv][bs][D]
+  const int64_t head_bytes = (int64_t)RG::kRowBytes << p.bs_log2;
+  const TileAddr ta{p.num_blocks, p.bs_log2, head_bytes * p.num_kv_heads, kvh * head_bytes,
+                    RG::kRowBytes};
   const int32_t* bt_row = p.block_table + (size_t)b * p.stride;
   const size_t base = ((size_t)b * p.num_kv_heads + kvh) * p.max_rows;
   const int t0 = pr.lo / kTileTokens;

@@ -209,7 +209,8 @@ void balanced_decode_kernel(const BalancedParams bp) {
       ctx.advance(iss);
       phys_next = ctx.phys(iss);
     }
-    const TileAddr ta{p.num_blocks, p.num_kv_heads, s.at.kvh, p.bs_log2, QK::kRowBytes};
+    const TileAddr ta{p.num_blocks, p.bs_log2, p.kv_block_stride, s.at.kvh * p.kv_head_stride,
+                      p.kv_row_stride};
     const int64_t off = ta.offset(phys, s.at.s.t0 + s.at.ti);
     s.ok = off >= 0;
     if (s.ok) qk.issue(t, p.k_cache + off, p.v_cache + off, lane);

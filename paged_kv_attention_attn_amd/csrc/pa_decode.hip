@@ -60,7 +60,8 @@ void decode_kernel(const DecodeParams p) {
   // first batch is requested before the sequence length arrives, for the range a partition has
   // without a window (indices clamped into the row, so always in bounds); a window start that
   // moves the range triggers a reload below.
-  const TileAddr ta{p.num_blocks, p.num_kv_heads, it.kvh, p.bs_log2, QK::kRowBytes};
+  const TileAddr ta{p.num_blocks, p.bs_log2, p.kv_block_stride, it.kvh * p.kv_head_stride,
+                    p.kv_row_stride};
   const int32_t* bt_row = p.block_table + (size_t)it.b * p.stride;
   const int lo_guess =
       split ? (int)((int64_t)it.part * p.psize < 0x7FFFFFF0 ? (int64_t)it.part * p.psize

@@ -179,17 +179,19 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Tile addressing (block-table walk).  Tile t covers tokens [16t, 16t+16), which never straddle
 // a block because block_size is a multiple of 16.  Token 16t is slot (16t mod block_size) of
 // logical block 16t / block_size; its physical block comes from the sequence's block-table row.
-// Byte offset of the tile's first row in a pool [num_blocks][Hkv][block_size][D]:
-//   ((phys * Hkv + kvh) * block_size + slot) * D * 2, computed in 64 bits.
-// A table entry outside [0, num_blocks) yields -1: the caller must not read.  All operands are
-// wave-uniform, so this is scalar code.
+// Byte offset of the tile's first row: phys * block_stride + kvh * head_stride + slot *
+// row_stride, computed in 64 bits.  The default pool [num_blocks][Hkv][block_size][D] has
+// row_stride = D * element bytes, head_stride = block_size * row_stride and block_stride =
+// Hkv * head_stride; other layouts (token-major, K and V interleaved per block, padded rows)
+// only change the three strides.  A table entry outside [0, num_blocks) yields -1: the caller
+// must not read.  All operands are wave-uniform, so this is scalar code.
 // ---------------------------------------------------------------------------------------------
 struct TileAddr {
   int32_t num_blocks;
-  int32_t num_kv_heads;
-  int32_t kvh;
   int32_t bs_log2;
-  int32_t row_bytes;
+  int64_t block_stride;   // bytes between physical blocks
+  int64_t head_off;       // kvh * head stride, bytes
+  int64_t row_stride;     // bytes between a block's consecutive tokens
 
   // index into the sequence's block-table row of the block holding tile t
   __device__ __forceinline__ int logical_block(int tile) const {
@@ -199,7 +201,7 @@ struct TileAddr {
   __device__ __forceinline__ int64_t offset(int phys, int tile) const {
     if (phys < 0 || phys >= num_blocks) return -1;
     const int slot = (tile * kTileTokens) & ((1 << bs_log2) - 1);
-    return ((((int64_t)phys * num_kv_heads + kvh) << bs_log2) + slot) * (int64_t)row_bytes;
+    return (int64_t)phys * block_stride + head_off + (int64_t)slot * row_stride;
   }
 };
 

@@ -8,8 +8,8 @@ namespace pa {
 
 struct DecodeParams {
   const uint16_t* q;          // bf16 [B][Hq][D]
-  const char* k_cache;        // bf16 [NB][Hkv][bs][D], or FP8 E4M3 bytes for the FP8 path
-  const char* v_cache;
+  const char* k_cache;        // bf16 rows of D values (FP8 path: E4M3 bytes), placed by the
+  const char* v_cache;        // layout strides below (default [NB][Hkv][bs][D])
   const int32_t* block_table; // [B][stride]
   const int32_t* seq_lens;    // [B]
   const float* sinks;         // [Hq] or null
@@ -32,6 +32,11 @@ struct DecodeParams {
   // G template parameter counts columns (query token, head) per KV head, q_len * group <= G.
   int32_t q_len;
   int32_t group;
+  // KV pool layout in bytes, the same for K and V: row of (block phys, head kvh, slot s) at
+  // phys * kv_block_stride + kvh * kv_head_stride + s * kv_row_stride.  Rows are 16-byte aligned.
+  int64_t kv_block_stride;
+  int64_t kv_head_stride;
+  int64_t kv_row_stride;
   // Split only, optional: the last partition of each (sequence, KV head) to finish merges them
   // all into final_out [B][Hq][D] / final_lse [B][Hq] (or null).  merge_counters [B][Hkv] are
   // zero on entry and left zero.

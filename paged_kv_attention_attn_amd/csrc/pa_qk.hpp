@@ -55,11 +55,11 @@ __device__ __forceinline__ float row_bcast_dyn(float x, int h) {
 // row holds slice c of the head dim.
 template <int D>
 __device__ __forceinline__ void load_v_rows(uint32_t (&v)[kTileSteps][RowGeom<D>::kWords],
-                                            const char* vb, int lane) {
+                                            const char* vb, int lane, int rs) {
   const int r = lane >> 4, c = lane & 15;
 #pragma unroll
   for (int j = 0; j < kTileSteps; ++j)
-    load_row<D>(vb + (kRows * j + r) * RowGeom<D>::kRowBytes, c, v[j]);
+    load_row<D>(vb + (kRows * j + r) * rs, c, v[j]);
 }
 
 template <int NWORDS>
@@ -121,9 +121,11 @@ struct QkValu {
       for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
     }
   }
+  int rs;   // bytes between a block's consecutive K/V rows (the pool layout's row stride)
   __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
                                        uint32_t qflip, float c2_) {
     c2 = c2_;
+    rs = (int)p.kv_row_stride;
     load_q(p, b, h0, lane, qflip);
     reset();
   }
@@ -132,8 +134,8 @@ struct QkValu {
     const int r = lane >> 4, c = lane & 15;
 #pragma unroll
     for (int j = 0; j < kTileSteps; ++j)
-      load_row<D>(kb + (kRows * j + r) * RowGeom<D>::kRowBytes, c, t.k[j]);
-    load_v_rows<D>(t.v, vb, lane);
+      load_row<D>(kb + (kRows * j + r) * rs, c, t.k[j]);
+    load_v_rows<D>(t.v, vb, lane, rs);
   }
 
   template <bool MASKED>
@@ -274,9 +276,11 @@ struct QkMfma {
       for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
     }
   }
+  int rs;   // bytes between a block's consecutive K/V rows (the pool layout's row stride)
   __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
                                        uint32_t qflip, float c2_) {
     c2 = c2_;
+    rs = (int)p.kv_row_stride;
     load_q(p, b, h0, lane, qflip);
     reset();
   }
@@ -284,11 +288,11 @@ struct QkMfma {
   __device__ __forceinline__ void issue(Tile& t, const char* kb, const char* vb, int lane) const {
     const int mrow = lane & 15;
     const int tok = 4 * (mrow & 3) + (mrow >> 2);
-    const char* krow = kb + tok * RowGeom<D>::kRowBytes + 16 * (lane >> 4);
+    const char* krow = kb + tok * rs + 16 * (lane >> 4);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       t.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + 64 * kk));
-    load_v_rows<D>(t.v, vb, lane);
+    load_v_rows<D>(t.v, vb, lane, rs);
   }
 
   template <bool MASKED>
@@ -472,9 +476,11 @@ struct QkMfmaPvT {
 #pragma unroll
     for (int e = 0; e < E; ++e) cacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  int rs;   // bytes between a block's consecutive K/V rows (the pool layout's row stride)
   __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
                                        uint32_t qflip, float c2_) {
     c2 = c2_;
+    rs = (int)p.kv_row_stride;
     vs = p.v_scale;
     load_q(p, b, h0, lane, qflip);
     reset();
@@ -487,14 +493,14 @@ struct QkMfmaPvT {
       // K: bytes 64i + 16(lane/16) .. +16 of the token's row, i < KK/2 (16-byte pieces: 8-byte
       // ones, one per score MFMA, halve the streaming rate); its halves feed MFMAs 2i, 2i+1.
       // V: the lane's slice of each of its four rows, E bytes (two 8-byte pieces at D = 256)
-      const char* krow = kb + tok * kRowBytes + 16 * (lane >> 4);
+      const char* krow = kb + tok * rs + 16 * (lane >> 4);
 #pragma unroll
       for (int i = 0; i < KL; ++i)
         t.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + 64 * i));
       const int r = lane >> 4, c = lane & 15;
 #pragma unroll
       for (int j = 0; j < kTileSteps; ++j) {
-        const char* row = vb + (kRows * j + r) * kRowBytes;
+        const char* row = vb + (kRows * j + r) * rs;
         if constexpr (D == 64) {
           t.v[j][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row + 4 * c));
         } else {
@@ -511,11 +517,11 @@ struct QkMfmaPvT {
         }
       }
     } else {
-      const char* krow = kb + tok * kRowBytes + 16 * (lane >> 4);
+      const char* krow = kb + tok * rs + 16 * (lane >> 4);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         t.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + 64 * kk));
-      load_v_rows<D>(t.v, vb, lane);
+      load_v_rows<D>(t.v, vb, lane, rs);
     }
   }
 

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert pa.abi_version() == 4
+    assert pa.abi_version() == 5
     for code, name in pa.STATUS_NAMES.items():
         s = pa.status_string(code)
         assert s and s != "unknown status", name
@@ -237,10 +237,11 @@ def test_balanced_empty_batch_is_ok_without_launch():
 # prepared decode (plans): creation-time checks, workspace sizes, run-time argument checks
 # ---------------------------------------------------------------------------------------------
 def plan_create(s, *, head_dim=128, block_size=16, window=0, schedule=0, workers=0, max_len=0,
-                kv_dtype=0, q_len=1):
+                kv_dtype=0, q_len=1, layout=None):
     h = ctypes.c_void_p()
+    lay = None if layout is None else ctypes.byref(pa.KvLayout(*layout))
     st = pa.lib().paged_attn_plan_create(ctypes.byref(s), head_dim, block_size, window, schedule,
-                                         kv_dtype, q_len, max_len, workers, ctypes.byref(h))
+                                         kv_dtype, lay, q_len, max_len, workers, ctypes.byref(h))
     return st, h
 
 
@@ -298,6 +299,13 @@ def test_plan_create_and_workspace_sizes():
     st, h = plan_create(shape(), schedule=2, workers=100, q_len=2, kv_dtype=1)
     assert st == 0 and b"mfmapv_fp8_d128_g4_q2_c8" in pa.lib().paged_attn_plan_name(h)
     pa.lib().paged_attn_plan_destroy(h)
+    # KV layouts: token-major, K/V interleaved per block, padded rows; FP8 token-major
+    for sched, lay, kv in ((0, (16 * 2 * 128, 128, 2 * 128), 0), (2, (2 * 2 * 16 * 128, 16 * 128, 128), 0),
+                           (1, (2 * 16 * 136, 16 * 136, 136), 0), (2, (16 * 2 * 128, 128, 256), 1)):
+        sh = shape(partition_size=512, max_partitions=4) if sched == 1 else shape()
+        st, h = plan_create(sh, schedule=sched, workers=64, layout=lay, kv_dtype=kv)
+        assert st == 0, (sched, lay, kv)
+        pa.lib().paged_attn_plan_destroy(h)
     pa.lib().paged_attn_plan_destroy(None)
 
 
@@ -311,6 +319,13 @@ def test_plan_create_and_workspace_sizes():
     (dict(q_len=2), -3),                         # several query tokens: balanced schedule only
     (dict(q_len=5, schedule=2, workers=64), -3),  # 5 tokens x 4 heads > 16 columns
     (dict(q_len=2, schedule=2, workers=64, window=0x7FFFFFFF), -2),
+    # layouts (elements; head_dim 128, block 16, 2 KV heads)
+    (dict(layout=(4096, 2048, 120)), -2),          # token stride below head_dim
+    (dict(layout=(0, 2048, 128)), -2), (dict(layout=(4096, -1, 128)), -2),
+    (dict(layout=(4096, 2048, 132)), -2),          # 264-byte rows: not 16-byte aligned
+    (dict(layout=(4100, 2048, 128)), -2),          # block stride not 16-byte aligned
+    (dict(layout=(4096, 2048, 136), kv_dtype=1), -2),   # FP8: 136-byte rows
+    (dict(layout=(4096, 2048, 1 << 26)), -2),      # row stride above 2^26 bytes
 ])
 def test_plan_create_rejects(kw, expect):
     st, h = plan_create(shape(), **kw)
@@ -321,7 +336,8 @@ def test_plan_unsplit_rejects_a_partitioned_shape_and_null_out_pointer():
     st, h = plan_create(shape(partition_size=512, max_partitions=4), schedule=0)
     assert st == -2
     s = shape()
-    assert pa.lib().paged_attn_plan_create(ctypes.byref(s), 128, 16, 0, 0, 0, 1, 0, 0, None) == -1
+    assert pa.lib().paged_attn_plan_create(ctypes.byref(s), 128, 16, 0, 0, 0, None, 1, 0, 0,
+                                           None) == -1
 
 
 def test_plan_run_argument_checks_without_launch():

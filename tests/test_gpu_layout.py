@@ -1,0 +1,106 @@
+"""GPU parity for KV pools in other layouts, given to a plan as (block, head, token) strides:
+token-major [NB][bs][Hkv][D], K and V interleaved per block [NB][2][Hkv][bs][D], and padded rows
+whose padding holds NaN.  The oracle reads the same values from the default layout, so every
+schedule, both KV formats and several query tokens must match it exactly as before."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_attn_amd as pa
+from workloads import make_config, make_workload
+
+from gpu_helpers import compare, log, max_len, oracle_full, run_plan, to_dev
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = ["token_major", "interleaved", "padded"]
+
+
+def relayout(wl, t, layout):
+    """Device K/V tensors of the workload in `layout`, and the plan's strides (elements)."""
+    k, v = wl.k_cache, wl.v_cache               # [NB][Hkv][bs][D], raw bits or codes
+    NB, H, bs, D = k.shape
+    code = np.uint8 if wl.kv_format == "fp8_e4m3" else np.int16
+    dev = torch.device("cuda")
+    if layout == "token_major":
+        kd = torch.from_numpy(np.ascontiguousarray(k.transpose(0, 2, 1, 3)).view(code)).to(dev)
+        vd = torch.from_numpy(np.ascontiguousarray(v.transpose(0, 2, 1, 3)).view(code)).to(dev)
+        strides = (bs * H * D, D, H * D)
+    elif layout == "interleaved":
+        buf = torch.from_numpy(np.ascontiguousarray(np.stack([k, v], axis=1)).view(code)).to(dev)
+        kd, vd = buf[:, 0], buf[:, 1]            # views: v starts H*bs*D elements after k
+        strides = (2 * H * bs * D, bs * D, D)
+    else:
+        pad = 16 if wl.kv_format == "fp8_e4m3" else 8     # 16 bytes of NaN after every row
+        nan = 0x7F if wl.kv_format == "fp8_e4m3" else 0x7FC0
+        kp = np.full((NB, H, bs, D + pad), nan, dtype=k.dtype)
+        vp = np.full((NB, H, bs, D + pad), nan, dtype=v.dtype)
+        kp[..., :D] = k
+        vp[..., :D] = v
+        kd = torch.from_numpy(kp.view(code)).to(dev)
+        vd = torch.from_numpy(vp.view(code)).to(dev)
+        strides = (H * bs * (D + pad), bs * (D + pad), D + pad)
+    torch.cuda.synchronize()
+    return dict(t, k=kd, v=vd), strides
+
+
+def plan_for(wl, schedule, strides, partition_size=64, num_workers=0):
+    return pa.Plan(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.stride,
+                   wl.head_dim, wl.block_size, window=wl.window, schedule=schedule,
+                   partition_size=partition_size, max_seq_len=max_len(wl),
+                   num_workers=num_workers, kv_dtype=wl.kv_format, q_len=wl.q_len,
+                   kv_layout=strides)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("schedule", ["unsplit", "partitioned", "balanced", "fused"])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_layouts_small(layout, schedule, kv):
+    wl = make_workload(name="layout", seq_lens=[0, 1, 15, 16, 17, 100, 257, 33], num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=32, seed=[3], window=40,
+                       with_sinks=True, poison=True, kv_format=kv,
+                       kv_scales=(0.0625, 0.05) if kv != "bf16" else (1.0, 1.0))
+    t, strides = relayout(wl, to_dev(wl), layout)
+    plan = plan_for(wl, schedule, strides, num_workers=7)
+    compare(*run_plan(plan, wl, t), *oracle_full(wl), f"{layout} {schedule} {kv}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("D,g", [(64, 8), (128, 1), (256, 4)])
+def test_layouts_head_dims_and_groups(D, g, layout):
+    wl = make_workload(name="layout", seq_lens=[300, 17, 1, 1000, 64], num_q_heads=2 * g,
+                       num_kv_heads=2, head_dim=D, block_size=16, seed=[D, g], poison=True)
+    t, strides = relayout(wl, to_dev(wl), layout)
+    for schedule in ("balanced", "unsplit"):
+        plan = plan_for(wl, schedule, strides)
+        compare(*run_plan(plan, wl, t), *oracle_full(wl), f"{layout} D={D} g={g} {schedule}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_layouts_several_query_tokens(layout):
+    wl = make_workload(name="layout multi", seq_lens=[0, 2, 17, 100, 257], num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=16, seed=[4], window=20,
+                       with_sinks=True, poison=True, q_len=4)
+    t, strides = relayout(wl, to_dev(wl), layout)
+    plan = plan_for(wl, "balanced", strides, num_workers=9)
+    log(f"[layout] {plan.name}")
+    compare(*run_plan(plan, wl, t), *oracle_full(wl), f"{layout} q_len=4")
+
+
+def test_token_major_decode_batch_workload():
+    """The Llama-8B-shaped step with a token-major pool, against the oracle in full."""
+    wl = make_config(2, poison=True)
+    t, strides = relayout(wl, to_dev(wl), "token_major")
+    compare(*run_plan(plan_for(wl, "balanced", strides), wl, t), *oracle_full(wl),
+            "token-major Llama-8B step")
+
+
+def test_default_strides_equal_no_layout_bitwise():
+    wl = make_config(5, seq_lens=[5000, 17, 9000, 4096, 1, 300, 0], poison=True)
+    t = to_dev(wl)
+    H, bs, D = wl.num_kv_heads, wl.block_size, wl.head_dim
+    a = run_plan(plan_for(wl, "balanced", None, num_workers=40), wl, t)
+    b = run_plan(plan_for(wl, "balanced", (H * bs * D, bs * D, D), num_workers=40), wl, t)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
