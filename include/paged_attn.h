@@ -246,9 +246,12 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  *                  This is the query length the one-token decode benchmark of ROCm/rocm-libraries
  *                  PR #13700 fixes at 1, and the longer-query case vllm.cpp PR #564 ("What is
  *                  deliberately not here") leaves out; the causal rule is this library's reading.
- *                  Every K/V row is read once per KV head for all q_len tokens: the (token, head)
- *                  pairs of a KV head share the tile.  Requires PA_SCHEDULE_BALANCED and
- *                  q_len * Hq/Hkv <= 16 (else PA_ERR_UNSUPPORTED); bf16 and FP8 caches alike.
+ *                  Up to 16 (token, head) pairs per KV head share each K/V tile, so with
+ *                  q_len * Hq/Hkv <= 16 every K/V row is read once per KV head for all q_len
+ *                  tokens; more tokens run in passes of 16 / (Hq/Hkv) tokens, each pass reading
+ *                  the keys its tokens attend.  Requires PA_SCHEDULE_BALANCED (else
+ *                  PA_ERR_UNSUPPORTED) and q_len <= 4096 (else PA_ERR_SHAPE); bf16 and FP8
+ *                  caches alike.
  *   max_seq_len    host-side upper bound on the lengths the plan will see, or 0 if unknown.
  *                  Balanced plans launch no more workers than that many tiles can keep busy
  *                  (a small batch then does not pay for thousands of idle workers); a length

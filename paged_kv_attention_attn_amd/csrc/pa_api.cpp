@@ -182,6 +182,8 @@ pa_status paged_attn_decode(const pa_shape* shape, const void* q, const void* k_
   p.psize = shape->partition_size;
   p.max_parts = split ? shape->max_partitions : 1;
   p.q_len = 1;
+  p.q_total = 1;
+  p.q_first = 0;
   p.group = group;
   set_default_layout(p, shape->num_kv_heads, block_size, 2 * (int64_t)head_dim);
   if (debug_log())
@@ -279,6 +281,8 @@ pa_status balanced_setup(const pa_shape* shape, int32_t head_dim, int32_t block_
   p.psize = 0;
   p.max_parts = 1;
   p.q_len = 1;
+  p.q_total = 1;
+  p.q_first = 0;
   p.group = group;
   set_default_layout(p, shape->num_kv_heads, block_size, 2 * (int64_t)head_dim);
   char* ws = static_cast<char*>(workspace);
@@ -469,6 +473,8 @@ struct pa_plan {
   int32_t head_dim;
   int32_t group;          // kernel columns: Hq/Hkv, or (q_len > 1) q_len*Hq/Hkv rounded up to 2^k
   int32_t waves, num_workers;
+  int32_t q_len;          // query tokens per sequence
+  int32_t pass_tokens;    // tokens per launch pair (all of them unless q_len * Hq/Hkv > 16)
   pa::QkPath path;
   pa::DecodeParams dec;   // sizes; pointers are filled per run
   pa::ReduceParams red;   // partitioned schedule: sizes
@@ -482,6 +488,7 @@ struct pa_plan {
 namespace {
 
 constexpr int32_t kMaxColumns = 16;   // (query token, head) pairs per KV head and kernel
+constexpr int32_t kMaxQueryTokens = 4096;
 
 // Largest row stride in bytes: 16 rows of a tile stay within 32-bit lane offsets.
 constexpr int64_t kMaxRowStrideBytes = int64_t(1) << 26;
@@ -507,16 +514,18 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
        num_workers > kMaxWorkers))
     return PA_ERR_SHAPE;
   if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
-  if (q_len < 1) return PA_ERR_SHAPE;
+  if (q_len < 1 || q_len > kMaxQueryTokens) return PA_ERR_SHAPE;
   int32_t columns = group;
+  int32_t pass_tokens = q_len;
   if (q_len > 1) {
-    // several query tokens: the balanced schedule, (token, head) columns on the matrix cores
+    // several query tokens: the balanced schedule, (token, head) columns on the matrix cores;
+    // more tokens than 16 columns hold run in passes of 16 / group tokens, each reading the KV
     if (schedule != PA_SCHEDULE_BALANCED) return PA_ERR_UNSUPPORTED;
-    if ((int64_t)q_len * group > kMaxColumns) return PA_ERR_UNSUPPORTED;
-    if (window > 0x7FFFFFFF - q_len) return PA_ERR_SHAPE;
     if ((int64_t)shape->num_seqs * q_len * shape->num_q_heads > 0x7FFFFFFF) return PA_ERR_SHAPE;
+    if ((int64_t)q_len * group > kMaxColumns) pass_tokens = kMaxColumns / group;
+    if (window > 0x7FFFFFFF - pass_tokens) return PA_ERR_SHAPE;
     columns = 1;
-    while (columns < q_len * group) columns *= 2;
+    while (columns < pass_tokens * group) columns *= 2;
   }
   pa::QkPath path;
   if (kv_dtype == PA_KV_FP8_E4M3)
@@ -532,6 +541,8 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   pl->kv_dtype = kv_dtype;
   pl->head_dim = head_dim;
   pl->group = columns;
+  pl->q_len = q_len;
+  pl->pass_tokens = pass_tokens;
   pl->waves = waves;
   pl->path = path;
   pl->num_workers = 0;
@@ -549,7 +560,9 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   p.window = window;
   p.psize = parted ? shape->partition_size : 0;
   p.max_parts = parted ? shape->max_partitions : 1;
-  p.q_len = q_len;
+  p.q_len = pass_tokens;
+  p.q_total = q_len;
+  p.q_first = 0;
   p.group = group;
   const int64_t elem = kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2;
   set_default_layout(p, shape->num_kv_heads, block_size, elem * head_dim);
@@ -593,7 +606,7 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
     if (max_seq_len > 0) {
       // at most this many 16-token tiles (a window start may add one), four per worker; the
       // query tokens' windows together span window + q_len - 1 keys
-      const int64_t wspan = window > 0 ? (int64_t)window + q_len - 1 : 0;
+      const int64_t wspan = window > 0 ? (int64_t)window + pass_tokens - 1 : 0;
       const int64_t span = wspan > 0 && wspan < max_seq_len ? wspan : max_seq_len;
       const int64_t tiles = (int64_t)shape->num_seqs * shape->num_kv_heads * ((span + 15) / 16 + 1);
       const int64_t cap = (tiles + 3) / 4;
@@ -602,8 +615,12 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
     pl->num_workers = num_workers;
     pl->bal = ws_layout(shape->num_seqs, columns, head_dim, num_workers);
     pl->workspace_bytes = (int64_t)pl->bal.total;
-    char qtag[32] = "";
-    if (q_len > 1) std::snprintf(qtag, sizeof(qtag), "_q%d_c%d", q_len, columns);
+    char qtag[48] = "";
+    const int32_t passes = (q_len + pass_tokens - 1) / pass_tokens;
+    if (passes > 1)
+      std::snprintf(qtag, sizeof(qtag), "_q%d_c%d_passes%d", q_len, columns, passes);
+    else if (q_len > 1)
+      std::snprintf(qtag, sizeof(qtag), "_q%d_c%d", q_len, columns);
     std::snprintf(pl->name, sizeof(pl->name), "pa_balanced_%s_d%d_g%d%s_workers%d + fixup",
                   pa::qk_path_name(path), head_dim, group, qtag, num_workers);
   }
@@ -708,8 +725,16 @@ pa_status paged_attn_plan_run(const pa_plan* plan, const void* q, const void* k_
     bp.ws_lse = reinterpret_cast<float*>(ws + plan->bal.lse);
     bp.ws_o = reinterpret_cast<float*>(ws + plan->bal.o);
     bp.num_workers = plan->num_workers;
-    e = pa::launch_balanced(bp, plan->head_dim, plan->group, plan->path, s);
-    if (e == hipSuccess) e = pa::launch_balanced_fixup(bp, plan->head_dim, plan->group, s);
+    // one decode + fix-up per pass of query tokens (a single pass unless there are more
+    // (token, head) columns than a kernel holds); the passes share the workspace in order
+    for (int32_t first = 0; first < plan->q_len && e == hipSuccess;
+         first += plan->pass_tokens) {
+      bp.d.q_first = first;
+      bp.d.q_len = plan->q_len - first < plan->pass_tokens ? plan->q_len - first
+                                                           : plan->pass_tokens;
+      e = pa::launch_balanced(bp, plan->head_dim, plan->group, plan->path, s);
+      if (e == hipSuccess) e = pa::launch_balanced_fixup(bp, plan->head_dim, plan->group, s);
+    }
   }
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

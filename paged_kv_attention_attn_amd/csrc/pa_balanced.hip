@@ -47,11 +47,12 @@ struct SeqSpan {
   bool bad;
 };
 
-__device__ __forceinline__ SeqSpan seq_span(int L, int window, int64_t cap) {
+// (q_rest: query tokens after this launch's last one; its keys end q_rest before L)
+__device__ __forceinline__ SeqSpan seq_span(int L, int window, int64_t cap, int q_rest = 0) {
   SeqSpan s;
-  s.L = L;
   s.bad = L < 0 || (int64_t)L > cap;
-  const int Lc = s.bad ? 0 : L;
+  const int Lc = s.bad ? 0 : (L > q_rest ? L - q_rest : 0);
+  s.L = s.bad ? L : Lc;
   s.start = (window > 0 && Lc > window) ? Lc - window : 0;
   s.t0 = s.start / kTileTokens;
   s.T = Lc > 0 ? (Lc + kTileTokens - 1) / kTileTokens - s.t0 : 0;
@@ -63,6 +64,11 @@ __device__ __forceinline__ SeqSpan seq_span(int L, int window, int64_t cap) {
 // in range.
 __device__ __forceinline__ int span_window(const DecodeParams& p) {
   return p.window > 0 ? p.window + p.q_len - 1 : 0;
+}
+
+// Query tokens of the sequence after this launch's last one.
+__device__ __forceinline__ int q_rest(const DecodeParams& p) {
+  return p.q_total - p.q_first - p.q_len;
 }
 
 // Workers actually used for T_total tiles, out of at most n.
@@ -116,7 +122,8 @@ struct BalancedCtx {
   const DecodeParams* p;
   int64_t cap;
   __device__ __forceinline__ SeqSpan span(int b) const {
-    return seq_span(__builtin_amdgcn_readfirstlane(p->seq_lens[b]), span_window(*p), cap);
+    return seq_span(__builtin_amdgcn_readfirstlane(p->seq_lens[b]), span_window(*p), cap,
+                    q_rest(*p));
   }
   // next tile; skips sequences without tiles (callers never step past the last tile)
   __device__ __forceinline__ void advance(Cursor& c) const {
@@ -152,7 +159,8 @@ void balanced_decode_kernel(const BalancedParams bp) {
   int64_t carry = 0;
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int j = base + lane;
-    const int64_t T = j < p.num_seqs ? seq_span(p.seq_lens[j], span_window(p), ctx.cap).T : 0;
+    const int64_t T =
+        j < p.num_seqs ? seq_span(p.seq_lens[j], span_window(p), ctx.cap, q_rest(p)).T : 0;
     const int64_t incl = wave_incl_scan64(T, lane) + carry;
     if (w == 0 && j < p.num_seqs) bp.prefix[j] = incl - T;
     carry = readlane64(incl, kWave - 1);
@@ -170,7 +178,8 @@ void balanced_decode_kernel(const BalancedParams bp) {
   carry = 0;
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int j = base + lane;
-    const int64_t T = j < p.num_seqs ? seq_span(p.seq_lens[j], span_window(p), ctx.cap).T : 0;
+    const int64_t T =
+        j < p.num_seqs ? seq_span(p.seq_lens[j], span_window(p), ctx.cap, q_rest(p)).T : 0;
     const int64_t incl = wave_incl_scan64(T, lane) + carry;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(j < p.num_seqs &&
                                                      incl * p.num_kv_heads > A);
@@ -250,7 +259,8 @@ void balanced_decode_kernel(const BalancedParams bp) {
           if (piece_bad) lv = __builtin_nanf("");
           float* dst;
           if (whole) {
-            const size_t row = ((size_t)at.b * p.q_len + (n >> sh)) * p.num_q_heads + hq;
+            const size_t row =
+                ((size_t)at.b * p.q_total + p.q_first + (n >> sh)) * p.num_q_heads + hq;
             dst = p.out + row * D;
             if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
           } else {
@@ -297,7 +307,8 @@ void balanced_decode_kernel(const BalancedParams bp) {
         if (piece_bad) lv = __builtin_nanf("");
         float* dst;
         if (whole) {
-          const size_t row = ((size_t)at.b * p.q_len + (h >> sh)) * p.num_q_heads + hq;
+          const size_t row =
+              ((size_t)at.b * p.q_total + p.q_first + (h >> sh)) * p.num_q_heads + hq;
           dst = p.out + row * D;
           if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
         } else {
@@ -412,7 +423,7 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
   const int Lb = p.seq_lens[b];
   const int64_t pre_b = bp.prefix[b];
   const int64_t pre_B = bp.prefix[p.num_seqs];
-  const SeqSpan s = seq_span(Lb, span_window(p), (int64_t)p.stride << p.bs_log2);
+  const SeqSpan s = seq_span(Lb, span_window(p), (int64_t)p.stride << p.bs_log2, q_rest(p));
   const int64_t total = pre_B * p.num_kv_heads;
   const int n_eff = effective_workers(total, bp.num_workers);
 
@@ -492,7 +503,7 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
       ov = __builtin_nanf("");
       lv = __builtin_nanf("");
     }
-    const size_t row = ((size_t)b * p.q_len + (n >> sh)) * p.num_q_heads + hq;
+    const size_t row = ((size_t)b * p.q_total + p.q_first + (n >> sh)) * p.num_q_heads + hq;
     p.out[row * D + (e - h * D)] = ov;
     if (e == h * D && p.lse != nullptr) p.lse[row] = lv;
   }

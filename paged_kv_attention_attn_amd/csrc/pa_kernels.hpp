@@ -26,11 +26,14 @@ struct DecodeParams {
   int32_t window;
   int32_t psize;              // 0 = unsplit
   int32_t max_parts;          // split: partition slots; unsplit: 1
-  // Query tokens per sequence (1 = one-token decode; more only on the balanced schedule):
-  // q [B][q_len][Hq][D], out [B][q_len][Hq][D], lse [B][q_len][Hq]; token i of sequence b sits
-  // at position seq_lens[b] - q_len + i and attends causally.  group = Hq / Hkv; a kernel's
-  // G template parameter counts columns (query token, head) per KV head, q_len * group <= G.
+  // Query tokens (1 = one-token decode; more only on the balanced schedule): q
+  // [B][q_total][Hq][D], out [B][q_total][Hq][D], lse [B][q_total][Hq]; token t of sequence b
+  // sits at position seq_lens[b] - q_total + t and attends causally.  A launch serves tokens
+  // [q_first, q_first + q_len).  group = Hq / Hkv; a kernel's G template parameter counts
+  // columns (query token, head) per KV head, q_len * group <= G.
   int32_t q_len;
+  int32_t q_total;
+  int32_t q_first;
   int32_t group;
   // KV pool layout in bytes, the same for K and V: row of (block phys, head kvh, slot s) at
   // phys * kv_block_stride + kvh * kv_head_stride + s * kv_row_stride.  Rows are 16-byte aligned.

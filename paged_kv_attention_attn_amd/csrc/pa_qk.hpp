@@ -453,7 +453,7 @@ struct QkMfmaPvT {
     head_lane = n < G && col_q < p.q_len;
     const int hh = n & (p.group - 1);
     const char* qrow = reinterpret_cast<const char*>(
-        p.q + (((size_t)b * p.q_len + (head_lane ? col_q : 0)) * p.num_q_heads + h0 +
+        p.q + (((size_t)b * p.q_total + p.q_first + (head_lane ? col_q : 0)) * p.num_q_heads + h0 +
                (head_lane ? hh : 0)) * D);
     const uint32_t keep = head_lane ? 0xFFFFFFFFu : 0u;
 #pragma unroll

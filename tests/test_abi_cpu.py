@@ -296,6 +296,10 @@ def test_plan_create_and_workspace_sizes():
     ws = a(3 * 8) + a(100 * 2 * 16 * 4) + a(100 * 2 * 16 * 128 * 4)
     assert pa.lib().paged_attn_plan_workspace_size(h) == ws
     pa.lib().paged_attn_plan_destroy(h)
+    # more tokens than 16 columns: passes of 16 / group tokens (here 4 + 4 + 1)
+    st, h = plan_create(shape(), schedule=2, workers=100, q_len=9)
+    assert st == 0 and b"_g4_q9_c16_passes3_workers100" in pa.lib().paged_attn_plan_name(h)
+    pa.lib().paged_attn_plan_destroy(h)
     st, h = plan_create(shape(), schedule=2, workers=100, q_len=2, kv_dtype=1)
     assert st == 0 and b"mfmapv_fp8_d128_g4_q2_c8" in pa.lib().paged_attn_plan_name(h)
     pa.lib().paged_attn_plan_destroy(h)
@@ -317,7 +321,7 @@ def test_plan_create_and_workspace_sizes():
     (dict(max_len=-1), -2), (dict(kv_dtype=2), -3), (dict(kv_dtype=-1), -3),
     (dict(q_len=0), -2), (dict(q_len=-3), -2),
     (dict(q_len=2), -3),                         # several query tokens: balanced schedule only
-    (dict(q_len=5, schedule=2, workers=64), -3),  # 5 tokens x 4 heads > 16 columns
+    (dict(q_len=4097, schedule=2, workers=64), -2),  # above 4096 query tokens
     (dict(q_len=2, schedule=2, workers=64, window=0x7FFFFFFF), -2),
     # layouts (elements; head_dim 128, block 16, 2 KV heads)
     (dict(layout=(4096, 2048, 120)), -2),          # token stride below head_dim

@@ -1,9 +1,9 @@
 """GPU parity of several query tokens per sequence (q_len > 1, causal, token i at position
 L - q_len + i) against the fp64 oracle, through paged_attn_plan_run on the balanced schedule:
 every (group, q_len) with q_len * group <= 16, every head size, windows, sinks, lengths shorter
-than q_len, bf16 and FP8 caches, the decode-batch and mixed workloads (sampled), and the
-argument checks.  The (token, head) pairs of a KV head are the kernels' columns, so q_len = 1
-must equal the one-token plan bit for bit."""
+than q_len, bf16 and FP8 caches, the decode-batch and mixed workloads (sampled), more tokens
+than 16 columns (run in passes), and the argument checks.  The (token, head) pairs of a KV head
+are the kernels' columns, so q_len = 1 must equal the one-token plan bit for bit."""
 from __future__ import annotations
 
 import numpy as np
@@ -96,10 +96,26 @@ def test_multi_mixed_workload_window_sinks():
     compare(out, lse, *oracle_full(wl), "multi mixed Q=3 window 4096 + sinks")
 
 
+# more (token, head) pairs than 16 columns: passes of 16 / group tokens
+PASS_COMBOS = [(8, 3), (8, 4), (4, 13), (2, 9), (1, 40)]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("g,Q", PASS_COMBOS)
+def test_multi_in_passes(g, Q, kv):
+    lens = [0, 1, Q - 1, Q, Q + 1, 17, 100, 257, 1000]
+    wl = multi_workload(128, g, Q, window=0 if Q % 2 else 50, sinks=True, kv=kv, lens=lens)
+    plan = make_plan(wl, "balanced", num_workers=23)
+    log(f"[multi] {plan.name}")
+    assert "passes" in plan.name
+    compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl),
+            f"multi passes g={g} Q={Q} kv={kv} W={wl.window}")
+
+
 def test_multi_plan_rejects_unsupported_requests():
     wl = multi_workload(128, 8, 2)
-    with pytest.raises(pa.PagedAttnError):     # 3 x 8 columns > 16
-        pa.Plan(2, 16, 2, wl.num_blocks, wl.stride, 128, 16, schedule="balanced", q_len=3)
+    with pytest.raises(pa.PagedAttnError):     # above 4096 query tokens
+        pa.Plan(2, 16, 2, wl.num_blocks, wl.stride, 128, 16, schedule="balanced", q_len=4097)
     with pytest.raises(pa.PagedAttnError):     # only the balanced schedule takes q_len > 1
         pa.Plan(2, 16, 2, wl.num_blocks, wl.stride, 128, 16, schedule="unsplit", q_len=2)
     with pytest.raises(pa.PagedAttnError):
