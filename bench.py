@@ -129,17 +129,22 @@ def latency_mode(args, torch, pa, dev) -> int:
     """Small-batch latency rows (not the headline): the tiny workload and the two context shapes
     (32 q / 4 KV heads, D 128, bs 16, B1 L2048 and B4 L4096), each schedule run three ways:
     the eager binding (checks + launches per call), a prepared plan, and a HIP graph replaying
-    the plan's launches.  Prints one JSON line with a row per (shape, schedule)."""
+    the plan's launches.  With --kv fp8_e4m3 or --q-len > 1 only plans exist (the eager
+    columns are null), and several query tokens run on the balanced schedule only.  Prints one
+    JSON line with a row per (shape, schedule)."""
     import numpy as np
 
-    from workloads import make_config, make_workload
+    from workloads import FP8_SCALES, make_config, make_workload
 
-    shapes = [("tiny B2 L{37,100} 4q/2kv", make_config(1))]
+    fp8 = args.kv != "bf16"
+    Q = args.q_len
+    shapes = [("tiny B2 L{37,100} 4q/2kv", make_config(1, kv_format=args.kv, q_len=Q))]
     for B, L in ((1, 2048), (4, 4096)):
         shapes.append((f"context B{B} L{L} 32q/4kv D128 bs16",
                        make_workload(name="context", seq_lens=[L] * B, num_q_heads=32,
                                      num_kv_heads=4, head_dim=128, block_size=16,
-                                     seed=[11, B, L])))
+                                     seed=[11, B, L], kv_format=args.kv,
+                                     kv_scales=FP8_SCALES if fp8 else (1.0, 1.0), q_len=Q)))
     K = args.steps
     rows = []
     for label, wl in shapes:
@@ -148,14 +153,16 @@ def latency_mode(args, torch, pa, dev) -> int:
             return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
         q, k, v, bt, L = up(wl.q), up(wl.k_cache), up(wl.v_cache), up(wl.block_table), \
             up(wl.seq_lens)
-        B, Hq, D = wl.q.shape
+        B, Hq, D = wl.num_seqs, wl.num_q_heads, wl.head_dim
         maxL = int(wl.seq_lens.max())
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-        for sched in ("unsplit", "partitioned", "fused", "balanced"):
+        out = torch.empty(wl.q.shape, dtype=torch.float32, device=dev)
+        lse = torch.empty(wl.q.shape[:-1], dtype=torch.float32, device=dev)
+        scheds = ("balanced",) if Q > 1 else ("unsplit", "partitioned", "fused", "balanced")
+        for sched in scheds:
             P = 256 if sched in ("partitioned", "fused") else 0
             plan = pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
-                           schedule=sched, partition_size=P, max_seq_len=maxL)
+                           schedule=sched, partition_size=P, max_seq_len=maxL,
+                           kv_dtype=args.kv, q_len=Q)
             ws = plan.workspace(dev)
             if ws is not None:
                 ws.zero_()
@@ -179,10 +186,13 @@ def latency_mode(args, torch, pa, dev) -> int:
                                        workspace=bws)
 
             def planned():
-                plan.run(q, k, v, bt, L, float(wl.scale), out=out, lse=lse, workspace=ws)
+                plan.run(q, k, v, bt, L, float(wl.scale), out=out, lse=lse, workspace=ws,
+                         k_scale=wl.k_scale, v_scale=wl.v_scale)
 
-            res = {"shape": label, "schedule": sched, "variant": plan.name}
-            for name, fn in (("eager", eager), ("plan", planned)):
+            res = {"shape": label, "schedule": sched, "variant": plan.name, "kv_dtype": args.kv,
+                   "q_len": Q}
+            ways = (("plan", planned),) if (fp8 or Q > 1) else (("eager", eager), ("plan", planned))
+            for name, fn in ways:
                 for _ in range(10):
                     fn()
                 torch.cuda.synchronize()
