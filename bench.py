@@ -80,6 +80,17 @@ def measured_traffic(workload: str, schedule: str):
     return None
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
     """The fp64 oracle on this host, one thread, over the whole step's batch, repeated until at
     least ``min_seconds`` have passed; the value is the mean rate."""
@@ -99,6 +110,7 @@ def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
             reps += 1
     return {"value": round(wl.kv_bytes() * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "seconds_per_step": round(dt / reps, 3), "repeats": reps,
+            "cpu_model": _cpu_model(),
             "sample": f"the whole step ({wl.num_seqs} sequences, all heads) of the same "
                       f"workload, NumPy float64, 1 BLAS thread, repeated {reps} times"}
 
@@ -436,6 +448,8 @@ def main() -> int:
             "partition_size": P if P > 0 else None,
             "workers": workers if P < 0 else None, "kv_bytes_per_step": kv_bytes,
             "variant": variant, "kv_pool_copies": copies, "parallelism": "none (1 GPU)",
+            "device": {"name": props.name, "arch": props.gcnArchName,
+                       "hip": str(torch.version.hip), "torch": torch.__version__},
         },
         "roofline": {
             "bound": "hbm",
@@ -449,6 +463,7 @@ def main() -> int:
             "interval": "decode and merge launches" if planned else "decode launch",
             "algorithmic_bytes_per_launch": kv_bytes,
             "attainable_stream_read_GBps": round(attainable, 1),
+            "frac_of_attainable": round(achieved / attainable, 4),
         },
     }
     if not args.no_cpu_baseline:
