@@ -487,7 +487,9 @@ struct pa_plan {
 
 namespace {
 
-constexpr int32_t kMaxColumns = 16;   // (query token, head) pairs per KV head and kernel
+// (query token, head) pairs per KV head one kernel holds: 32 (two 16-column halves sharing the
+// tile) at head_dim <= 128, 16 at 256
+int32_t max_columns(int32_t head_dim) { return head_dim <= 128 ? 32 : 16; }
 constexpr int32_t kMaxQueryTokens = 4096;
 
 // Largest row stride in bytes: 16 rows of a tile stay within 32-bit lane offsets.
@@ -522,7 +524,8 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
     // more tokens than 16 columns hold run in passes of 16 / group tokens, each reading the KV
     if (schedule != PA_SCHEDULE_BALANCED) return PA_ERR_UNSUPPORTED;
     if ((int64_t)shape->num_seqs * q_len * shape->num_q_heads > 0x7FFFFFFF) return PA_ERR_SHAPE;
-    if ((int64_t)q_len * group > kMaxColumns) pass_tokens = kMaxColumns / group;
+    if ((int64_t)q_len * group > max_columns(head_dim))
+      pass_tokens = max_columns(head_dim) / group;
     if (window > 0x7FFFFFFF - pass_tokens) return PA_ERR_SHAPE;
     columns = 1;
     while (columns < pass_tokens * group) columns *= 2;

@@ -232,46 +232,56 @@ void balanced_decode_kernel(const BalancedParams bp) {
   // flush the current piece of unit (at.b, at.kvh), which ends at tile at.ti
   auto flush = [&](const Cursor& at) {
     if constexpr (QK::kColumns) {
-      // by columns: lane (r, c) finishes columns 4r + i, i < 4, that exist
-      qk.merge_cols();
+      // by columns: lane (r, c) finishes columns cb + 4r + i, i < 4, that exist, of each
+      // 16-column half (cb = 0, 16)
       const bool whole = piece_start == 0 && at.ti == at.s.T - 1;
       const int ncols = p.q_len * p.group;
       const int sh = __builtin_ctz((unsigned)p.group);
+      auto finish_half = [&](auto& half, int cb) {
+        half.merge_cols();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = 4 * (lane >> 4) + i;
-        float M = qk.col_m(n), lt = qk.col_l(n);   // every lane takes part in the reads
-        if (n < ncols) {
-          const int hq = at.kvh * p.group + (n & (p.group - 1));
-          float scale_o = 1.f;
-          if (whole && p.sinks != nullptr) {
-            // the sink logit joins the max and the denominator with a zero value row
-            const float s2 = p.sinks[hq] * kLog2e;
-            const float M2 = fmaxf(M, s2);
-            const float M2u = M2 == -INFINITY ? 0.f : M2;
-            scale_o = fast_exp2(M - M2u);
-            lt = fmaf(lt, scale_o, fast_exp2(s2 - M2u));
-            M = M2;
-          }
-          // lt is 0 only for an empty piece; a NaN input (lt = NaN) must reach the outputs
-          const float inv = lt != 0.f ? scale_o / lt : 0.f;
-          float lv = lt != 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
-          if (piece_bad) lv = __builtin_nanf("");
-          float* dst;
-          if (whole) {
-            const size_t row =
-                ((size_t)at.b * p.q_total + p.q_first + (n >> sh)) * p.num_q_heads + hq;
-            dst = p.out + row * D;
-            if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
-          } else {
-            const size_t slot = ((size_t)w * 2 + (first_piece ? 0 : 1)) * G + n;
-            dst = bp.ws_o + slot * D;
-            if (c == 0) bp.ws_lse[slot] = lv;
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int nl = 4 * (lane >> 4) + i;         // column within the half
+          const int n = cb + nl;
+          float M = half.col_m(nl), lt = half.col_l(nl);   // every lane takes part in the reads
+          if (n < ncols) {
+            const int hq = at.kvh * p.group + (n & (p.group - 1));
+            float scale_o = 1.f;
+            if (whole && p.sinks != nullptr) {
+              // the sink logit joins the max and the denominator with a zero value row
+              const float s2 = p.sinks[hq] * kLog2e;
+              const float M2 = fmaxf(M, s2);
+              const float M2u = M2 == -INFINITY ? 0.f : M2;
+              scale_o = fast_exp2(M - M2u);
+              lt = fmaf(lt, scale_o, fast_exp2(s2 - M2u));
+              M = M2;
+            }
+            // lt is 0 only for an empty piece; a NaN input (lt = NaN) must reach the outputs
+            const float inv = lt != 0.f ? scale_o / lt : 0.f;
+            float lv = lt != 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
+            if (piece_bad) lv = __builtin_nanf("");
+            float* dst;
+            if (whole) {
+              const size_t row =
+                  ((size_t)at.b * p.q_total + p.q_first + (n >> sh)) * p.num_q_heads + hq;
+              dst = p.out + row * D;
+              if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
+            } else {
+              const size_t slot = ((size_t)w * 2 + (first_piece ? 0 : 1)) * G + n;
+              dst = bp.ws_o + slot * D;
+              if (c == 0) bp.ws_lse[slot] = lv;
+            }
 #pragma unroll
-          for (int e = 0; e < E; ++e)
-            dst[RG::dim(c, e)] = piece_bad ? __builtin_nanf("") : qk.acc(i, e) * inv;
+            for (int e = 0; e < E; ++e)
+              dst[RG::dim(c, e)] = piece_bad ? __builtin_nanf("") : half.acc(i, e) * inv;
+          }
         }
+      };
+      if constexpr (QK::kHalves == 2) {
+        finish_half(qk.h[0], 0);
+        finish_half(qk.h[1], 16);
+      } else {
+        finish_half(qk, 0);
       }
       first_piece = false;
       piece_bad = false;
@@ -339,10 +349,8 @@ void balanced_decode_kernel(const BalancedParams bp) {
         if (tok0 >= lo_all && tok0 + kTileTokens <= hi_all) {
           qk.template consume<false>(t, 0, 0, 0, lane);
         } else {
-          // this lane's column: its query token's keys [lo, hi)
-          const int hi = at.s.L - p.q_len + qk.col_q + 1;
-          const int lo = p.window > 0 ? max(hi - p.window, 0) : 0;
-          qk.template consume<true>(t, tok0, lo, hi, at.s.start, at.s.L, lane);
+          // each lane's column: its query token's keys
+          qk.consume_cols(t, tok0, hi_all, p.window, at.s.start, at.s.L, lane);
         }
       } else {
         if (tok0 >= at.s.start && tok0 + kTileTokens <= at.s.L)
@@ -521,7 +529,7 @@ using BQK = QkPolicy<D, G, PATH>;
 // for the same bytes in flight, measured slower)
 template <int D, int G, QkPath PATH>
 constexpr int bal_depth() {
-  return D * G <= 512 ? 2 : 1;
+  return (D * G <= 512 || G == 32) ? 2 : 1;
 }
 
 template <int D, int G, QkPath PATH>
@@ -554,14 +562,22 @@ hipError_t launch_fix_g(const BalancedParams& bp, int group, hipStream_t stream)
     case 4: return launch_fix<D, 4>(bp, stream);
     case 8: return launch_fix<D, 8>(bp, stream);
     case 16: return launch_fix<D, 16>(bp, stream);
+    case 32:
+      if constexpr (D <= 128) return launch_fix<D, 32>(bp, stream);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
-// Sixteen columns exist only for the matrix-core P.V policies (several query tokens).
+// Sixteen columns exist only for the matrix-core P.V policies (several query tokens), and
+// thirty-two (a pair of sixteen) for those at D <= 128.
 template <QkPath PATH>
 constexpr bool has_16_columns() {
   return PATH == QkPath::kMfmaPv || PATH == QkPath::kMfmaPvFp8;
+}
+template <int D, QkPath PATH>
+constexpr bool has_32_columns() {
+  return has_16_columns<PATH>() && D <= 128;
 }
 
 template <int D, QkPath PATH>
@@ -573,6 +589,9 @@ hipError_t launch_bal_g(const BalancedParams& bp, int group, hipStream_t stream)
     case 8: return launch_bal<D, 8, PATH>(bp, stream);
     case 16:
       if constexpr (has_16_columns<PATH>()) return launch_bal<D, 16, PATH>(bp, stream);
+      return hipErrorInvalidValue;
+    case 32:
+      if constexpr (has_32_columns<D, PATH>()) return launch_bal<D, 32, PATH>(bp, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -600,6 +619,10 @@ const void* bal_ptr(int head_dim, int group) {
       case 16:                                                     \
         if constexpr (has_16_columns<PATH>())                      \
           return balanced_kernel_ptr<D, 16, PATH>();               \
+        return nullptr;                                            \
+      case 32:                                                     \
+        if constexpr (has_32_columns<D, PATH>())                   \
+          return balanced_kernel_ptr<D, 32, PATH>();               \
         return nullptr;                                            \
       default: return nullptr;                                     \
     }                                                              \

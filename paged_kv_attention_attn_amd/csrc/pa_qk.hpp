@@ -433,6 +433,7 @@ struct QkMfmaPvT {
   // scalar registers and costs about 28 fewer VGPRs.
   static constexpr bool kColumns = G == 16;
   static constexpr bool kQueryTokens = true;   // columns may be several query tokens
+  static constexpr int kHalves = 1;
   u32x4_t qb[KK];
   float c2;
   float vs;   // FP8: V scale
@@ -443,14 +444,15 @@ struct QkMfmaPvT {
   f32x4_t cacc[E];
   float up[(G > 4 && G <= 8) ? 4 : 1][E];   // G = 8: heads 4..7 brought up by merge_rows
 
-  // q rows of the unit whose first head is h0 (= KV head * group): lane column n reads query
-  // token n / group, head h0 + n % group.
+  // q rows of the unit whose first head is h0 (= KV head * group): lane column n (col_base +
+  // lane % 16; col_base = 16 for the second half of a 32-column pair) reads query token
+  // n / group, head h0 + n % group.  Columns past q_len * group are padding (zero q).
   __device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int lane,
-                                         uint32_t qflip) {
-    const int n = lane & 15;
+                                         uint32_t qflip, int col_base = 0) {
+    const int n = col_base + (lane & 15);
     const int sh = __builtin_ctz((unsigned)p.group);   // group is a power of two
     col_q = n >> sh;
-    head_lane = n < G && col_q < p.q_len;
+    head_lane = col_q < p.q_len;
     const int hh = n & (p.group - 1);
     const char* qrow = reinterpret_cast<const char*>(
         p.q + (((size_t)b * p.q_total + p.q_first + (head_lane ? col_q : 0)) * p.num_q_heads + h0 +
@@ -478,11 +480,11 @@ struct QkMfmaPvT {
   }
   int rs;   // bytes between a block's consecutive K/V rows (the pool layout's row stride)
   __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
-                                       uint32_t qflip, float c2_) {
+                                       uint32_t qflip, float c2_, int col_base = 0) {
     c2 = c2_;
     rs = (int)p.kv_row_stride;
     vs = p.v_scale;
-    load_q(p, b, h0, lane, qflip);
+    load_q(p, b, h0, lane, qflip, col_base);
     reset();
   }
 
@@ -528,6 +530,14 @@ struct QkMfmaPvT {
   template <bool MASKED>
   __device__ __forceinline__ void consume(Tile& t, int tok0, int lo, int hi, int lane) {
     consume<MASKED>(t, tok0, lo, hi, lo, hi, lane);
+  }
+  // Masked tile with query tokens: this lane's column sees keys [max(hi - window, 0), hi) with
+  // hi = hi_base + its query token (hi_base: the first token's position + 1).
+  __device__ __forceinline__ void consume_cols(Tile& t, int tok0, int hi_base, int window,
+                                               int vlo, int vhi, int lane) {
+    const int hi = hi_base + col_q;
+    const int lo = window > 0 ? max(hi - window, 0) : 0;
+    consume<true>(t, tok0, lo, hi, vlo, vhi, lane);
   }
   // Masked form: scores of column (lane) keys outside [lo, hi) drop out (lo, hi may differ by
   // lane: the column's query token); V rows outside [vlo, vhi), the union, are zeroed so that a
@@ -676,13 +686,59 @@ using QkMfmaPv = QkMfmaPvT<D, G, false>;
 template <int D, int G>
 using QkMfmaPvFp8 = QkMfmaPvT<D, G, true>;
 
-// The policy of a path.
+// Thirty-two columns (query tokens x heads) as two 16-column halves that share every K/V tile:
+// the tile is loaded once and each half runs its own q.k, softmax and P.V on it.  Finished
+// column-wise, half by half (col_base 0 and 16).
+template <int D, bool FP8>
+struct QkMfmaPvPair {
+  using Half = QkMfmaPvT<D, 16, FP8>;
+  using Tile = typename Half::Tile;
+  static constexpr int kRowBytes = Half::kRowBytes;
+  static constexpr int kMinWavesPerEu = 1;
+  static constexpr bool kColumns = true;
+  static constexpr bool kQueryTokens = true;
+  static constexpr int kHalves = 2;
+  Half h[2];
+
+  __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
+                                       uint32_t qflip, float c2) {
+    h[0].init(p, b, h0, lane, qflip, c2, 0);
+    h[1].init(p, b, h0, lane, qflip, c2, 16);
+  }
+  __device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int lane,
+                                         uint32_t qflip) {
+    h[0].load_q(p, b, h0, lane, qflip, 0);
+    h[1].load_q(p, b, h0, lane, qflip, 16);
+  }
+  __device__ __forceinline__ void reset() {
+    h[0].reset();
+    h[1].reset();
+  }
+  __device__ __forceinline__ void issue(Tile& t, const char* kb, const char* vb,
+                                        int lane) const {
+    h[0].issue(t, kb, vb, lane);
+  }
+  template <bool MASKED>
+  __device__ __forceinline__ void consume(Tile& t, int tok0, int lo, int hi, int lane) {
+    h[0].template consume<MASKED>(t, tok0, lo, hi, lane);
+    h[1].template consume<MASKED>(t, tok0, lo, hi, lane);
+  }
+  __device__ __forceinline__ void consume_cols(Tile& t, int tok0, int hi_base, int window,
+                                               int vlo, int vhi, int lane) {
+    h[0].consume_cols(t, tok0, hi_base, window, vlo, vhi, lane);
+    h[1].consume_cols(t, tok0, hi_base, window, vlo, vhi, lane);
+  }
+};
+
+// The policy of a path (32 columns: the matrix-core P.V pair).
 template <int D, int G, QkPath PATH>
 using QkPolicy = typename std::conditional<
-    PATH == QkPath::kValu, QkValu<D, G>,
+    G == 32, QkMfmaPvPair<D, PATH == QkPath::kMfmaPvFp8>,
     typename std::conditional<
-        PATH == QkPath::kMfma, QkMfma<D, G>,
-        typename std::conditional<PATH == QkPath::kMfmaPv, QkMfmaPv<D, G>,
-                                  QkMfmaPvFp8<D, G>>::type>::type>::type;
+        PATH == QkPath::kValu, QkValu<D, G>,
+        typename std::conditional<
+            PATH == QkPath::kMfma, QkMfma<D, G>,
+            typename std::conditional<PATH == QkPath::kMfmaPv, QkMfmaPv<D, G>,
+                                      QkMfmaPvFp8<D, G>>::type>::type>::type>::type;
 
 }  // namespace pa

@@ -296,8 +296,15 @@ def test_plan_create_and_workspace_sizes():
     ws = a(3 * 8) + a(100 * 2 * 16 * 4) + a(100 * 2 * 16 * 128 * 4)
     assert pa.lib().paged_attn_plan_workspace_size(h) == ws
     pa.lib().paged_attn_plan_destroy(h)
-    # more tokens than 16 columns: passes of 16 / group tokens (here 4 + 4 + 1)
+    # 17 to 32 columns: one pass of the two-half kernels at D <= 128; more: passes of
+    # 32 / group tokens (here 8 + 1), or of 16 / group at D = 256 (4 + 4 + 1)
+    st, h = plan_create(shape(), schedule=2, workers=100, q_len=8)
+    assert st == 0 and b"_g4_q8_c32_workers100" in pa.lib().paged_attn_plan_name(h)
+    pa.lib().paged_attn_plan_destroy(h)
     st, h = plan_create(shape(), schedule=2, workers=100, q_len=9)
+    assert st == 0 and b"_g4_q9_c32_passes2_workers100" in pa.lib().paged_attn_plan_name(h)
+    pa.lib().paged_attn_plan_destroy(h)
+    st, h = plan_create(shape(), schedule=2, workers=100, q_len=9, head_dim=256)
     assert st == 0 and b"_g4_q9_c16_passes3_workers100" in pa.lib().paged_attn_plan_name(h)
     pa.lib().paged_attn_plan_destroy(h)
     st, h = plan_create(shape(), schedule=2, workers=100, q_len=2, kv_dtype=1)

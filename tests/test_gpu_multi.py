@@ -96,20 +96,38 @@ def test_multi_mixed_workload_window_sinks():
     compare(out, lse, *oracle_full(wl), "multi mixed Q=3 window 4096 + sinks")
 
 
-# more (token, head) pairs than 16 columns: passes of 16 / group tokens
-PASS_COMBOS = [(8, 3), (8, 4), (4, 13), (2, 9), (1, 40)]
+# 17 to 32 (token, head) pairs: the two-half (32-column) kernels at D <= 128
+COMBOS_32 = [(8, 3), (8, 4), (4, 5), (4, 8), (2, 9), (2, 16), (1, 17), (1, 32)]
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
-@pytest.mark.parametrize("g,Q", PASS_COMBOS)
-def test_multi_in_passes(g, Q, kv):
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("g,Q", COMBOS_32)
+def test_multi_32_columns(g, Q, D, kv):
+    lens = [0, 1, Q - 1, Q, Q + 1, 17, 100, 257]
+    wl = multi_workload(D, g, Q, window=0 if Q % 2 else 9, sinks=g % 2 == 0, kv=kv, lens=lens)
+    plan = make_plan(wl, "balanced", num_workers=19)
+    log(f"[multi] {plan.name}")
+    assert "_c32_" in plan.name and "passes" not in plan.name
+    compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl),
+            f"multi 32 columns D={D} g={g} Q={Q} kv={kv} W={wl.window}")
+
+
+# more (token, head) pairs than one kernel holds (32 at D <= 128, 16 at 256): passes
+PASS_COMBOS = [(128, 8, 5), (128, 4, 13), (128, 2, 17), (128, 1, 40), (64, 8, 6),
+               (256, 8, 3), (256, 4, 5), (256, 1, 20)]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("D,g,Q", PASS_COMBOS)
+def test_multi_in_passes(D, g, Q, kv):
     lens = [0, 1, Q - 1, Q, Q + 1, 17, 100, 257, 1000]
-    wl = multi_workload(128, g, Q, window=0 if Q % 2 else 50, sinks=True, kv=kv, lens=lens)
+    wl = multi_workload(D, g, Q, window=0 if Q % 2 else 50, sinks=True, kv=kv, lens=lens)
     plan = make_plan(wl, "balanced", num_workers=23)
     log(f"[multi] {plan.name}")
     assert "passes" in plan.name
     compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl),
-            f"multi passes g={g} Q={Q} kv={kv} W={wl.window}")
+            f"multi passes D={D} g={g} Q={Q} kv={kv} W={wl.window}")
 
 
 def test_multi_plan_rejects_unsupported_requests():
