@@ -246,10 +246,10 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  *                  This is the query length the one-token decode benchmark of ROCm/rocm-libraries
  *                  PR #13700 fixes at 1, and the longer-query case vllm.cpp PR #564 ("What is
  *                  deliberately not here") leaves out; the causal rule is this library's reading.
- *                  Up to 16 (token, head) pairs per KV head share each K/V tile, so with
- *                  q_len * Hq/Hkv <= 16 every K/V row is read once per KV head for all q_len
- *                  tokens; more tokens run in passes of 16 / (Hq/Hkv) tokens, each pass reading
- *                  the keys its tokens attend.  Requires PA_SCHEDULE_BALANCED (else
+ *                  Up to 32 (token, head) pairs per KV head share each K/V tile (16 at
+ *                  head_dim 256), so with q_len * Hq/Hkv within that every K/V row is read once
+ *                  per KV head for all q_len tokens; more tokens run in passes of 32 / (Hq/Hkv)
+ *                  (16 / (Hq/Hkv)) tokens, each pass reading the keys its tokens attend.  Requires PA_SCHEDULE_BALANCED (else
  *                  PA_ERR_UNSUPPORTED) and q_len <= 4096 (else PA_ERR_SHAPE); bf16 and FP8
  *                  caches alike.
  *   max_seq_len    host-side upper bound on the lengths the plan will see, or 0 if unknown.
