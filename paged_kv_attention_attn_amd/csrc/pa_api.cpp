@@ -324,7 +324,7 @@ pa_status paged_attn_decode_balanced(const pa_shape* shape, const void* q, const
                  pa::qk_path_name(path), shape->num_seqs,
                  shape->num_q_heads, shape->num_kv_heads, block_size, window, bp.num_workers);
   const hipError_t e =
-      pa::launch_balanced(bp, head_dim, group, path, static_cast<hipStream_t>(stream));
+      pa::launch_balanced(bp, head_dim, group, path, false, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -603,7 +603,7 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
     std::snprintf(pl->name, sizeof(pl->name), "%s + merge by the last partition", dname);
   } else {
     if (num_workers == 0) {
-      num_workers = pa::balanced_default_workers(head_dim, columns, path);
+      num_workers = pa::balanced_default_workers(head_dim, columns, path, q_len > 1);
       if (num_workers <= 0) return PA_ERR_LAUNCH;
     }
     if (max_seq_len > 0) {
@@ -735,7 +735,7 @@ pa_status paged_attn_plan_run(const pa_plan* plan, const void* q, const void* k_
       bp.d.q_first = first;
       bp.d.q_len = plan->q_len - first < plan->pass_tokens ? plan->q_len - first
                                                            : plan->pass_tokens;
-      e = pa::launch_balanced(bp, plan->head_dim, plan->group, plan->path, s);
+      e = pa::launch_balanced(bp, plan->head_dim, plan->group, plan->path, plan->q_len > 1, s);
       if (e == hipSuccess) e = pa::launch_balanced_fixup(bp, plan->head_dim, plan->group, s);
     }
   }

@@ -62,13 +62,13 @@ __device__ __forceinline__ SeqSpan seq_span(int L, int window, int64_t cap, int 
 // Window that decides a unit's tiles: with q_len query tokens the union of their windows is
 // window + q_len - 1 keys ending at the last position (0 = no window).  The host keeps the sum
 // in range.
-__device__ __forceinline__ int span_window(const DecodeParams& p) {
-  return p.window > 0 ? p.window + p.q_len - 1 : 0;
+__device__ __forceinline__ int span_window(const DecodeParams& p, const QShape& qs) {
+  return p.window > 0 ? p.window + qs.q_len - 1 : 0;
 }
 
 // Query tokens of the sequence after this launch's last one.
-__device__ __forceinline__ int q_rest(const DecodeParams& p) {
-  return p.q_total - p.q_first - p.q_len;
+__device__ __forceinline__ int q_rest(const QShape& qs) {
+  return qs.q_total - qs.q_first - qs.q_len;
 }
 
 // Workers actually used for T_total tiles, out of at most n.
@@ -121,9 +121,9 @@ struct Cursor {
 struct BalancedCtx {
   const DecodeParams* p;
   int64_t cap;
+  int swin, qrest;   // span_window and q_rest of the launch
   __device__ __forceinline__ SeqSpan span(int b) const {
-    return seq_span(__builtin_amdgcn_readfirstlane(p->seq_lens[b]), span_window(*p), cap,
-                    q_rest(*p));
+    return seq_span(__builtin_amdgcn_readfirstlane(p->seq_lens[b]), swin, cap, qrest);
   }
   // next tile; skips sequences without tiles (callers never step past the last tile)
   __device__ __forceinline__ void advance(Cursor& c) const {
@@ -144,23 +144,26 @@ struct BalancedCtx {
   }
 };
 
-template <int D, int G, int DEPTH, class QK>
+// MULTI: the launch may have several query tokens (reads q_len, q_total, q_first, group);
+// otherwise they are the constants of one token, which keeps them out of the scalar registers.
+template <int D, int G, int DEPTH, class QK, bool MULTI>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(QK::kMinWavesPerEu)))
 void balanced_decode_kernel(const BalancedParams bp) {
   using RG = RowGeom<D>;
   constexpr int E = RG::kElems;
   const DecodeParams& p = bp.d;
+  const QShape qs = make_qshape<MULTI, G>(p);
   const int lane = threadIdx.x;
   const int c = lane & (kRowLanes - 1);
   const int w = blockIdx.x;
-  const BalancedCtx ctx{&p, (int64_t)p.stride << p.bs_log2};
+  const BalancedCtx ctx{&p, (int64_t)p.stride << p.bs_log2, span_window(p, qs), q_rest(qs)};
 
   // pass 1: total tiles (worker 0 also records the per-sequence prefix for the fix-up)
   int64_t carry = 0;
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int j = base + lane;
     const int64_t T =
-        j < p.num_seqs ? seq_span(p.seq_lens[j], span_window(p), ctx.cap, q_rest(p)).T : 0;
+        j < p.num_seqs ? seq_span(p.seq_lens[j], ctx.swin, ctx.cap, ctx.qrest).T : 0;
     const int64_t incl = wave_incl_scan64(T, lane) + carry;
     if (w == 0 && j < p.num_seqs) bp.prefix[j] = incl - T;
     carry = readlane64(incl, kWave - 1);
@@ -179,7 +182,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int j = base + lane;
     const int64_t T =
-        j < p.num_seqs ? seq_span(p.seq_lens[j], span_window(p), ctx.cap, q_rest(p)).T : 0;
+        j < p.num_seqs ? seq_span(p.seq_lens[j], ctx.swin, ctx.cap, ctx.qrest).T : 0;
     const int64_t incl = wave_incl_scan64(T, lane) + carry;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(j < p.num_seqs &&
                                                      incl * p.num_kv_heads > A);
@@ -200,7 +203,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
   const float c2 = fabsf(p.qk_scale_log2);
   const uint32_t qflip = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
   QK qk;
-  qk.init(p, cur.b, cur.kvh * p.group, lane, qflip, c2);
+  qk.init(p, qs, cur.b, cur.kvh * qs.group, lane, qflip, c2);
 
   // the issue cursor, with the block-table entry of the next tile fetched one issue ahead; it
   // only advances while another tile of this worker follows, so it never walks past the last
@@ -235,8 +238,8 @@ void balanced_decode_kernel(const BalancedParams bp) {
       // by columns: lane (r, c) finishes columns cb + 4r + i, i < 4, that exist, of each
       // 16-column half (cb = 0, 16)
       const bool whole = piece_start == 0 && at.ti == at.s.T - 1;
-      const int ncols = p.q_len * p.group;
-      const int sh = __builtin_ctz((unsigned)p.group);
+      const int ncols = qs.q_len * qs.group;
+      const int sh = __builtin_ctz((unsigned)qs.group);
       auto finish_half = [&](auto& half, int cb) {
         half.merge_cols();
 #pragma unroll
@@ -245,7 +248,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
           const int n = cb + nl;
           float M = half.col_m(nl), lt = half.col_l(nl);   // every lane takes part in the reads
           if (n < ncols) {
-            const int hq = at.kvh * p.group + (n & (p.group - 1));
+            const int hq = at.kvh * qs.group + (n & (qs.group - 1));
             float scale_o = 1.f;
             if (whole && p.sinks != nullptr) {
               // the sink logit joins the max and the denominator with a zero value row
@@ -263,7 +266,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
             float* dst;
             if (whole) {
               const size_t row =
-                  ((size_t)at.b * p.q_total + p.q_first + (n >> sh)) * p.num_q_heads + hq;
+                  ((size_t)at.b * qs.q_total + qs.q_first + (n >> sh)) * p.num_q_heads + hq;
               dst = p.out + row * D;
               if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
             } else {
@@ -292,14 +295,14 @@ void balanced_decode_kernel(const BalancedParams bp) {
     float Mh[G], lh[G];
     qk.merge_rows(Mh, lh);
     const bool whole = piece_start == 0 && at.ti == at.s.T - 1;
-    const int h0 = at.kvh * p.group;
-    const int ncols = p.q_len * p.group;
-    const int sh = __builtin_ctz((unsigned)p.group);
+    const int h0 = at.kvh * qs.group;
+    const int ncols = qs.q_len * qs.group;
+    const int sh = __builtin_ctz((unsigned)qs.group);
     if (lane < kRowLanes) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         if (h >= ncols) break;   // padding columns (uniform)
-        const int hq = h0 + (h & (p.group - 1));
+        const int hq = h0 + (h & (qs.group - 1));
         float M = Mh[h], lt = lh[h];
         float scale_o = 1.f;
         if (whole && p.sinks != nullptr) {
@@ -318,7 +321,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
         float* dst;
         if (whole) {
           const size_t row =
-              ((size_t)at.b * p.q_total + p.q_first + (h >> sh)) * p.num_q_heads + hq;
+              ((size_t)at.b * qs.q_total + qs.q_first + (h >> sh)) * p.num_q_heads + hq;
           dst = p.out + row * D;
           if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
         } else {
@@ -344,7 +347,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
       if constexpr (QK::kQueryTokens) {
         // every column sees the keys inside [lo_all, hi_all): from the last query token's
         // window start to the first query token's position (with one token: the attended range)
-        const int hi_all = at.s.L - p.q_len + 1;
+        const int hi_all = at.s.L - qs.q_len + 1;
         const int lo_all = (p.window > 0 && at.s.L > p.window) ? at.s.L - p.window : 0;
         if (tok0 >= lo_all && tok0 + kTileTokens <= hi_all) {
           qk.template consume<false>(t, 0, 0, 0, lane);
@@ -365,7 +368,7 @@ void balanced_decode_kernel(const BalancedParams bp) {
       flush(at);
       if (k + 1 < n) {
         // the next tile starts the next unit: its q, fresh state
-        qk.load_q(p, next->at.b, next->at.kvh * p.group, lane, qflip);
+        qk.load_q(p, qs, next->at.b, next->at.kvh * qs.group, lane, qflip);
         qk.reset();
       }
     }
@@ -431,7 +434,8 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
   const int Lb = p.seq_lens[b];
   const int64_t pre_b = bp.prefix[b];
   const int64_t pre_B = bp.prefix[p.num_seqs];
-  const SeqSpan s = seq_span(Lb, span_window(p), (int64_t)p.stride << p.bs_log2, q_rest(p));
+  const QShape qs = make_qshape<true, G>(p);
+  const SeqSpan s = seq_span(Lb, span_window(p, qs), (int64_t)p.stride << p.bs_log2, q_rest(qs));
   const int64_t total = pre_B * p.num_kv_heads;
   const int n_eff = effective_workers(total, bp.num_workers);
 
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
   const int pr = tid / F;
   const int f = tid - pr * F;                           // slice f covers column h0 + 4f / D
   const int hl = (4 * f) / D;
-  const int ncols = p.q_len * p.group;                  // columns past it are padding
+  const int ncols = qs.q_len * qs.group;                // columns past it are padding
   const bool col_ok = h0 + hl < ncols;
   float m = -INFINITY, z = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -486,12 +490,12 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
   }
   __syncthreads();
 
-  const int sh = __builtin_ctz((unsigned)p.group);
+  const int sh = __builtin_ctz((unsigned)qs.group);
   for (int e = tid; e < H * D; e += kFixupThreads) {
     const int h = e / D;
     const int n = h0 + h;                               // column: query token n / group
     if (n >= ncols) continue;
-    const int hq = kvh * p.group + (n & (p.group - 1));
+    const int hq = kvh * qs.group + (n & (qs.group - 1));
     // the sink logit joins the max and the denominator with a zero value row
     const float sink = p.sinks != nullptr ? p.sinks[hq] : -INFINITY;
     float M = sink;
@@ -511,7 +515,7 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
       ov = __builtin_nanf("");
       lv = __builtin_nanf("");
     }
-    const size_t row = ((size_t)b * p.q_total + p.q_first + (n >> sh)) * p.num_q_heads + hq;
+    const size_t row = ((size_t)b * qs.q_total + qs.q_first + (n >> sh)) * p.num_q_heads + hq;
     p.out[row * D + (e - h * D)] = ov;
     if (e == h * D && p.lse != nullptr) p.lse[row] = lv;
   }
@@ -532,16 +536,17 @@ constexpr int bal_depth() {
   return (D * G <= 512 || G == 32) ? 2 : 1;
 }
 
-template <int D, int G, QkPath PATH>
+template <int D, int G, QkPath PATH, bool MULTI>
 const void* balanced_kernel_ptr() {
   return reinterpret_cast<const void*>(
-      &balanced_decode_kernel<D, G, bal_depth<D, G, PATH>(), BQK<D, G, PATH>>);
+      &balanced_decode_kernel<D, G, bal_depth<D, G, PATH>(), BQK<D, G, PATH>, MULTI>);
 }
 
-template <int D, int G, QkPath PATH>
+template <int D, int G, QkPath PATH, bool MULTI>
 hipError_t launch_bal(const BalancedParams& bp, hipStream_t stream) {
-  hipLaunchKernelGGL((balanced_decode_kernel<D, G, bal_depth<D, G, PATH>(), BQK<D, G, PATH>>),
-                     dim3(bp.num_workers), dim3(kWave), 0, stream, bp);
+  hipLaunchKernelGGL(
+      (balanced_decode_kernel<D, G, bal_depth<D, G, PATH>(), BQK<D, G, PATH>, MULTI>),
+      dim3(bp.num_workers), dim3(kWave), 0, stream, bp);
   return hipGetLastError();
 }
 
@@ -580,50 +585,73 @@ constexpr bool has_32_columns() {
   return has_16_columns<PATH>() && D <= 128;
 }
 
+// The kernel for (D, columns, path, several query tokens or one).  One token: every path at
+// up to 8 columns (heads); several: the matrix-core P.V paths at 2 to 32 columns.
+template <int D, int G, QkPath PATH, bool MULTI>
+constexpr bool bal_exists() {
+  if constexpr (G == 32) return MULTI && has_32_columns<D, PATH>();
+  if constexpr (G == 16) return MULTI && has_16_columns<PATH>();
+  if constexpr (MULTI) return G >= 2 && has_16_columns<PATH>();
+  return true;
+}
+
+template <int D, int G, QkPath PATH>
+hipError_t launch_bal_m(const BalancedParams& bp, bool multi, hipStream_t stream) {
+  if (multi) {
+    if constexpr (bal_exists<D, G, PATH, true>()) return launch_bal<D, G, PATH, true>(bp, stream);
+  } else {
+    if constexpr (bal_exists<D, G, PATH, false>())
+      return launch_bal<D, G, PATH, false>(bp, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D, int G, QkPath PATH>
+const void* bal_ptr_m(bool multi) {
+  if (multi) {
+    if constexpr (bal_exists<D, G, PATH, true>()) return balanced_kernel_ptr<D, G, PATH, true>();
+  } else {
+    if constexpr (bal_exists<D, G, PATH, false>())
+      return balanced_kernel_ptr<D, G, PATH, false>();
+  }
+  return nullptr;
+}
+
 template <int D, QkPath PATH>
-hipError_t launch_bal_g(const BalancedParams& bp, int group, hipStream_t stream) {
+hipError_t launch_bal_g(const BalancedParams& bp, int group, bool multi, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_bal<D, 1, PATH>(bp, stream);
-    case 2: return launch_bal<D, 2, PATH>(bp, stream);
-    case 4: return launch_bal<D, 4, PATH>(bp, stream);
-    case 8: return launch_bal<D, 8, PATH>(bp, stream);
-    case 16:
-      if constexpr (has_16_columns<PATH>()) return launch_bal<D, 16, PATH>(bp, stream);
-      return hipErrorInvalidValue;
-    case 32:
-      if constexpr (has_32_columns<D, PATH>()) return launch_bal<D, 32, PATH>(bp, stream);
-      return hipErrorInvalidValue;
+    case 1: return launch_bal_m<D, 1, PATH>(bp, multi, stream);
+    case 2: return launch_bal_m<D, 2, PATH>(bp, multi, stream);
+    case 4: return launch_bal_m<D, 4, PATH>(bp, multi, stream);
+    case 8: return launch_bal_m<D, 8, PATH>(bp, multi, stream);
+    case 16: return launch_bal_m<D, 16, PATH>(bp, multi, stream);
+    case 32: return launch_bal_m<D, 32, PATH>(bp, multi, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <QkPath PATH>
-hipError_t launch_bal_d(const BalancedParams& bp, int head_dim, int group, hipStream_t stream) {
+hipError_t launch_bal_d(const BalancedParams& bp, int head_dim, int group, bool multi,
+                        hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_bal_g<64, PATH>(bp, group, stream);
-    case 128: return launch_bal_g<128, PATH>(bp, group, stream);
-    case 256: return launch_bal_g<256, PATH>(bp, group, stream);
+    case 64: return launch_bal_g<64, PATH>(bp, group, multi, stream);
+    case 128: return launch_bal_g<128, PATH>(bp, group, multi, stream);
+    case 256: return launch_bal_g<256, PATH>(bp, group, multi, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <QkPath PATH>
-const void* bal_ptr(int head_dim, int group) {
+const void* bal_ptr(int head_dim, int group, bool multi) {
 #define PA_BP(D)                                                   \
   if (head_dim == D) {                                             \
     switch (group) {                                               \
-      case 1: return balanced_kernel_ptr<D, 1, PATH>();            \
-      case 2: return balanced_kernel_ptr<D, 2, PATH>();            \
-      case 4: return balanced_kernel_ptr<D, 4, PATH>();            \
-      case 8: return balanced_kernel_ptr<D, 8, PATH>();            \
-      case 16:                                                     \
-        if constexpr (has_16_columns<PATH>())                      \
-          return balanced_kernel_ptr<D, 16, PATH>();               \
-        return nullptr;                                            \
-      case 32:                                                     \
-        if constexpr (has_32_columns<D, PATH>())                   \
-          return balanced_kernel_ptr<D, 32, PATH>();               \
-        return nullptr;                                            \
+      case 1: return bal_ptr_m<D, 1, PATH>(multi);                 \
+      case 2: return bal_ptr_m<D, 2, PATH>(multi);                 \
+      case 4: return bal_ptr_m<D, 4, PATH>(multi);                 \
+      case 8: return bal_ptr_m<D, 8, PATH>(multi);                 \
+      case 16: return bal_ptr_m<D, 16, PATH>(multi);               \
+      case 32: return bal_ptr_m<D, 32, PATH>(multi);               \
       default: return nullptr;                                     \
     }                                                              \
   }
@@ -635,12 +663,13 @@ const void* bal_ptr(int head_dim, int group) {
 }  // namespace
 
 hipError_t launch_balanced(const BalancedParams& bp, int head_dim, int group, QkPath path,
-                           hipStream_t stream) {
+                           bool multi, hipStream_t stream) {
   switch (path) {
-    case QkPath::kValu: return launch_bal_d<QkPath::kValu>(bp, head_dim, group, stream);
-    case QkPath::kMfma: return launch_bal_d<QkPath::kMfma>(bp, head_dim, group, stream);
-    case QkPath::kMfmaPvFp8: return launch_bal_d<QkPath::kMfmaPvFp8>(bp, head_dim, group, stream);
-    default: return launch_bal_d<QkPath::kMfmaPv>(bp, head_dim, group, stream);
+    case QkPath::kValu: return launch_bal_d<QkPath::kValu>(bp, head_dim, group, multi, stream);
+    case QkPath::kMfma: return launch_bal_d<QkPath::kMfma>(bp, head_dim, group, multi, stream);
+    case QkPath::kMfmaPvFp8:
+      return launch_bal_d<QkPath::kMfmaPvFp8>(bp, head_dim, group, multi, stream);
+    default: return launch_bal_d<QkPath::kMfmaPv>(bp, head_dim, group, multi, stream);
   }
 }
 
@@ -654,11 +683,12 @@ hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int gro
   }
 }
 
-int balanced_default_workers(int head_dim, int group, QkPath path) {
-  const void* k = path == QkPath::kValu         ? bal_ptr<QkPath::kValu>(head_dim, group)
-                  : path == QkPath::kMfma       ? bal_ptr<QkPath::kMfma>(head_dim, group)
-                  : path == QkPath::kMfmaPvFp8  ? bal_ptr<QkPath::kMfmaPvFp8>(head_dim, group)
-                                                : bal_ptr<QkPath::kMfmaPv>(head_dim, group);
+int balanced_default_workers(int head_dim, int group, QkPath path, bool multi) {
+  const void* k = path == QkPath::kValu ? bal_ptr<QkPath::kValu>(head_dim, group, multi)
+                  : path == QkPath::kMfma ? bal_ptr<QkPath::kMfma>(head_dim, group, multi)
+                  : path == QkPath::kMfmaPvFp8
+                      ? bal_ptr<QkPath::kMfmaPvFp8>(head_dim, group, multi)
+                      : bal_ptr<QkPath::kMfmaPv>(head_dim, group, multi);
   if (k == nullptr) return -1;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;

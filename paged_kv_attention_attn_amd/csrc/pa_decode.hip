@@ -54,7 +54,7 @@ void decode_kernel(const DecodeParams p) {
   const float c2 = fabsf(p.qk_scale_log2);
   const uint32_t qflip = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
   QK qk;
-  qk.init(p, it.b, h0, lane, qflip, c2);
+  qk.init(p, make_qshape<false, G>(p), it.b, h0, lane, qflip, c2);
 
   // Block-table entries of this wave's tiles, 64 at a time in one VGPR (lane i: tile i).  The
   // first batch is requested before the sequence length arrives, for the range a partition has

@@ -48,6 +48,17 @@ struct DecodeParams {
   float* final_lse;
 };
 
+// The query tokens of a launch (see DecodeParams).  Kernels built for one query token use the
+// constant shape {1, 1, 0, G}, so that the general fields cost no registers there.
+struct QShape {
+  int q_len, q_total, q_first, group;
+};
+template <bool MULTI, int G>
+__host__ __device__ inline QShape make_qshape(const DecodeParams& p) {
+  if constexpr (MULTI) return QShape{p.q_len, p.q_total, p.q_first, p.group};
+  return QShape{1, 1, 0, G};
+}
+
 // Balanced decode: persistent workers over the flattened tiles, partials in a workspace.
 struct BalancedParams {
   DecodeParams d;             // out/lse are the final outputs; psize/max_parts unused
@@ -106,14 +117,15 @@ hipError_t launch_reduce(const ReduceParams& p, int head_dim, int num_seqs, hipS
 
 // Balanced decode: the worker kernel, and the fix-up merge, each on `stream`.  `group` is the
 // kernels' column count: Hq/Hkv, or with q_len > 1 the (token, head) pairs rounded up to a power
-// of two (16 at most, matrix-core P.V paths only).
+// of two (32 at most, matrix-core P.V paths only).  `multi` selects the kernels that read the
+// query-token fields (needed whenever q_len or q_total is above 1).
 hipError_t launch_balanced(const BalancedParams& bp, int head_dim, int group, QkPath path,
-                           hipStream_t stream);
+                           bool multi, hipStream_t stream);
 hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int group,
                                  hipStream_t stream);
 // Workers that fit on the current device at once (CUs x resident one-wave workgroups per CU),
 // or -1 if the query fails.
-int balanced_default_workers(int head_dim, int group, QkPath path);
+int balanced_default_workers(int head_dim, int group, QkPath path, bool multi = false);
 
 hipError_t launch_witness(const WitnessParams& p, int head_dim, int num_seqs, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int num_wg, uint32_t* sink,

@@ -122,8 +122,12 @@ struct QkValu {
     }
   }
   int rs;   // bytes between a block's consecutive K/V rows (the pool layout's row stride)
-  __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
-                                       uint32_t qflip, float c2_) {
+  __device__ __forceinline__ void load_q(const DecodeParams& p, const QShape&, int b, int h0,
+                                         int lane, uint32_t qflip) {
+    load_q(p, b, h0, lane, qflip);
+  }
+  __device__ __forceinline__ void init(const DecodeParams& p, const QShape&, int b, int h0,
+                                       int lane, uint32_t qflip, float c2_) {
     c2 = c2_;
     rs = (int)p.kv_row_stride;
     load_q(p, b, h0, lane, qflip);
@@ -277,8 +281,12 @@ struct QkMfma {
     }
   }
   int rs;   // bytes between a block's consecutive K/V rows (the pool layout's row stride)
-  __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
-                                       uint32_t qflip, float c2_) {
+  __device__ __forceinline__ void load_q(const DecodeParams& p, const QShape&, int b, int h0,
+                                         int lane, uint32_t qflip) {
+    load_q(p, b, h0, lane, qflip);
+  }
+  __device__ __forceinline__ void init(const DecodeParams& p, const QShape&, int b, int h0,
+                                       int lane, uint32_t qflip, float c2_) {
     c2 = c2_;
     rs = (int)p.kv_row_stride;
     load_q(p, b, h0, lane, qflip);
@@ -447,16 +455,16 @@ struct QkMfmaPvT {
   // q rows of the unit whose first head is h0 (= KV head * group): lane column n (col_base +
   // lane % 16; col_base = 16 for the second half of a 32-column pair) reads query token
   // n / group, head h0 + n % group.  Columns past q_len * group are padding (zero q).
-  __device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int lane,
-                                         uint32_t qflip, int col_base = 0) {
+  __device__ __forceinline__ void load_q(const DecodeParams& p, const QShape& qs, int b, int h0,
+                                         int lane, uint32_t qflip, int col_base = 0) {
     const int n = col_base + (lane & 15);
-    const int sh = __builtin_ctz((unsigned)p.group);   // group is a power of two
+    const int sh = __builtin_ctz((unsigned)qs.group);   // group is a power of two
     col_q = n >> sh;
-    head_lane = col_q < p.q_len;
-    const int hh = n & (p.group - 1);
+    head_lane = col_q < qs.q_len;
+    const int hh = n & (qs.group - 1);
     const char* qrow = reinterpret_cast<const char*>(
-        p.q + (((size_t)b * p.q_total + p.q_first + (head_lane ? col_q : 0)) * p.num_q_heads + h0 +
-               (head_lane ? hh : 0)) * D);
+        p.q + (((size_t)b * qs.q_total + qs.q_first + (head_lane ? col_q : 0)) * p.num_q_heads +
+               h0 + (head_lane ? hh : 0)) * D);
     const uint32_t keep = head_lane ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -479,12 +487,12 @@ struct QkMfmaPvT {
     for (int e = 0; e < E; ++e) cacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   int rs;   // bytes between a block's consecutive K/V rows (the pool layout's row stride)
-  __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
-                                       uint32_t qflip, float c2_, int col_base = 0) {
+  __device__ __forceinline__ void init(const DecodeParams& p, const QShape& qs, int b, int h0,
+                                       int lane, uint32_t qflip, float c2_, int col_base = 0) {
     c2 = c2_;
     rs = (int)p.kv_row_stride;
     vs = p.v_scale;
-    load_q(p, b, h0, lane, qflip, col_base);
+    load_q(p, qs, b, h0, lane, qflip, col_base);
     reset();
   }
 
@@ -700,15 +708,15 @@ struct QkMfmaPvPair {
   static constexpr int kHalves = 2;
   Half h[2];
 
-  __device__ __forceinline__ void init(const DecodeParams& p, int b, int h0, int lane,
-                                       uint32_t qflip, float c2) {
-    h[0].init(p, b, h0, lane, qflip, c2, 0);
-    h[1].init(p, b, h0, lane, qflip, c2, 16);
+  __device__ __forceinline__ void init(const DecodeParams& p, const QShape& qs, int b, int h0,
+                                       int lane, uint32_t qflip, float c2) {
+    h[0].init(p, qs, b, h0, lane, qflip, c2, 0);
+    h[1].init(p, qs, b, h0, lane, qflip, c2, 16);
   }
-  __device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int lane,
-                                         uint32_t qflip) {
-    h[0].load_q(p, b, h0, lane, qflip, 0);
-    h[1].load_q(p, b, h0, lane, qflip, 16);
+  __device__ __forceinline__ void load_q(const DecodeParams& p, const QShape& qs, int b, int h0,
+                                         int lane, uint32_t qflip) {
+    h[0].load_q(p, qs, b, h0, lane, qflip, 0);
+    h[1].load_q(p, qs, b, h0, lane, qflip, 16);
   }
   __device__ __forceinline__ void reset() {
     h[0].reset();
