@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV-read GB/s (% of HBM peak) + µs/decode step, bf16 d=128 GQA paged decode"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of one MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = ["paged_kv_attention_attn_amd/csrc/pa_decode.hip",
                   "paged_kv_attention_attn_amd/csrc/pa_balanced.hip",
@@ -78,6 +79,20 @@ def measured_traffic(workload: str, schedule: str):
         if r.get("workload") == workload and r.get("schedule") == schedule:
             return r.get("hbm_bytes_per_launch")
     return None
+
+
+def attended_pairs(wl) -> int:
+    """(query token, key) pairs one query head attends over the batch: token i of q_len new
+    tokens sits at position p = L - q_len + i and attends keys max(0, p + 1 - W) .. p (all keys
+    up to p when W = 0); p < 0 attends nothing."""
+    import numpy as np
+
+    L = wl.seq_lens.astype(np.int64)[:, None]
+    p = L - wl.q_len + np.arange(wl.q_len, dtype=np.int64)[None, :]
+    n = np.where(p >= 0, p + 1, 0)
+    if wl.window > 0:
+        n = np.minimum(n, wl.window)
+    return int(n.sum())
 
 
 def _cpu_model() -> str:
@@ -250,10 +265,13 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--head-dim", type=int, default=128)
     ap.add_argument("--q-heads", type=int, default=None)
-    ap.add_argument("--schedule", choices=["balanced", "partitioned", "unsplit"],
+    ap.add_argument("--schedule", choices=["balanced", "partitioned", "unsplit",
+                                           "query_blocks"],
                     default="balanced",
                     help="balanced: persistent workers + fix-up (default); partitioned: fixed "
-                         "partitions + reduce; unsplit: one workgroup per (sequence, KV head)")
+                         "partitions + reduce; unsplit: one workgroup per (sequence, KV head); "
+                         "query_blocks: one wave per (sequence, KV head, block of query "
+                         "tokens), through a prepared plan (several query tokens)")
     ap.add_argument("--partition", type=int, default=None,
                     help="partitioned schedule: partition size (default: library suggestion)")
     ap.add_argument("--workers", type=int, default=0,
@@ -300,10 +318,11 @@ def main() -> int:
         kw = dict(head_dim=args.head_dim, num_q_heads=args.q_heads or 32)
     wl = make_config(args.config, kv_format=args.kv, q_len=args.q_len, **kw)
     fp8 = args.kv != "bf16"
-    planned = fp8 or args.q_len > 1
+    qblocks = args.schedule == "query_blocks"
+    planned = fp8 or args.q_len > 1 or qblocks
     B, Hq, D = wl.num_seqs, wl.num_q_heads, wl.head_dim
     maxL = int(wl.seq_lens.max())
-    if args.schedule == "unsplit":
+    if args.schedule == "unsplit" or qblocks:
         P = 0
     elif args.schedule == "partitioned":
         P = args.partition
@@ -347,6 +366,8 @@ def main() -> int:
         variant = plan.name
         if P < 0:
             workers = int(variant.split("workers")[1].split()[0])
+        if qblocks:
+            workers = None
     elif P < 0:
         workers = workers or pa.balanced_default_workers(D, Hq // wl.num_kv_heads)
         ws = torch.empty(pa.balanced_workspace_size(shape, D, workers), dtype=torch.uint8,
@@ -466,6 +487,18 @@ def main() -> int:
             "frac_of_attainable": round(achieved / attainable, 4),
         },
     }
+    if qblocks:
+        # query blocks with many tokens per sequence are a dense contraction: 4 D flops per
+        # attended (query token, key) pair and query head (q.k and P.V, 2 D each)
+        flops = attended_pairs(wl) * Hq * 4 * D
+        res["roofline"].update({
+            "bound": "mfma", "achieved": round(flops / dec_avg_s / 1e12, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(flops / dec_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops_per_launch": flops,
+            "kv_read_GBps": round(achieved, 2)})
+        for key in ("attainable_stream_read_GBps", "frac_of_attainable"):
+            res["roofline"].pop(key)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)

@@ -298,7 +298,8 @@ enum {
   PA_SCHEDULE_UNSPLIT = 0,
   PA_SCHEDULE_PARTITIONED = 1,
   PA_SCHEDULE_BALANCED = 2,
-  PA_SCHEDULE_PARTITIONED_FUSED = 3
+  PA_SCHEDULE_PARTITIONED_FUSED = 3,
+  PA_SCHEDULE_QUERY_BLOCKS = 4
 };
 
 pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,

@@ -354,7 +354,7 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, scale, *, window
                   stream=stream)
 
 
-SCHEDULES = {"unsplit": 0, "partitioned": 1, "balanced": 2, "fused": 3}
+SCHEDULES = {"unsplit": 0, "partitioned": 1, "balanced": 2, "fused": 3, "query_blocks": 4}
 
 
 class KvLayout(ctypes.Structure):

@@ -24,7 +24,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpaged_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_balanced.hip", "pa_reduce.hip", "pa_aux.hip"]
+SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_balanced.hip", "pa_qblock.hip", "pa_reduce.hip",
+           "pa_aux.hip"]
 HEADERS = ["pa_device.hpp", "pa_kernels.hpp", "pa_qk.hpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

@@ -481,6 +481,7 @@ struct pa_plan {
   size_t part_bytes;      // partitioned: partials, then their LSEs
   size_t counter_off;     // fused: merge counters [B][Hkv] after the LSEs
   WsLayout bal;           // balanced workspace layout
+  pa::QBlockParams qb;    // query-block grid: geometry (pointers filled per run)
   int64_t workspace_bytes;
   char name[128];
 };
@@ -508,8 +509,10 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   const bool parted =
       schedule == PA_SCHEDULE_PARTITIONED || schedule == PA_SCHEDULE_PARTITIONED_FUSED;
   if (parted && shape->partition_size <= 0) return PA_ERR_SHAPE;
-  if (!parted && schedule != PA_SCHEDULE_UNSPLIT && schedule != PA_SCHEDULE_BALANCED)
+  const bool qblocks = schedule == PA_SCHEDULE_QUERY_BLOCKS;
+  if (!parted && !qblocks && schedule != PA_SCHEDULE_UNSPLIT && schedule != PA_SCHEDULE_BALANCED)
     return PA_ERR_SHAPE;
+  if (qblocks && shape->partition_size != 0) return PA_ERR_SHAPE;
   if (parted && shape->num_q_heads > kMaxGridYZ * 32) return PA_ERR_SHAPE;
   if (schedule == PA_SCHEDULE_BALANCED &&
       ((int64_t)shape->num_seqs * shape->num_q_heads > 0x7FFFFFFF || num_workers < 0 ||
@@ -519,7 +522,12 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   if (q_len < 1 || q_len > kMaxQueryTokens) return PA_ERR_SHAPE;
   int32_t columns = group;
   int32_t pass_tokens = q_len;
-  if (q_len > 1) {
+  if (qblocks) {
+    // query blocks: one wave per (sequence, KV head, max_columns / group tokens)
+    if (group > max_columns(head_dim)) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)shape->num_seqs * q_len * shape->num_q_heads > 0x7FFFFFFF) return PA_ERR_SHAPE;
+    if (window > 0x7FFFFFFF - max_columns(head_dim)) return PA_ERR_SHAPE;
+  } else if (q_len > 1) {
     // several query tokens: the balanced schedule, (token, head) columns on the matrix cores;
     // more tokens than 16 columns hold run in passes of 16 / group tokens, each reading the KV
     if (schedule != PA_SCHEDULE_BALANCED) return PA_ERR_UNSUPPORTED;
@@ -533,7 +541,7 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   pa::QkPath path;
   if (kv_dtype == PA_KV_FP8_E4M3)
     path = pa::QkPath::kMfmaPvFp8;   // the one path that reads FP8 rows
-  else if (q_len > 1)
+  else if (q_len > 1 || qblocks)
     path = pa::QkPath::kMfmaPv;      // the one path with column-wise query tokens
   else if (decode_path(head_dim, group, &path) != 0)
     return PA_ERR_UNSUPPORTED;
@@ -586,6 +594,14 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   const char* dname = pa::decode_variant_name(head_dim, group, waves, parted, path);
   if (schedule == PA_SCHEDULE_UNSPLIT) {
     std::snprintf(pl->name, sizeof(pl->name), "%s", dname);
+  } else if (qblocks) {
+    pl->qb = pa::QBlockParams{};
+    pl->qb.d = p;
+    pa::qblock_geometry(pl->qb, head_dim);
+    pl->group = pa::qblock_columns(head_dim);
+    std::snprintf(pl->name, sizeof(pl->name), "pa_qblock_%s_d%d_g%d_q%d_t%d%s",
+                  pa::qk_path_name(path), head_dim, group, q_len, pl->qb.tokens_per_block,
+                  pl->qb.xcd_pinned ? "_xcd" : "");
   } else if (schedule == PA_SCHEDULE_PARTITIONED) {
     const size_t rows = (size_t)shape->num_seqs * shape->num_q_heads * shape->max_partitions;
     pl->part_bytes = align256(rows * head_dim * sizeof(float));
@@ -696,6 +712,12 @@ pa_status paged_attn_plan_run(const pa_plan* plan, const void* q, const void* k_
     p.out = out;
     p.lse = lse;
     e = pa::launch_decode(p, plan->head_dim, plan->group, plan->waves, plan->path, s);
+  } else if (plan->schedule == PA_SCHEDULE_QUERY_BLOCKS) {
+    pa::QBlockParams qp = plan->qb;
+    qp.d = p;
+    qp.d.out = out;
+    qp.d.lse = lse;
+    e = pa::launch_qblock(qp, plan->head_dim, plan->path, s);
   } else if (plan->schedule == PA_SCHEDULE_PARTITIONED_FUSED) {
     char* ws = static_cast<char*>(workspace);
     p.out = reinterpret_cast<float*>(ws);

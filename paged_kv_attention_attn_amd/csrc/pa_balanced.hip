@@ -40,25 +40,6 @@ namespace pa {
 // A worker gets at least this many tiles (fewer workers for tiny batches).
 constexpr int kMinTilesPerWorker = 4;
 
-// One sequence's attended range [start, L) in 16-token tiles: tiles [t0, t0 + T).  T = 0 for an
-// empty sequence or one whose length the block table cannot hold (bad).
-struct SeqSpan {
-  int L, start, t0, T;
-  bool bad;
-};
-
-// (q_rest: query tokens after this launch's last one; its keys end q_rest before L)
-__device__ __forceinline__ SeqSpan seq_span(int L, int window, int64_t cap, int q_rest = 0) {
-  SeqSpan s;
-  s.bad = L < 0 || (int64_t)L > cap;
-  const int Lc = s.bad ? 0 : (L > q_rest ? L - q_rest : 0);
-  s.L = s.bad ? L : Lc;
-  s.start = (window > 0 && Lc > window) ? Lc - window : 0;
-  s.t0 = s.start / kTileTokens;
-  s.T = Lc > 0 ? (Lc + kTileTokens - 1) / kTileTokens - s.t0 : 0;
-  return s;
-}
-
 // Window that decides a unit's tiles: with q_len query tokens the union of their windows is
 // window + q_len - 1 keys ending at the last position (0 = no window).  The host keeps the sum
 // in range.

@@ -43,22 +43,28 @@ struct RowGeom {
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// Load the kWords words lane c holds of the row starting at byte address `row`.  KV rows are
-// read exactly once per step, so the loads carry the non-temporal hint: on gfx950 streaming
-// reads with it reach a markedly higher HBM rate than plain loads.
-template <int D>
+// A KV load: non-temporal (NT) where a row is read exactly once per step (on gfx950 streaming
+// reads with the hint reach a markedly higher HBM rate than plain loads), plain where several
+// workgroups read the same rows and should find them in L2.
+template <bool NT, class T>
+__device__ __forceinline__ T kv_load(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+// Load the kWords words lane c holds of the row starting at byte address `row`.
+template <int D, bool NT = true>
 __device__ __forceinline__ void load_row(const char* __restrict__ row, int c,
                                          uint32_t (&w)[RowGeom<D>::kWords]) {
   if constexpr (D == 64) {
-    const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(row + c * 8));
+    const u32x2_t x = kv_load<NT>(reinterpret_cast<const u32x2_t*>(row + c * 8));
     w[0] = x.x; w[1] = x.y;
   } else if constexpr (D == 128) {
-    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + c * 16));
+    const u32x4_t x = kv_load<NT>(reinterpret_cast<const u32x4_t*>(row + c * 16));
     w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
   } else {
-    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + c * 16));
-    const u32x4_t y =
-        __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 256 + c * 16));
+    const u32x4_t x = kv_load<NT>(reinterpret_cast<const u32x4_t*>(row + c * 16));
+    const u32x4_t y = kv_load<NT>(reinterpret_cast<const u32x4_t*>(row + 256 + c * 16));
     w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
     w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
   }
@@ -174,6 +180,25 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// One sequence's attended range [start, L) in 16-token tiles: tiles [t0, t0 + T).  T = 0 for an
+// empty sequence or one whose length the block table cannot hold (bad).
+struct SeqSpan {
+  int L, start, t0, T;
+  bool bad;
+};
+
+// (q_rest: query tokens after this launch's last one; its keys end q_rest before L)
+__device__ __forceinline__ SeqSpan seq_span(int L, int window, int64_t cap, int q_rest = 0) {
+  SeqSpan s;
+  s.bad = L < 0 || (int64_t)L > cap;
+  const int Lc = s.bad ? 0 : (L > q_rest ? L - q_rest : 0);
+  s.L = s.bad ? L : Lc;
+  s.start = (window > 0 && Lc > window) ? Lc - window : 0;
+  s.t0 = s.start / kTileTokens;
+  s.T = Lc > 0 ? (Lc + kTileTokens - 1) / kTileTokens - s.t0 : 0;
+  return s;
+}
 
 // ---------------------------------------------------------------------------------------------
 // Tile addressing (block-table walk).  Tile t covers tokens [16t, 16t+16), which never straddle

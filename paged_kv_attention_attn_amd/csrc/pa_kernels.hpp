@@ -68,6 +68,17 @@ struct BalancedParams {
   int32_t num_workers;        // N, one wave each
 };
 
+// Query-block grid for several query tokens per sequence: one one-wave workgroup per
+// (sequence, KV head, block of tokens_per_block query tokens), each streaming the keys its
+// tokens attend and writing its outputs; no split, no merge.
+struct QBlockParams {
+  DecodeParams d;             // q_total = query tokens per sequence; q_len and q_first unused
+  int32_t tokens_per_block;   // columns per wave / group
+  int32_t blocks_per_seq;     // ceil(q_total / tokens_per_block)
+  int32_t xcd_pinned;         // 1: every block of a (sequence, KV head) on one XCD
+  uint32_t grid;              // workgroups launched
+};
+
 struct ReduceParams {
   const float* partials;      // [B][Hq][Pmax][D]
   const float* lse_partials;  // [B][Hq][Pmax]
@@ -126,6 +137,12 @@ hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int gro
 // Workers that fit on the current device at once (CUs x resident one-wave workgroups per CU),
 // or -1 if the query fails.
 int balanced_default_workers(int head_dim, int group, QkPath path, bool multi = false);
+
+// Query-block grid: (token, head) columns per wave (32 at head_dim <= 128, 16 at 256; the
+// matrix-core P.V paths only), the grid for the shape, and the launch.
+int qblock_columns(int head_dim);
+void qblock_geometry(QBlockParams& qp, int head_dim);
+hipError_t launch_qblock(const QBlockParams& qp, int head_dim, QkPath path, hipStream_t stream);
 
 hipError_t launch_witness(const WitnessParams& p, int head_dim, int num_seqs, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int num_wg, uint32_t* sink,

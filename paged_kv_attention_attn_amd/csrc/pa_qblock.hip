@@ -1,0 +1,214 @@
+// Query-block grid for several query tokens per sequence (chunked prefill, speculative decode)
+// on gfx950.
+//
+// One one-wave workgroup per (sequence b, KV head kvh, block of query tokens).  A block holds
+// the columns of one wave, 32 (token, head) pairs at head_dim <= 128 and 16 at 256, so
+// tokens_per_block = columns / group.  The wave streams the 16-token K/V tiles its tokens attend
+// (the union of their causal, windowed ranges) with the next tile's loads in flight, forms q.k
+// and P.V on the matrix cores exactly as the one-token kernels do for their columns (each
+// column masked to its own token's range inside the shared tiles), and writes its outputs and
+// LSEs: nothing is split, so nothing is merged.
+//
+// All blocks of a (sequence, KV head) read the same keys.  The chip deals workgroups to its
+// 8 XCDs round-robin by linear id; with xcd_pinned every block of one (sequence, KV head) gets
+// an id of the same residue mod 8, so they run on one XCD, close in time, and share its L2: the
+// K/V loads are plain (cached) here, not non-temporal.  Within a (sequence, KV head) the blocks
+// of the last tokens, which attend the most keys, are dealt first.
+//
+// Token i of q_total new tokens sits at position L - q_total + i and attends keys t <= its
+// position, the last `window` of them when window > 0: the longer-query case that vllm.cpp
+// PR #564 "spec(BACKEND-ROCM): the ROCm head_dim=128 decode arm" ("What is deliberately not
+// here") leaves out and ROCm/rocm-libraries PR #13700 "prepare saved paged decode bindings
+// once" fixes at one token; the causal rule is this library's reading.  Sinks: randomvariable/
+// vllm issue #23, table "Current state" (a sink logit joins the softmax with a zero value row).
+#include "pa_device.hpp"
+#include "pa_kernels.hpp"
+#include "pa_qk.hpp"
+
+namespace pa {
+
+namespace {
+
+constexpr int kXcds = 8;
+
+struct QBlockItem {
+  int b, kvh, qb;
+};
+
+// The (sequence, KV head, query block) of this workgroup; false for an idle id.
+__device__ __forceinline__ bool qblock_item(const QBlockParams& qp, QBlockItem& it) {
+  const int U = qp.d.num_seqs * qp.d.num_kv_heads;
+  const int nqb = qp.blocks_per_seq;
+  const unsigned id = blockIdx.x;
+  unsigned u, j;
+  if (qp.xcd_pinned) {
+    // XCD x = id mod 8 runs units x, x + 8, ... one after another, each block by block
+    const unsigned x = id % kXcds, jj = id / kXcds;
+    const unsigned uu = jj / (unsigned)nqb;
+    j = jj - uu * (unsigned)nqb;
+    u = uu * kXcds + x;
+  } else {
+    u = id / (unsigned)nqb;
+    j = id - u * (unsigned)nqb;
+  }
+  if (u >= (unsigned)U) return false;
+  it.b = (int)(u / (unsigned)qp.d.num_kv_heads);
+  it.kvh = (int)(u - (unsigned)it.b * (unsigned)qp.d.num_kv_heads);
+  it.qb = nqb - 1 - (int)j;
+  return true;
+}
+
+template <int D, class QK>
+__global__ __launch_bounds__(kWave) void qblock_kernel(const QBlockParams qp) {
+  using RG = RowGeom<D>;
+  constexpr int E = RG::kElems;
+  const DecodeParams& p = qp.d;
+  QBlockItem it;
+  if (!qblock_item(qp, it)) return;
+  const int lane = threadIdx.x;
+  const int c = lane & (kRowLanes - 1);
+  const int q0 = it.qb * qp.tokens_per_block;
+  const int nq = min(qp.tokens_per_block, p.q_total - q0);
+  const QShape qs{nq, p.q_total, q0, p.group};
+  // this block's keys: the union of its tokens' ranges, ending at its last token's position
+  const int swin = p.window > 0 ? p.window + nq - 1 : 0;
+  const SeqSpan s = seq_span(__builtin_amdgcn_readfirstlane(p.seq_lens[it.b]), swin,
+                             (int64_t)p.stride << p.bs_log2, p.q_total - q0 - nq);
+
+  const float c2 = fabsf(p.qk_scale_log2);
+  const uint32_t qflip = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
+  const int h0 = it.kvh * qs.group;
+  QK qk;
+  qk.init(p, qs, it.b, h0, lane, qflip, c2);
+
+  const TileAddr ta{p.num_blocks, p.bs_log2, p.kv_block_stride, it.kvh * p.kv_head_stride,
+                    p.kv_row_stride};
+  const int32_t* bt = p.block_table + (size_t)it.b * p.stride;
+  bool bad = s.bad;
+  // every column sees the keys in [lo_all, hi_all): from the last token's window start to the
+  // first token's position
+  const int hi_all = s.L - nq + 1;
+  const int lo_all = (p.window > 0 && s.L > p.window) ? s.L - p.window : 0;
+
+  // tiles s.t0 .. s.t0 + s.T - 1, the next one's loads in flight; the block-table entry is
+  // fetched one issue ahead
+  int phys_next = s.T > 0 ? __builtin_amdgcn_readfirstlane(bt[ta.logical_block(s.t0)]) : 0;
+  auto issue = [&](int k, typename QK::Tile& t) -> bool {
+    const int tile = s.t0 + k;
+    const int phys = phys_next;
+    if (k + 1 < s.T) phys_next = __builtin_amdgcn_readfirstlane(bt[ta.logical_block(tile + 1)]);
+    const int64_t off = ta.offset(phys, tile);
+    if (off < 0) return false;
+    qk.issue(t, p.k_cache + off, p.v_cache + off, lane);
+    return true;
+  };
+  auto consume = [&](int k, typename QK::Tile& t, bool ok) {
+    if (!ok) {   // a table entry outside the pool: never read through, NaN outputs
+      bad = true;
+      return;
+    }
+    const int tok0 = (s.t0 + k) * kTileTokens;
+    if (tok0 >= lo_all && tok0 + kTileTokens <= hi_all)
+      qk.template consume<false>(t, 0, 0, 0, lane);
+    else
+      qk.consume_cols(t, tok0, hi_all, p.window, s.start, s.L, lane);
+  };
+  typename QK::Tile t0, t1;
+  bool ok0 = false, ok1 = false;
+  if (s.T > 0) ok0 = issue(0, t0);
+  for (int k = 0; k < s.T; k += 2) {
+    if (k + 1 < s.T) ok1 = issue(k + 1, t1);
+    consume(k, t0, ok0);
+    if (k + 1 < s.T) {
+      if (k + 2 < s.T) ok0 = issue(k + 2, t0);
+      consume(k + 1, t1, ok1);
+    }
+  }
+
+  // finish column-wise: lane (r, c) writes columns cb + 4r + i, i < 4, that exist, of each
+  // 16-column half (cb = 0, 16)
+  const int ncols = nq * qs.group;
+  const int sh = __builtin_ctz((unsigned)qs.group);
+  auto finish_half = [&](auto& half, int cb) {
+    half.merge_cols();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nl = 4 * (lane >> 4) + i;               // column within the half
+      const int n = cb + nl;
+      float M = half.col_m(nl), lt = half.col_l(nl);    // every lane takes part in the reads
+      if (n < ncols) {
+        const int hq = h0 + (n & (qs.group - 1));
+        float scale_o = 1.f;
+        if (p.sinks != nullptr) {
+          // the sink logit joins the max and the denominator with a zero value row
+          const float s2 = p.sinks[hq] * kLog2e;
+          const float M2 = fmaxf(M, s2);
+          const float M2u = M2 == -INFINITY ? 0.f : M2;
+          scale_o = fast_exp2(M - M2u);
+          lt = fmaf(lt, scale_o, fast_exp2(s2 - M2u));
+          M = M2;
+        }
+        // lt is 0 only for a column without keys; a NaN input (lt = NaN) reaches the outputs
+        const float inv = lt != 0.f ? scale_o / lt : 0.f;
+        float lv = lt != 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
+        if (bad) lv = __builtin_nanf("");
+        const size_t row = ((size_t)it.b * qs.q_total + q0 + (n >> sh)) * p.num_q_heads + hq;
+        float* dst = p.out + row * D;
+        if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          dst[RG::dim(c, e)] = bad ? __builtin_nanf("") : half.acc(i, e) * inv;
+      }
+    }
+  };
+  if constexpr (QK::kHalves == 2) {
+    finish_half(qk.h[0], 0);
+    finish_half(qk.h[1], 16);
+  } else {
+    finish_half(qk, 0);
+  }
+}
+
+template <int D>
+using QbQk = typename std::conditional<D <= 128, QkMfmaPvPair<D, false, false>,
+                                       QkMfmaPvT<D, 16, false, false>>::type;
+template <int D>
+using QbQkFp8 = typename std::conditional<D <= 128, QkMfmaPvPair<D, true, false>,
+                                          QkMfmaPvT<D, 16, true, false>>::type;
+
+template <int D>
+hipError_t launch_d(const QBlockParams& qp, QkPath path, hipStream_t stream) {
+  if (path == QkPath::kMfmaPvFp8)
+    hipLaunchKernelGGL((qblock_kernel<D, QbQkFp8<D>>), dim3(qp.grid), dim3(kWave), 0, stream, qp);
+  else
+    hipLaunchKernelGGL((qblock_kernel<D, QbQk<D>>), dim3(qp.grid), dim3(kWave), 0, stream, qp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int qblock_columns(int head_dim) { return head_dim <= 128 ? 32 : 16; }
+
+void qblock_geometry(QBlockParams& qp, int head_dim) {
+  const int cols = qblock_columns(head_dim);
+  qp.tokens_per_block = cols / qp.d.group;
+  qp.blocks_per_seq = (qp.d.q_total + qp.tokens_per_block - 1) / qp.tokens_per_block;
+  const long long units = (long long)qp.d.num_seqs * qp.d.num_kv_heads;
+  qp.xcd_pinned = units % kXcds == 0 ? 1 : 0;
+  const long long grid = qp.xcd_pinned
+                             ? (units / kXcds) * kXcds * qp.blocks_per_seq
+                             : units * qp.blocks_per_seq;
+  qp.grid = (uint32_t)grid;
+}
+
+hipError_t launch_qblock(const QBlockParams& qp, int head_dim, QkPath path, hipStream_t stream) {
+  if (qp.grid == 0) return hipSuccess;
+  switch (head_dim) {
+    case 64: return launch_d<64>(qp, path, stream);
+    case 128: return launch_d<128>(qp, path, stream);
+    case 256: return launch_d<256>(qp, path, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

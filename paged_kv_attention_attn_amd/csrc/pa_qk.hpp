@@ -53,13 +53,13 @@ __device__ __forceinline__ float row_bcast_dyn(float x, int h) {
 
 // V rows of a tile in the P.V layout: row group r (lane / 16) holds tokens 4j + r, lane c of the
 // row holds slice c of the head dim.
-template <int D>
+template <int D, bool NT = true>
 __device__ __forceinline__ void load_v_rows(uint32_t (&v)[kTileSteps][RowGeom<D>::kWords],
                                             const char* vb, int lane, int rs) {
   const int r = lane >> 4, c = lane & 15;
 #pragma unroll
   for (int j = 0; j < kTileSteps; ++j)
-    load_row<D>(vb + (kRows * j + r) * rs, c, v[j]);
+    load_row<D, NT>(vb + (kRows * j + r) * rs, c, v[j]);
 }
 
 template <int NWORDS>
@@ -412,8 +412,8 @@ __device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t x) {
 // FP8 = true: the KV cache holds OCP FP8 E4M3 codes (one byte per value, rows of D bytes) with
 // one fp32 scale per tensor.  K and V are converted to bf16 in registers (exactly) and go
 // through the same MFMAs; the K scale is folded into the score scale by the host and the V
-// scale multiplies the output.
-template <int D, int G, bool FP8>
+// scale multiplies the output.  NT: K/V loads carry the non-temporal hint (rows read once).
+template <int D, int G, bool FP8, bool NT = true>
 struct QkMfmaPvT {
   static constexpr int KK = D / 32;
   static constexpr int W = RowGeom<D>::kWords;
@@ -506,21 +506,21 @@ struct QkMfmaPvT {
       const char* krow = kb + tok * rs + 16 * (lane >> 4);
 #pragma unroll
       for (int i = 0; i < KL; ++i)
-        t.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + 64 * i));
+        t.k[i] = kv_load<NT>(reinterpret_cast<const u32x4_t*>(krow + 64 * i));
       const int r = lane >> 4, c = lane & 15;
 #pragma unroll
       for (int j = 0; j < kTileSteps; ++j) {
         const char* row = vb + (kRows * j + r) * rs;
         if constexpr (D == 64) {
-          t.v[j][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row + 4 * c));
+          t.v[j][0] = kv_load<NT>(reinterpret_cast<const uint32_t*>(row + 4 * c));
         } else {
           const u32x2_t x =
-              __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(row + 8 * c));
+              kv_load<NT>(reinterpret_cast<const u32x2_t*>(row + 8 * c));
           t.v[j][0] = x.x;
           t.v[j][1] = x.y;
           if constexpr (D == 256) {
             const u32x2_t y =
-                __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(row + 128 + 8 * c));
+                kv_load<NT>(reinterpret_cast<const u32x2_t*>(row + 128 + 8 * c));
             t.v[j][2] = y.x;
             t.v[j][3] = y.y;
           }
@@ -530,8 +530,8 @@ struct QkMfmaPvT {
       const char* krow = kb + tok * rs + 16 * (lane >> 4);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        t.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + 64 * kk));
-      load_v_rows<D>(t.v, vb, lane, rs);
+        t.k[kk] = kv_load<NT>(reinterpret_cast<const u32x4_t*>(krow + 64 * kk));
+      load_v_rows<D, NT>(t.v, vb, lane, rs);
     }
   }
 
@@ -697,9 +697,9 @@ using QkMfmaPvFp8 = QkMfmaPvT<D, G, true>;
 // Thirty-two columns (query tokens x heads) as two 16-column halves that share every K/V tile:
 // the tile is loaded once and each half runs its own q.k, softmax and P.V on it.  Finished
 // column-wise, half by half (col_base 0 and 16).
-template <int D, bool FP8>
+template <int D, bool FP8, bool NT = true>
 struct QkMfmaPvPair {
-  using Half = QkMfmaPvT<D, 16, FP8>;
+  using Half = QkMfmaPvT<D, 16, FP8, NT>;
   using Tile = typename Half::Tile;
   static constexpr int kRowBytes = Half::kRowBytes;
   static constexpr int kMinWavesPerEu = 1;

@@ -245,6 +245,27 @@ def plan_create(s, *, head_dim=128, block_size=16, window=0, schedule=0, workers
     return st, h
 
 
+def test_query_block_plans():
+    # one wave per (sequence, KV head, 32 / group tokens; 16 / group at D = 256), no workspace
+    st, h = plan_create(shape(), schedule=4, q_len=70)
+    assert st == 0
+    assert pa.lib().paged_attn_plan_workspace_size(h) == 0
+    assert pa.lib().paged_attn_plan_name(h) == b"pa_qblock_mfmapv_d128_g4_q70_t8"
+    pa.lib().paged_attn_plan_destroy(h)
+    st, h = plan_create(shape(), schedule=4, q_len=5, head_dim=256, kv_dtype=1)
+    assert st == 0 and pa.lib().paged_attn_plan_name(h) == b"pa_qblock_mfmapv_fp8_d256_g4_q5_t4"
+    pa.lib().paged_attn_plan_destroy(h)
+    # 4 sequences x 2 KV heads = 8 units: every block of a unit on one XCD
+    st, h = plan_create(shape(num_seqs=4), schedule=4, q_len=1)
+    assert st == 0 and pa.lib().paged_attn_plan_name(h).endswith(b"_xcd")
+    pa.lib().paged_attn_plan_destroy(h)
+    assert plan_create(shape(partition_size=512, max_partitions=4), schedule=4, q_len=3)[0] == -2
+    assert plan_create(shape(), schedule=4, q_len=0)[0] == -2
+    assert plan_create(shape(), schedule=4, q_len=4097)[0] == -2
+    assert plan_create(shape(), schedule=5, q_len=3)[0] == -2
+    assert plan_create(shape(), schedule=4, q_len=3, head_dim=96)[0] == -3
+
+
 def test_plan_create_and_workspace_sizes():
     a = lambda x: (x + 255) // 256 * 256
     st, h = plan_create(shape())
@@ -322,12 +343,13 @@ def test_plan_create_and_workspace_sizes():
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(schedule=1), -2),                      # partitioned without a partition size
-    (dict(schedule=3), -2), (dict(schedule=4), -2), (dict(schedule=-1), -2),
+    (dict(schedule=3), -2), (dict(schedule=5), -2), (dict(schedule=-1), -2),
     (dict(head_dim=96), -3), (dict(block_size=8), -3), (dict(window=-1), -2),
     (dict(schedule=2, workers=-1), -2), (dict(schedule=2, workers=(1 << 20) + 1), -2),
     (dict(max_len=-1), -2), (dict(kv_dtype=2), -3), (dict(kv_dtype=-1), -3),
     (dict(q_len=0), -2), (dict(q_len=-3), -2),
-    (dict(q_len=2), -3),                         # several query tokens: balanced schedule only
+    (dict(q_len=2), -3),                         # several query tokens: balanced or query
+                                                 # blocks only
     (dict(q_len=4097, schedule=2, workers=64), -2),  # above 4096 query tokens
     (dict(q_len=2, schedule=2, workers=64, window=0x7FFFFFFF), -2),
     # layouts (elements; head_dim 128, block 16, 2 KV heads)

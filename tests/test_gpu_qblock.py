@@ -1,0 +1,159 @@
+"""GPU parity of the query-block schedule (several query tokens per sequence: chunked prefill,
+speculative decode) against the fp64 oracle, through paged_attn_plan_run: one wave per
+(sequence, KV head, block of 32 / group tokens; 16 / group at head_dim 256), causal tokens at
+positions L - q_len + i.  Covered: every head size and group, token counts inside one block and
+across many, lengths shorter than q_len (positions below 0) and zero, windows, sinks, block
+sizes, bf16 and FP8 caches, XCD-pinned and plain grids, whole-prompt prefill (q_len = L), the
+decode-batch workload (sampled), one token, a table entry outside the pool, graph replay, and
+the argument checks."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_attn_amd as pa
+from workloads import make_config, make_workload
+
+from gpu_helpers import (compare, log, make_plan, oracle_full, oracle_multi_triples, run_plan,
+                         to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def qb_workload(D, g, Q, *, window=0, sinks=False, kv="bf16", bs=16, lens=None, kv_heads=2,
+                seed=0):
+    if lens is None:
+        lens = [0, 1, Q - 1, Q, Q + 1, 17, 100, 257, 1000]
+        lens = [max(x, 0) for x in lens]
+    return make_workload(name=f"qblock D{D} g{g} Q{Q}", seq_lens=lens, num_q_heads=kv_heads * g,
+                         num_kv_heads=kv_heads, head_dim=D, block_size=bs,
+                         seed=[D, g, Q, window, seed, 7], window=window, with_sinks=sinks,
+                         poison=True, kv_format=kv,
+                         kv_scales=(0.0625, 0.05) if kv != "bf16" else (1.0, 1.0), q_len=Q)
+
+
+# (D, group, q_len): one block, several blocks, a ragged last block, one token per block
+COMBOS = [(64, 1, 40), (64, 2, 100), (64, 4, 9), (64, 8, 70), (128, 1, 1), (128, 1, 33),
+          (128, 2, 16), (128, 4, 8), (128, 4, 70), (128, 8, 5), (128, 8, 4), (256, 1, 17),
+          (256, 2, 40), (256, 4, 9), (256, 8, 6), (256, 8, 2)]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("D,g,Q", COMBOS)
+def test_qblock_edges(D, g, Q, kv):
+    wl = qb_workload(D, g, Q, window=0 if (g + Q) % 2 else 11, sinks=(g * Q) % 3 == 0, kv=kv)
+    plan = make_plan(wl, "query_blocks")
+    log(f"[qblock] {plan.name}")
+    assert plan.name.startswith("pa_qblock_") and plan.workspace_size == 0
+    compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl),
+            f"qblock D={D} g={g} Q={Q} kv={kv} W={wl.window} sinks={wl.sinks is not None}")
+
+
+@pytest.mark.parametrize("bs,window", [(16, 0), (64, 33), (32, 1), (256, 100)])
+def test_qblock_block_sizes_windows(bs, window):
+    wl = qb_workload(128, 4, 40, window=window, sinks=True, bs=bs,
+                     lens=[300, 17, 1, 1000, 3, 40, 41, 2049], seed=1)
+    plan = make_plan(wl, "query_blocks")
+    compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl),
+            f"qblock {plan.name} bs={bs} W={window}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_qblock_xcd_pinned_grid(kv):
+    """8 sequences x 2 KV heads = 16 units, a multiple of the 8 XCDs: every block of a unit on
+    one XCD."""
+    wl = qb_workload(128, 4, 50, window=0, sinks=False, kv=kv,
+                     lens=[50, 60, 1, 0, 500, 49, 51, 1300], seed=2)
+    plan = make_plan(wl, "query_blocks")
+    log(f"[qblock] {plan.name}")
+    assert plan.name.endswith("_xcd")
+    compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl), f"qblock xcd-pinned kv={kv}")
+
+
+@pytest.mark.parametrize("D,g", [(128, 4), (128, 8), (64, 1), (256, 8)])
+def test_qblock_whole_prompt_prefill(D, g):
+    """Every token of every sequence is new (q_len = L): plain causal self-attention."""
+    Q = 300
+    wl = qb_workload(D, g, Q, lens=[Q] * 4, kv_heads=2, seed=3)
+    plan = make_plan(wl, "query_blocks")
+    compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl), f"qblock prefill D={D} g={g}")
+
+
+def sampled(wl, n, seed):
+    rng = np.random.default_rng(seed)
+    B, Q, Hq = wl.num_seqs, wl.q_len, wl.num_q_heads
+    trip = {(int(np.argmax(wl.seq_lens)), Q - 1, 0), (int(np.argmin(wl.seq_lens)), 0, Hq - 1)}
+    while len(trip) < n:
+        trip.add((int(rng.integers(B)), int(rng.integers(Q)), int(rng.integers(Hq))))
+    return sorted(trip)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_qblock_decode_batch_workload(kv):
+    """The Llama-8B-shaped batch (B64, 32 q / 8 KV heads) with 64 new tokens per sequence:
+    sampled (sequence, token, head) triples against the oracle, every output finite."""
+    wl = make_config(2, poison=True, kv_format=kv, q_len=64)
+    plan = make_plan(wl, "query_blocks")
+    log(f"[qblock] {plan.name}")
+    out, lse = run_plan(plan, wl, to_dev(wl))
+    trip = sampled(wl, 48, seed=11)
+    eo, el = oracle_multi_triples(wl, trip)
+    idx = tuple(np.array(trip).T)
+    compare(out[idx], lse[idx], eo, el, f"qblock cfg2 Q=64 kv={kv} ({len(trip)} sampled)")
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_qblock_mixed_workload_window_sinks():
+    wl = make_config(5, poison=True, q_len=9, seq_lens=[5000, 17, 2, 9000, 4096, 4097, 1, 300])
+    out, lse = run_plan(make_plan(wl, "query_blocks"), wl, to_dev(wl))
+    compare(out, lse, *oracle_full(wl), "qblock mixed Q=9 window 4096 + sinks")
+
+
+def test_qblock_bad_table_entry_gives_nan_for_that_sequence_only():
+    wl = qb_workload(128, 4, 20, lens=[200, 150, 90], seed=4)
+    t = to_dev(wl)
+    bt = t["bt"].clone()
+    bt[1, 3] = wl.num_blocks          # outside the pool, inside sequence 1's attended range
+    t["bt"] = bt
+    out, lse = run_plan(make_plan(wl, "query_blocks"), wl, t)
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+    eo, el = oracle_full(wl)
+    keep = [0, 2]
+    compare(out[keep], lse[keep], eo[keep], el[keep], "qblock sequences with good tables")
+
+
+def test_qblock_graph_replay_matches_eager():
+    wl = qb_workload(128, 4, 33, window=20, sinks=True, lens=[100, 33, 500, 7], seed=5)
+    t = to_dev(wl)
+    plan = make_plan(wl, "query_blocks")
+    args = (t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale))
+    out = torch.empty(wl.q.shape, device="cuda")
+    lse = torch.empty(wl.q.shape[:-1], device="cuda")
+    plan.run(*args, out=out, lse=lse, sinks=t["sinks"])
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            plan.run(*args, out=out, lse=lse, sinks=t["sinks"])
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+    compare(ref_out.cpu().numpy().astype(np.float64), ref_lse.cpu().numpy().astype(np.float64),
+            *oracle_full(wl), "qblock eager (graph reference)")
+
+
+def test_qblock_plan_rejects_unsupported_requests():
+    wl = qb_workload(128, 4, 2, lens=[10, 20])
+    with pytest.raises(pa.PagedAttnError):     # 16 heads per KV head: no kernel
+        pa.Plan(2, 32, 2, wl.num_blocks, wl.stride, 128, 16, schedule="query_blocks", q_len=2)
+    with pytest.raises(pa.PagedAttnError):
+        pa.Plan(2, 8, 2, wl.num_blocks, wl.stride, 128, 16, schedule="query_blocks", q_len=0)
+    with pytest.raises(pa.PagedAttnError):
+        pa.Plan(2, 8, 2, wl.num_blocks, wl.stride, 128, 16, schedule="query_blocks", q_len=4097)
