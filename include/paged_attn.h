@@ -227,7 +227,13 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  *                  PA_SCHEDULE_PARTITIONED_FUSED (fixed partitions as PARTITIONED, merged in
  *                  the same launch by whichever partition of a (sequence, KV head) finishes
  *                  last: one kernel per step, for small batches; its device-scope release per
- *                  partition makes it slow for large ones).
+ *                  partition makes it slow for large ones), or PA_SCHEDULE_QUERY_BLOCKS (one
+ *                  one-wave workgroup per (sequence, KV head, block of 32 / (Hq/Hkv) query
+ *                  tokens, 16 / (Hq/Hkv) at head_dim 256), each reading the keys its tokens
+ *                  attend and writing its outputs, no merge; the blocks of a (sequence, KV head)
+ *                  share the keys through one XCD's L2 when num_seqs * num_kv_heads is a
+ *                  multiple of 8: chunked prefill and whole prompts; requires
+ *                  shape->partition_size == 0 and needs no workspace).
  *   kv_dtype       PA_KV_BF16, or PA_KV_FP8_E4M3: k_cache and v_cache then hold one byte per
  *                  value, [num_blocks][Hkv][block_size][head_dim] uint8, each code standing for
  *                  its E4M3 value times the tensor's scale (given per run).  The FP8 KV cache is
@@ -246,12 +252,14 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  *                  This is the query length the one-token decode benchmark of ROCm/rocm-libraries
  *                  PR #13700 fixes at 1, and the longer-query case vllm.cpp PR #564 ("What is
  *                  deliberately not here") leaves out; the causal rule is this library's reading.
- *                  Up to 32 (token, head) pairs per KV head share each K/V tile (16 at
- *                  head_dim 256), so with q_len * Hq/Hkv within that every K/V row is read once
- *                  per KV head for all q_len tokens; more tokens run in passes of 32 / (Hq/Hkv)
- *                  (16 / (Hq/Hkv)) tokens, each pass reading the keys its tokens attend.  Requires PA_SCHEDULE_BALANCED (else
- *                  PA_ERR_UNSUPPORTED) and q_len <= 4096 (else PA_ERR_SHAPE); bf16 and FP8
- *                  caches alike.
+ *                  On the balanced schedule up to 32 (token, head) pairs per KV head share each
+ *                  K/V tile (16 at head_dim 256), so with q_len * Hq/Hkv within that every K/V
+ *                  row is read once per KV head for all q_len tokens; more tokens run in passes
+ *                  of 32 / (Hq/Hkv) (16 / (Hq/Hkv)) tokens, each pass reading the keys its tokens
+ *                  attend.  The query-block schedule runs every block of tokens at once instead.
+ *                  Requires PA_SCHEDULE_BALANCED or PA_SCHEDULE_QUERY_BLOCKS (else
+ *                  PA_ERR_UNSUPPORTED) and q_len <= 4096 (else PA_ERR_SHAPE); bf16 and FP8 caches
+ *                  alike.
  *   max_seq_len    host-side upper bound on the lengths the plan will see, or 0 if unknown.
  *                  Balanced plans launch no more workers than that many tiles can keep busy
  *                  (a small batch then does not pay for thousands of idle workers); a length

@@ -375,15 +375,16 @@ class Plan:
     """A prepared decode step (paged_attn_plan_*): checks, variant choice and launch geometry
     done once; run() fills pointers and launches decode (+ merge).  ``schedule`` is "unsplit",
     "partitioned" (``partition_size`` tokens, partition slots for ``max_seq_len``), "fused"
-    (partitioned, merged in the same launch by the last partition to finish) or
-    "balanced" (``num_workers``, 0 = the device default; ``max_seq_len``, a bound on the
-    lengths, caps the workers of a small batch).  ``kv_dtype`` is "bf16" or "fp8_e4m3" (KV
-    pools of one byte per value, uint8 tensors, with per-tensor scales given to run()).
+    (partitioned, merged in the same launch by the last partition to finish), "balanced"
+    (``num_workers``, 0 = the device default; ``max_seq_len``, a bound on the lengths, caps the
+    workers of a small batch) or "query_blocks" (several query tokens: one wave per (sequence,
+    KV head, block of tokens), no workspace).  ``kv_dtype`` is "bf16" or "fp8_e4m3" (KV pools
+    of one byte per value, uint8 tensors, with per-tensor scales given to run()).
     ``kv_layout``: None for the pool [num_blocks][Hkv][bs][D], else (block, head, token) strides
     in elements of the cache type (pa_kv_layout).
-    ``q_len`` > 1 (balanced schedule): q_len causal query tokens per sequence, q [B][q_len][Hq][D]
-    -> out [B][q_len][Hq][D], lse [B][q_len][Hq].  run() records only kernel launches on the
-    stream, so it can be captured in a CUDA/HIP graph."""
+    ``q_len`` > 1 (balanced or query_blocks): q_len causal query tokens per sequence,
+    q [B][q_len][Hq][D] -> out [B][q_len][Hq][D], lse [B][q_len][Hq].  run() records only
+    kernel launches on the stream, so it can be captured in a CUDA/HIP graph."""
 
     def __init__(self, num_seqs: int, num_q_heads: int, num_kv_heads: int, num_blocks: int,
                  block_table_stride: int, head_dim: int, block_size: int, *, window: int = 0,
