@@ -74,8 +74,11 @@ struct BalancedParams {
 struct QBlockParams {
   DecodeParams d;             // q_total = query tokens per sequence; q_len and q_first unused
   int32_t tokens_per_block;   // columns per wave / group
-  int32_t blocks_per_seq;     // ceil(q_total / tokens_per_block)
-  int32_t xcd_pinned;         // 1: every block of a (sequence, KV head) on one XCD
+  int32_t waves;              // waves per workgroup, each one block of tokens (1, or 4 sharing
+                              // the K/V tiles through LDS)
+  int32_t blocks_per_seq;     // workgroups per (sequence, KV head):
+                              // ceil(q_total / (tokens_per_block * waves))
+  int32_t xcd_pinned;         // 1: every workgroup of a (sequence, KV head) on one XCD
   uint32_t grid;              // workgroups launched
 };
 

@@ -21,6 +21,8 @@
 // here") leaves out and ROCm/rocm-libraries PR #13700 "prepare saved paged decode bindings
 // once" fixes at one token; the causal rule is this library's reading.  Sinks: randomvariable/
 // vllm issue #23, table "Current state" (a sink logit joins the softmax with a zero value row).
+#include <cstdlib>
+
 #include "pa_device.hpp"
 #include "pa_kernels.hpp"
 #include "pa_qk.hpp"
@@ -173,6 +175,186 @@ void qblock_kernel(const QBlockParams qp) {
   }
 }
 
+// The workgroup form: kQbWaves waves share each K/V tile through LDS.  A workgroup takes
+// kQbWaves consecutive token blocks of one (sequence, KV head), wave w the w-th, and streams the
+// union of their key ranges: the tile A tiles ahead is copied straight from the pool into an LDS
+// ring of A + 1 tiles by direct-to-LDS loads (no registers hold it in flight), every wave waits
+// for its own copies of the current tile and meets the others at a barrier, then reads the tile
+// from LDS into its registers and folds it into its columns.  Each key row is read from L2 or
+// HBM once per workgroup, not once per wave, and a wave never waits on its own tile loads.
+constexpr int kQbWaves = 4;
+constexpr int kQbTableTiles = kQbWaves * kWave;   // block-table window in LDS, one per thread
+
+// One 16-byte piece per lane from global memory straight into LDS, lane i's piece at
+// lds_wave_base + 16 i (global_load_lds_dwordx4; M0 holds the wave's LDS base).  Written as
+// inline assembly so that the compiler does not treat every later LDS read as possibly aliasing
+// the copy and wait for all copies in flight before it; the caller waits for the copies itself
+// (vmcnt) before the barrier that publishes them.  The instruction writes no register.
+__device__ __forceinline__ void copy_piece_to_lds(const char* src, const char* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               ::"s"(lds), "v"(src)
+               : "memory", "m0");
+}
+
+template <int D, class QK, int A>
+__global__ __launch_bounds__(kQbWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void qblock_lds_kernel(const QBlockParams qp) {
+  using RG = RowGeom<D>;
+  constexpr int E = RG::kElems;
+  constexpr int RB = QK::kRowBytes;
+  constexpr int PR = RB / 16;                          // 16-byte pieces per row
+  constexpr int TB = 2 * kTileTokens * RB;             // K rows, then V rows
+  constexpr int NBUF = A + 1;
+  constexpr int PIECES = TB / 16;
+  static_assert(PIECES % kWave == 0, "a tile is whole wave copies");
+  // copies (one 16-byte piece per lane) each loading wave makes per tile
+  constexpr int PW = PIECES / (kQbWaves * kWave);
+  constexpr int LOADERS = PW > 0 ? kQbWaves : PIECES / kWave;
+  constexpr int PL = PW > 0 ? PW : 1;
+  __shared__ __attribute__((aligned(16))) char s_tiles[NBUF * TB];
+
+  const DecodeParams& p = qp.d;
+  QBlockItem it;
+  if (!qblock_item(qp, it)) return;   // uniform over the workgroup
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int c = lane & (kRowLanes - 1);
+  const int tpb = qp.tokens_per_block;
+  const int64_t cap = (int64_t)p.stride << p.bs_log2;
+  const int Lraw = __builtin_amdgcn_readfirstlane(p.seq_lens[it.b]);
+  // the workgroup's tokens and the union of their keys
+  const int q0w = it.qb * kQbWaves * tpb;
+  const int nqw = min(kQbWaves * tpb, p.q_total - q0w);
+  const SeqSpan sw = seq_span(Lraw, p.window > 0 ? p.window + nqw - 1 : 0, cap,
+                              p.q_total - q0w - nqw);
+  // this wave's tokens (none for a wave past the last block) and their keys
+  const int q0 = q0w + wave * tpb;
+  const int nq = max(0, min(tpb, p.q_total - q0));
+  const bool active = nq > 0;
+  const QShape qs{nq, p.q_total, q0, p.group};
+  const SeqSpan s = seq_span(Lraw, p.window > 0 ? p.window + nq - 1 : 0, cap,
+                             max(0, p.q_total - q0 - nq));
+
+  const float c2 = fabsf(p.qk_scale_log2);
+  const uint32_t qflip = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
+  const int h0 = it.kvh * p.group;
+  QK qk;
+  if (active) qk.init(p, qs, it.b, h0, lane, qflip, c2);
+
+  const TileAddr ta{p.num_blocks, p.bs_log2, p.kv_block_stride, it.kvh * p.kv_head_stride,
+                    p.kv_row_stride};
+  const int rs = (int)p.kv_row_stride;
+  const int32_t* bt = p.block_table + (size_t)it.b * p.stride;
+  bool bad = sw.bad;
+
+  // the physical blocks of workgroup tiles [base, base + kQbTableTiles), one per thread, in LDS:
+  // reading them there keeps the tile loop free of vector loads other than the copies (a vector
+  // load's wait would also wait for every copy in flight)
+  __shared__ int s_phys[kQbTableTiles];
+  auto fill_table = [&](int base) {
+    const int k = base + (int)threadIdx.x;
+    s_phys[threadIdx.x] = k < sw.T ? bt[ta.logical_block(sw.t0 + k)] : -1;
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  fill_table(0);
+
+  // copy workgroup tile k (tile sw.t0 + k) into ring slot k % NBUF; past the last tile, or for
+  // a table entry outside the pool, the lanes copy from q instead (valid memory, never read
+  // back), so that every wave always has the same number of copies in flight
+  uint32_t okbits = 0;   // bit k % NBUF: tile k came from the pool
+  auto copy = [&](int k) {
+    int64_t off = -1;
+    if (k < sw.T)
+      off = ta.offset(__builtin_amdgcn_readfirstlane(s_phys[k % kQbTableTiles]), sw.t0 + k);
+    const int slot = k % NBUF;
+    okbits = (okbits & ~(1u << slot)) | ((off >= 0 ? 1u : 0u) << slot);
+    if (wave < LOADERS) {
+#pragma unroll
+      for (int m = 0; m < PL; ++m) {
+        const int piece = (wave * PL + m) * kWave + lane;   // its place in the tile copy
+        const int h = piece / (kTileTokens * PR);
+        const int row = (piece / PR) % kTileTokens;
+        const int col = (piece % PR) ^ (row & QK::kLdsSwizzle);   // the pool's piece
+        const char* src = off >= 0 ? (h ? p.v_cache : p.k_cache) + off + row * rs + col * 16
+                                   : reinterpret_cast<const char*>(p.q) + (lane & 7) * 16;
+        copy_piece_to_lds(src, s_tiles + slot * TB + (wave * PL + m) * kWave * 16);
+      }
+    }
+  };
+
+  // every column of this wave sees the keys in [lo_all, hi_all)
+  const int hi_all = s.L - nq + 1;
+  const int lo_all = (p.window > 0 && s.L > p.window) ? s.L - p.window : 0;
+  typename QK::Tile t;
+#pragma unroll
+  for (int k = 0; k < A; ++k) copy(k);
+  for (int k = 0; k < sw.T; ++k) {
+    // this wave's copies of tile k are done once at most those of the A - 1 later tiles are
+    // outstanding; the barrier then makes the whole tile visible, and every wave has finished
+    // reading tile k - 1, whose slot the next copy reuses
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PL * (A - 1)) : "memory");
+    if ((k + A) % kQbTableTiles == 0 && k + A < sw.T) fill_table(k + A);   // uniform
+    copy(k + A);
+    const int tile = sw.t0 + k;
+    if (active && tile >= s.t0 && tile < s.t0 + s.T) {
+      if (!((okbits >> (k % NBUF)) & 1u)) {
+        bad = true;   // a table entry outside the pool: never read through, NaN outputs
+      } else {
+        qk.fill_from_lds(t, s_tiles + (k % NBUF) * TB, lane);
+        const int tok0 = tile * kTileTokens;
+        if (tok0 >= lo_all && tok0 + kTileTokens <= hi_all)
+          qk.template consume<false>(t, 0, 0, 0, lane);
+        else
+          qk.consume_cols(t, tok0, hi_all, p.window, s.start, s.L, lane);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the copies past the last tile
+  if (!active) return;
+  bad = bad || s.bad;
+
+  const int ncols = nq * qs.group;
+  const int sh = __builtin_ctz((unsigned)qs.group);
+  auto finish_half = [&](auto& half, int cb) {
+    half.merge_cols();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nl = 4 * (lane >> 4) + i;
+      const int n = cb + nl;
+      float M = half.col_m(nl), lt = half.col_l(nl);
+      if (n < ncols) {
+        const int hq = h0 + (n & (qs.group - 1));
+        float scale_o = 1.f;
+        if (p.sinks != nullptr) {
+          const float s2 = p.sinks[hq] * kLog2e;
+          const float M2 = fmaxf(M, s2);
+          const float M2u = M2 == -INFINITY ? 0.f : M2;
+          scale_o = fast_exp2(M - M2u);
+          lt = fmaf(lt, scale_o, fast_exp2(s2 - M2u));
+          M = M2;
+        }
+        const float inv = lt != 0.f ? scale_o / lt : 0.f;
+        float lv = lt != 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
+        if (bad) lv = __builtin_nanf("");
+        const size_t row = ((size_t)it.b * qs.q_total + q0 + (n >> sh)) * p.num_q_heads + hq;
+        float* dst = p.out + row * D;
+        if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          dst[RG::dim(c, e)] = bad ? __builtin_nanf("") : half.acc(i, e) * inv;
+      }
+    }
+  };
+  if constexpr (QK::kHalves == 2) {
+    finish_half(qk.h[0], 0);
+    finish_half(qk.h[1], 16);
+  } else {
+    finish_half(qk, 0);
+  }
+}
+
 template <int D>
 using QbQk = typename std::conditional<D <= 128, QkMfmaPvPair<D, false, false>,
                                        QkMfmaPvT<D, 16, false, false>>::type;
@@ -188,6 +370,16 @@ using QbQkFp8 = typename std::conditional<D <= 128, QkMfmaPvPair<D, true, false>
 template <int D>
 hipError_t launch_d(const QBlockParams& qp, QkPath path, hipStream_t stream) {
   constexpr int DEPTH = 1, WPE = 2;
+  constexpr int A = D == 256 ? 3 : 4;   // tiles copied ahead (LDS ring of A + 1)
+  if (qp.waves == kQbWaves) {
+    if (path == QkPath::kMfmaPvFp8)
+      hipLaunchKernelGGL((qblock_lds_kernel<D, QbQkFp8<D>, A>), dim3(qp.grid),
+                         dim3(kQbWaves * kWave), 0, stream, qp);
+    else
+      hipLaunchKernelGGL((qblock_lds_kernel<D, QbQk<D>, A>), dim3(qp.grid),
+                         dim3(kQbWaves * kWave), 0, stream, qp);
+    return hipGetLastError();
+  }
   if (path == QkPath::kMfmaPvFp8)
     hipLaunchKernelGGL((qblock_kernel<D, QbQkFp8<D>, DEPTH, WPE>), dim3(qp.grid), dim3(kWave), 0,
                        stream, qp);
@@ -204,7 +396,10 @@ int qblock_columns(int head_dim) { return head_dim <= 128 ? 32 : 16; }
 void qblock_geometry(QBlockParams& qp, int head_dim) {
   const int cols = qblock_columns(head_dim);
   qp.tokens_per_block = cols / qp.d.group;
-  qp.blocks_per_seq = (qp.d.q_total + qp.tokens_per_block - 1) / qp.tokens_per_block;
+  const char* env = std::getenv("PA_QB_WAVES");   // (temporary)
+  qp.waves = env != nullptr ? std::atoi(env) : kQbWaves;
+  const int per_wg = qp.tokens_per_block * qp.waves;
+  qp.blocks_per_seq = (qp.d.q_total + per_wg - 1) / per_wg;
   const long long units = (long long)qp.d.num_seqs * qp.d.num_kv_heads;
   qp.xcd_pinned = units % kXcds == 0 ? 1 : 0;
   const long long grid = qp.xcd_pinned

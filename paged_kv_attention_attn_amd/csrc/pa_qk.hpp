@@ -535,6 +535,55 @@ struct QkMfmaPvT {
     }
   }
 
+  // A tile copied to LDS: K rows then V rows, kRowBytes each; within a row the 16-byte piece p
+  // sits at piece p ^ (row & kLdsSwizzle), which spreads a column of pieces over the rows'
+  // banks.  Byte `off` of row `row` of half h (0 = K, 1 = V):
+  static constexpr int kLdsSwizzle = kRowBytes / 16 < 16 ? kRowBytes / 16 - 1 : 15;
+  __device__ __forceinline__ static const char* lds_at(const char* tile, int h, int row,
+                                                       int off) {
+    return tile + (h * kTileTokens + row) * kRowBytes +
+           ((((off >> 4) ^ (row & kLdsSwizzle))) << 4) + (off & 15);
+  }
+  // Fill t from such a copy: the same pieces issue() reads from the pool.
+  __device__ __forceinline__ void fill_from_lds(Tile& t, const char* tile, int lane) const {
+    const int mrow = lane & 15;
+    const int tok = 4 * (mrow & 3) + (mrow >> 2);
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int i = 0; i < KL; ++i)
+      t.k[i] = *reinterpret_cast<const u32x4_t*>(lds_at(tile, 0, tok, 64 * i + 16 * g));
+#pragma unroll
+    for (int j = 0; j < kTileSteps; ++j) {
+      const int row = kRows * j + g;
+      if constexpr (FP8) {
+        if constexpr (D == 64) {
+          t.v[j][0] = *reinterpret_cast<const uint32_t*>(lds_at(tile, 1, row, 4 * c));
+        } else {
+          const u32x2_t x = *reinterpret_cast<const u32x2_t*>(lds_at(tile, 1, row, 8 * c));
+          t.v[j][0] = x.x;
+          t.v[j][1] = x.y;
+          if constexpr (D == 256) {
+            const u32x2_t y =
+                *reinterpret_cast<const u32x2_t*>(lds_at(tile, 1, row, 128 + 8 * c));
+            t.v[j][2] = y.x;
+            t.v[j][3] = y.y;
+          }
+        }
+      } else if constexpr (D == 64) {
+        const u32x2_t x = *reinterpret_cast<const u32x2_t*>(lds_at(tile, 1, row, 8 * c));
+        t.v[j][0] = x.x;
+        t.v[j][1] = x.y;
+      } else {
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(lds_at(tile, 1, row, 16 * c));
+        t.v[j][0] = x.x; t.v[j][1] = x.y; t.v[j][2] = x.z; t.v[j][3] = x.w;
+        if constexpr (D == 256) {
+          const u32x4_t y = *reinterpret_cast<const u32x4_t*>(lds_at(tile, 1, row, 256 + 16 * c));
+          t.v[j][4] = y.x; t.v[j][5] = y.y; t.v[j][6] = y.z; t.v[j][7] = y.w;
+        }
+      }
+    }
+  }
+
   template <bool MASKED>
   __device__ __forceinline__ void consume(Tile& t, int tok0, int lo, int hi, int lane) {
     consume<MASKED>(t, tok0, lo, hi, lo, hi, lane);
@@ -725,6 +774,10 @@ struct QkMfmaPvPair {
   __device__ __forceinline__ void issue(Tile& t, const char* kb, const char* vb,
                                         int lane) const {
     h[0].issue(t, kb, vb, lane);
+  }
+  static constexpr int kLdsSwizzle = Half::kLdsSwizzle;
+  __device__ __forceinline__ void fill_from_lds(Tile& t, const char* tile, int lane) const {
+    h[0].fill_from_lds(t, tile, lane);
   }
   template <bool MASKED>
   __device__ __forceinline__ void consume(Tile& t, int tok0, int lo, int hi, int lane) {
