@@ -599,9 +599,9 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
     pl->qb.d = p;
     pa::qblock_geometry(pl->qb, head_dim);
     pl->group = pa::qblock_columns(head_dim);
-    std::snprintf(pl->name, sizeof(pl->name), "pa_qblock_%s_d%d_g%d_q%d_t%d%s",
+    std::snprintf(pl->name, sizeof(pl->name), "pa_qblock_%s_d%d_g%d_q%d_t%d_w%d%s",
                   pa::qk_path_name(path), head_dim, group, q_len, pl->qb.tokens_per_block,
-                  pl->qb.xcd_pinned ? "_xcd" : "");
+                  pl->qb.waves, pl->qb.xcd_pinned ? "_xcd" : "");
   } else if (schedule == PA_SCHEDULE_PARTITIONED) {
     const size_t rows = (size_t)shape->num_seqs * shape->num_q_heads * shape->max_partitions;
     pl->part_bytes = align256(rows * head_dim * sizeof(float));

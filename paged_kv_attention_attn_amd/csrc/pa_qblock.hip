@@ -21,8 +21,6 @@
 // here") leaves out and ROCm/rocm-libraries PR #13700 "prepare saved paged decode bindings
 // once" fixes at one token; the causal rule is this library's reading.  Sinks: randomvariable/
 // vllm issue #23, table "Current state" (a sink logit joins the softmax with a zero value row).
-#include <cstdlib>
-
 #include "pa_device.hpp"
 #include "pa_kernels.hpp"
 #include "pa_qk.hpp"
@@ -396,8 +394,9 @@ int qblock_columns(int head_dim) { return head_dim <= 128 ? 32 : 16; }
 void qblock_geometry(QBlockParams& qp, int head_dim) {
   const int cols = qblock_columns(head_dim);
   qp.tokens_per_block = cols / qp.d.group;
-  const char* env = std::getenv("PA_QB_WAVES");   // (temporary)
-  qp.waves = env != nullptr ? std::atoi(env) : kQbWaves;
+  // the workgroup form once there are blocks for all its waves; one wave per block otherwise
+  const int blocks = (qp.d.q_total + qp.tokens_per_block - 1) / qp.tokens_per_block;
+  qp.waves = blocks >= kQbWaves ? kQbWaves : 1;
   const int per_wg = qp.tokens_per_block * qp.waves;
   qp.blocks_per_seq = (qp.d.q_total + per_wg - 1) / per_wg;
   const long long units = (long long)qp.d.num_seqs * qp.d.num_kv_heads;

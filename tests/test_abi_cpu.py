@@ -250,10 +250,13 @@ def test_query_block_plans():
     st, h = plan_create(shape(), schedule=4, q_len=70)
     assert st == 0
     assert pa.lib().paged_attn_plan_workspace_size(h) == 0
-    assert pa.lib().paged_attn_plan_name(h) == b"pa_qblock_mfmapv_d128_g4_q70_t8"
+    # 70 tokens = 9 blocks of 8: workgroups of four waves sharing the tiles through LDS
+    assert pa.lib().paged_attn_plan_name(h) == b"pa_qblock_mfmapv_d128_g4_q70_t8_w4"
     pa.lib().paged_attn_plan_destroy(h)
+    # 5 tokens = 2 blocks of 4: one wave per block
     st, h = plan_create(shape(), schedule=4, q_len=5, head_dim=256, kv_dtype=1)
-    assert st == 0 and pa.lib().paged_attn_plan_name(h) == b"pa_qblock_mfmapv_fp8_d256_g4_q5_t4"
+    assert st == 0
+    assert pa.lib().paged_attn_plan_name(h) == b"pa_qblock_mfmapv_fp8_d256_g4_q5_t4_w1"
     pa.lib().paged_attn_plan_destroy(h)
     # 4 sequences x 2 KV heads = 8 units: every block of a unit on one XCD
     st, h = plan_create(shape(num_seqs=4), schedule=4, q_len=1)
