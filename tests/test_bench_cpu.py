@@ -1,5 +1,6 @@
-"""Host logic of bench.py that needs no GPU: the refusal of several GPUs, and the kernel-source
-hash that keys the committed HBM-traffic counters (comment edits keep it, code edits change it)."""
+"""Host logic of bench.py that needs no GPU: the refusal of several GPUs, the kernel-source
+hash that keys the committed HBM-traffic counters (comment edits keep it, code edits change it),
+and the attended-pair count that the query-block roofline's flops come from."""
 import importlib.util
 import json
 import os
@@ -43,3 +44,24 @@ def test_several_gpus_are_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_attended_pairs_matches_a_brute_force_count():
+    """(query token, key) pairs per query head: token i of q_len sits at L - q_len + i and
+    attends keys max(0, p + 1 - W) .. p; counted here key by key."""
+    b = load_bench()
+    from workloads import make_workload
+
+    for window in (0, 5, 40):
+        wl = make_workload(name="pairs", seq_lens=[0, 1, 3, 7, 30, 100], num_q_heads=4,
+                           num_kv_heads=2, head_dim=64, block_size=16, seed=[1, window],
+                           window=window, q_len=7)
+        want = 0
+        for L in wl.seq_lens:
+            for i in range(wl.q_len):
+                p = int(L) - wl.q_len + i
+                for t in range(0, max(p + 1, 0)):
+                    if window == 0 or t > p - window:
+                        want += 1
+        assert b.attended_pairs(wl) == want
+        assert isinstance(b.attended_pairs(wl), int) and want > 0
