@@ -1,7 +1,8 @@
 """GPU parity for KV pools in other layouts, given to a plan as (block, head, token) strides:
 token-major [NB][bs][Hkv][D], K and V interleaved per block [NB][2][Hkv][bs][D], and padded rows
 whose padding holds NaN.  The oracle reads the same values from the default layout, so every
-schedule, both KV formats and several query tokens must match it exactly as before."""
+schedule (the query-block one included), both KV formats and several query tokens must match it
+exactly as before."""
 from __future__ import annotations
 
 import numpy as np
@@ -87,6 +88,24 @@ def test_layouts_several_query_tokens(layout):
     plan = plan_for(wl, "balanced", strides, num_workers=9)
     log(f"[layout] {plan.name}")
     compare(*run_plan(plan, wl, t), *oracle_full(wl), f"{layout} q_len=4")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("Q", [4, 40])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_layouts_query_blocks(layout, Q, kv):
+    """The query-block schedule reads the pool through the same strides: one wave per block
+    (Q = 4: one block of 8 tokens) and workgroups sharing tiles through LDS (Q = 40: 5 blocks),
+    whose copies address each 16-byte piece of a row through the row stride."""
+    wl = make_workload(name="layout qblock", seq_lens=[0, 2, 17, Q, 100, 257], num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=32, seed=[5, Q], window=30,
+                       with_sinks=True, poison=True, q_len=Q, kv_format=kv,
+                       kv_scales=(0.0625, 0.05) if kv != "bf16" else (1.0, 1.0))
+    t, strides = relayout(wl, to_dev(wl), layout)
+    plan = plan_for(wl, "query_blocks", strides)
+    log(f"[layout] {plan.name}")
+    assert ("_w4" in plan.name) == (Q == 40)
+    compare(*run_plan(plan, wl, t), *oracle_full(wl), f"{layout} query blocks q_len={Q} {kv}")
 
 
 def test_token_major_decode_batch_workload():
