@@ -1,19 +1,21 @@
-// Query-block grid for several query tokens per sequence (chunked prefill, speculative decode)
-// on gfx950.
+// Query blocks for several query tokens per sequence (chunked prefill, speculative decode) on
+// gfx950.
 //
-// One one-wave workgroup per (sequence b, KV head kvh, block of query tokens).  A block holds
-// the columns of one wave, 32 (token, head) pairs at head_dim <= 128 and 16 at 256, so
-// tokens_per_block = columns / group.  The wave streams the 16-token K/V tiles its tokens attend
-// (the union of their causal, windowed ranges), forms q.k
-// and P.V on the matrix cores exactly as the one-token kernels do for their columns (each
-// column masked to its own token's range inside the shared tiles), and writes its outputs and
-// LSEs: nothing is split, so nothing is merged.
+// A block of tokens holds the columns of one wave, 32 (token, head) pairs at head_dim <= 128
+// and 16 at 256, so tokens_per_block = columns / group.  A wave folds the 16-token K/V tiles its
+// tokens attend (the union of their causal, windowed ranges) into its columns, forming q.k and
+// P.V on the matrix cores exactly as the one-token kernels do (each column masked to its own
+// token's range inside the shared tiles), and writes its outputs and LSEs: nothing is split,
+// so nothing is merged.  Two forms:
+//   - qblock_lds_kernel: four waves per workgroup, four consecutive blocks of one (sequence,
+//     KV head), sharing every tile through an LDS ring (used from four blocks per sequence);
+//   - qblock_kernel: one wave per block, loading its own tiles (fewer blocks).
 //
 // All blocks of a (sequence, KV head) read the same keys.  The chip deals workgroups to its
-// 8 XCDs round-robin by linear id; with xcd_pinned every block of one (sequence, KV head) gets
-// an id of the same residue mod 8, so they run on one XCD, close in time, and share its L2: the
-// K/V loads are plain (cached) here, not non-temporal.  Within a (sequence, KV head) the blocks
-// of the last tokens, which attend the most keys, are dealt first.
+// 8 XCDs round-robin by linear id; with xcd_pinned every workgroup of one (sequence, KV head)
+// gets an id of the same residue mod 8, so they run on one XCD, close in time, and share its
+// L2: the K/V loads are plain (cached) here, not non-temporal.  Within a (sequence, KV head)
+// the blocks of the last tokens, which attend the most keys, are dealt first.
 //
 // Token i of q_total new tokens sits at position L - q_total + i and attends keys t <= its
 // position, the last `window` of them when window > 0: the longer-query case that vllm.cpp
@@ -360,15 +362,16 @@ template <int D>
 using QbQkFp8 = typename std::conditional<D <= 128, QkMfmaPvPair<D, true, false>,
                                           QkMfmaPvT<D, 16, true, false>>::type;
 
-// One tile in flight and at least two waves per SIMD: the keys mostly come from L2 here, and a
-// second wave hides the tile step's latency better than a second tile buffer (which leaves room
-// for one wave only).  Measured on the Llama-8B-shaped batch with 512 new tokens per sequence:
-// 3555 us per step against 6044 us for two tiles in flight at one wave per SIMD; two tiles at
-// two waves spill registers (9278 us).
+// One wave per block: one tile in flight and at least two waves per SIMD.  The keys mostly come
+// from L2 here, and a second wave hides the tile step's latency better than a second tile buffer
+// (which leaves room for one wave only).  Measured on the Llama-8B-shaped batch with 512 new
+// tokens per sequence: 3555 us per step against 6044 us for two tiles in flight at one wave per
+// SIMD; two tiles at two waves spill registers (9278 us).  The workgroup form: 3068 us.
 template <int D>
 hipError_t launch_d(const QBlockParams& qp, QkPath path, hipStream_t stream) {
   constexpr int DEPTH = 1, WPE = 2;
-  constexpr int A = D == 256 ? 3 : 4;   // tiles copied ahead (LDS ring of A + 1)
+  constexpr int A = D == 256 ? 3 : 4;   // tiles copied ahead (LDS ring of A + 1; 4, 6 and 8
+                                        // measured the same at D = 128)
   if (qp.waves == kQbWaves) {
     if (path == QkPath::kMfmaPvFp8)
       hipLaunchKernelGGL((qblock_lds_kernel<D, QbQkFp8<D>, A>), dim3(qp.grid),
