@@ -139,13 +139,18 @@ void balanced_decode_kernel(const BalancedParams bp) {
   const int w = blockIdx.x;
   const BalancedCtx ctx{&p, (int64_t)p.stride << p.bs_log2, span_window(p, qs), q_rest(qs)};
 
-  // pass 1: total tiles (worker 0 also records the per-sequence prefix for the fix-up)
-  int64_t carry = 0;
+  // pass 1: total tiles (worker 0 also records the per-sequence prefix for the fix-up); the
+  // first 64 sequences' tiles and inclusive prefix stay in registers for pass 2
+  int64_t carry = 0, T_first = 0, incl_first = 0;
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int j = base + lane;
     const int64_t T =
         j < p.num_seqs ? seq_span(p.seq_lens[j], ctx.swin, ctx.cap, ctx.qrest).T : 0;
     const int64_t incl = wave_incl_scan64(T, lane) + carry;
+    if (base == 0) {
+      T_first = T;
+      incl_first = incl;
+    }
     if (w == 0 && j < p.num_seqs) bp.prefix[j] = incl - T;
     carry = readlane64(incl, kWave - 1);
   }
@@ -157,14 +162,17 @@ void balanced_decode_kernel(const BalancedParams bp) {
   const int n = (int)(worker_begin(total, n_eff, w + 1) - A);
   if (n <= 0) return;
 
-  // pass 2: the unit holding tile A
+  // pass 2: the unit holding tile A (the first 64 sequences from pass 1's registers: with up to
+  // 64 sequences nothing is loaded again)
   Cursor cur{0, 0, 0, {}};
   carry = 0;
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int j = base + lane;
-    const int64_t T =
-        j < p.num_seqs ? seq_span(p.seq_lens[j], ctx.swin, ctx.cap, ctx.qrest).T : 0;
-    const int64_t incl = wave_incl_scan64(T, lane) + carry;
+    int64_t T = T_first, incl = incl_first;
+    if (base != 0) {
+      T = j < p.num_seqs ? seq_span(p.seq_lens[j], ctx.swin, ctx.cap, ctx.qrest).T : 0;
+      incl = wave_incl_scan64(T, lane) + carry;
+    }
     const uint64_t hit = __builtin_amdgcn_ballot_w64(j < p.num_seqs &&
                                                      incl * p.num_kv_heads > A);
     if (hit != 0) {
