@@ -391,27 +391,32 @@ void balanced_decode_kernel(const BalancedParams bp) {
   }
 }
 
-// Fix-up: one workgroup per (sequence b, KV head kvh, group of H of its G query heads), with
-// H = min(G, 1024 / D), at most 4 KiB of every piece per workgroup, so that a one-token unit at
-// D = 128 (G <= 8) is one workgroup.  Units inside one worker were written by the decode
-// kernel; empty units get 0 (or the sink alone); a cut unit merges its pieces head by head:
-// M = max lse_i, out = sum e^(lse_i - M) o_i / sum e^(lse_i - M), lse = M + ln sum e^(lse_i - M).
-// The H heads of a piece are H*D contiguous floats; each thread takes a 16-byte slice of every
-// RPS-th piece (one pass, a running max per slice, the piece's lse loaded with its slice), and
-// the row slots then meet in LDS with the same rule.
-// The kernel is latency-bound, and at these sizes dealing out its workgroups weighs: with
-// H = min(G, 256 / D) (two workgroups per unit at D = 128, G = 4) it took 7.45 us on the
-// 128-sequence mixed batch and 4.88 us on the Llama-8B step, against 5.76 and 4.65 us now.
+// Fix-up: one workgroup per (sequence b, KV head kvh, group of H of its G query heads).  Units
+// inside one worker were written by the decode kernel; empty units get 0 (or the sink alone); a
+// cut unit merges its pieces head by head: M = max lse_i, out = sum e^(lse_i - M) o_i /
+// sum e^(lse_i - M), lse = M + ln sum e^(lse_i - M).  The H heads of a piece are H*D contiguous
+// floats; each thread takes a 16-byte slice of every RPS-th piece (one pass, a running max per
+// slice, the piece's lse loaded with its slice), and the row slots then meet in LDS with the
+// same rule.
+// The kernel is latency-bound.  Two tilings: with few pieces per unit (workers <= 8 per unit),
+// wide workgroups, H = min(G, 1024 / D), one per unit at D = 128 for one query token, because
+// dealing out the workgroups then weighs most (7.45 -> 5.76 us on the 128-sequence mixed batch,
+// 4.88 -> 4.65 us on the Llama-8B step); with many pieces per unit (long or few sequences),
+// H = min(G, 256 / D), four piece rows in flight per step and more workgroups per unit (the wide
+// tiling took 6.7 us more on the long-context step, 64 pieces per unit).
 constexpr int kFixupThreads = 256;
 
-template <int D, int G>
+template <int D, int G, bool WIDE>
 constexpr int fixup_heads() {
-  return G < 1024 / D ? G : 1024 / D;
+  constexpr int cap = (WIDE ? 1024 : 256) / D;
+  return G < cap ? G : (cap < 1 ? 1 : cap);
 }
+// the wide tiling when a unit averages at most this many pieces
+constexpr int kFixupWideMaxWorkersPerUnit = 8;
 
-template <int D, int G>
+template <int D, int G, bool WIDE>
 __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const BalancedParams bp) {
-  constexpr int H = fixup_heads<D, G>();
+  constexpr int H = fixup_heads<D, G, WIDE>();
   constexpr int F = H * D / 4;                          // float4 slices per piece row
   constexpr int RPS = kFixupThreads / F;                // piece rows per step
   static_assert(G % H == 0 && kFixupThreads % F == 0, "fix-up tiling");
@@ -541,13 +546,21 @@ hipError_t launch_bal(const BalancedParams& bp, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int G>
-hipError_t launch_fix(const BalancedParams& bp, hipStream_t stream) {
-  hipLaunchKernelGGL((balanced_fixup_kernel<D, G>),
+template <int D, int G, bool WIDE>
+hipError_t launch_fix_t(const BalancedParams& bp, hipStream_t stream) {
+  hipLaunchKernelGGL((balanced_fixup_kernel<D, G, WIDE>),
                      dim3((unsigned)bp.d.num_seqs * (unsigned)bp.d.num_kv_heads *
-                          (unsigned)(G / fixup_heads<D, G>())),
+                          (unsigned)(G / fixup_heads<D, G, WIDE>())),
                      dim3(kFixupThreads), 0, stream, bp);
   return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_fix(const BalancedParams& bp, hipStream_t stream) {
+  const long long units = (long long)bp.d.num_seqs * bp.d.num_kv_heads;
+  if ((long long)bp.num_workers <= kFixupWideMaxWorkersPerUnit * units)
+    return launch_fix_t<D, G, true>(bp, stream);
+  return launch_fix_t<D, G, false>(bp, stream);
 }
 
 template <int D>
