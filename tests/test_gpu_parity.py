@@ -438,3 +438,36 @@ def test_balanced_many_pieces(hkv, g, workers):
     compare(*a, *oracle_full(wl), f"many pieces Hkv={hkv} g={g} workers={workers}")
     b = run_gpu(wl, t, partition_size=BALANCED, num_workers=workers)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("schedule", ["balanced", "unsplit", "partitioned"])
+def test_large_batch_of_short_sequences(schedule):
+    """2048 sequences of 0..80 tokens (16384 (sequence, KV head) units, eight per worker and
+    more), 32 q / 8 KV heads, window 50 and sinks: every unit in full against the oracle."""
+    rng = np.random.default_rng(2048)
+    lens = rng.integers(0, 81, size=2048)
+    wl = make_workload(name="large batch", seq_lens=lens, num_q_heads=32, num_kv_heads=8,
+                       head_dim=128, block_size=16, seed=[2048], window=50, with_sinks=True,
+                       poison=True)
+    t = to_dev(wl)
+    P = {"balanced": BALANCED, "unsplit": 0, "partitioned": 32}[schedule]
+    out, lse = run_gpu(wl, t, partition_size=P)
+    compare(out, lse, *oracle_full(wl), f"large batch B=2048 {schedule}")
+
+
+@pytest.mark.parametrize("schedule", ["balanced", "partitioned"])
+def test_widest_heads_largest_blocks(schedule):
+    """head_dim 256, 64 q / 8 KV heads, 256-token blocks, one length around every block edge and
+    one of 16384: sampled (sequence, head) pairs against the oracle, every output finite."""
+    wl = make_workload(name="widest", seq_lens=[16384, 1, 255, 256, 257, 9000, 0, 513],
+                       num_q_heads=64, num_kv_heads=8, head_dim=256, block_size=256,
+                       seed=[256, 64], window=0, with_sinks=True, poison=True)
+    t = to_dev(wl)
+    P = {"balanced": BALANCED, "partitioned": 512}[schedule]
+    out, lse = run_gpu(wl, t, partition_size=P)
+    pairs = sample_pairs(wl, 64, seed=256)
+    pairs = sorted(set(pairs) | {(b, h) for b in (1, 2, 3, 4, 7) for h in (0, 63)})
+    eo, el = oracle_pairs(wl, pairs)
+    idx = tuple(np.array(pairs).T)
+    compare(out[idx], lse[idx], eo, el, f"widest D=256 g=8 bs=256 {schedule}")
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
