@@ -288,6 +288,9 @@ def main() -> int:
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per sequence (> 1: causal, balanced schedule, through a "
                          "prepared plan like --kv fp8_e4m3)")
+    ap.add_argument("--seq-lens", default=None,
+                    help="replace the workload's lengths (its head geometry kept): 'BxL' for B "
+                         "sequences of L tokens, or a comma-separated list")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -316,6 +319,12 @@ def main() -> int:
     kw = {}
     if args.config == 3:
         kw = dict(head_dim=args.head_dim, num_q_heads=args.q_heads or 32)
+    if args.seq_lens:
+        if "x" in args.seq_lens:
+            nb, ln = (int(x) for x in args.seq_lens.split("x"))
+            kw["seq_lens"] = [ln] * nb
+        else:
+            kw["seq_lens"] = [int(x) for x in args.seq_lens.split(",")]
     wl = make_config(args.config, kv_format=args.kv, q_len=args.q_len, **kw)
     fp8 = args.kv != "bf16"
     qblocks = args.schedule == "query_blocks"
@@ -442,7 +451,8 @@ def main() -> int:
     del probe
 
     workload = f"config{args.config}" + (f"_d{D}_hq{Hq}" if args.config == 3 else "") + \
-        ("_fp8" if fp8 else "") + (f"_q{args.q_len}" if args.q_len > 1 else "")
+        ("_fp8" if fp8 else "") + (f"_q{args.q_len}" if args.q_len > 1 else "") + \
+        (f"_lens{args.seq_lens}" if args.seq_lens else "")
     traffic = measured_traffic(workload, args.schedule)
     res = {
         "metric": METRIC if not fp8 else METRIC.replace("bf16 d=128", "FP8 E4M3 KV d=128"),
@@ -460,7 +470,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{workload}: {wl.name}",
+            "workload": f"{workload}: {wl.name}" +
+                        (f" (lengths replaced: {args.seq_lens})" if args.seq_lens else ""),
             "batch": B, "q_heads": Hq, "kv_heads": wl.num_kv_heads, "head_dim": D,
             "block_size": wl.block_size, "window": wl.window,
             "sinks": wl.sinks is not None, "seq_len_sum": int(wl.seq_lens.sum()),

@@ -228,12 +228,16 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  *                  the same launch by whichever partition of a (sequence, KV head) finishes
  *                  last: one kernel per step, for small batches; its device-scope release per
  *                  partition makes it slow for large ones), or PA_SCHEDULE_QUERY_BLOCKS (one
- *                  one-wave workgroup per (sequence, KV head, block of 32 / (Hq/Hkv) query
- *                  tokens, 16 / (Hq/Hkv) at head_dim 256), each reading the keys its tokens
- *                  attend and writing its outputs, no merge; the blocks of a (sequence, KV head)
- *                  share the keys through one XCD's L2 when num_seqs * num_kv_heads is a
- *                  multiple of 8: chunked prefill and whole prompts; requires
- *                  shape->partition_size == 0 and needs no workspace).
+ *                  wave per (sequence, KV head, block of 32 / (Hq/Hkv) query tokens,
+ *                  16 / (Hq/Hkv) at head_dim 256), each reading the keys its tokens attend and
+ *                  writing its outputs; the blocks of a (sequence, KV head) share the keys
+ *                  through one XCD's L2 when num_seqs * num_kv_heads is a multiple of 8:
+ *                  chunked prefill and whole prompts; requires shape->partition_size == 0.
+ *                  When the batch has too few blocks to fill the GPU and max_seq_len is given,
+ *                  each block's key range is cut into up to 64 key splits whose partial outputs
+ *                  a merge kernel combines; the plan then needs a workspace of
+ *                  B * q_len * Hq * splits * (head_dim + 1) floats (256-byte aligned sections),
+ *                  and its name carries "_s<splits>".  Otherwise it needs none).
  *   kv_dtype       PA_KV_BF16, or PA_KV_FP8_E4M3: k_cache and v_cache then hold one byte per
  *                  value, [num_blocks][Hkv][block_size][head_dim] uint8, each code standing for
  *                  its E4M3 value times the tensor's scale (given per run).  The FP8 KV cache is
@@ -309,6 +313,28 @@ enum {
   PA_SCHEDULE_PARTITIONED_FUSED = 3,
   PA_SCHEDULE_QUERY_BLOCKS = 4
 };
+
+/*
+ * The schedule a plan for these sizes should use, from timings of every schedule on one MI355X
+ * over batches of 1-128 sequences, 256-16384 keys and 4-128 query tokens (HIP-graph replay of
+ * plan runs): returns a PA_SCHEDULE_* value (>= 0) and sets *partition_size to the tokens per
+ * partition for PA_SCHEDULE_PARTITIONED (256, or block_size if larger), else 0.  Negative
+ * pa_status for bad arguments (PA_ERR_NULL for a NULL partition_size, PA_ERR_UNSUPPORTED for a
+ * head_dim or block_size no kernel takes).
+ *   one query token: BALANCED when max_seq_len is 0 (unknown); UNSPLIT when the attended keys
+ *     (max_seq_len, or the window if smaller) are at most 256, or at most 1024 with at least
+ *     num_cus (sequence, KV head) units; PARTITIONED when units * keys <= 1024 * num_cus (little
+ *     work: the small-batch latency case); BALANCED otherwise, which also absorbs any spread of
+ *     lengths the bound does not show.
+ *   q_len > 1: QUERY_BLOCKS from 32 (token, head) pairs per KV head (16 at head_dim 256), and
+ *     from 17 (9) pairs when num_seqs * num_kv_heads > 32; BALANCED below.
+ *   num_cus: compute units of the target device, 0 = query the current device (PA_ERR_LAUNCH
+ *     if there is none).  Reads nothing else; launches nothing.
+ */
+int32_t paged_attn_suggest_schedule(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t window,
+                                    int32_t q_len, int32_t max_seq_len, int32_t num_cus,
+                                    int32_t* partition_size);
 
 pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,
                                  int32_t window, int32_t schedule, int32_t kv_dtype,

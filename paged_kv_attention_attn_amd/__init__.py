@@ -59,6 +59,8 @@ def _load() -> ctypes.CDLL:
         "paged_attn_status_string": (ctypes.c_char_p, [i32]),
         "paged_attn_check_tables": (i32, [sp, i32, i32, vp, vp]),
         "paged_attn_suggest_partition_size": (i32, [i32, i32, i32, i32, i32]),
+        "paged_attn_suggest_schedule": (i32, [i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                              ctypes.POINTER(i32)]),
         "paged_attn_abi_version": (i32, []),
         "paged_attn_decode_balanced": (i32, [sp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp,
                                              vp, vp, ctypes.c_size_t, i32, vp]),
@@ -91,7 +93,8 @@ EXPORTED = ("paged_attn_decode", "paged_attn_reduce", "paged_attn_decode_balance
             "paged_attn_balanced_workspace_size", "paged_attn_balanced_default_workers",
             "paged_attn_num_partitions",
             "paged_attn_variant_name", "paged_attn_status_string", "paged_attn_check_tables",
-            "paged_attn_suggest_partition_size", "paged_attn_abi_version",
+            "paged_attn_suggest_partition_size", "paged_attn_suggest_schedule",
+            "paged_attn_abi_version",
             "paged_attn_gather_witness", "paged_attn_stream_read", "paged_attn_copy",
             "paged_attn_plan_create", "paged_attn_plan_workspace_size", "paged_attn_plan_run",
             "paged_attn_plan_name", "paged_attn_plan_destroy")
@@ -117,6 +120,21 @@ def suggest_partition_size(num_seqs: int, num_kv_heads: int, max_seq_len: int, b
                            num_cus: int) -> int:
     return int(_lib.paged_attn_suggest_partition_size(num_seqs, num_kv_heads, max_seq_len,
                                                       block_size, num_cus))
+
+
+def suggest_schedule(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     block_size: int, *, window: int = 0, q_len: int = 1, max_seq_len: int = 0,
+                     num_cus: int = 0) -> Tuple[str, int]:
+    """(schedule name, partition_size) the library suggests for a plan of these sizes
+    (paged_attn_suggest_schedule; num_cus 0 = the current device's)."""
+    P = ctypes.c_int32(0)
+    r = int(_lib.paged_attn_suggest_schedule(int(num_seqs), int(num_q_heads), int(num_kv_heads),
+                                             int(head_dim), int(block_size), int(window),
+                                             int(q_len), int(max_seq_len), int(num_cus),
+                                             ctypes.byref(P)))
+    if r < 0:
+        raise PagedAttnError(r, "paged_attn_suggest_schedule")
+    return {v: k for k, v in SCHEDULES.items()}[r], int(P.value)
 
 
 def make_shape(num_seqs: int, num_q_heads: int, num_kv_heads: int, num_blocks: int,
@@ -378,7 +396,10 @@ class Plan:
     (partitioned, merged in the same launch by the last partition to finish), "balanced"
     (``num_workers``, 0 = the device default; ``max_seq_len``, a bound on the lengths, caps the
     workers of a small batch) or "query_blocks" (several query tokens: one wave per (sequence,
-    KV head, block of tokens), no workspace).  ``kv_dtype`` is "bf16" or "fp8_e4m3" (KV pools
+    KV head, block of tokens); with ``max_seq_len`` given and too few blocks to fill the GPU,
+    key splits merged by a second kernel, which take a workspace), or "auto": the schedule and
+    partition size suggest_schedule() gives for these sizes on the current device (the chosen
+    one is in ``schedule``).  ``kv_dtype`` is "bf16" or "fp8_e4m3" (KV pools
     of one byte per value, uint8 tensors, with per-tensor scales given to run()).
     ``kv_layout``: None for the pool [num_blocks][Hkv][bs][D], else (block, head, token) strides
     in elements of the cache type (pa_kv_layout).
@@ -392,8 +413,13 @@ class Plan:
                  max_seq_len: Optional[int] = None, num_workers: int = 0,
                  kv_dtype: str = "bf16", q_len: int = 1,
                  kv_layout: Optional[Tuple[int, int, int]] = None):
+        if schedule == "auto":
+            schedule, partition_size = suggest_schedule(
+                num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, window=window,
+                q_len=q_len, max_seq_len=max_seq_len or 0)
         if schedule not in SCHEDULES:
-            raise ValueError(f"schedule must be one of {sorted(SCHEDULES)}")
+            raise ValueError(f"schedule must be 'auto' or one of {sorted(SCHEDULES)}")
+        self.schedule = schedule
         if kv_dtype not in KV_DTYPES:
             raise ValueError(f"kv_dtype must be one of {sorted(KV_DTYPES)}")
         self.kv_dtype = kv_dtype

@@ -10,6 +10,7 @@
 // ROCm/rocm-libraries PR #13700 "prepare saved paged decode bindings once", review finding N1.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -597,11 +598,19 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   } else if (qblocks) {
     pl->qb = pa::QBlockParams{};
     pl->qb.d = p;
-    pa::qblock_geometry(pl->qb, head_dim);
+    pa::qblock_geometry(pl->qb, head_dim, max_seq_len);
     pl->group = pa::qblock_columns(head_dim);
-    std::snprintf(pl->name, sizeof(pl->name), "pa_qblock_%s_d%d_g%d_q%d_t%d_w%d%s",
+    if (pl->qb.splits > 1) {
+      // key splits: normalised partial outputs, then their LSEs
+      const size_t slots = (size_t)shape->num_seqs * q_len * shape->num_q_heads * pl->qb.splits;
+      pl->part_bytes = align256(slots * head_dim * sizeof(float));
+      pl->workspace_bytes = (int64_t)(pl->part_bytes + align256(slots * sizeof(float)));
+    }
+    char splits[16] = "";
+    if (pl->qb.splits > 1) std::snprintf(splits, sizeof(splits), "_s%d", pl->qb.splits);
+    std::snprintf(pl->name, sizeof(pl->name), "pa_qblock_%s_d%d_g%d_q%d_t%d_w%d%s%s",
                   pa::qk_path_name(path), head_dim, group, q_len, pl->qb.tokens_per_block,
-                  pl->qb.waves, pl->qb.xcd_pinned ? "_xcd" : "");
+                  pl->qb.waves, splits, pl->qb.xcd_pinned ? "_xcd" : "");
   } else if (schedule == PA_SCHEDULE_PARTITIONED) {
     const size_t rows = (size_t)shape->num_seqs * shape->num_q_heads * shape->max_partitions;
     pl->part_bytes = align256(rows * head_dim * sizeof(float));
@@ -649,6 +658,48 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
 }  // namespace
 
 extern "C" {
+
+int32_t paged_attn_suggest_schedule(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t window,
+                                    int32_t q_len, int32_t max_seq_len, int32_t num_cus,
+                                    int32_t* partition_size) {
+  if (partition_size == nullptr) return PA_ERR_NULL;
+  *partition_size = 0;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      window < 0 || q_len < 1 || max_seq_len < 0 || num_cus < 0)
+    return PA_ERR_SHAPE;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess ||
+        num_cus <= 0)
+      return PA_ERR_LAUNCH;
+  }
+  const int64_t group = num_q_heads / num_kv_heads;
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  if (q_len > 1) {
+    // Query blocks from a full block of (token, head) pairs up; below half a block the balanced
+    // schedule's one pass reads each tile once for all pairs at less cost, and up to a block it
+    // still wins while the batch is small.
+    const int64_t cols = max_columns(head_dim), pairs = (int64_t)q_len * group;
+    if (group > cols || pairs <= cols / 2 || (pairs <= cols && units <= 32))
+      return PA_SCHEDULE_BALANCED;
+    return PA_SCHEDULE_QUERY_BLOCKS;
+  }
+  if (max_seq_len == 0) return PA_SCHEDULE_BALANCED;   // nothing known: the robust choice
+  const int64_t keys = window > 0 ? std::min<int64_t>(max_seq_len, window) : max_seq_len;
+  // one workgroup per (sequence, KV head) when every range is short and the units cover the
+  // CUs (or there is a single 256-token range anyway)
+  if (keys <= 256 || (keys <= 1024 && units >= num_cus)) return PA_SCHEDULE_UNSPLIT;
+  // little work in all (at most 1024 keys per CU): fixed 256-token partitions start fastest
+  if (units * keys <= (int64_t)1024 * num_cus) {
+    *partition_size = std::max<int32_t>(256, block_size);
+    return PA_SCHEDULE_PARTITIONED;
+  }
+  return PA_SCHEDULE_BALANCED;   // the rest, and any spread of lengths
+}
 
 pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_t block_size,
                                  int32_t window, int32_t schedule, int32_t kv_dtype,
@@ -717,6 +768,11 @@ pa_status paged_attn_plan_run(const pa_plan* plan, const void* q, const void* k_
     qp.d = p;
     qp.d.out = out;
     qp.d.lse = lse;
+    if (qp.splits > 1) {
+      char* ws = static_cast<char*>(workspace);
+      qp.part_out = reinterpret_cast<float*>(ws);
+      qp.part_lse = reinterpret_cast<float*>(ws + plan->part_bytes);
+    }
     e = pa::launch_qblock(qp, plan->head_dim, plan->path, s);
   } else if (plan->schedule == PA_SCHEDULE_PARTITIONED_FUSED) {
     char* ws = static_cast<char*>(workspace);

@@ -68,18 +68,25 @@ struct BalancedParams {
   int32_t num_workers;        // N, one wave each
 };
 
-// Query-block grid for several query tokens per sequence: one one-wave workgroup per
-// (sequence, KV head, block of tokens_per_block query tokens), each streaming the keys its
-// tokens attend and writing its outputs; no split, no merge.
+// Query-block grid for several query tokens per sequence: one workgroup per (sequence, KV head,
+// waves blocks of tokens_per_block query tokens, key split), each streaming its share of the
+// keys its tokens attend.  With one split it writes the outputs; with several, each split writes
+// a normalised partial output and its LSE, and the merge kernel combines them.
 struct QBlockParams {
   DecodeParams d;             // q_total = query tokens per sequence; q_len and q_first unused
   int32_t tokens_per_block;   // columns per wave / group
   int32_t waves;              // waves per workgroup, each one block of tokens (1, or 4 sharing
                               // the K/V tiles through LDS)
-  int32_t blocks_per_seq;     // workgroups per (sequence, KV head):
+  int32_t blocks_per_seq;     // workgroup blocks per (sequence, KV head):
                               // ceil(q_total / (tokens_per_block * waves))
   int32_t xcd_pinned;         // 1: every workgroup of a (sequence, KV head) on one XCD
-  uint32_t grid;              // workgroups launched
+  int32_t splits;             // key splits per workgroup block (1 = none)
+  int32_t split_tiles;        // splits > 1: tiles per split, counted from the first tile of the
+                              // workgroup's key range; the last split takes the rest
+  uint32_t grid;              // workgroups launched: units * blocks_per_seq * splits (rounded
+                              // up to whole XCD rounds when xcd_pinned)
+  float* part_out;            // splits > 1: [B * q_total * Hq][splits][D] normalised partials
+  float* part_lse;            // splits > 1: [B * q_total * Hq][splits] (natural log, no sink)
 };
 
 struct ReduceParams {
@@ -144,7 +151,10 @@ int balanced_default_workers(int head_dim, int group, QkPath path, bool multi = 
 // Query-block grid: (token, head) columns per wave (32 at head_dim <= 128, 16 at 256; the
 // matrix-core P.V paths only), the grid for the shape, and the launch.
 int qblock_columns(int head_dim);
-void qblock_geometry(QBlockParams& qp, int head_dim);
+// Fills tokens_per_block, waves, blocks_per_seq, xcd_pinned, splits, split_tiles and grid;
+// max_seq_len (a host-side bound on the lengths, 0 if unknown) sizes the key splits.
+void qblock_geometry(QBlockParams& qp, int head_dim, int max_seq_len);
+// The query-block kernels, then (splits > 1) the merge of the partials into d.out / d.lse.
 hipError_t launch_qblock(const QBlockParams& qp, int head_dim, QkPath path, hipStream_t stream);
 
 hipError_t launch_witness(const WitnessParams& p, int head_dim, int num_seqs, hipStream_t stream);

@@ -5,8 +5,10 @@
 // and 16 at 256, so tokens_per_block = columns / group.  A wave folds the 16-token K/V tiles its
 // tokens attend (the union of their causal, windowed ranges) into its columns, forming q.k and
 // P.V on the matrix cores exactly as the one-token kernels do (each column masked to its own
-// token's range inside the shared tiles), and writes its outputs and LSEs: nothing is split,
-// so nothing is merged.  Two forms:
+// token's range inside the shared tiles), and writes its outputs and LSEs.  When a batch has
+// too few blocks to fill the GPU (one or a few sequences), each block's key range is cut into
+// key splits, one workgroup each, that write normalised partial outputs and LSEs; a merge
+// kernel then combines each row's splits by the log-sum-exp rule and folds the sink.  Two forms:
 //   - qblock_lds_kernel: four waves per workgroup, four consecutive blocks of one (sequence,
 //     KV head), sharing every tile through an LDS ring (used from four blocks per sequence);
 //   - qblock_kernel: one wave per block, loading its own tiles (fewer blocks).
@@ -23,6 +25,8 @@
 // here") leaves out and ROCm/rocm-libraries PR #13700 "prepare saved paged decode bindings
 // once" fixes at one token; the causal rule is this library's reading.  Sinks: randomvariable/
 // vllm issue #23, table "Current state" (a sink logit joins the softmax with a zero value row).
+#include <algorithm>
+
 #include "pa_device.hpp"
 #include "pa_kernels.hpp"
 #include "pa_qk.hpp"
@@ -32,15 +36,20 @@ namespace pa {
 namespace {
 
 constexpr int kXcds = 8;
+// key splits (small batches): waves aimed for, tiles per split at least, splits at most
+constexpr long long kQbTargetWaves = 2048;
+constexpr long long kQbMinSplitTiles = 8;
+constexpr int kQbMaxSplits = 64;
 
 struct QBlockItem {
-  int b, kvh, qb;
+  int b, kvh, qb, split;
 };
 
-// The (sequence, KV head, query block) of this workgroup; false for an idle id.
+// The (sequence, KV head, query block, key split) of this workgroup; false for an idle id.
+// Within a (sequence, KV head) the splits of one block are consecutive ids.
 __device__ __forceinline__ bool qblock_item(const QBlockParams& qp, QBlockItem& it) {
   const int U = qp.d.num_seqs * qp.d.num_kv_heads;
-  const int nqb = qp.blocks_per_seq;
+  const int nqb = qp.blocks_per_seq * qp.splits;
   const unsigned id = blockIdx.x;
   unsigned u, j;
   if (qp.xcd_pinned) {
@@ -56,15 +65,61 @@ __device__ __forceinline__ bool qblock_item(const QBlockParams& qp, QBlockItem& 
   if (u >= (unsigned)U) return false;
   it.b = (int)(u / (unsigned)qp.d.num_kv_heads);
   it.kvh = (int)(u - (unsigned)it.b * (unsigned)qp.d.num_kv_heads);
-  it.qb = nqb - 1 - (int)j;
+  const unsigned jb = j / (unsigned)qp.splits;
+  it.split = (int)(j - jb * (unsigned)qp.splits);
+  it.qb = qp.blocks_per_seq - 1 - (int)jb;
   return true;
+}
+
+// Restricts a key range (tiles t0 .. t0 + T - 1) to its key split: split k takes split_tiles
+// tiles from t0 + k * split_tiles, the last one everything after.
+__device__ __forceinline__ void clip_to_split(const QBlockParams& qp, int split, SeqSpan& s) {
+  if (qp.splits == 1) return;
+  const int lo = split * qp.split_tiles;
+  const int hi = split == qp.splits - 1 ? s.T : min(s.T, lo + qp.split_tiles);
+  s.t0 += lo;
+  s.T = max(0, hi - lo);
+}
+
+// Writes column n's result: with one split the final output row (sink folded, the caller's lse
+// if any), with several the split's normalised partial and its LSE.  M, lt: the column's max
+// (log2 units) and denominator; acc(e): its unnormalised output elements.
+template <int D, class ACC>
+__device__ __forceinline__ void write_column(const QBlockParams& qp, int split, size_t row, int hq,
+                                             float M, float lt, bool bad, int c, ACC acc) {
+  using RG = RowGeom<D>;
+  constexpr int E = RG::kElems;
+  const DecodeParams& p = qp.d;
+  float scale_o = 1.f;
+  if (p.sinks != nullptr && qp.splits == 1) {
+    // the sink logit joins the max and the denominator with a zero value row
+    const float s2 = p.sinks[hq] * kLog2e;
+    const float M2 = fmaxf(M, s2);
+    const float M2u = M2 == -INFINITY ? 0.f : M2;
+    scale_o = fast_exp2(M - M2u);
+    lt = fmaf(lt, scale_o, fast_exp2(s2 - M2u));
+    M = M2;
+  }
+  // lt is 0 only for a column without keys; a NaN input (lt = NaN) reaches the outputs
+  const float inv = lt != 0.f ? scale_o / lt : 0.f;
+  float lv = lt != 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
+  if (bad) lv = __builtin_nanf("");
+  float* dst;
+  if (qp.splits == 1) {
+    dst = p.out + row * D;
+    if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
+  } else {
+    const size_t slot = row * (size_t)qp.splits + split;
+    dst = qp.part_out + slot * D;
+    if (c == 0) qp.part_lse[slot] = lv;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) dst[RG::dim(c, e)] = bad ? __builtin_nanf("") : acc(e) * inv;
 }
 
 template <int D, class QK, int DEPTH, int WPE>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE)))
 void qblock_kernel(const QBlockParams qp) {
-  using RG = RowGeom<D>;
-  constexpr int E = RG::kElems;
   const DecodeParams& p = qp.d;
   QBlockItem it;
   if (!qblock_item(qp, it)) return;
@@ -75,8 +130,9 @@ void qblock_kernel(const QBlockParams qp) {
   const QShape qs{nq, p.q_total, q0, p.group};
   // this block's keys: the union of its tokens' ranges, ending at its last token's position
   const int swin = p.window > 0 ? p.window + nq - 1 : 0;
-  const SeqSpan s = seq_span(__builtin_amdgcn_readfirstlane(p.seq_lens[it.b]), swin,
-                             (int64_t)p.stride << p.bs_log2, p.q_total - q0 - nq);
+  SeqSpan s = seq_span(__builtin_amdgcn_readfirstlane(p.seq_lens[it.b]), swin,
+                       (int64_t)p.stride << p.bs_log2, p.q_total - q0 - nq);
+  clip_to_split(qp, it.split, s);
 
   const float c2 = fabsf(p.qk_scale_log2);
   const uint32_t qflip = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
@@ -141,29 +197,12 @@ void qblock_kernel(const QBlockParams qp) {
     for (int i = 0; i < 4; ++i) {
       const int nl = 4 * (lane >> 4) + i;               // column within the half
       const int n = cb + nl;
-      float M = half.col_m(nl), lt = half.col_l(nl);    // every lane takes part in the reads
+      const float M = half.col_m(nl), lt = half.col_l(nl);   // every lane takes part
       if (n < ncols) {
         const int hq = h0 + (n & (qs.group - 1));
-        float scale_o = 1.f;
-        if (p.sinks != nullptr) {
-          // the sink logit joins the max and the denominator with a zero value row
-          const float s2 = p.sinks[hq] * kLog2e;
-          const float M2 = fmaxf(M, s2);
-          const float M2u = M2 == -INFINITY ? 0.f : M2;
-          scale_o = fast_exp2(M - M2u);
-          lt = fmaf(lt, scale_o, fast_exp2(s2 - M2u));
-          M = M2;
-        }
-        // lt is 0 only for a column without keys; a NaN input (lt = NaN) reaches the outputs
-        const float inv = lt != 0.f ? scale_o / lt : 0.f;
-        float lv = lt != 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
-        if (bad) lv = __builtin_nanf("");
         const size_t row = ((size_t)it.b * qs.q_total + q0 + (n >> sh)) * p.num_q_heads + hq;
-        float* dst = p.out + row * D;
-        if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          dst[RG::dim(c, e)] = bad ? __builtin_nanf("") : half.acc(i, e) * inv;
+        write_column<D>(qp, it.split, row, hq, M, lt, bad, c,
+                        [&](int e) { return half.acc(i, e); });
       }
     }
   };
@@ -201,8 +240,6 @@ __device__ __forceinline__ void copy_piece_to_lds(const char* src, const char* l
 template <int D, class QK, int A>
 __global__ __launch_bounds__(kQbWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void qblock_lds_kernel(const QBlockParams qp) {
-  using RG = RowGeom<D>;
-  constexpr int E = RG::kElems;
   constexpr int RB = QK::kRowBytes;
   constexpr int PR = RB / 16;                          // 16-byte pieces per row
   constexpr int TB = 2 * kTileTokens * RB;             // K rows, then V rows
@@ -227,8 +264,9 @@ void qblock_lds_kernel(const QBlockParams qp) {
   // the workgroup's tokens and the union of their keys
   const int q0w = it.qb * kQbWaves * tpb;
   const int nqw = min(kQbWaves * tpb, p.q_total - q0w);
-  const SeqSpan sw = seq_span(Lraw, p.window > 0 ? p.window + nqw - 1 : 0, cap,
-                              p.q_total - q0w - nqw);
+  SeqSpan sw = seq_span(Lraw, p.window > 0 ? p.window + nqw - 1 : 0, cap,
+                        p.q_total - q0w - nqw);
+  clip_to_split(qp, it.split, sw);
   // this wave's tokens (none for a wave past the last block) and their keys
   const int q0 = q0w + wave * tpb;
   const int nq = max(0, min(tpb, p.q_total - q0));
@@ -323,27 +361,12 @@ void qblock_lds_kernel(const QBlockParams qp) {
     for (int i = 0; i < 4; ++i) {
       const int nl = 4 * (lane >> 4) + i;
       const int n = cb + nl;
-      float M = half.col_m(nl), lt = half.col_l(nl);
+      const float M = half.col_m(nl), lt = half.col_l(nl);   // every lane takes part
       if (n < ncols) {
         const int hq = h0 + (n & (qs.group - 1));
-        float scale_o = 1.f;
-        if (p.sinks != nullptr) {
-          const float s2 = p.sinks[hq] * kLog2e;
-          const float M2 = fmaxf(M, s2);
-          const float M2u = M2 == -INFINITY ? 0.f : M2;
-          scale_o = fast_exp2(M - M2u);
-          lt = fmaf(lt, scale_o, fast_exp2(s2 - M2u));
-          M = M2;
-        }
-        const float inv = lt != 0.f ? scale_o / lt : 0.f;
-        float lv = lt != 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
-        if (bad) lv = __builtin_nanf("");
         const size_t row = ((size_t)it.b * qs.q_total + q0 + (n >> sh)) * p.num_q_heads + hq;
-        float* dst = p.out + row * D;
-        if (c == 0 && p.lse != nullptr) p.lse[row] = lv;
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          dst[RG::dim(c, e)] = bad ? __builtin_nanf("") : half.acc(i, e) * inv;
+        write_column<D>(qp, it.split, row, hq, M, lt, bad, c,
+                        [&](int e) { return half.acc(i, e); });
       }
     }
   };
@@ -353,6 +376,65 @@ void qblock_lds_kernel(const QBlockParams qp) {
   } else {
     finish_half(qk, 0);
   }
+}
+
+// Merge of the key splits: one wave per output row (sequence, token, query head).  Over the
+// splits with a finite LSE l_k: M = max l_k, w_k = e^(l_k - M), out = sum w_k o_k / sum w_k and
+// lse = M + ln sum w_k, the log-sum-exp rule of split-KV decode (ROCm/rocm-libraries PR #13700,
+// the reducer's output and LSE arguments); the sink logit, when given, joins M and the
+// denominator with a zero output row.  A NaN partial LSE (a bad length or table entry, a NaN key)
+// makes the row NaN; a row with no keys and no sink gets out 0, lse -inf.
+constexpr int kMergeRows = 4;   // rows (waves) per workgroup
+
+template <int D>
+__global__ __launch_bounds__(kMergeRows * kWave) void qblock_merge_kernel(const QBlockParams qp) {
+  constexpr int E = D / kWave;   // contiguous floats per lane: 1, 2 or 4
+  const DecodeParams& p = qp.d;
+  const size_t rows = (size_t)p.num_seqs * p.q_total * p.num_q_heads;
+  const size_t row = (size_t)blockIdx.x * kMergeRows +
+                     (size_t)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (row >= rows) return;
+  const int lane = threadIdx.x % kWave;
+  const int S = qp.splits;
+  const float* lp = qp.part_lse + row * S;
+  const float* op = qp.part_out + row * S * D + lane * E;
+  float m = -INFINITY, den = 0.f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  bool nan = false;
+#pragma unroll 4
+  for (int k = 0; k < S; ++k) {
+    const float l = lp[k] * kLog2e;
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = op[(size_t)k * D + e];
+    nan = nan || l != l;
+    if (l > -INFINITY) {   // false for NaN and for an empty split
+      const float mn = fmaxf(m, l);
+      const float a = fast_exp2(m - mn), w = fast_exp2(l - mn);
+      den = fmaf(den, a, w);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(acc[e], a, w * o[e]);
+      m = mn;
+    }
+  }
+  if (p.sinks != nullptr) {
+    const float s2 = p.sinks[row % p.num_q_heads] * kLog2e;
+    const float M2 = fmaxf(m, s2);
+    const float M2u = M2 == -INFINITY ? 0.f : M2;
+    const float a = fast_exp2(m - M2u);
+    den = fmaf(den, a, fast_exp2(s2 - M2u));
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= a;
+    m = M2;
+  }
+  const float inv = den != 0.f ? 1.f / den : 0.f;
+  float lv = den != 0.f ? (m + fast_log2(den)) * kLn2 : -INFINITY;
+  if (nan) lv = __builtin_nanf("");
+  if (lane == 0 && p.lse != nullptr) p.lse[row] = lv;
+  float* dst = p.out + row * D + lane * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) dst[e] = nan ? __builtin_nanf("") : acc[e] * inv;
 }
 
 template <int D>
@@ -390,11 +472,20 @@ hipError_t launch_d(const QBlockParams& qp, QkPath path, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_merge(const QBlockParams& qp, hipStream_t stream) {
+  const size_t rows = (size_t)qp.d.num_seqs * qp.d.q_total * qp.d.num_q_heads;
+  const size_t grid = (rows + kMergeRows - 1) / kMergeRows;
+  hipLaunchKernelGGL((qblock_merge_kernel<D>), dim3((uint32_t)grid), dim3(kMergeRows * kWave), 0,
+                     stream, qp);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int qblock_columns(int head_dim) { return head_dim <= 128 ? 32 : 16; }
 
-void qblock_geometry(QBlockParams& qp, int head_dim) {
+void qblock_geometry(QBlockParams& qp, int head_dim, int max_seq_len) {
   const int cols = qblock_columns(head_dim);
   qp.tokens_per_block = cols / qp.d.group;
   // the workgroup form once there are blocks for all its waves; one wave per block otherwise
@@ -404,19 +495,44 @@ void qblock_geometry(QBlockParams& qp, int head_dim) {
   qp.blocks_per_seq = (qp.d.q_total + per_wg - 1) / per_wg;
   const long long units = (long long)qp.d.num_seqs * qp.d.num_kv_heads;
   qp.xcd_pinned = units % kXcds == 0 ? 1 : 0;
-  const long long grid = qp.xcd_pinned
-                             ? (units / kXcds) * kXcds * qp.blocks_per_seq
-                             : units * qp.blocks_per_seq;
+  // Key splits: with few workgroups (small batches) each one's key range is cut into up to
+  // kQbMaxSplits splits of at least kQbMinSplitTiles tiles, so that about kQbTargetWaves waves
+  // run; a merge then combines each row's partials.  Sized from the longest range a workgroup
+  // can attend (the length bound, within the window plus its tokens); a longer range only makes
+  // the last split longer.
+  qp.splits = 1;
+  qp.split_tiles = 0;
+  const long long waves_now = units * qp.blocks_per_seq * qp.waves;
+  if (max_seq_len > 0 && waves_now > 0 && waves_now < kQbTargetWaves) {
+    long long keys = max_seq_len;
+    if (qp.d.window > 0) keys = std::min(keys, (long long)qp.d.window + per_wg - 1);
+    const long long tiles = (keys + kTileTokens - 1) / kTileTokens + 1;   // one straddled tile
+    long long want = (kQbTargetWaves + waves_now - 1) / waves_now;
+    want = std::min(want, std::min(tiles / kQbMinSplitTiles, (long long)kQbMaxSplits));
+    if (want > 1) {
+      qp.split_tiles = (int)((tiles + want - 1) / want);
+      qp.splits = (int)((tiles + qp.split_tiles - 1) / qp.split_tiles);
+    }
+  }
+  const long long per_unit = (long long)qp.blocks_per_seq * qp.splits;
+  const long long grid = qp.xcd_pinned ? (units / kXcds) * kXcds * per_unit : units * per_unit;
   qp.grid = (uint32_t)grid;
 }
 
 hipError_t launch_qblock(const QBlockParams& qp, int head_dim, QkPath path, hipStream_t stream) {
   if (qp.grid == 0) return hipSuccess;
+  hipError_t e;
   switch (head_dim) {
-    case 64: return launch_d<64>(qp, path, stream);
-    case 128: return launch_d<128>(qp, path, stream);
-    case 256: return launch_d<256>(qp, path, stream);
+    case 64: e = launch_d<64>(qp, path, stream); break;
+    case 128: e = launch_d<128>(qp, path, stream); break;
+    case 256: e = launch_d<256>(qp, path, stream); break;
     default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess || qp.splits == 1) return e;
+  switch (head_dim) {
+    case 64: return launch_merge<64>(qp, stream);
+    case 128: return launch_merge<128>(qp, stream);
+    default: return launch_merge<256>(qp, stream);
   }
 }
 

@@ -269,6 +269,84 @@ def test_query_block_plans():
     assert plan_create(shape(), schedule=4, q_len=3, head_dim=96)[0] == -3
 
 
+
+def test_query_block_key_splits():
+    """Small batches cut each block's key range into key splits (about 2048 waves in all, at
+    least 8 tiles a split, at most 64 splits) and take a workspace for the partials."""
+    a = lambda x: (x + 255) // 256 * 256
+
+    def check(s, q_len, max_len, window=0, head_dim=128):
+        st, h = plan_create(s, schedule=4, q_len=q_len, max_len=max_len, window=window,
+                            head_dim=head_dim)
+        assert st == 0
+        name = pa.lib().paged_attn_plan_name(h).decode()
+        ws = pa.lib().paged_attn_plan_workspace_size(h)
+        pa.lib().paged_attn_plan_destroy(h)
+        return name, ws
+
+    # B2, 2 KV heads, group 4, 70 tokens: 3 workgroups of four waves per (sequence, KV head),
+    # 48 waves; 8192 keys = 513 tiles (one straddled) -> 43 splits of 12 tiles
+    name, ws = check(shape(), 70, 8192)
+    assert name == "pa_qblock_mfmapv_d128_g4_q70_t8_w4_s43"
+    slots = 2 * 70 * 8 * 43
+    assert ws == a(slots * 128 * 4) + a(slots * 4)
+    # one token per block at the most: 2 blocks of 4 tokens, 8 waves -> capped at 64 splits
+    name, ws = check(shape(), 5, 131072, head_dim=256)
+    assert name.endswith("_w1_s64")
+    assert ws == a(2 * 5 * 8 * 64 * 256 * 4) + a(2 * 5 * 8 * 64 * 4)
+    # unknown lengths, short lengths, a short window, a large batch: no split, no workspace
+    for s_, q, L, w in ((shape(), 70, 0, 0), (shape(), 2, 64, 0), (shape(), 70, 8192, 100),
+                        (shape(num_seqs=512, block_table_stride=8), 70, 8192, 0)):
+        name, ws = check(s_, q, L, w)
+        assert "_s" not in name.replace("_xcd", "") and ws == 0, (name, ws)
+
+
+# (B, Hq, Hkv, D, bs, window, q_len, max_seq_len) -> (schedule, partition_size) on 256 CUs
+SUGGESTIONS = [
+    ((2, 4, 2, 128, 16, 0, 1, 100), ("unsplit", 0)),          # tiny: one short range each
+    ((128, 32, 8, 128, 16, 0, 1, 256), ("unsplit", 0)),
+    ((32, 32, 8, 128, 16, 0, 1, 1024), ("unsplit", 0)),       # 256 units cover the CUs
+    ((1, 32, 8, 128, 16, 0, 1, 2048), ("partitioned", 256)),  # little work: latency case
+    ((4, 32, 4, 128, 16, 0, 1, 16384), ("partitioned", 256)),  # 16 units x 16384 = 1024 / CU
+    ((4, 32, 4, 128, 64, 0, 1, 16384), ("partitioned", 256)),
+    ((1, 32, 8, 128, 256, 0, 1, 2048), ("partitioned", 256)),
+    ((4, 32, 8, 128, 16, 0, 1, 16384), ("balanced", 0)),      # 32 units x 16384: past that
+    ((64, 32, 8, 128, 16, 0, 1, 4096), ("balanced", 0)),      # the Llama-8B-shaped step
+    ((128, 32, 8, 128, 16, 4096, 1, 32768), ("balanced", 0)),  # window 4096
+    ((128, 32, 8, 128, 16, 200, 1, 32768), ("unsplit", 0)),   # the window bounds the keys
+    ((64, 32, 8, 128, 16, 0, 1, 0), ("balanced", 0)),         # no bound given
+    ((1, 32, 8, 128, 16, 0, 4, 8192), ("balanced", 0)),       # 16 pairs: one balanced pass
+    ((1, 32, 8, 128, 16, 0, 8, 8192), ("balanced", 0)),       # 32 pairs, small batch
+    ((16, 32, 8, 128, 16, 0, 8, 2048), ("query_blocks", 0)),  # 32 pairs, 128 units
+    ((1, 32, 8, 128, 16, 0, 16, 8192), ("query_blocks", 0)),
+    ((1, 32, 8, 256, 16, 0, 4, 8192), ("balanced", 0)),       # 16 pairs fill a D=256 block,
+    ((16, 32, 8, 256, 16, 0, 4, 8192), ("query_blocks", 0)),  # a small batch stays balanced
+    ((1, 32, 8, 256, 16, 0, 2, 8192), ("balanced", 0)),
+    ((1, 64, 2, 128, 16, 0, 2, 8192), ("query_blocks", 0)),   # group 32: one token a block
+    ((1, 128, 2, 128, 16, 0, 2, 8192), ("balanced", 0)),      # group 64 > a block's columns
+]
+
+
+@pytest.mark.parametrize("args,expected", SUGGESTIONS)
+def test_suggest_schedule(args, expected):
+    B, Hq, Hkv, D, bs, W, Q, L = args
+    assert pa.suggest_schedule(B, Hq, Hkv, D, bs, window=W, q_len=Q, max_seq_len=L,
+                               num_cus=256) == expected
+
+
+def test_suggest_schedule_rejects_bad_arguments():
+    P = ctypes.c_int32(7)
+    f = pa.lib().paged_attn_suggest_schedule
+    assert f(1, 32, 8, 128, 16, 0, 1, 100, 256, None) == -1              # PA_ERR_NULL
+    assert f(1, 30, 8, 128, 16, 0, 1, 100, 256, ctypes.byref(P)) == -2   # Hq % Hkv
+    assert P.value == 0
+    assert f(1, 32, 8, 128, 16, -1, 1, 100, 256, ctypes.byref(P)) == -2  # window
+    assert f(1, 32, 8, 128, 16, 0, 0, 100, 256, ctypes.byref(P)) == -2   # q_len
+    assert f(1, 32, 8, 96, 16, 0, 1, 100, 256, ctypes.byref(P)) == -3    # head_dim
+    assert f(1, 32, 8, 128, 24, 0, 1, 100, 256, ctypes.byref(P)) == -3   # block size
+    with pytest.raises(ValueError):
+        pa.Plan(1, 32, 8, 10, 8, 128, 16, schedule="fastest")
+
 def test_plan_create_and_workspace_sizes():
     a = lambda x: (x + 255) // 256 * 256
     st, h = plan_create(shape())

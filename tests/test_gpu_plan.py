@@ -148,3 +148,33 @@ def test_plan_length_bound_caps_workers_and_a_violated_bound_stays_correct():
     exp = oracle_full(wl)
     compare(*run_plan(capped, wl, t), *exp, f"plan {capped.name}")
     compare(*run_plan(low, wl, t), *exp, f"plan {low.name} (bound below the lengths)")
+
+
+def auto_workload(case):
+    if case == "tiny":
+        return make_config(1, poison=True), "unsplit"
+    if case == "context":
+        return context_workload(1, 2048), "partitioned"
+    if case == "llama":
+        return make_config(2, poison=True), "balanced"
+    if case == "mixed":
+        return make_config(5, poison=True, seq_lens=[5000, 17, 9000, 4096, 1, 300, 0]), \
+            "partitioned"
+    Q = {"q4": 4, "q16": 16}[case]
+    wl = make_workload(name=f"auto {case}", seq_lens=[3000, 17, 600, Q - 1], num_q_heads=32,
+                       num_kv_heads=8, head_dim=128, block_size=16, seed=[12, Q],
+                       with_sinks=True, poison=True, q_len=Q)
+    return wl, ("balanced" if Q == 4 else "query_blocks")
+
+
+@pytest.mark.parametrize("case", ["tiny", "context", "llama", "mixed", "q4", "q16"])
+def test_auto_schedule(case):
+    """schedule="auto" takes the library's suggestion for the sizes (on this device) and runs
+    it: the expected schedule, and the oracle's results."""
+    wl, expected = auto_workload(case)
+    plan = pa.Plan(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.stride,
+                   wl.head_dim, wl.block_size, window=wl.window, schedule="auto",
+                   max_seq_len=int(wl.seq_lens.max()), q_len=wl.q_len)
+    log(f"[auto] {case}: {plan.schedule} {plan.name}")
+    assert plan.schedule == expected
+    compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl), f"auto {case} -> {plan.name}")

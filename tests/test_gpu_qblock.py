@@ -45,7 +45,8 @@ def test_qblock_edges(D, g, Q, kv):
     wl = qb_workload(D, g, Q, window=0 if (g + Q) % 2 else 11, sinks=(g * Q) % 3 == 0, kv=kv)
     plan = make_plan(wl, "query_blocks")
     log(f"[qblock] {plan.name}")
-    assert plan.name.startswith("pa_qblock_") and plan.workspace_size == 0
+    assert plan.name.startswith("pa_qblock_")
+    assert (plan.workspace_size > 0) == ("_s" in plan.name.replace("_xcd", ""))
     compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl),
             f"qblock D={D} g={g} Q={Q} kv={kv} W={wl.window} sinks={wl.sinks is not None}")
 
@@ -124,20 +125,22 @@ def test_qblock_bad_table_entry_gives_nan_for_that_sequence_only():
 
 
 def test_qblock_graph_replay_matches_eager():
-    wl = qb_workload(128, 4, 33, window=20, sinks=True, lens=[100, 33, 500, 7], seed=5)
+    wl = qb_workload(128, 4, 33, window=200, sinks=True, lens=[100, 33, 500, 7], seed=5)
     t = to_dev(wl)
     plan = make_plan(wl, "query_blocks")
+    assert "_s" in plan.name   # key splits and their merge, captured together
+    ws = plan.workspace("cuda")
     args = (t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale))
     out = torch.empty(wl.q.shape, device="cuda")
     lse = torch.empty(wl.q.shape[:-1], device="cuda")
-    plan.run(*args, out=out, lse=lse, sinks=t["sinks"])
+    plan.run(*args, out=out, lse=lse, sinks=t["sinks"], workspace=ws)
     torch.cuda.synchronize()
     ref_out, ref_lse = out.clone(), lse.clone()
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            plan.run(*args, out=out, lse=lse, sinks=t["sinks"])
+            plan.run(*args, out=out, lse=lse, sinks=t["sinks"], workspace=ws)
     torch.cuda.synchronize()
     for _ in range(3):
         out.fill_(float("nan"))
@@ -157,3 +160,46 @@ def test_qblock_plan_rejects_unsupported_requests():
         pa.Plan(2, 8, 2, wl.num_blocks, wl.stride, 128, 16, schedule="query_blocks", q_len=0)
     with pytest.raises(pa.PagedAttnError):
         pa.Plan(2, 8, 2, wl.num_blocks, wl.stride, 128, 16, schedule="query_blocks", q_len=4097)
+
+
+def plan_without_bound(wl):
+    """A query-block plan with no length bound: never key splits."""
+    return pa.Plan(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.stride,
+                   wl.head_dim, wl.block_size, window=wl.window, schedule="query_blocks",
+                   max_seq_len=0, kv_dtype=wl.kv_format, q_len=wl.q_len)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("D,g,Q", [(64, 2, 100), (128, 4, 70), (128, 8, 5), (256, 4, 9),
+                                   (256, 8, 2)])
+def test_qblock_with_and_without_key_splits(D, g, Q, kv):
+    """The same small batch with and without key splits: both against the oracle, and within
+    fp32 rounding of each other."""
+    wl = qb_workload(D, g, Q, window=0 if Q % 2 else 1500, sinks=True, kv=kv,
+                     lens=[0, 1, Q, Q + 1, 300, 1000, 4100], seed=9)
+    t = to_dev(wl)
+    split = make_plan(wl, "query_blocks")
+    whole = plan_without_bound(wl)
+    log(f"[qblock] {split.name} / {whole.name}")
+    assert "_s" in split.name and whole.workspace_size == 0
+    assert "_s" not in whole.name.replace("_xcd", "")
+    a = run_plan(split, wl, t)
+    b = run_plan(whole, wl, t)
+    ref = oracle_full(wl)
+    compare(*a, *ref, f"qblock split D={D} g={g} Q={Q} kv={kv}")
+    compare(*b, *ref, f"qblock whole D={D} g={g} Q={Q} kv={kv}")
+    fin = np.isfinite(a[1])
+    assert np.array_equal(fin, np.isfinite(b[1]))
+    assert np.abs(a[0] - b[0]).max() <= 1e-4 and np.abs(a[1][fin] - b[1][fin]).max() <= 1e-4
+
+
+def test_qblock_key_splits_with_lengths_above_the_bound():
+    """Lengths above the plan's bound: the last split takes the rest of the keys."""
+    wl = qb_workload(128, 4, 40, sinks=True, lens=[50, 3000, 700, 41], seed=10)
+    t = to_dev(wl)
+    plan = pa.Plan(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.stride,
+                   wl.head_dim, wl.block_size, schedule="query_blocks", max_seq_len=512,
+                   q_len=wl.q_len)
+    log(f"[qblock] {plan.name}")
+    assert "_s" in plan.name
+    compare(*run_plan(plan, wl, t), *oracle_full(wl), "qblock lengths above the bound")
