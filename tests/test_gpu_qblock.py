@@ -5,7 +5,8 @@ positions L - q_len + i.  Covered: every head size and group, token counts insid
 across many, lengths shorter than q_len (positions below 0) and zero, windows, sinks, block
 sizes, bf16 and FP8 caches, XCD-pinned and plain grids, whole-prompt prefill (q_len = L), the
 decode-batch workload (sampled), one token, a table entry outside the pool, graph replay, and
-the argument checks."""
+the argument checks.  Small batches run with key splits and their merge (plans given a length
+bound); the same batches without a bound run unsplit, and the two agree."""
 from __future__ import annotations
 
 import numpy as np
