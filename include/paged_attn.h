@@ -326,8 +326,10 @@ enum {
  *     num_cus (sequence, KV head) units; PARTITIONED when units * keys <= 1024 * num_cus (little
  *     work: the small-batch latency case); BALANCED otherwise, which also absorbs any spread of
  *     lengths the bound does not show.
- *   q_len > 1: QUERY_BLOCKS from 32 (token, head) pairs per KV head (16 at head_dim 256), and
- *     from 17 (9) pairs when num_seqs * num_kv_heads > 32; BALANCED below.
+ *   q_len > 1: QUERY_BLOCKS above 32 (token, head) pairs per KV head (16 at head_dim 256),
+ *     and from 17 (9) pairs when num_seqs * num_kv_heads > 32; BALANCED below.
+ *   PA_ERR_UNSUPPORTED as well for a group Hq/Hkv no kernel takes (1, 2, 4 and 8 are built),
+ *     since no plan could be created for it.
  *   num_cus: compute units of the target device, 0 = query the current device (PA_ERR_LAUNCH
  *     if there is none).  Reads nothing else; launches nothing.
  */

@@ -678,6 +678,8 @@ int32_t paged_attn_suggest_schedule(int32_t num_seqs, int32_t num_q_heads, int32
       return PA_ERR_LAUNCH;
   }
   const int64_t group = num_q_heads / num_kv_heads;
+  // no plan exists for a group size the kernels do not take, so suggest none
+  if (!pa::decode_supported(head_dim, (int)group)) return PA_ERR_UNSUPPORTED;
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
   if (q_len > 1) {
     // Query blocks from a full block of (token, head) pairs up; below half a block the balanced

@@ -9,6 +9,7 @@ import torch
 
 import paged_kv_attention_attn_amd as pa
 from oracle import ref
+from tests.oracle_rows import oracle_multi_triples  # noqa: F401 (re-exported)
 
 # Contract: max abs error <= 3e-2 against the fp64 oracle (bf16 inputs, fp32 accumulation).
 TOL = 3e-2
@@ -88,35 +89,6 @@ def oracle_full(wl):
                       k_scale=wl.k_scale, v_scale=wl.v_scale)
 
 
-def oracle_multi_triples(wl, triples):
-    """Oracle rows of (sequence, query token, head) triples, one by one (q_len > 1): each is the
-    one-token decode of the sequence's first L - q_len + i + 1 tokens (the causal rule, pinned
-    against decode_multi on the CPU)."""
-    outs, lses = [], []
-    Q = wl.q_len
-    for b, i, h in triples:
-        L = int(wl.seq_lens[b])
-        prefix = np.array([max(L - Q + i + 1, 0)], np.int32)
-        o, l = ref.decode_one(wl.q[b:b + 1, i], wl.k_cache, wl.v_cache, wl.block_table[b:b + 1],
-                              prefix, wl.scale, wl.block_size, 0, h, window=wl.window,
-                              sinks=wl.sinks, kv_format=wl.kv_format, k_scale=wl.k_scale,
-                              v_scale=wl.v_scale)
-        outs.append(o)
-        lses.append(l)
-    return np.array(outs), np.array(lses)
-
-
-def oracle_pairs(wl, pairs):
-    outs, lses = [], []
-    for b, h in pairs:
-        o, l = ref.decode_one(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens,
-                              wl.scale, wl.block_size, b, h, window=wl.window, sinks=wl.sinks,
-                              kv_format=wl.kv_format, k_scale=wl.k_scale, v_scale=wl.v_scale)
-        outs.append(o)
-        lses.append(l)
-    return np.array(outs), np.array(lses)
-
-
 def compare(got_out, got_lse, exp_out, exp_lse, tag: str, strict: bool = True) -> dict:
     """Element-wise comparison; asserts the contract (and the regression gates when strict)."""
     assert got_out.shape == exp_out.shape, (tag, got_out.shape, exp_out.shape)
@@ -142,15 +114,6 @@ def compare(got_out, got_lse, exp_out, exp_lse, tag: str, strict: bool = True) -
         assert lerr <= REG_ABS, f"{tag}: lse error {lerr} above the regression gate {REG_ABS}"
         assert nmse <= REG_NMSE, f"{tag}: nmse {nmse}"
     return dict(max_abs=emax, nmse=nmse, lse_max_abs=lerr)
-
-
-def sample_pairs(wl, n: int, seed: int = 0):
-    rng = np.random.default_rng(seed)
-    B, Hq = wl.num_seqs, wl.num_q_heads
-    pairs = {(int(np.argmax(wl.seq_lens)), 0), (int(np.argmin(wl.seq_lens)), Hq - 1)}
-    while len(pairs) < min(n, B * Hq):
-        pairs.add((int(rng.integers(B)), int(rng.integers(Hq))))
-    return sorted(pairs)
 
 
 def cus() -> int:

@@ -322,8 +322,7 @@ SUGGESTIONS = [
     ((1, 32, 8, 256, 16, 0, 4, 8192), ("balanced", 0)),       # 16 pairs fill a D=256 block,
     ((16, 32, 8, 256, 16, 0, 4, 8192), ("query_blocks", 0)),  # a small batch stays balanced
     ((1, 32, 8, 256, 16, 0, 2, 8192), ("balanced", 0)),
-    ((1, 64, 2, 128, 16, 0, 2, 8192), ("query_blocks", 0)),   # group 32: one token a block
-    ((1, 128, 2, 128, 16, 0, 2, 8192), ("balanced", 0)),      # group 64 > a block's columns
+    ((1, 16, 2, 128, 16, 0, 8, 8192), ("query_blocks", 0)),   # group 8: 64 pairs
 ]
 
 
@@ -344,6 +343,9 @@ def test_suggest_schedule_rejects_bad_arguments():
     assert f(1, 32, 8, 128, 16, 0, 0, 100, 256, ctypes.byref(P)) == -2   # q_len
     assert f(1, 32, 8, 96, 16, 0, 1, 100, 256, ctypes.byref(P)) == -3    # head_dim
     assert f(1, 32, 8, 128, 24, 0, 1, 100, 256, ctypes.byref(P)) == -3   # block size
+    # groups no kernel takes (plan creation rejects them too): nothing is suggested
+    for hq, hkv, q in ((64, 2, 2), (128, 2, 2), (48, 8, 1), (16, 1, 1)):
+        assert f(1, hq, hkv, 128, 16, 0, q, 8192, 256, ctypes.byref(P)) == -3, (hq, hkv)
     with pytest.raises(ValueError):
         pa.Plan(1, 32, 8, 10, 8, 128, 16, schedule="fastest")
 

@@ -125,6 +125,28 @@ def test_qblock_bad_table_entry_gives_nan_for_that_sequence_only():
     compare(out[keep], lse[keep], eo[keep], el[keep], "qblock sequences with good tables")
 
 
+def test_qblock_key_splits_bad_table_entry_and_length():
+    """A plan with key splits: a table entry outside the pool in a middle split of sequence 0,
+    and a length above what sequence 2's table row holds.  Both sequences come out NaN (their
+    splits' NaN LSEs travel through the merge); sequence 1 matches the oracle."""
+    wl = qb_workload(128, 4, 20, lens=[4000, 150, 3000], seed=12)
+    t = to_dev(wl)
+    plan = make_plan(wl, "query_blocks")
+    log(f"[qblock] {plan.name}")
+    splits = int(plan.name.split("_s")[-1].split("_")[0])
+    assert splits >= 8, plan.name
+    bt = t["bt"].clone()
+    bt[0, 120] = wl.num_blocks        # tile 120 of 250: a middle split of sequence 0
+    L = t["L"].clone()
+    L[2] = wl.stride * wl.block_size + 5
+    t["bt"], t["L"] = bt, L
+    out, lse = run_plan(plan, wl, t)
+    for b in (0, 2):
+        assert np.isnan(out[b]).all() and np.isnan(lse[b]).all(), b
+    eo, el = oracle_full(wl)
+    compare(out[[1]], lse[[1]], eo[[1]], el[[1]], "qblock split plan, the good sequence")
+
+
 def test_qblock_graph_replay_matches_eager():
     wl = qb_workload(128, 4, 33, window=200, sinks=True, lens=[100, 33, 500, 7], seed=5)
     t = to_dev(wl)

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import tests.test_oracle_pins as pins
+import tests.test_oracle_rows as rows
 from oracle import ref
 
 
@@ -63,6 +64,51 @@ def _causal_off_by_one(L, q_len, i, window):
     return start, p
 
 
+def _max_not_subtracted(qv, K, V, scale, sink=None):
+    # exp of the raw logits: the same function until a logit passes float64's exp range
+    D = V.shape[1] if V.ndim == 2 else qv.shape[0]
+    logits = scale * (K @ qv) if K.shape[0] else np.zeros(0)
+    if not logits.size and sink is None:
+        return np.zeros(D), -math.inf
+    w = np.exp(logits)
+    Z = float(w.sum()) + (math.exp(float(sink)) if sink is not None else 0.0)
+    out = (w @ V) / Z if K.shape[0] else np.zeros(D)
+    return out, math.log(Z)
+
+
+def _block_and_slot_transposed(cache, block_table, b, kvh, start, stop, block_size):
+    # the table indexed by the slot and the block read at the logical block index
+    t = np.arange(start, max(start, stop), dtype=np.int64)
+    phys = block_table[b, (t % block_size) % block_table.shape[1]].astype(np.int64)
+    return np.ascontiguousarray(cache[phys, kvh, (t // block_size) % block_size, :])
+
+
+def _tail_dropped(cache, block_table, b, kvh, start, stop, block_size):
+    # only whole blocks: the partly filled last block of the sequence is left out
+    stop = max(start, stop - stop % block_size)
+    t = np.arange(start, stop, dtype=np.int64)
+    phys = block_table[b, t // block_size].astype(np.int64)
+    return np.ascontiguousarray(cache[phys, kvh, t % block_size, :])
+
+
+_orig_decode_one = ref.decode_one
+
+
+def _decode_one_sink_by_kv_head(q, k_cache, v_cache, block_table, seq_lens, scale, block_size,
+                                b, h, window=0, sinks=None, **kw):
+    if sinks is not None:
+        g = q.shape[1] // k_cache.shape[1]
+        sinks = np.repeat(np.asarray(sinks)[::g], g)   # the first head of each group's sink
+    return _orig_decode_one(q, k_cache, v_cache, block_table, seq_lens, scale, block_size, b, h,
+                            window=window, sinks=sinks, **kw)
+
+
+def _decode_one_window_ignored(q, k_cache, v_cache, block_table, seq_lens, scale, block_size,
+                               b, h, window=0, **kw):
+    return _orig_decode_one(q, k_cache, v_cache, block_table, seq_lens, scale, block_size, b, h,
+                            window=0, **kw)
+
+
 MUTATIONS = {
     "gqa head map interleaved": ("kv_head_of", _wrong_kv_head,
                            [(pins.test_paged_equals_dense_unpaged, 0, False, 8, 2),
@@ -76,6 +122,23 @@ MUTATIONS = {
     "sink dropped": ("softmax_attention", _sink_dropped,
                      [(pins.test_sink_single_token_logistic,),
                       (pins.test_hand_worked_golden,)]),
+    "max not subtracted": ("softmax_attention", _max_not_subtracted,
+                           [(pins.test_large_logits_identical_keys_give_mean_of_v,)]),
+    "block and slot index transposed": ("gather_rows", _block_and_slot_transposed,
+                                        [(pins.test_paged_equals_dense_unpaged, 0, False, 4, 2),
+                                         (pins.test_hand_worked_golden,)]),
+    "tail of the last block dropped": ("gather_rows", _tail_dropped,
+                                       [(pins.test_paged_equals_dense_unpaged, 0, False, 4, 2),
+                                        (pins.test_seq_len_one_returns_that_v_row_exactly,)]),
+    "decode_one sink read by KV head": ("decode_one", _decode_one_sink_by_kv_head,
+                                        [(rows.test_decode_one_equals_decode_row_by_row, 8, 2, 0,
+                                          True, "bf16"),
+                                         (rows.test_oracle_pairs_equals_decode,)]),
+    "decode_one window ignored": ("decode_one", _decode_one_window_ignored,
+                                  [(rows.test_decode_one_equals_decode_row_by_row, 4, 4, 5,
+                                    False, "bf16"),
+                                   (rows.test_multi_triples_equal_decode_multi, 3, 5, True,
+                                    "bf16")]),
     "scale ignored": ("softmax_attention", _scale_ignored,
                       [(pins.test_paged_equals_dense_unpaged, 0, False, 4, 2),
                        (pins.test_hand_worked_golden,)]),

@@ -148,6 +148,25 @@ def test_identical_keys_give_mean_of_v():
             assert abs(lse[b, h] - (l + math.log(L))) < 1e-12
 
 
+def test_large_logits_identical_keys_give_mean_of_v():
+    """Logits near 1000, far past where exp overflows in float64 (about 709): identical keys
+    must still give the mean of V and lse = l + ln L.  Shift invariance of softmax is what
+    makes this finite; evaluating exp(logit) without subtracting the max cannot."""
+    wl = small([3, 16, 21], hq=2, hkv=1, d=16)
+    key = f32_to_bf16_bits(f64(wl.q[0, 0]).astype(np.float32) * 256)   # exact: a power of two
+    for b, L in enumerate(wl.seq_lens):
+        for t in range(L):
+            wl.k_cache[wl.block_table[b, t // wl.block_size], 0, t % wl.block_size] = key
+    out, lse = run(wl)
+    for b, L in enumerate(wl.seq_lens):
+        V = np.array([f64(wl.v_cache[wl.block_table[b, t // 4], 0, t % 4]) for t in range(L)])
+        l = float(wl.scale) * math.fsum(f64(wl.q[b, 0]) * f64(key))
+        if b == 0:
+            assert l > 800.0   # the case this pin is about
+        assert np.abs(out[b, 0] - V.mean(axis=0)).max() < 1e-12
+        assert abs(lse[b, 0] - (l + math.log(L))) < 1e-9
+
+
 def test_scale_zero_gives_mean_over_window():
     wl = small([30, 12], window=9, poison=True)
     out, _ = run(wl)  # sanity: finite
