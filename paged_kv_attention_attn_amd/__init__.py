@@ -23,7 +23,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
+# The in-tree build; PA_LIBRARY names another build of the same sources to load instead (the
+# sanitizer build of the host code that a CPU test runs the ABI tests against).
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpaged_attn.so")
 
 PA_OK = 0
 STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
@@ -76,7 +78,11 @@ def _load() -> ctypes.CDLL:
         "paged_attn_plan_name": (ctypes.c_char_p, [vp]),
         "paged_attn_plan_destroy": (None, [vp]),
         "paged_attn_gather_witness": (i32, [sp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]),
+        "paged_attn_gather_witness_balanced": (i32, [sp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
+                                                     i32, i32, vp, vp, vp]),
         "paged_attn_stream_read": (i32, [vp, ctypes.c_size_t, i32, vp, vp]),
+        "paged_attn_gather_read": (i32, [vp, ctypes.c_size_t, i32, vp, ctypes.c_int64, i32, vp,
+                                         vp]),
         "paged_attn_copy": (i32, [vp, vp, ctypes.c_size_t, vp]),
     }
     for name, (res, args) in sigs.items():
@@ -95,7 +101,9 @@ EXPORTED = ("paged_attn_decode", "paged_attn_reduce", "paged_attn_decode_balance
             "paged_attn_variant_name", "paged_attn_status_string", "paged_attn_check_tables",
             "paged_attn_suggest_partition_size", "paged_attn_suggest_schedule",
             "paged_attn_abi_version",
-            "paged_attn_gather_witness", "paged_attn_stream_read", "paged_attn_copy",
+            "paged_attn_gather_witness", "paged_attn_gather_witness_balanced",
+            "paged_attn_stream_read", "paged_attn_gather_read",
+            "paged_attn_copy",
             "paged_attn_plan_create", "paged_attn_plan_workspace_size", "paged_attn_plan_run",
             "paged_attn_plan_name", "paged_attn_plan_destroy")
 

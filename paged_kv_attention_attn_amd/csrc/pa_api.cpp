@@ -456,6 +456,20 @@ pa_status paged_attn_stream_read(const void* buf, size_t bytes, int32_t num_work
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+pa_status paged_attn_gather_read(const void* buf, size_t bytes, int32_t chunk_bytes,
+                                 const int32_t* chunk_ids, int64_t num_ids,
+                                 int32_t num_workgroups, uint32_t* sink, void* stream) {
+  if (buf == nullptr || sink == nullptr || (chunk_ids == nullptr && num_ids > 0))
+    return PA_ERR_NULL;
+  if (chunk_bytes != 2048 && chunk_bytes != 4096 && chunk_bytes != 8192) return PA_ERR_SHAPE;
+  if (bytes < (size_t)chunk_bytes || num_ids < 0 || num_workgroups < 1) return PA_ERR_SHAPE;
+  if (num_ids == 0) return PA_OK;
+  const hipError_t e = pa::launch_gather_read(
+      buf, (int64_t)(bytes / (size_t)chunk_bytes), chunk_bytes, chunk_ids, num_ids,
+      num_workgroups, sink, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 pa_status paged_attn_copy(void* dst, const void* src, size_t bytes, void* stream) {
   if (dst == nullptr || src == nullptr) return PA_ERR_NULL;
   if (bytes % 16 != 0) return PA_ERR_SHAPE;
@@ -496,6 +510,27 @@ constexpr int32_t kMaxQueryTokens = 4096;
 
 // Largest row stride in bytes: 16 rows of a tile stay within 32-bit lane offsets.
 constexpr int64_t kMaxRowStrideBytes = int64_t(1) << 26;
+
+// The pool layout's byte strides in p: the default [num_blocks][Hkv][bs][D] for a NULL layout,
+// else the given strides (elements of `elem` bytes), each row 16-byte aligned and rows of a block
+// at least a row apart.
+pa_status apply_kv_layout(pa::DecodeParams& p, const pa_kv_layout* kv_layout,
+                          int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                          int64_t elem) {
+  set_default_layout(p, num_kv_heads, block_size, elem * head_dim);
+  if (kv_layout == nullptr) return PA_OK;
+  const int64_t bsb = kv_layout->block_stride * elem, hsb = kv_layout->head_stride * elem,
+                rsb = kv_layout->token_stride * elem;
+  if (kv_layout->block_stride <= 0 || kv_layout->head_stride <= 0 ||
+      kv_layout->token_stride < head_dim || rsb > kMaxRowStrideBytes ||
+      kv_layout->block_stride > (int64_t(1) << 40) || kv_layout->head_stride > (int64_t(1) << 40))
+    return PA_ERR_SHAPE;
+  if (bsb % 16 != 0 || hsb % 16 != 0 || rsb % 16 != 0) return PA_ERR_SHAPE;
+  p.kv_block_stride = bsb;
+  p.kv_head_stride = hsb;
+  p.kv_row_stride = rsb;
+  return PA_OK;
+}
 
 pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size, int32_t window,
                      int32_t schedule, int32_t kv_dtype, const pa_kv_layout* kv_layout,
@@ -577,20 +612,8 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
   p.q_first = 0;
   p.group = group;
   const int64_t elem = kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2;
-  set_default_layout(p, shape->num_kv_heads, block_size, elem * head_dim);
-  if (kv_layout != nullptr) {
-    // strides in elements; every row 16-byte aligned, rows of a block at least a row apart
-    const int64_t bsb = kv_layout->block_stride * elem, hsb = kv_layout->head_stride * elem,
-                  rsb = kv_layout->token_stride * elem;
-    if (kv_layout->block_stride <= 0 || kv_layout->head_stride <= 0 ||
-        kv_layout->token_stride < head_dim || rsb > kMaxRowStrideBytes ||
-        kv_layout->block_stride > (int64_t(1) << 40) || kv_layout->head_stride > (int64_t(1) << 40))
-      return PA_ERR_SHAPE;
-    if (bsb % 16 != 0 || hsb % 16 != 0 || rsb % 16 != 0) return PA_ERR_SHAPE;
-    p.kv_block_stride = bsb;
-    p.kv_head_stride = hsb;
-    p.kv_row_stride = rsb;
-  }
+  if (apply_kv_layout(p, kv_layout, shape->num_kv_heads, block_size, head_dim, elem) != PA_OK)
+    return PA_ERR_SHAPE;
   pl->red = pa::ReduceParams{};
   const char* dname = pa::decode_variant_name(head_dim, group, waves, parted, path);
   if (schedule == PA_SCHEDULE_UNSPLIT) {
@@ -819,6 +842,54 @@ pa_status paged_attn_plan_run(const pa_plan* plan, const void* q, const void* k_
       if (e == hipSuccess) e = pa::launch_balanced_fixup(bp, plan->head_dim, plan->group, s);
     }
   }
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+pa_status paged_attn_gather_witness_balanced(const pa_shape* shape, const void* k_cache,
+                                             const void* v_cache, const int32_t* block_table,
+                                             const int32_t* seq_lens, int32_t head_dim,
+                                             int32_t block_size, int32_t window,
+                                             int32_t kv_dtype, const pa_kv_layout* kv_layout,
+                                             int32_t num_workers, int32_t max_rows, void* k_rows,
+                                             void* v_rows, void* stream) {
+  const pa_status st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+  if (window < 0 || max_rows < 1 || num_workers < 1 || num_workers > kMaxWorkers)
+    return PA_ERR_SHAPE;
+  const int64_t elem = kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2;
+  pa::BalancedParams bp{};
+  pa::DecodeParams& p = bp.d;
+  if (apply_kv_layout(p, kv_layout, shape->num_kv_heads, block_size, head_dim, elem) != PA_OK)
+    return PA_ERR_SHAPE;
+  if (shape->num_seqs == 0) return PA_OK;
+  if (k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+      seq_lens == nullptr || k_rows == nullptr || v_rows == nullptr)
+    return PA_ERR_NULL;
+  p.k_cache = static_cast<const char*>(k_cache);
+  p.v_cache = static_cast<const char*>(v_cache);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.num_seqs = shape->num_seqs;
+  p.num_q_heads = shape->num_q_heads;
+  p.num_kv_heads = shape->num_kv_heads;
+  p.num_blocks = shape->num_blocks;
+  p.stride = shape->block_table_stride;
+  p.bs_log2 = log2_exact(block_size);
+  p.window = window;
+  p.max_parts = 1;
+  p.q_len = 1;
+  p.q_total = 1;
+  p.group = shape->num_q_heads / shape->num_kv_heads;
+  bp.num_workers = num_workers;
+  const hipError_t e = pa::launch_balanced_witness(
+      bp, static_cast<char*>(k_rows), static_cast<char*>(v_rows), (int)(elem * head_dim),
+      max_rows, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -104,6 +104,85 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, int num_wg, uint32_
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// gather read: the access pattern of the decode kernels without their arithmetic.  Chunks of
+// 1024 * P bytes (a 16-token tile of one KV head: 4 KiB at head_dim 128) are read in the order of
+// a caller-given id list, each by one wave with P 16-byte non-temporal loads per lane; wave w of
+// the grid takes the contiguous share [w n / N, (w+1) n / N) of the list and keeps two chunks in
+// flight.  An id outside [0, num_chunks) is skipped, never read.
+// ---------------------------------------------------------------------------------------------
+constexpr int kGatherThreads = 256;
+
+template <int P>
+__global__ __launch_bounds__(kGatherThreads) void gather_read_kernel(
+    const char* __restrict__ buf, int64_t num_chunks, const int32_t* __restrict__ ids,
+    int64_t n_ids, uint32_t* sink) {
+  constexpr int kChunk = 1024 * P;
+  const int lane = threadIdx.x % kWave;
+  const int64_t nw = (int64_t)gridDim.x * (kGatherThreads / kWave);
+  const int64_t w = (int64_t)blockIdx.x * (kGatherThreads / kWave) + threadIdx.x / kWave;
+  const int64_t q = n_ids / nw, r = n_ids - q * nw;
+  const int64_t lo = w * q + (w * r) / nw, hi = (w + 1) * q + ((w + 1) * r) / nw;
+  uint32_t x = 0;
+  auto load = [&](int64_t k, u32x4_t (&v)[P]) {
+    const int64_t id = __builtin_amdgcn_readfirstlane(ids[k]);
+    if (id < 0 || id >= num_chunks) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) v[j] = u32x4_t{0u, 0u, 0u, 0u};
+      return;
+    }
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(buf + id * kChunk) + lane;
+#pragma unroll
+    for (int j = 0; j < P; ++j) v[j] = __builtin_nontemporal_load(src + j * kWave);
+  };
+  u32x4_t a[P], b[P];
+  int64_t k = lo;
+  for (; k + 1 < hi; k += 2) {
+    load(k, a);
+    load(k + 1, b);
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const u32x4_t e = a[j] ^ b[j];
+      x ^= e.x ^ e.y ^ e.z ^ e.w;
+    }
+  }
+  if (k < hi) {
+    load(k, a);
+#pragma unroll
+    for (int j = 0; j < P; ++j) x ^= a[j].x ^ a[j].y ^ a[j].z ^ a[j].w;
+  }
+  __shared__ uint32_t red[kGatherThreads];
+  red[threadIdx.x] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t y = 0;
+    for (int i = 0; i < kGatherThreads; ++i) y ^= red[i];
+    sink[blockIdx.x] = y;
+  }
+}
+
+hipError_t launch_gather_read(const void* buf, int64_t num_chunks, int chunk_bytes,
+                              const int32_t* ids, int64_t n_ids, int num_wg, uint32_t* sink,
+                              hipStream_t stream) {
+  const char* b = static_cast<const char*>(buf);
+  switch (chunk_bytes) {
+    case 2048:
+      hipLaunchKernelGGL(gather_read_kernel<2>, dim3(num_wg), dim3(kGatherThreads), 0, stream, b,
+                         num_chunks, ids, n_ids, sink);
+      break;
+    case 4096:
+      hipLaunchKernelGGL(gather_read_kernel<4>, dim3(num_wg), dim3(kGatherThreads), 0, stream, b,
+                         num_chunks, ids, n_ids, sink);
+      break;
+    case 8192:
+      hipLaunchKernelGGL(gather_read_kernel<8>, dim3(num_wg), dim3(kGatherThreads), 0, stream, b,
+                         num_chunks, ids, n_ids, sink);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(uint4* __restrict__ dst,
                                                   const uint4* __restrict__ src, size_t n16) {
   const size_t stride = (size_t)gridDim.x * 256;

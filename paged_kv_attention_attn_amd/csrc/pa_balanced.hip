@@ -125,22 +125,14 @@ struct BalancedCtx {
   }
 };
 
-// MULTI: the launch may have several query tokens (reads q_len, q_total, q_first, group);
-// otherwise they are the constants of one token, which keeps them out of the scalar registers.
-template <int D, int G, int DEPTH, class QK, bool MULTI>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(QK::kMinWavesPerEu)))
-void balanced_decode_kernel(const BalancedParams bp) {
-  using RG = RowGeom<D>;
-  constexpr int E = RG::kElems;
-  const DecodeParams& p = bp.d;
-  const QShape qs = make_qshape<MULTI, G>(p);
-  const int lane = threadIdx.x;
-  const int c = lane & (kRowLanes - 1);
-  const int w = blockIdx.x;
-  const BalancedCtx ctx{&p, (int64_t)p.stride << p.bs_log2, span_window(p, qs), q_rest(qs)};
-
-  // pass 1: total tiles (worker 0 also records the per-sequence prefix for the fix-up); the
-  // first 64 sequences' tiles and inclusive prefix stay in registers for pass 2
+// Worker w's share of the flattened tiles: n tiles from the tile under `cur`.  Pass 1 totals
+// the tiles (worker 0 also records the per-sequence prefix the fix-up reads, when `prefix` is
+// given); the first 64 sequences' tiles and inclusive prefix stay in registers for pass 2, which
+// finds the unit holding the worker's first tile (with up to 64 sequences nothing is loaded
+// again).  False when the worker has no tiles.
+__device__ __forceinline__ bool worker_share(const DecodeParams& p, const BalancedCtx& ctx,
+                                             int num_workers, int w, int lane, int64_t* prefix,
+                                             int& n, Cursor& cur) {
   int64_t carry = 0, T_first = 0, incl_first = 0;
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int j = base + lane;
@@ -151,20 +143,18 @@ void balanced_decode_kernel(const BalancedParams bp) {
       T_first = T;
       incl_first = incl;
     }
-    if (w == 0 && j < p.num_seqs) bp.prefix[j] = incl - T;
+    if (prefix != nullptr && w == 0 && j < p.num_seqs) prefix[j] = incl - T;
     carry = readlane64(incl, kWave - 1);
   }
-  if (w == 0 && lane == 0) bp.prefix[p.num_seqs] = carry;
+  if (prefix != nullptr && w == 0 && lane == 0) prefix[p.num_seqs] = carry;
   const int64_t total = carry * p.num_kv_heads;
-  const int n_eff = effective_workers(total, bp.num_workers);
-  if (w >= n_eff) return;
+  const int n_eff = effective_workers(total, num_workers);
+  if (w >= n_eff) return false;
   const int64_t A = worker_begin(total, n_eff, w);
-  const int n = (int)(worker_begin(total, n_eff, w + 1) - A);
-  if (n <= 0) return;
+  n = (int)(worker_begin(total, n_eff, w + 1) - A);
+  if (n <= 0) return false;
 
-  // pass 2: the unit holding tile A (the first 64 sequences from pass 1's registers: with up to
-  // 64 sequences nothing is loaded again)
-  Cursor cur{0, 0, 0, {}};
+  cur = Cursor{0, 0, 0, {}};
   carry = 0;
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int j = base + lane;
@@ -188,31 +178,62 @@ void balanced_decode_kernel(const BalancedParams bp) {
     }
     carry = readlane64(incl, kWave - 1);
   }
+  return true;
+}
+
+// The issue side of a worker's walk: the cursor of the next tile to load, with its block-table
+// entry fetched one issue ahead.  It only advances while another tile of the worker follows, so
+// it never walks past the last sequence that has tiles.
+struct IssueWalk {
+  Cursor iss;
+  int phys_next;
+  __device__ __forceinline__ IssueWalk(const BalancedCtx& ctx, const Cursor& first)
+      : iss(first), phys_next(ctx.phys(first)) {}
+  // tile k of n: its cursor and the byte offset of its first K/V row (-1 for a table entry
+  // outside the pool, which must not be read)
+  __device__ __forceinline__ int64_t next(const BalancedCtx& ctx, int k, int n, Cursor& at) {
+    const DecodeParams& p = *ctx.p;
+    at = iss;
+    const int phys = phys_next;
+    if (k + 1 < n) {
+      ctx.advance(iss);
+      phys_next = ctx.phys(iss);
+    }
+    const TileAddr ta{p.num_blocks, p.bs_log2, p.kv_block_stride, at.kvh * p.kv_head_stride,
+                      p.kv_row_stride};
+    return ta.offset(phys, at.s.t0 + at.ti);
+  }
+};
+
+// MULTI: the launch may have several query tokens (reads q_len, q_total, q_first, group);
+// otherwise they are the constants of one token, which keeps them out of the scalar registers.
+template <int D, int G, int DEPTH, class QK, bool MULTI>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(QK::kMinWavesPerEu)))
+void balanced_decode_kernel(const BalancedParams bp) {
+  using RG = RowGeom<D>;
+  constexpr int E = RG::kElems;
+  const DecodeParams& p = bp.d;
+  const QShape qs = make_qshape<MULTI, G>(p);
+  const int lane = threadIdx.x;
+  const int c = lane & (kRowLanes - 1);
+  const int w = blockIdx.x;
+  const BalancedCtx ctx{&p, (int64_t)p.stride << p.bs_log2, span_window(p, qs), q_rest(qs)};
+  int n = 0;
+  Cursor cur;
+  if (!worker_share(p, ctx, bp.num_workers, w, lane, bp.prefix, n, cur)) return;
 
   const float c2 = fabsf(p.qk_scale_log2);
   const uint32_t qflip = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
   QK qk;
   qk.init(p, qs, cur.b, cur.kvh * qs.group, lane, qflip, c2);
 
-  // the issue cursor, with the block-table entry of the next tile fetched one issue ahead; it
-  // only advances while another tile of this worker follows, so it never walks past the last
-  // sequence that has tiles
-  Cursor iss = cur;
-  int phys_next = ctx.phys(iss);
+  IssueWalk walk(ctx, cur);
   struct Slot {
     Cursor at;
     bool ok;
   };
   auto issue = [&](int k, typename QK::Tile& t, Slot& s) {
-    s.at = iss;
-    const int phys = phys_next;
-    if (k + 1 < n) {
-      ctx.advance(iss);
-      phys_next = ctx.phys(iss);
-    }
-    const TileAddr ta{p.num_blocks, p.bs_log2, p.kv_block_stride, s.at.kvh * p.kv_head_stride,
-                      p.kv_row_stride};
-    const int64_t off = ta.offset(phys, s.at.s.t0 + s.at.ti);
+    const int64_t off = walk.next(ctx, k, n, s.at);
     s.ok = off >= 0;
     if (s.ok) qk.issue(t, p.k_cache + off, p.v_cache + off, lane);
   };
@@ -385,8 +406,55 @@ void balanced_decode_kernel(const BalancedParams bp) {
     for (int k = 0; k < n; ++k) {
       issue(k, t0_, s0);
       // the next tile's unit, for the flush that may follow this tile
-      s1.at = iss;
+      s1.at = walk.iss;
       consume(k, t0_, s0, &s1);
+    }
+  }
+}
+
+// Gather witness of the balanced schedule: each worker runs the decode kernel's walk over its
+// share (worker_share, IssueWalk: unit cursor, block-table entry one issue ahead, tile offset
+// under the pool layout's strides) and copies the rows of every tile it would load, the attended
+// ones only, to row (token - window start) of its (sequence, KV head) in k_rows / v_rows, 32-bit
+// words spread over the 16 lanes of each row group.  A tile whose table entry lies outside the
+// pool is not read: its attended rows are written as 0xFF bytes.
+__global__ __launch_bounds__(kWave) void balanced_witness_kernel(const BalancedParams bp,
+                                                                 char* k_rows, char* v_rows,
+                                                                 int row_bytes, int max_rows) {
+  const DecodeParams& p = bp.d;
+  const QShape qs = make_qshape<false, 1>(p);
+  const int lane = threadIdx.x;
+  const BalancedCtx ctx{&p, (int64_t)p.stride << p.bs_log2, span_window(p, qs), q_rest(qs)};
+  int n = 0;
+  Cursor cur;
+  if (!worker_share(p, ctx, bp.num_workers, blockIdx.x, lane, nullptr, n, cur)) return;
+  IssueWalk walk(ctx, cur);
+  const int r = lane >> 4, c = lane & (kRowLanes - 1);
+  const int words = row_bytes / 4;
+  for (int k = 0; k < n; ++k) {
+    Cursor at;
+    const int64_t off = walk.next(ctx, k, n, at);
+    const int tok0 = (at.s.t0 + at.ti) * kTileTokens;
+#pragma unroll
+    for (int j = 0; j < kTileSteps; ++j) {
+      const int row = kRows * j + r;
+      const int i = tok0 + row - at.s.start;
+      if (tok0 + row < at.s.start || tok0 + row >= at.s.L || i >= max_rows) continue;
+      const size_t dst =
+          (((size_t)at.b * p.num_kv_heads + at.kvh) * max_rows + i) * (size_t)row_bytes;
+      uint32_t* kd = reinterpret_cast<uint32_t*>(k_rows + dst);
+      uint32_t* vd = reinterpret_cast<uint32_t*>(v_rows + dst);
+      if (off < 0) {
+        for (int x = c; x < words; x += kRowLanes) kd[x] = vd[x] = 0xFFFFFFFFu;
+      } else {
+        const int64_t src = off + (int64_t)row * p.kv_row_stride;
+        const uint32_t* ks = reinterpret_cast<const uint32_t*>(p.k_cache + src);
+        const uint32_t* vs = reinterpret_cast<const uint32_t*>(p.v_cache + src);
+        for (int x = c; x < words; x += kRowLanes) {
+          kd[x] = ks[x];
+          vd[x] = vs[x];
+        }
+      }
     }
   }
 }
@@ -685,6 +753,13 @@ hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int gro
     case 256: return launch_fix_g<256>(bp, group, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_balanced_witness(const BalancedParams& bp, char* k_rows, char* v_rows,
+                                   int row_bytes, int max_rows, hipStream_t stream) {
+  hipLaunchKernelGGL(balanced_witness_kernel, dim3(bp.num_workers), dim3(kWave), 0, stream, bp,
+                     k_rows, v_rows, row_bytes, max_rows);
+  return hipGetLastError();
 }
 
 int balanced_default_workers(int head_dim, int group, QkPath path, bool multi) {

@@ -144,6 +144,11 @@ hipError_t launch_balanced(const BalancedParams& bp, int head_dim, int group, Qk
                            bool multi, hipStream_t stream);
 hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int group,
                                  hipStream_t stream);
+// The balanced workers' walk (shares, cursors, table entries, tile offsets under the layout
+// strides of bp.d) copying each attended K/V row of (b, kvh) to row (token - window start) of
+// k_rows / v_rows [B][Hkv][max_rows][row_bytes] instead of computing; bp.prefix is not used.
+hipError_t launch_balanced_witness(const BalancedParams& bp, char* k_rows, char* v_rows,
+                                   int row_bytes, int max_rows, hipStream_t stream);
 // Workers that fit on the current device at once (CUs x resident one-wave workgroups per CU),
 // or -1 if the query fails.
 int balanced_default_workers(int head_dim, int group, QkPath path, bool multi = false);
@@ -159,6 +164,9 @@ hipError_t launch_qblock(const QBlockParams& qp, int head_dim, QkPath path, hipS
 
 hipError_t launch_witness(const WitnessParams& p, int head_dim, int num_seqs, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int num_wg, uint32_t* sink,
+                              hipStream_t stream);
+hipError_t launch_gather_read(const void* buf, int64_t num_chunks, int chunk_bytes,
+                              const int32_t* ids, int64_t n_ids, int num_wg, uint32_t* sink,
                               hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 

@@ -1,12 +1,13 @@
 """Test and measurement entry points (include/paged_attn_debug.h): the gather witness, the
-streaming-read probe and the plain copy kernel.  Argument marshalling only."""
+streaming-read and gather-read probes and the plain copy kernel.  Argument marshalling only."""
 from __future__ import annotations
 
 import ctypes
 
 import torch
 
-from . import PA_OK, PagedAttnError, _dev, _ptr, _stream, _BF16_LIKE, lib, make_shape
+from . import (KV_DTYPES, PA_OK, PagedAttnError, _BF16_LIKE, _dev, _layout_ptr, _ptr, _stream,
+               lib, make_shape)
 
 
 def gather_witness(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
@@ -32,12 +33,51 @@ def gather_witness(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: to
     return k_rows, v_rows
 
 
+def gather_witness_balanced(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_table: torch.Tensor, seq_lens: torch.Tensor, *, num_seqs: int,
+                            num_kv_heads: int, num_blocks: int, head_dim: int, block_size: int,
+                            num_workers: int, max_rows: int, window: int = 0,
+                            kv_dtype: str = "bf16", kv_layout=None, stream=None):
+    """Rows the balanced decode kernel's walk selects with ``num_workers`` workers: uint8
+    [B][Hkv][max_rows][row bytes] for K and V (unwritten rows keep 0xEE bytes).  The pools may
+    be in any layout given by ``kv_layout`` strides (elements), as for Plan."""
+    _dev(block_table, "block_table", (torch.int32,))
+    _dev(seq_lens, "seq_lens", (torch.int32,))
+    if not (k_cache.is_cuda and v_cache.is_cuda):
+        raise ValueError("k_cache and v_cache must be GPU tensors")
+    row = head_dim * (1 if kv_dtype == "fp8_e4m3" else 2)
+    k_rows = torch.full((num_seqs, num_kv_heads, max_rows, row), 0xEE, dtype=torch.uint8,
+                        device=k_cache.device)
+    v_rows = k_rows.clone()
+    shape = make_shape(num_seqs, num_kv_heads, num_kv_heads, num_blocks, block_table.shape[1])
+    st = lib().paged_attn_gather_witness_balanced(
+        ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+        int(head_dim), int(block_size), int(window), KV_DTYPES[kv_dtype], _layout_ptr(kv_layout),
+        int(num_workers), int(max_rows), _ptr(k_rows), _ptr(v_rows),
+        _stream(k_cache.device, stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "paged_attn_gather_witness_balanced")
+    return k_rows, v_rows
+
+
 def stream_read(buf: torch.Tensor, num_workgroups: int, sink: torch.Tensor, stream=None) -> None:
     nbytes = buf.numel() * buf.element_size()
     st = lib().paged_attn_stream_read(_ptr(buf), nbytes, int(num_workgroups), _ptr(sink),
                                       _stream(buf.device, stream))
     if st != PA_OK:
         raise PagedAttnError(st, "paged_attn_stream_read")
+
+
+def gather_read(buf: torch.Tensor, chunk_bytes: int, chunk_ids: torch.Tensor,
+                num_workgroups: int, sink: torch.Tensor, stream=None) -> None:
+    """Read the chunks of `buf` listed in chunk_ids (int32, device) in that order."""
+    _dev(chunk_ids, "chunk_ids", (torch.int32,))
+    nbytes = buf.numel() * buf.element_size()
+    st = lib().paged_attn_gather_read(_ptr(buf), nbytes, int(chunk_bytes), _ptr(chunk_ids),
+                                      int(chunk_ids.numel()), int(num_workgroups), _ptr(sink),
+                                      _stream(buf.device, stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "paged_attn_gather_read")
 
 
 def copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

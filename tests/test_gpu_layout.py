@@ -123,3 +123,71 @@ def test_default_strides_equal_no_layout_bitwise():
     a = run_plan(plan_for(wl, "balanced", None, num_workers=40), wl, t)
     b = run_plan(plan_for(wl, "balanced", (H * bs * D, bs * D, D), num_workers=40), wl, t)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------------------------
+# gather witness of the balanced schedule: the workers' own walk, under every layout
+# ---------------------------------------------------------------------------------------------
+def check_balanced_witness(wl, t, strides, workers, tag):
+    """The rows the balanced walk selects, byte for byte against the oracle's gather from the
+    default-layout pool (raw bits or codes), and nothing written past each attended count."""
+    from oracle import ref
+    from paged_kv_attention_attn_amd import debug
+
+    att = [int(min(L, wl.window)) if wl.window > 0 else int(L) for L in wl.seq_lens]
+    max_rows = max(max(att), 1)
+    kr, vr = debug.gather_witness_balanced(
+        t["k"], t["v"], t["bt"], t["L"], num_seqs=wl.num_seqs, num_kv_heads=wl.num_kv_heads,
+        num_blocks=wl.num_blocks, head_dim=wl.head_dim, block_size=wl.block_size,
+        num_workers=workers, max_rows=max_rows, window=wl.window, kv_dtype=wl.kv_format,
+        kv_layout=strides)
+    torch.cuda.synchronize()
+    kr, vr = kr.cpu().numpy(), vr.cpu().numpy()
+    for b, L in enumerate(wl.seq_lens):
+        L = int(L)
+        start = max(0, L - wl.window) if wl.window > 0 else 0
+        n = L - start
+        for kvh in range(wl.num_kv_heads):
+            for got, cache in ((kr, wl.k_cache), (vr, wl.v_cache)):
+                want = ref.gather_rows(cache, wl.block_table, b, kvh, start, L, wl.block_size)
+                want = want.view(np.uint8).reshape(n, got.shape[-1])
+                assert np.array_equal(got[b, kvh, :n], want), (tag, b, kvh)
+                assert (got[b, kvh, n:] == 0xEE).all(), (tag, b, kvh, "written past the rows")
+    log(f"[witness] balanced {tag}: bit-exact over {sum(att) * wl.num_kv_heads} rows")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("layout", ["default"] + LAYOUTS)
+@pytest.mark.parametrize("bs,window", [(16, 0), (32, 40), (64, 100)])
+def test_balanced_witness_layouts(layout, bs, window, kv):
+    wl = make_workload(name="witness", seq_lens=[0, 1, 15, 16, 17, 100, 257, 33, 1000],
+                       num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=bs,
+                       seed=[bs, window, 5], window=window, poison=True, kv_format=kv,
+                       kv_scales=(0.0625, 0.05) if kv != "bf16" else (1.0, 1.0))
+    t = to_dev(wl)
+    strides = None
+    if layout != "default":
+        t, strides = relayout(wl, t, layout)
+    # one worker, a few, many (units cut between workers), and more than the tiles allow
+    for workers in (1, 3, 17, 333, 5000):
+        check_balanced_witness(wl, t, strides, workers, f"{layout} bs={bs} W={window} {kv} "
+                                                        f"workers={workers}")
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_balanced_witness_head_dims(D):
+    wl = make_workload(name="witness", seq_lens=[700, 3, 2049, 0, 64], num_q_heads=4,
+                       num_kv_heads=4, head_dim=D, block_size=16, seed=[D, 6], window=0,
+                       poison=True)
+    t, strides = relayout(wl, to_dev(wl), "token_major")
+    for workers in (7, 64):
+        check_balanced_witness(wl, t, strides, workers, f"D={D} token-major workers={workers}")
+
+
+def test_balanced_witness_mixed_batch_2048_workers():
+    """The first 24 sequences of the mixed batch (window 4096) cut by 2048 workers, about a
+    dozen tiles each, default layout."""
+    from workloads import config_seq_lens
+
+    wl = make_config(5, seq_lens=config_seq_lens(5)[:24])
+    check_balanced_witness(wl, to_dev(wl), None, 2048, "cfg5 first 24 seqs")
