@@ -36,7 +36,8 @@
  *   - L = 0 yields out = 0 and lse = -inf (lse = sink when a sink is given).
  *
  * Ownership and concurrency: the caller owns every buffer.  The library allocates nothing, keeps
- * no global state and is safe to call from several host threads.  Calls are asynchronous on the
+ * no global state (apart from the device array of paged_attn_decode_balanced_noalloc and its
+ * address per GPU) and is safe to call from several host threads.  Calls are asynchronous on the
  * given stream (a hipStream_t passed as void*, NULL = the null stream); outputs are valid once
  * that stream reaches the call.
  *
@@ -165,6 +166,31 @@ pa_status paged_attn_reduce_balanced(const pa_shape* shape, const int32_t* seq_l
                                      const float* sinks, float* out, float* lse,
                                      void* workspace, size_t workspace_bytes,
                                      int32_t num_workers, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the whole balanced step, paged_attn_decode_balanced
+ * followed by paged_attn_reduce_balanced, with the partials kept in a device array the library
+ * holds instead of a caller workspace.  Same arguments, results and errors as those two calls
+ * (out/lse complete when the stream reaches the call), minus the workspace.
+ *
+ *   Limit: the balanced workspace of the shape and worker count
+ *   (paged_attn_balanced_workspace_size) must fit in 32 MiB, else PA_ERR_SHAPE; for example the
+ *   default 2048 workers at head_dim 128 and Hq/Hkv 4 need 8.4 MB (plus 8 bytes per sequence).
+ *   Allocates nothing: the array is a static device array of the library, one per GPU, which the
+ *   GPU holds from the library's loading until the process ends.  Its address on the current
+ *   device is looked up on the first call there (the only global state of the library).  No
+ *   initialisation is needed: each call writes what it reads.  Every call on one GPU uses the
+ *   same array, so calls that overlap in time on one GPU (several streams, several host threads)
+ *   race and corrupt each other's results: serialise them (one stream) or use
+ *   paged_attn_decode_balanced with separate workspaces.
+ */
+pa_status paged_attn_decode_balanced_noalloc(const pa_shape* shape, const void* q,
+                                             const void* k_cache, const void* v_cache,
+                                             const int32_t* block_table, const int32_t* seq_lens,
+                                             float scale, int32_t head_dim, int32_t block_size,
+                                             int32_t window, const float* sinks, float* out,
+                                             float* lse, int32_t num_workers, void* stream);
 
 /* Workspace bytes paged_attn_decode_balanced needs for this shape and worker count (0 = the
  * default count on the current device), or a negative pa_status. */

@@ -68,6 +68,8 @@ def _load() -> ctypes.CDLL:
                                              vp, vp, ctypes.c_size_t, i32, vp]),
         "paged_attn_reduce_balanced": (i32, [sp, vp, i32, i32, i32, vp, vp, vp, vp,
                                              ctypes.c_size_t, i32, vp]),
+        "paged_attn_decode_balanced_noalloc": (i32, [sp, vp, vp, vp, vp, vp, f32, i32, i32, i32,
+                                                     vp, vp, vp, i32, vp]),
         "paged_attn_balanced_workspace_size": (ctypes.c_int64, [sp, i32, i32]),
         "paged_attn_balanced_default_workers": (i32, [i32, i32]),
         "paged_attn_plan_create": (i32, [sp, i32, i32, i32, i32, i32, vp, i32, i32, i32,
@@ -95,7 +97,7 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 
 EXPORTED = ("paged_attn_decode", "paged_attn_reduce", "paged_attn_decode_balanced",
-            "paged_attn_reduce_balanced",
+            "paged_attn_reduce_balanced", "paged_attn_decode_balanced_noalloc",
             "paged_attn_balanced_workspace_size", "paged_attn_balanced_default_workers",
             "paged_attn_num_partitions",
             "paged_attn_variant_name", "paged_attn_status_string", "paged_attn_check_tables",
@@ -280,6 +282,41 @@ def balanced_default_workers(head_dim: int, group: int) -> int:
     if n <= 0:
         raise PagedAttnError(n, "paged_attn_balanced_default_workers")
     return n
+
+
+def decode_balanced_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float, *,
+                            out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                            window: int = 0, sinks: Optional[torch.Tensor] = None,
+                            num_workers: int = 0, stream=None) -> None:
+    """paged_attn_decode_balanced_noalloc: the balanced step (decode + merge) into the caller's
+    out (fp32 [B][Hq][D]) and lse (fp32 [B][Hq] or None) with the library's own device array for
+    the partials; allocates nothing."""
+    _dev(q, "q", _BF16_LIKE)
+    _dev(k_cache, "k_cache", _BF16_LIKE)
+    _dev(v_cache, "v_cache", _BF16_LIKE)
+    _dev(block_table, "block_table", (torch.int32,))
+    _dev(seq_lens, "seq_lens", (torch.int32,))
+    _dev(out, "out", (torch.float32,))
+    if lse is not None:
+        _dev(lse, "lse", (torch.float32,))
+    if sinks is not None:
+        _dev(sinks, "sinks", (torch.float32,))
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B][Hq][D]; k_cache/v_cache [num_blocks][Hkv][bs][D], equal")
+    B, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,) \
+            or out.shape != (B, Hq, D) or (lse is not None and lse.shape != (B, Hq)) \
+            or (sinks is not None and sinks.shape != (Hq,)):
+        raise ValueError("inconsistent q / cache / block_table / seq_lens / out / lse / sinks")
+    shape = make_shape(B, Hq, Hkv, NB, block_table.shape[1])
+    st = _lib.paged_attn_decode_balanced_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), float(scale), int(D), int(bs), int(window), _ptr(sinks), _ptr(out),
+        _ptr(lse), int(num_workers), _stream(q.device, stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "paged_attn_decode_balanced_noalloc")
 
 
 def balanced_workspace_size(shape: PaShape, head_dim: int, num_workers: int = 0) -> int:

@@ -16,6 +16,7 @@
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/paged_attn.h"
@@ -343,6 +344,82 @@ pa_status paged_attn_reduce_balanced(const pa_shape* shape, const int32_t* seq_l
   if (st != PA_OK || shape->num_seqs == 0) return st;
   const hipError_t e =
       pa::launch_balanced_fixup(bp, head_dim, group, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// The balanced step without a caller workspace: the partials live in a device array of the
+// library, one per GPU (each GPU holds its own copy of a __device__ array, at its own address).
+// Host code never passes the array's name to a kernel (on the host it only stands in for the
+// symbol); each device's address is looked up once, with that device current, and kept.
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch array, looked up on the first call per device.
+pa_status current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+    return PA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return PA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status paged_attn_decode_balanced_noalloc(const pa_shape* shape, const void* q,
+                                             const void* k_cache, const void* v_cache,
+                                             const int32_t* block_table, const int32_t* seq_lens,
+                                             float scale, int32_t head_dim, int32_t block_size,
+                                             int32_t window, const float* sinks, float* out,
+                                             float* lse, int32_t num_workers, void* stream) {
+  if (!std::isfinite(scale)) {
+    const pa_status st = check_shape(shape);
+    return st != PA_OK ? st : PA_ERR_SHAPE;
+  }
+  // every check first, against a stand-in of the scratch array's size and alignment (nothing is
+  // read through it); the array's device address only once they pass
+  pa::BalancedParams bp{};
+  pa::QkPath path;
+  int group = 0;
+  void* ws = reinterpret_cast<void*>((uintptr_t)256);
+  pa_status st = balanced_setup(shape, head_dim, block_size, window, seq_lens, sinks, out, lse,
+                                ws, kScratchBytes, num_workers, &bp, &path, &group);
+  if (st != PA_OK || shape->num_seqs == 0) return st;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr)
+    return PA_ERR_NULL;
+  st = current_scratch(&ws);
+  if (st != PA_OK) return st;
+  st = balanced_setup(shape, head_dim, block_size, window, seq_lens, sinks, out, lse, ws,
+                      kScratchBytes, bp.num_workers, &bp, &path, &group);
+  if (st != PA_OK) return st;
+  pa::DecodeParams& p = bp.d;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const char*>(k_cache);
+  p.v_cache = static_cast<const char*>(v_cache);
+  p.block_table = block_table;
+  p.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.v_scale = 1.f;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = pa::launch_balanced(bp, head_dim, group, path, false, hs);
+  if (e == hipSuccess) e = pa::launch_balanced_fixup(bp, head_dim, group, hs);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

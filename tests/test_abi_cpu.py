@@ -233,6 +233,31 @@ def test_balanced_empty_batch_is_ok_without_launch():
     assert call_balanced(shape(num_seqs=0), ws=None, out=None) == 0
 
 
+def call_noalloc(s, *, head_dim=128, block_size=16, window=0, workers=64, q=FAKE, out=FAKE,
+                 scale=0.1):
+    return pa.lib().paged_attn_decode_balanced_noalloc(ctypes.byref(s), q, FAKE, FAKE, FAKE,
+                                                       FAKE, scale, head_dim, block_size, window,
+                                                       None, out, None, workers, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(head_dim=96), -3), (dict(block_size=8), -3), (dict(window=-2), -2),
+    (dict(workers=-1), -2), (dict(workers=(1 << 20) + 1), -2), (dict(scale=float("nan")), -2),
+    (dict(q=None), -1), (dict(out=None), -1),
+    # partials beyond the 32 MiB device array: 2 * 4 * 128 * 4 bytes per worker at G = 4
+    (dict(workers=(32 << 20) // 4096 + 1), -2),
+])
+def test_noalloc_rejects_before_touching_the_device(kw, expect):
+    """Every refusal of the no-allocation entry point comes from host checks (this machine has
+    no GPU): bad sizes, NULL pointers, and partials too large for its device array."""
+    assert call_noalloc(shape(), **kw) == expect
+    assert pa.balanced_workspace_size(shape(), 128, (32 << 20) // 4096 + 1) > 32 << 20
+
+
+def test_noalloc_empty_batch_is_ok_without_launch():
+    assert call_noalloc(shape(num_seqs=0), q=None, out=None) == 0
+
+
 # ---------------------------------------------------------------------------------------------
 # prepared decode (plans): creation-time checks, workspace sizes, run-time argument checks
 # ---------------------------------------------------------------------------------------------
