@@ -378,6 +378,427 @@ void qblock_lds_kernel(const QBlockParams qp) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// The workgroup form on 32-key tiles (bf16 caches, head_dim 64 and 128): four waves, each with
+// 32 (token, head) rows, share a ring of 32-key K/V tiles in LDS as in qblock_lds_kernel, and each
+// wave folds a tile into its rows with 32x32x16 MFMAs in the transposed form of the two
+// contractions:
+//   S^T = K Q^T     A = the tile's K rows (32 keys x 16 dims per MFMA), B = the wave's q rows;
+//                   lane l ends with the scores of row l % 32 for 16 of the 32 keys (C row
+//                   8 (v / 4) + 4 (l / 32) + v % 4 is key v of its half), so the other 16 of its
+//                   row sit in lane l ^ 32;
+//   O^T += V^T P^T  A = V^T (32 head-dim values x 16 keys), B = P^T: lane l gives row l % 32's
+//                   probabilities of keys 8 (j / 4) + 4 (l / 32) + j % 4 (+16 for the second half
+//                   of the tile), exactly the scores it holds, so nothing moves between the two
+//                   contractions; A takes, per lane, one head-dim slice of eight key rows read from
+//                   LDS (rows of the lane's half, slice E (l % 32) .. + E of the row, E = D / 32)
+//                   and regrouped into E operands by byte permutes: MFMA e's A row i is head-dim
+//                   E i + e.
+// Lanes l and l ^ 32 hold the same (token, head) row, so its running max, rescale and output
+// live in its own lanes: no broadcast of softmax factors across the wave.  P enters as two bf16
+// terms (hi + lo), both products exact with fp32 accumulation, as in the one-token kernels.
+// ---------------------------------------------------------------------------------------------
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int D>
+struct Fa {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static constexpr int kKeys = 32;             // keys per tile (two 16-token tiles)
+  static constexpr int RB = 2 * D;             // bytes per K/V row
+  static constexpr int PR = RB / 16;           // 16-byte pieces per row
+  static constexpr int TB = 2 * kKeys * RB;    // bytes per tile: K rows, then V rows
+  static constexpr int KS = D / 16;            // score MFMAs per tile (16 head dims each)
+  static constexpr int E = D / 32;             // P.V MFMAs per 16 keys (head-dim slices)
+  // Where piece p of a row sits: K row r at p ^ (r % PR), which spreads the 32 rows a score
+  // operand read touches over the banks; V row r at p ^ (PR / 2 if bit 2 of r is set), so that
+  // the two lane halves of a P.V operand read (rows 4 apart) fall on opposite halves of the
+  // banks while a lane's slice keeps the same place in every row it reads.
+  __device__ __host__ static constexpr int swz(int hk, int r) {
+    return hk == 0 ? (r & (PR - 1)) : ((r >> 2) & 1) * (PR / 2);
+  }
+};
+
+// Key of score v (0..15) in lane half h, within a 32-key tile.
+__device__ __forceinline__ constexpr int fa_key(int v, int h) {
+  return 8 * (v >> 2) + 4 * h + (v & 3);
+}
+
+// One 16-byte piece per lane from global memory straight into LDS: lane i's piece from
+// base + voff (base wave-uniform, in scalar registers) to lds_wave_base + 16 i.  As
+// copy_piece_to_lds, with the per-lane part of the address a 32-bit offset.
+__device__ __forceinline__ void copy_piece_to_lds_s(const char* base, uint32_t voff,
+                                                    const char* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               ::"s"(lds), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
+constexpr int kFaAhead = 3;   // 32-key tiles copied ahead (LDS ring of kFaAhead + 1)
+
+// max and sum over the two lane halves (lanes l and l ^ 32), without the LDS crossbar:
+// v_permlane32_swap exchanges the halves of its two operands, so the pair it returns holds, at
+// every lane position, the values of both lanes l % 32 and l % 32 + 32
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+template <int D, bool HILO, int A>
+__global__ __launch_bounds__(kQbWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void qblock_fa_kernel(const QBlockParams qp) {
+  using F = Fa<D>;
+  constexpr int NBUF = A + 1;
+  constexpr int PIECES = F::TB / 16;
+  static_assert(PIECES % (kQbWaves * kWave) == 0, "a tile is whole workgroup copies");
+  constexpr int PL = PIECES / (kQbWaves * kWave);   // copies per lane per tile
+  constexpr int kTablePairs = kQbTableTiles / 2;    // 32-key tiles per table window
+  static_assert(kTablePairs % NBUF == 0, "table refills fall on unrolled iterations");
+  __shared__ __attribute__((aligned(16))) char s_tiles[NBUF * F::TB];
+  __shared__ int s_phys[kQbTableTiles];
+
+  const DecodeParams& p = qp.d;
+  QBlockItem it;
+  if (!qblock_item(qp, it)) return;   // uniform over the workgroup
+  // the wave index is uniform over the wave: kept in a scalar register, so that everything
+  // derived from it (the wave's tokens, key range and tile checks) is scalar too
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int h = lane >> 5;            // lane half
+  const int c = lane & 31;            // this lane's row of the wave
+  const int tpb = qp.tokens_per_block;
+  const int g = p.group;
+  const int64_t cap = (int64_t)p.stride << p.bs_log2;
+  const int Lraw = __builtin_amdgcn_readfirstlane(p.seq_lens[it.b]);
+  // the workgroup's tokens and the union of their keys, in 16-token tiles
+  const int q0w = it.qb * kQbWaves * tpb;
+  const int nqw = min(kQbWaves * tpb, p.q_total - q0w);
+  SeqSpan sw = seq_span(Lraw, p.window > 0 ? p.window + nqw - 1 : 0, cap,
+                        p.q_total - q0w - nqw);
+  clip_to_split(qp, it.split, sw);
+  const int npairs = (sw.T + 1) >> 1;
+  // this wave's tokens (none past the last block) and their keys
+  const int q0 = q0w + wave * tpb;
+  const int nq = max(0, min(tpb, p.q_total - q0));
+  const bool active = nq > 0;
+  const SeqSpan s = seq_span(Lraw, p.window > 0 ? p.window + nq - 1 : 0, cap,
+                             max(0, p.q_total - q0 - nq));
+  // this lane's row: token q0 + c / g, head kvh * g + c % g, at position pos; padding rows
+  // (token past q_total) have zero q, and their results are not written
+  const int sh = __builtin_ctz((unsigned)g);
+  const int tok = q0 + (c >> sh);
+  const bool row_ok = active && (c >> sh) < nq;
+  const int pos = s.L - nq + (c >> sh);
+  const int lo_row = p.window > 0 ? max(pos + 1 - p.window, 0) : 0;
+  const int hq = it.kvh * g + (c & (g - 1));
+
+  // q rows as B operands of the score MFMAs: dims 16 ks + 8 h .. + 8 of row c
+  const float c2 = fabsf(p.qk_scale_log2);
+  const uint32_t qflip = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
+  u32x4_t qb[F::KS];
+  {
+    const uint32_t keep = row_ok ? 0xFFFFFFFFu : 0u;
+    const char* qrow = reinterpret_cast<const char*>(
+        p.q + (((size_t)it.b * p.q_total + (row_ok ? tok : 0)) * p.num_q_heads + hq) * D);
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ++ks) {
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + 32 * ks + 16 * h);
+      x.x = (x.x ^ qflip) & keep;
+      x.y = (x.y ^ qflip) & keep;
+      x.z = (x.z ^ qflip) & keep;
+      x.w = (x.w ^ qflip) & keep;
+      qb[ks] = x;
+    }
+  }
+  f32x16_t o[F::E];
+#pragma unroll
+  for (int e = 0; e < F::E; ++e)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[e][v] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const TileAddr ta{p.num_blocks, p.bs_log2, p.kv_block_stride, it.kvh * p.kv_head_stride,
+                    p.kv_row_stride};
+  const int rs = (int)p.kv_row_stride;
+  const int32_t* bt = p.block_table + (size_t)it.b * p.stride;
+  bool bad = sw.bad;
+  // a 16-token tile that is past the range or has a bad table entry is copied from the first
+  // rows of block 0 instead (valid memory under the same per-lane offsets; never used unmasked)
+  const int64_t fallback = ta.offset(0, 0);
+
+  // per copy m of a tile: the lane's offset inside its 16-token tile, and which K/V half and
+  // 16-row half of the tile it fills (both uniform over the wave)
+  uint32_t cp_off[PL];
+  int cp_hk[PL], cp_hf[PL];
+#pragma unroll
+  for (int mcp = 0; mcp < PL; ++mcp) {
+    const int piece = (mcp * kQbWaves + wave) * kWave + lane;   // its place in the tile copy
+    const int hk = piece / (F::kKeys * F::PR);                   // 0 K, 1 V
+    const int row = (piece / F::PR) % F::kKeys;
+    const int col = (piece % F::PR) ^ F::swz(hk, row);           // the pool's piece
+    cp_off[mcp] = (uint32_t)((row & 15) * rs + col * 16);
+    cp_hk[mcp] = __builtin_amdgcn_readfirstlane(hk);
+    cp_hf[mcp] = __builtin_amdgcn_readfirstlane(row >> 4);
+  }
+
+  // physical blocks of the workgroup's 16-token tiles [base, base + kQbTableTiles), in LDS
+  auto fill_table = [&](int base) {
+    const int k = base + (int)threadIdx.x;
+    s_phys[threadIdx.x] = k < sw.T ? bt[ta.logical_block(sw.t0 + k)] : -1;
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  fill_table(0);
+
+  // copy 32-key tile k (16-token tiles sw.t0 + 2k, + 1) into ring slot k % NBUF
+  uint32_t badbits = 0;   // bit 2 (k % NBUF) + half: that half's table entry is outside the pool
+  auto copy = [&](int k, int slot) {
+    int64_t off[2];
+    uint32_t bits = 0;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int t16 = 2 * k + hf;
+      off[hf] = fallback;
+      if (t16 < sw.T) {
+        const int64_t o16 =
+            ta.offset(__builtin_amdgcn_readfirstlane(s_phys[t16 % kQbTableTiles]), sw.t0 + t16);
+        bits |= (o16 < 0 ? 1u : 0u) << hf;
+        if (o16 >= 0) off[hf] = o16;
+      }
+    }
+    badbits = (badbits & ~(3u << (2 * slot))) | (bits << (2 * slot));
+#pragma unroll
+    for (int mcp = 0; mcp < PL; ++mcp) {
+      const char* base = (cp_hk[mcp] ? p.v_cache : p.k_cache) + off[cp_hf[mcp]];
+      copy_piece_to_lds_s(base, cp_off[mcp],
+                          s_tiles + slot * F::TB + (mcp * kQbWaves + wave) * kWave * 16);
+    }
+  };
+
+  // every row of this wave sees the keys in [lo_all, hi_all); keys from t_end on lie past the
+  // workgroup's range (its key split's end, or the half tile after its last tile)
+  const int hi_all = s.L - nq + 1;
+  const int lo_all = (p.window > 0 && s.L > p.window) ? s.L - p.window : 0;
+  const int t_end = (sw.t0 + sw.T) * kTileTokens;
+  // LDS addresses of this lane's reads: the score operand of step ks is K row c, piece
+  // (2 ks + h) ^ (c % PR), at k_lane ^ 32 ks; the P.V operands are V rows 16 half + fa_key(j, h),
+  // slice 2 E c .. of each, at v_lane + (16 half + fa_key(j, 0)) * RB
+  const uint32_t k_lane = (uint32_t)(c * F::RB + ((h ^ (c & (F::PR - 1))) << 4));
+  const uint32_t v_lane =
+      (uint32_t)((F::kKeys + 4 * h) * F::RB + ((((2 * F::E * c) >> 4) ^ (h * (F::PR / 2))) << 4) +
+                 ((2 * F::E * c) & 15));
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(s_tiles);
+
+  // fold tile k, which sits in ring slot SLOT, into this wave's rows
+  auto step = [&](int k, auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    // this wave's copies of tile k are done once at most those of the A - 1 later tiles are
+    // outstanding; the barrier then makes the whole tile visible, and every wave has finished
+    // reading tile k - 1, whose slot the next copy reuses
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PL * (A - 1)) : "memory");
+    if ((k + A) % kTablePairs == 0 && k + A < npairs) fill_table(2 * (k + A));   // uniform
+    copy(k + A, (SLOT + A) % NBUF);
+    const int tok0 = (sw.t0 + 2 * k) * kTileTokens;
+    if (!active || tok0 + F::kKeys <= s.start || tok0 >= s.L) return;   // uniform per wave
+    // a table entry outside the pool in this wave's keys: never read through, NaN outputs
+    const uint32_t tb = badbits >> (2 * SLOT);
+    if (((tb & 1u) && tok0 + kTileTokens > s.start) ||
+        ((tb & 2u) && tok0 + kTileTokens < s.L)) {
+      bad = true;
+      return;
+    }
+    const uint32_t tile = lds0 + SLOT * F::TB;
+    // scores S^T: 32 keys x 32 rows; every K read is issued before the first MFMA that waits
+    u32x4_t kw[F::KS];
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ++ks)
+      kw[ks] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+          (uintptr_t)(tile + (k_lane ^ (32u * ks))));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16_t sc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ++ks)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kw[ks]),
+                                                   __builtin_bit_cast(bf16x8_t, qb[ks]), sc, 0,
+                                                   0, 0);
+    // the V reads of both halves go out now, under the softmax: head-dim slice E c .. E c + E
+    // of the eight V rows this lane's half contributes to each 16-key half
+    uint32_t vw[2][8][(F::E + 1) / 2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t at = tile + v_lane + (16 * half + 8 * (j >> 2) + (j & 3)) * F::RB;
+        if constexpr (F::E == 4) {
+          const u32x2_t x =
+              *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(
+                  (uintptr_t)at);
+          vw[half][j][0] = x.x;
+          vw[half][j][1] = x.y;
+        } else {
+          vw[half][j][0] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
+              (uintptr_t)at);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int full = __builtin_amdgcn_readfirstlane(
+        (tok0 >= lo_all && tok0 + F::kKeys <= min(hi_all, t_end)) ? 1 : 0);
+    float mx;
+    mx = -INFINITY;
+    if (full) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+      mx *= c2;
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = tok0 + fa_key(v, h);
+        sc[v] = (key >= lo_row && key <= pos && key < t_end) ? sc[v] * c2 : -INFINITY;
+        mx = fmaxf(mx, sc[v]);
+      }
+    }
+    mx = halves_max(mx);   // the row's other 16 keys
+    if (__builtin_amdgcn_ballot_w64(row_ok && mx > m + kRescaleSlack) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
+      l *= alpha;
+      m = mn;
+#pragma unroll
+      for (int e = 0; e < F::E; ++e)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[e][v] *= alpha;
+    }
+    const float mu = m == -INFINITY ? 0.f : m;
+    float pr[16];
+    if (full) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) pr[v] = fast_exp2(fmaf(sc[v], c2, -mu));
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) pr[v] = fast_exp2(sc[v] - mu);
+    }
+    float ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ls += pr[v];
+    l += ls;
+    // P^T as B operands, p = hi + lo in bf16, eight keys per 16-key half of the tile
+    u32x4_t bhi[2], blo[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float a0 = pr[8 * half + 2 * w], a1 = pr[8 * half + 2 * w + 1];
+        const bf16x2_t hv = {(__bf16)a0, (__bf16)a1};
+        const uint32_t hu = __builtin_bit_cast(uint32_t, hv);
+        bhi[half][w] = hu;
+        if constexpr (HILO) {
+          const bf16x2_t lv = {(__bf16)(a0 - __builtin_bit_cast(float, hu << 16)),
+                               (__bf16)(a1 - __builtin_bit_cast(float, hu & 0xFFFF0000u))};
+          blo[half][w] = __builtin_bit_cast(uint32_t, lv);
+        }
+      }
+    }
+    // O^T += V^T P^T, one 16-key half at a time
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (!full) {
+        // rows outside the wave's keys are zeroed: a stray NaN there must not meet p = 0
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = tok0 + 16 * half + fa_key(j, h);
+          const bool keep = t >= s.start && t < s.L && t < t_end;
+#pragma unroll
+          for (int w = 0; w < (F::E + 1) / 2; ++w)
+            vw[half][j][w] = keep ? vw[half][j][w] : 0u;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < F::E; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t av;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          av[w] = __builtin_amdgcn_perm(vw[half][2 * w + 1][e >> 1], vw[half][2 * w][e >> 1],
+                                        sel);
+        o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                       __builtin_bit_cast(bf16x8_t, bhi[half]),
+                                                       o[e], 0, 0, 0);
+        if constexpr (HILO)
+          o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                         __builtin_bit_cast(bf16x8_t, blo[half]),
+                                                         o[e], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int k = 0; k < A; ++k) copy(k, k);
+  // the ring slot of tile k is k % NBUF: unrolled NBUF times, so that every LDS address is a
+  // lane register plus a constant
+  for (int k = 0; k < npairs; k += NBUF) {
+    step(k, std::integral_constant<int, 0>{});
+    if (k + 1 < npairs) step(k + 1, std::integral_constant<int, 1>{});
+    if (k + 2 < npairs) step(k + 2, std::integral_constant<int, 2>{});
+    if (k + 3 < npairs) step(k + 3, std::integral_constant<int, 3>{});
+  }
+  static_assert(NBUF == 4, "the loop above is unrolled for a ring of four");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the copies past the last tile
+  if (!active) return;
+  bad = bad || s.bad;
+
+  // finish: the row's sum over both halves, the sink (one split), normalise, write
+  const float lt = halves_sum(l);
+  if (!row_ok) return;
+  float M = m, L2 = lt, scale_o = 1.f;
+  if (p.sinks != nullptr && qp.splits == 1) {
+    const float s2 = p.sinks[hq] * kLog2e;
+    const float M2 = fmaxf(M, s2);
+    const float M2u = M2 == -INFINITY ? 0.f : M2;
+    scale_o = fast_exp2(M - M2u);
+    L2 = fmaf(L2, scale_o, fast_exp2(s2 - M2u));
+    M = M2;
+  }
+  const float inv = L2 != 0.f ? scale_o / L2 : 0.f;
+  float lv = L2 != 0.f ? (M + fast_log2(L2)) * kLn2 : -INFINITY;
+  if (bad) lv = __builtin_nanf("");
+  const size_t row = ((size_t)it.b * p.q_total + tok) * p.num_q_heads + hq;
+  float* dst;
+  if (qp.splits == 1) {
+    dst = p.out + row * D;
+    if (h == 0 && p.lse != nullptr) p.lse[row] = lv;
+  } else {
+    const size_t slot = row * (size_t)qp.splits + it.split;
+    dst = qp.part_out + slot * D;
+    if (h == 0) qp.part_lse[slot] = lv;
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int i = fa_key(v, h);   // head-dim slice E i .. E i + E
+    if constexpr (F::E == 4) {
+      float4 x;
+      x.x = bad ? __builtin_nanf("") : o[0][v] * inv;
+      x.y = bad ? __builtin_nanf("") : o[1][v] * inv;
+      x.z = bad ? __builtin_nanf("") : o[2][v] * inv;
+      x.w = bad ? __builtin_nanf("") : o[3][v] * inv;
+      *reinterpret_cast<float4*>(dst + 4 * i) = x;
+    } else {
+      float2 x;
+      x.x = bad ? __builtin_nanf("") : o[0][v] * inv;
+      x.y = bad ? __builtin_nanf("") : o[1][v] * inv;
+      *reinterpret_cast<float2*>(dst + 2 * i) = x;
+    }
+  }
+}
+
 // Merge of the key splits: one wave per output row (sequence, token, query head).  Over the
 // splits with a finite LSE l_k: M = max l_k, w_k = e^(l_k - M), out = sum w_k o_k / sum w_k and
 // lse = M + ln sum w_k, the log-sum-exp rule of split-KV decode (ROCm/rocm-libraries PR #13700,
@@ -457,6 +878,9 @@ hipError_t launch_d(const QBlockParams& qp, QkPath path, hipStream_t stream) {
   if (qp.waves == kQbWaves) {
     if (path == QkPath::kMfmaPvFp8)
       hipLaunchKernelGGL((qblock_lds_kernel<D, QbQkFp8<D>, A>), dim3(qp.grid),
+                         dim3(kQbWaves * kWave), 0, stream, qp);
+    else if constexpr (D <= 128)
+      hipLaunchKernelGGL((qblock_fa_kernel<D, true, kFaAhead>), dim3(qp.grid),
                          dim3(kQbWaves * kWave), 0, stream, qp);
     else
       hipLaunchKernelGGL((qblock_lds_kernel<D, QbQk<D>, A>), dim3(qp.grid),
