@@ -462,7 +462,7 @@ void qblock_fa_kernel(const QBlockParams qp) {
   constexpr int kTablePairs = kQbTableTiles / 2;    // 32-key tiles per table window
   static_assert(kTablePairs % NBUF == 0, "table refills fall on unrolled iterations");
   __shared__ __attribute__((aligned(16))) char s_tiles[NBUF * F::TB];
-  __shared__ int s_phys[kQbTableTiles];
+  __shared__ int64_t s_off[kQbTableTiles];
 
   const DecodeParams& p = qp.d;
   QBlockItem it;
@@ -548,10 +548,12 @@ void qblock_fa_kernel(const QBlockParams qp) {
     cp_hf[mcp] = __builtin_amdgcn_readfirstlane(row >> 4);
   }
 
-  // physical blocks of the workgroup's 16-token tiles [base, base + kQbTableTiles), in LDS
+  // byte offsets of the workgroup's 16-token tiles [base, base + kQbTableTiles) in the pool, in
+  // LDS: past the range, the fallback; a table entry outside the pool, -1
   auto fill_table = [&](int base) {
     const int k = base + (int)threadIdx.x;
-    s_phys[threadIdx.x] = k < sw.T ? bt[ta.logical_block(sw.t0 + k)] : -1;
+    s_off[threadIdx.x] =
+        k < sw.T ? ta.offset(bt[ta.logical_block(sw.t0 + k)], sw.t0 + k) : fallback;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   fill_table(0);
@@ -563,14 +565,12 @@ void qblock_fa_kernel(const QBlockParams qp) {
     uint32_t bits = 0;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const int t16 = 2 * k + hf;
-      off[hf] = fallback;
-      if (t16 < sw.T) {
-        const int64_t o16 =
-            ta.offset(__builtin_amdgcn_readfirstlane(s_phys[t16 % kQbTableTiles]), sw.t0 + t16);
-        bits |= (o16 < 0 ? 1u : 0u) << hf;
-        if (o16 >= 0) off[hf] = o16;
-      }
+      const int64_t o16 = s_off[(2 * k + hf) % kQbTableTiles];
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)o16);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)o16 >> 32));
+      off[hf] = (int64_t)(((uint64_t)hi << 32) | lo);
+      bits |= (off[hf] < 0 ? 1u : 0u) << hf;
+      if (off[hf] < 0) off[hf] = fallback;
     }
     badbits = (badbits & ~(3u << (2 * slot))) | (bits << (2 * slot));
 #pragma unroll
@@ -586,6 +586,12 @@ void qblock_fa_kernel(const QBlockParams qp) {
   const int hi_all = s.L - nq + 1;
   const int lo_all = (p.window > 0 && s.L > p.window) ? s.L - p.window : 0;
   const int t_end = (sw.t0 + sw.T) * kTileTokens;
+  // keys in [z_lo, z_hi) are rows some token of the workgroup attends: real cache rows.  Rows
+  // outside (before the window, past the sequence, past the range or from the fallback copy)
+  // may hold anything and are zeroed before P.V, in the tiles that reach them: a stray NaN there
+  // must not meet p = 0
+  const int z_lo = sw.start;
+  const int z_hi = min(sw.L, t_end);
   // LDS addresses of this lane's reads: the score operand of step ks is K row c, piece
   // (2 ks + h) ^ (c % PR), at k_lane ^ 32 ks; the P.V operands are V rows 16 half + fa_key(j, h),
   // slice 2 E c .. of each, at v_lane + (16 half + fa_key(j, 0)) * RB
@@ -696,31 +702,35 @@ void qblock_fa_kernel(const QBlockParams qp) {
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
+        // hi: the upper halves of the two floats (p truncated to bf16, one byte permute); lo:
+        // the exact remainder p - hi, rounded to bf16: |hi + lo - p| <= 2^-16 |p|
         const float a0 = pr[8 * half + 2 * w], a1 = pr[8 * half + 2 * w + 1];
-        const bf16x2_t hv = {(__bf16)a0, (__bf16)a1};
-        const uint32_t hu = __builtin_bit_cast(uint32_t, hv);
-        bhi[half][w] = hu;
+        const uint32_t u0 = __builtin_bit_cast(uint32_t, a0);
+        const uint32_t u1 = __builtin_bit_cast(uint32_t, a1);
+        bhi[half][w] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
         if constexpr (HILO) {
-          const bf16x2_t lv = {(__bf16)(a0 - __builtin_bit_cast(float, hu << 16)),
-                               (__bf16)(a1 - __builtin_bit_cast(float, hu & 0xFFFF0000u))};
+          const bf16x2_t lv = {(__bf16)(a0 - __builtin_bit_cast(float, u0 & 0xFFFF0000u)),
+                               (__bf16)(a1 - __builtin_bit_cast(float, u1 & 0xFFFF0000u))};
           blo[half][w] = __builtin_bit_cast(uint32_t, lv);
+        }
+      }
+    }
+    if (__builtin_amdgcn_readfirstlane((tok0 < z_lo || tok0 + F::kKeys > z_hi) ? 1 : 0)) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = tok0 + 16 * half + fa_key(j, h);
+          const bool keep = t >= z_lo && t < z_hi;
+#pragma unroll
+          for (int w = 0; w < (F::E + 1) / 2; ++w)
+            vw[half][j][w] = keep ? vw[half][j][w] : 0u;
         }
       }
     }
     // O^T += V^T P^T, one 16-key half at a time
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      if (!full) {
-        // rows outside the wave's keys are zeroed: a stray NaN there must not meet p = 0
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = tok0 + 16 * half + fa_key(j, h);
-          const bool keep = t >= s.start && t < s.L && t < t_end;
-#pragma unroll
-          for (int w = 0; w < (F::E + 1) / 2; ++w)
-            vw[half][j][w] = keep ? vw[half][j][w] : 0u;
-        }
-      }
 #pragma unroll
       for (int e = 0; e < F::E; ++e) {
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
