@@ -617,7 +617,9 @@ def main() -> int:
     print(f"[bench] headline {m}", file=sys.stderr, flush=True)
     label = workload_label(args.config, D, Hq, args.kv, args.q_len, args.seq_lens)
     qblocks = args.schedule == "query_blocks"
-    probe = gather_probe(dv, 16 * D * (1 if args.kv != "bf16" else 2))
+    # chunks of one 16-token tile of one KV head (the probe takes 2 to 8 KiB; an FP8 tile at
+    # head_dim 64 is 1 KiB and is compared with 2 KiB chunks)
+    probe = gather_probe(dv, min(max(16 * D * (1 if args.kv != "bf16" else 2), 2048), 8192))
     print(f"[bench] gather probe {probe}", file=sys.stderr, flush=True)
 
     us = m["us_per_step"]

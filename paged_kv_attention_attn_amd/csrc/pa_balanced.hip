@@ -99,12 +99,19 @@ struct Cursor {
   SeqSpan s;
 };
 
+// A wave-uniform read of a kernel-constant int32 array through the scalar data cache (a scalar
+// load, counted apart from the vector loads): waiting for it does not wait for the K/V loads in
+// flight, as a vector load's would (vector loads complete in order).  Reads only.
+__device__ __forceinline__ int32_t scalar_read(const int32_t* base, size_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)(uintptr_t)base)[i];
+}
+
 struct BalancedCtx {
   const DecodeParams* p;
   int64_t cap;
   int swin, qrest;   // span_window and q_rest of the launch
   __device__ __forceinline__ SeqSpan span(int b) const {
-    return seq_span(__builtin_amdgcn_readfirstlane(p->seq_lens[b]), swin, cap, qrest);
+    return seq_span(scalar_read(p->seq_lens, b), swin, cap, qrest);
   }
   // next tile; skips sequences without tiles (callers never step past the last tile)
   __device__ __forceinline__ void advance(Cursor& c) const {
@@ -120,8 +127,8 @@ struct BalancedCtx {
   // physical block of the cursor's tile
   __device__ __forceinline__ int phys(const Cursor& c) const {
     const int tile = c.s.t0 + c.ti;
-    return __builtin_amdgcn_readfirstlane(
-        p->block_table[(size_t)c.b * p->stride + ((tile * kTileTokens) >> p->bs_log2)]);
+    return scalar_read(p->block_table,
+                       (size_t)c.b * p->stride + ((tile * kTileTokens) >> p->bs_log2));
   }
 };
 
@@ -227,15 +234,15 @@ void balanced_decode_kernel(const BalancedParams bp) {
   QK qk;
   qk.init(p, qs, cur.b, cur.kvh * qs.group, lane, qflip, c2);
 
+  // the issue side walks ahead of the consume side by the tiles in flight; each keeps its own
+  // cursor, so a tile in flight carries nothing but its registers and whether it was read
   IssueWalk walk(ctx, cur);
-  struct Slot {
+  Cursor con = cur;   // the tile consumed next
+  auto issue = [&](int k, typename QK::Tile& t, bool& ok) {
     Cursor at;
-    bool ok;
-  };
-  auto issue = [&](int k, typename QK::Tile& t, Slot& s) {
-    const int64_t off = walk.next(ctx, k, n, s.at);
-    s.ok = off >= 0;
-    if (s.ok) qk.issue(t, p.k_cache + off, p.v_cache + off, lane);
+    const int64_t off = walk.next(ctx, k, n, at);
+    ok = off >= 0;
+    if (ok) qk.issue(t, p.k_cache + off, p.v_cache + off, lane);
   };
 
   int piece_start = cur.ti;
@@ -350,9 +357,9 @@ void balanced_decode_kernel(const BalancedParams bp) {
     }
   };
 
-  auto consume = [&](int k, typename QK::Tile& t, const Slot& s, const Slot* next) {
-    const Cursor& at = s.at;
-    if (s.ok) {
+  auto consume = [&](int k, typename QK::Tile& t, bool ok) {
+    const Cursor& at = con;
+    if (ok) {
       const int tok0 = (at.s.t0 + at.ti) * kTileTokens;
       if constexpr (QK::kQueryTokens) {
         // every column sees the keys inside [lo_all, hi_all): from the last query token's
@@ -378,9 +385,12 @@ void balanced_decode_kernel(const BalancedParams bp) {
       flush(at);
       if (k + 1 < n) {
         // the next tile starts the next unit: its q, fresh state
-        qk.load_q(p, qs, next->at.b, next->at.kvh * qs.group, lane, qflip);
+        ctx.advance(con);
+        qk.load_q(p, qs, con.b, con.kvh * qs.group, lane, qflip);
         qk.reset();
       }
+    } else {
+      ++con.ti;   // the next tile is in the same unit
     }
   };
 
@@ -388,26 +398,24 @@ void balanced_decode_kernel(const BalancedParams bp) {
     // DEPTH tiles in flight: the loads of tiles k+1 .. k+DEPTH-1 are issued before tile k is
     // consumed; the loop is unrolled DEPTH times so every buffer index is a constant
     typename QK::Tile t[DEPTH];
-    Slot sl[DEPTH];
+    bool ok[DEPTH];
 #pragma unroll
     for (int j = 0; j + 1 < DEPTH; ++j)
-      if (j < n) issue(j, t[j], sl[j]);
+      if (j < n) issue(j, t[j], ok[j]);
     for (int k = 0; k < n; k += DEPTH) {
 #pragma unroll
       for (int j = 0; j < DEPTH; ++j) {
         if (k + j + DEPTH - 1 < n)
-          issue(k + j + DEPTH - 1, t[(j + DEPTH - 1) % DEPTH], sl[(j + DEPTH - 1) % DEPTH]);
-        if (k + j < n) consume(k + j, t[j], sl[j], &sl[(j + 1) % DEPTH]);
+          issue(k + j + DEPTH - 1, t[(j + DEPTH - 1) % DEPTH], ok[(j + DEPTH - 1) % DEPTH]);
+        if (k + j < n) consume(k + j, t[j], ok[j]);
       }
     }
   } else {
     typename QK::Tile t0_;
-    Slot s0, s1;
+    bool ok0;
     for (int k = 0; k < n; ++k) {
-      issue(k, t0_, s0);
-      // the next tile's unit, for the flush that may follow this tile
-      s1.at = walk.iss;
-      consume(k, t0_, s0, &s1);
+      issue(k, t0_, ok0);
+      consume(k, t0_, ok0);
     }
   }
 }
