@@ -361,9 +361,8 @@ def measure(dv: Device, wl, *, schedule: str, partition: int, steps: int, warmup
             workers: int = 0, copies=None, graph: bool = True) -> dict:
     """One workload on one schedule through a prepared plan (one library call per step: decode
     plus its merge).  Returns the wall time per step over ``steps`` back-to-back runs, the same
-    steps replayed from a HIP graph, and the decode kernel's own duration from HIP events on the
-    launch stream (a separate pass of the same launches: around the decode launch alone where
-    the eager binding issues it alone, else around the whole step)."""
+    steps replayed from a HIP graph, and the decode kernel's own duration from HIP events that
+    the library records on the launch stream around it (a separate pass of the same steps)."""
     torch, pa = dv.torch, dv.pa
     B, Hq, D = wl.num_seqs, wl.num_q_heads, wl.head_dim
     maxL = int(wl.seq_lens.max())
@@ -403,46 +402,21 @@ def measure(dv: Device, wl, *, schedule: str, partition: int, steps: int, warmup
         graph_step = _graph_step(torch, plan, stream, copies, steps, q, ks, vs, bt, L, wl, out,
                                  lse, sinks, ws)
 
-    # kernel pass: HIP events on the launch stream around each decode launch
-    # kernel pass: HIP events on the launch stream around each decode launch
-    eager = wl.kv_format == "bf16" and wl.q_len == 1 and schedule in ("balanced",
-                                                                       "partitioned", "unsplit")
-    if eager and schedule == "balanced":
-        shape = pa.make_shape(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride)
-        bws = torch.empty(pa.balanced_workspace_size(shape, D, nworkers), dtype=torch.uint8,
-                          device=dv.dev)
-    elif eager and schedule == "partitioned":
-        pmax = pa.num_partitions(maxL, partition)
-        part = torch.empty((B, Hq, pmax, D), dtype=torch.float32, device=dv.dev)
-        plse = torch.empty((B, Hq, pmax), dtype=torch.float32, device=dv.dev)
+    # kernel pass: the same plan steps, with HIP events recorded on the launch stream by the
+    # library right before and right after the decode kernel (its merge launch follows)
+    from paged_kv_attention_attn_amd import debug
 
     def timed(i, ev):
         c = i % copies
-        ev[0].record(stream)
-        if not eager:
-            run(i)
-            ev[1].record(stream)
-        elif schedule == "balanced":
-            pa.decode_balanced(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window,
-                               sinks=sinks, out=out, lse=lse, workspace=bws,
-                               num_workers=nworkers, merge=False, stream=stream)
-            ev[1].record(stream)
-            pa.reduce_balanced(L, out, lse, shape=shape, head_dim=D, block_size=wl.block_size,
-                               window=wl.window, sinks=sinks, workspace=bws,
-                               num_workers=nworkers, stream=stream)
-        elif schedule == "partitioned":
-            pa.decode(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window, sinks=sinks,
-                      partition_size=partition, max_partitions=pmax, out=part, lse=plse,
-                      stream=stream)
-            ev[1].record(stream)
-            pa.reduce(part, plse, L, partition_size=partition, out=out, lse=lse, stream=stream)
-        else:
-            pa.decode(q, ks[c], vs[c], bt, L, float(wl.scale), window=wl.window, sinks=sinks,
-                      out=out, lse=lse, stream=stream)
-            ev[1].record(stream)
+        debug.plan_run_timed(plan, q, ks[c], vs[c], bt, L, float(wl.scale), out=out, lse=lse,
+                             sinks=sinks, workspace=ws, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                             stream=stream, ev_before=ev[0], ev_after=ev[1])
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
+    for a, b in evs:   # creates the events
+        a.record(stream)
+        b.record(stream)
     for i in range(warmup):
         timed(i, evs[0])
     torch.cuda.synchronize()
@@ -455,7 +429,7 @@ def measure(dv: Device, wl, *, schedule: str, partition: int, steps: int, warmup
            "us_per_step": round(wall * 1e6, 2),
            "graph_us_per_step": None if graph_step is None else round(graph_step * 1e6, 2),
            "decode_us_avg": round(dec * 1e6, 3),
-           "interval": "decode launch" if eager else "decode and merge launches"}
+           "interval": "decode launch"}
     del ks, vs, k0, v0, ws, plan
     torch.cuda.empty_cache()
     return res
@@ -655,8 +629,9 @@ def main() -> int:
             "kv_pool_copies": m["kv_pool_copies"], "parallelism": "none (1 GPU)",
             "timing": "value and us_per_step: wall clock over back-to-back prepared-plan runs "
                       "(one library call per step: decode + merge); graph_us_per_step: the same "
-                      "steps replayed from a HIP graph; roofline: HIP events around each decode "
-                      "launch in a second pass of the same launches",
+                      "steps replayed from a HIP graph; roofline: HIP events the library records "
+                      "on the launch stream right before and after the decode kernel, in a "
+                      "second pass of the same plan steps",
             "device": {"name": dv.props.name, "arch": dv.props.gcnArchName,
                        "hip": str(dv.torch.version.hip), "torch": dv.torch.__version__},
         },

@@ -97,6 +97,22 @@ pa_status paged_attn_gather_read(const void* buf, size_t bytes, int32_t chunk_by
  * hardware byte counters. */
 pa_status paged_attn_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/*
+ * paged_attn_plan_run with the decode kernel bracketed by two HIP events: ev_before (a
+ * hipEvent_t, NULL for none) is recorded on `stream` right before the plan's decode launch
+ * (the query-block launch on that schedule) and ev_after right after it, ahead of any merge
+ * launch, so that hipEventElapsedTime(ev_before, ev_after) is that kernel's own duration.  When
+ * a plan runs several passes of query tokens, the events bracket the first pass's decode
+ * launch.  Arguments, checks and results otherwise as paged_attn_plan_run; an event that fails
+ * to record is PA_ERR_LAUNCH.
+ */
+pa_status paged_attn_plan_run_timed(const pa_plan* plan, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_table,
+                                    const int32_t* seq_lens, float scale, float k_scale,
+                                    float v_scale, const float* sinks, float* out, float* lse,
+                                    void* workspace, void* stream, void* ev_before,
+                                    void* ev_after);
+
 #ifdef __cplusplus
 }
 #endif

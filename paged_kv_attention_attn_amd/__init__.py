@@ -77,6 +77,8 @@ def _load() -> ctypes.CDLL:
         "paged_attn_plan_workspace_size": (ctypes.c_int64, [vp]),
         "paged_attn_plan_run": (i32, [vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp, vp,
                                       vp]),
+        "paged_attn_plan_run_timed": (i32, [vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp,
+                                            vp, vp, vp, vp]),
         "paged_attn_plan_name": (ctypes.c_char_p, [vp]),
         "paged_attn_plan_destroy": (None, [vp]),
         "paged_attn_gather_witness": (i32, [sp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]),
@@ -107,7 +109,7 @@ EXPORTED = ("paged_attn_decode", "paged_attn_reduce", "paged_attn_decode_balance
             "paged_attn_stream_read", "paged_attn_gather_read",
             "paged_attn_copy",
             "paged_attn_plan_create", "paged_attn_plan_workspace_size", "paged_attn_plan_run",
-            "paged_attn_plan_name", "paged_attn_plan_destroy")
+            "paged_attn_plan_run_timed", "paged_attn_plan_name", "paged_attn_plan_destroy")
 
 
 def lib() -> ctypes.CDLL:

@@ -214,7 +214,11 @@ struct IssueWalk {
 
 // MULTI: the launch may have several query tokens (reads q_len, q_total, q_first, group);
 // otherwise they are the constants of one token, which keeps them out of the scalar registers.
-template <int D, int G, int DEPTH, class QK, bool MULTI>
+// Tiles in flight: AHEAD = 0, DEPTH tiles held in registers (the loads of tile k + DEPTH - 1
+// issued before tile k is consumed); AHEAD > 0, AHEAD tiles copied ahead into a ring of
+// AHEAD + 1 tile slots in LDS by direct-to-LDS loads, which hold no registers while in flight,
+// and read from there into the tile registers just before they are consumed.
+template <int D, int G, int DEPTH, class QK, bool MULTI, int AHEAD = 0>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(QK::kMinWavesPerEu)))
 void balanced_decode_kernel(const BalancedParams bp) {
   using RG = RowGeom<D>;
@@ -366,12 +370,10 @@ void balanced_decode_kernel(const BalancedParams bp) {
         // window start to the first query token's position (with one token: the attended range)
         const int hi_all = at.s.L - qs.q_len + 1;
         const int lo_all = (p.window > 0 && at.s.L > p.window) ? at.s.L - p.window : 0;
-        if (tok0 >= lo_all && tok0 + kTileTokens <= hi_all) {
-          qk.template consume<false>(t, 0, 0, 0, lane);
-        } else {
-          // each lane's column: its query token's keys
-          qk.consume_cols(t, tok0, hi_all, p.window, at.s.start, at.s.L, lane);
-        }
+        // each lane's column: its query token's keys, masked only where some column's range
+        // ends inside the tile
+        qk.consume_cols_flex(t, tok0 >= lo_all && tok0 + kTileTokens <= hi_all, tok0, hi_all,
+                             p.window, at.s.start, at.s.L, lane);
       } else {
         if (tok0 >= at.s.start && tok0 + kTileTokens <= at.s.L)
           qk.template consume<false>(t, 0, 0, 0, lane);
@@ -394,7 +396,69 @@ void balanced_decode_kernel(const BalancedParams bp) {
     }
   };
 
-  if constexpr (DEPTH > 1) {
+  if constexpr (AHEAD > 0) {
+    // the ring: slot k % NBUF holds tile k (per head of the unit: K rows, then V rows,
+    // kRowBytes each, pieces placed as QK::fill_from_lds reads them); copy m of a tile moves
+    // pieces 64 m .. 64 m + 63, lane i piece 64 m + i, which is, within its head's part, one
+    // half's row (piece / PR) % 16, pool piece (piece % PR) ^ (row & swizzle)
+    constexpr int RB = QK::kRowBytes;
+    constexpr int PR = RB / 16;
+    constexpr int HP = QK::kHeads;
+    constexpr int TBH = 2 * kTileTokens * RB;   // one head's part
+    constexpr int TB = HP * TBH;
+    constexpr int NBUF = AHEAD + 1;
+    constexpr int PL = TB / (16 * kWave);
+    constexpr int PLH = PL / HP;                // copies per head
+    static_assert(PLH * 16 * kWave == TBH && (kTileTokens * PR) % kWave == 0,
+                  "a tile half is whole copies");
+    __shared__ __attribute__((aligned(16))) char s_tiles[NBUF * TB];
+    const int rs = (int)p.kv_row_stride;
+    uint32_t voff[PLH];
+#pragma unroll
+    for (int m = 0; m < PLH; ++m) {
+      const int piece = m * kWave + lane;
+      const int row = (piece / PR) % kTileTokens;
+      voff[m] = (uint32_t)(row * rs + (((piece % PR) ^ (row & QK::kLdsSwizzle)) << 4));
+    }
+    uint32_t okbits = 0;   // bit k % NBUF: tile k came from the pool
+    // copy tile k into its slot; a tile whose table entry lies outside the pool is copied from
+    // q instead (valid memory, never read back) so that every tile counts the same copies
+    auto copy = [&](int k) {
+      Cursor at;
+      const int64_t off = walk.next(ctx, k, n, at);
+      const int slot = k % NBUF;
+      const bool good = off >= 0;
+      okbits = (okbits & ~(1u << slot)) | ((good ? 1u : 0u) << slot);
+#pragma unroll
+      for (int m = 0; m < PL; ++m) {
+        const int mh = m % PLH;                                  // constants
+        const bool vh = mh * kWave >= kTileTokens * PR;          // the copy's half
+        const int64_t ho = m / PLH == 0 ? 0 : p.kv_pair_off;     // the copy's head
+        const char* base = good ? (vh ? p.v_cache : p.k_cache) + off + ho
+                                : reinterpret_cast<const char*>(p.q);
+        copy_piece_to_lds_s<true>(base, good ? voff[mh] : (uint32_t)(lane & 7) * 16,
+                                  s_tiles + slot * TB + m * kWave * 16);
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < AHEAD; ++j)
+      if (j < n) copy(j);
+    for (int k = 0; k < n; ++k) {
+      // tile k's copies are done once at most those of the AHEAD - 1 later tiles are in flight
+      // (vector memory operations complete in order; anything else issued since only makes the
+      // wait stricter); near the end fewer follow and everything is waited for.  The slot the
+      // next copy fills held tile k - 1, read into registers and consumed before this point.
+      if (k + AHEAD - 1 < n)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PL * (AHEAD - 1)) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (k + AHEAD < n) copy(k + AHEAD);
+      typename QK::Tile t;
+      const bool ok = (okbits >> (k % NBUF)) & 1u;
+      if (ok) qk.fill_from_lds(t, s_tiles + (k % NBUF) * TB, lane);
+      consume(k, t, ok);
+    }
+  } else if constexpr (DEPTH > 1) {
     // DEPTH tiles in flight: the loads of tiles k+1 .. k+DEPTH-1 are issued before tile k is
     // consumed; the loop is unrolled DEPTH times so every buffer index is a constant
     typename QK::Tile t[DEPTH];
@@ -551,10 +615,13 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
 
   __shared__ float s_acc[RPS][H * D];
   __shared__ float s_m[RPS][H], s_z[RPS][H];
-  __shared__ int s_nan;
-  if (tid == 0) s_nan = 0;
+  // NaN column by column: a NaN key or length reaches only the columns whose pieces carry it
+  // (with KV-head pairs a unit holds two KV heads, and with several query tokens a column may
+  // not attend the key)
+  __shared__ int s_nan[H];
+  if (tid < H) s_nan[tid] = 0;
   __syncthreads();
-  if (nan) s_nan = 1;
+  if (nan) s_nan[hl] = 1;
   *reinterpret_cast<float4*>(&s_acc[pr][4 * f]) = a;
   if ((4 * f) % D == 0) {   // the first slice of a head carries the head's (max, sum)
     s_m[pr][hl] = m;
@@ -583,7 +650,7 @@ __global__ __launch_bounds__(kFixupThreads) void balanced_fixup_kernel(const Bal
     }
     float ov = Z > 0.f ? o / Z : 0.f;
     float lv = Z > 0.f ? M + fast_log2(Z) * kLn2 : -INFINITY;
-    if (s_nan) {
+    if (s_nan[h]) {
       ov = __builtin_nanf("");
       lv = __builtin_nanf("");
     }
@@ -601,24 +668,39 @@ namespace {
 template <int D, int G, QkPath PATH>
 using BQK = QkPolicy<D, G, PATH>;
 
-// tiles in flight per worker: two where the registers allow it (for FP8 tiles too: four,
-// for the same bytes in flight, measured slower)
+// tiles in flight per worker: two in registers where the registers allow it
 template <int D, int G, QkPath PATH>
 constexpr int bal_depth() {
   return (D * G <= 512 || G == 32) ? 2 : 1;
+}
+// or, for FP8 tiles (half the bytes of a bf16 tile, and twice the instructions per byte), tiles
+// copied ahead into a ring in LDS: its registers are then free for more workers per SIMD.
+// Measured (decode µs, FP8 Llama-8B-shaped step / mixed batch / head_dim 256 sweep point):
+// one tile ahead 62.5 / 109.3 / 172.9, two 63.6 / 119.9 / 179.8, three 63.8 / 124.4 / 174.7;
+// at head_dim 64 two ahead (52.5) beat one (57.8).  bf16 tiles stay in registers: a ring of
+// three or four 8 KiB tiles at one worker per SIMD measured 113.9 µs against 110.4 for the
+// register form at two.
+#ifndef PA_BAL_AHEAD_FP8_PAIRS
+#define PA_BAL_AHEAD_FP8_PAIRS 1
+#endif
+template <int D, int G, QkPath PATH>
+constexpr int bal_ahead() {
+  if (PATH == QkPath::kMfmaPvFp8Heads2) return PA_BAL_AHEAD_FP8_PAIRS;
+  return PATH == QkPath::kMfmaPvFp8 ? (D == 64 ? 2 : 1) : 0;
 }
 
 template <int D, int G, QkPath PATH, bool MULTI>
 const void* balanced_kernel_ptr() {
   return reinterpret_cast<const void*>(
-      &balanced_decode_kernel<D, G, bal_depth<D, G, PATH>(), BQK<D, G, PATH>, MULTI>);
+      &balanced_decode_kernel<D, G, bal_depth<D, G, PATH>(), BQK<D, G, PATH>, MULTI,
+                              bal_ahead<D, G, PATH>()>);
 }
 
 template <int D, int G, QkPath PATH, bool MULTI>
 hipError_t launch_bal(const BalancedParams& bp, hipStream_t stream) {
-  hipLaunchKernelGGL(
-      (balanced_decode_kernel<D, G, bal_depth<D, G, PATH>(), BQK<D, G, PATH>, MULTI>),
-      dim3(bp.num_workers), dim3(kWave), 0, stream, bp);
+  hipLaunchKernelGGL((balanced_decode_kernel<D, G, bal_depth<D, G, PATH>(), BQK<D, G, PATH>,
+                                             MULTI, bal_ahead<D, G, PATH>()>),
+                     dim3(bp.num_workers), dim3(kWave), 0, stream, bp);
   return hipGetLastError();
 }
 
@@ -669,6 +751,10 @@ constexpr bool has_32_columns() {
 // up to 8 columns (heads); several: the matrix-core P.V paths at 2 to 32 columns.
 template <int D, int G, QkPath PATH, bool MULTI>
 constexpr bool bal_exists() {
+  // head pairs: one query token, 4 or 8 columns (the query heads of two KV heads of a group of
+  // 2 or 4), head_dim 64 (the plans pair KV heads there only)
+  if constexpr (PATH == QkPath::kMfmaPvHeads2 || PATH == QkPath::kMfmaPvFp8Heads2)
+    return !MULTI && (G == 4 || G == 8) && D == 64;
   if constexpr (G == 32) return MULTI && has_32_columns<D, PATH>();
   if constexpr (G == 16) return MULTI && has_16_columns<PATH>();
   if constexpr (MULTI) return G >= 2 && has_16_columns<PATH>();
@@ -749,6 +835,10 @@ hipError_t launch_balanced(const BalancedParams& bp, int head_dim, int group, Qk
     case QkPath::kMfma: return launch_bal_d<QkPath::kMfma>(bp, head_dim, group, multi, stream);
     case QkPath::kMfmaPvFp8:
       return launch_bal_d<QkPath::kMfmaPvFp8>(bp, head_dim, group, multi, stream);
+    case QkPath::kMfmaPvHeads2:
+      return launch_bal_d<QkPath::kMfmaPvHeads2>(bp, head_dim, group, multi, stream);
+    case QkPath::kMfmaPvFp8Heads2:
+      return launch_bal_d<QkPath::kMfmaPvFp8Heads2>(bp, head_dim, group, multi, stream);
     default: return launch_bal_d<QkPath::kMfmaPv>(bp, head_dim, group, multi, stream);
   }
 }
@@ -775,6 +865,10 @@ int balanced_default_workers(int head_dim, int group, QkPath path, bool multi) {
                   : path == QkPath::kMfma ? bal_ptr<QkPath::kMfma>(head_dim, group, multi)
                   : path == QkPath::kMfmaPvFp8
                       ? bal_ptr<QkPath::kMfmaPvFp8>(head_dim, group, multi)
+                  : path == QkPath::kMfmaPvHeads2
+                      ? bal_ptr<QkPath::kMfmaPvHeads2>(head_dim, group, multi)
+                  : path == QkPath::kMfmaPvFp8Heads2
+                      ? bal_ptr<QkPath::kMfmaPvFp8Heads2>(head_dim, group, multi)
                       : bal_ptr<QkPath::kMfmaPv>(head_dim, group, multi);
   if (k == nullptr) return -1;
   int dev = 0, cus = 0, per_cu = 0;
@@ -783,6 +877,10 @@ int balanced_default_workers(int head_dim, int group, QkPath path, bool multi) {
     return -1;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kWave, 0) != hipSuccess)
     return -1;
+  // a whole number of workers per SIMD (four per CU): a SIMD with one worker more than the
+  // others runs each of its workers slower, and the launch waits for the slowest (measured:
+  // ten FP8 workers per CU took 83 us where eight took 66)
+  if (per_cu >= 4) per_cu &= ~3;
   const long long n = (long long)cus * (per_cu > 0 ? per_cu : 1);
   return (int)(n < (1 << 20) ? n : (1 << 20));
 }

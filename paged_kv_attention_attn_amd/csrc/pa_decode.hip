@@ -363,6 +363,8 @@ const char* qk_path_name(QkPath path) {
     case QkPath::kValu: return "valu";
     case QkPath::kMfma: return "mfma";
     case QkPath::kMfmaPvFp8: return "mfmapv_fp8";
+    case QkPath::kMfmaPvHeads2: return "mfmapv_headpairs";
+    case QkPath::kMfmaPvFp8Heads2: return "mfmapv_fp8_headpairs";
     default: return "mfmapv";
   }
 }

@@ -52,6 +52,28 @@ __device__ __forceinline__ T kv_load(const T* p) {
   else return *p;
 }
 
+// One 16-byte piece per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i's piece from base + voff (base wave-uniform, in scalar registers; voff the lane's
+// 32-bit offset) to lds_wave_base + 16 i (M0 holds the wave's LDS base).  NT: with the
+// non-temporal hint.  The instruction writes no register and is counted by vmcnt until its
+// data sits in LDS, so the caller waits for it (s_waitcnt vmcnt) before reading the piece.
+// Inline assembly, so that the compiler does not take every later LDS read as possibly
+// aliasing a copy in flight and wait for all copies before it.
+template <bool NT = false>
+__device__ __forceinline__ void copy_piece_to_lds_s(const char* base, uint32_t voff,
+                                                    const char* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>(lds_wave_base));
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 ::"s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 ::"s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+
 // Load the kWords words lane c holds of the row starting at byte address `row`.
 template <int D, bool NT = true>
 __device__ __forceinline__ void load_row(const char* __restrict__ row, int c,

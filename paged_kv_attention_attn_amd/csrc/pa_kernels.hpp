@@ -40,6 +40,10 @@ struct DecodeParams {
   int64_t kv_block_stride;
   int64_t kv_head_stride;
   int64_t kv_row_stride;
+  // Head-pair kernels (QkPath::kMfmaPvHeads2, kMfmaPvFp8Heads2): a unit is KV heads 2u and 2u + 1, num_kv_heads
+  // and kv_head_stride count pairs, group counts the pair's query heads, and the second head's
+  // rows sit kv_pair_off bytes after the first's.  0 otherwise.
+  int64_t kv_pair_off;
   // Split only, optional: the last partition of each (sequence, KV head) to finish merges them
   // all into final_out [B][Hq][D] / final_lse [B][Hq] (or null).  merge_counters [B][Hkv] are
   // zero on entry and left zero.
@@ -121,7 +125,14 @@ struct WitnessParams {
 // (kValu); q.k on the matrix cores with P.V on the vector ALUs (kMfma); or both on the matrix
 // cores, P carried as two bf16 terms (kMfmaPv); the same for a KV cache of FP8 E4M3 codes with
 // per-tensor scales, converted to bf16 in registers (kMfmaPvFp8).
-enum class QkPath { kValu = 0, kMfma = 1, kMfmaPv = 2, kMfmaPvFp8 = 3 };
+enum class QkPath {
+  kValu = 0,
+  kMfma = 1,
+  kMfmaPv = 2,
+  kMfmaPvFp8 = 3,
+  kMfmaPvHeads2 = 4,      // bf16 KV-head pairs (balanced, one query token)
+  kMfmaPvFp8Heads2 = 5,   // FP8 KV-head pairs
+};
 // Short name of a path ("valu", "mfma", "mfmapv").
 const char* qk_path_name(QkPath path);
 // Grid: one workgroup per (partition slot, KV head, sequence), 1-D.
@@ -159,8 +170,10 @@ int qblock_columns(int head_dim);
 // Fills tokens_per_block, waves, blocks_per_seq, xcd_pinned, splits, split_tiles and grid;
 // max_seq_len (a host-side bound on the lengths, 0 if unknown) sizes the key splits.
 void qblock_geometry(QBlockParams& qp, int head_dim, int max_seq_len);
-// The query-block kernels, then (splits > 1) the merge of the partials into d.out / d.lse.
+// The query-block kernels; with key splits (splits > 1) launch_qblock_merge then merges the
+// partials into d.out / d.lse (a no-op without splits).
 hipError_t launch_qblock(const QBlockParams& qp, int head_dim, QkPath path, hipStream_t stream);
+hipError_t launch_qblock_merge(const QBlockParams& qp, int head_dim, hipStream_t stream);
 
 hipError_t launch_witness(const WitnessParams& p, int head_dim, int num_seqs, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int num_wg, uint32_t* sink,

@@ -423,18 +423,6 @@ __device__ __forceinline__ constexpr int fa_key(int v, int h) {
   return 8 * (v >> 2) + 4 * h + (v & 3);
 }
 
-// One 16-byte piece per lane from global memory straight into LDS: lane i's piece from
-// base + voff (base wave-uniform, in scalar registers) to lds_wave_base + 16 i.  As
-// copy_piece_to_lds, with the per-lane part of the address a 32-bit offset.
-__device__ __forceinline__ void copy_piece_to_lds_s(const char* base, uint32_t voff,
-                                                    const char* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)reinterpret_cast<uintptr_t>(lds_wave_base));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               ::"s"(lds), "v"(voff), "s"(base)
-               : "memory", "m0");
-}
-
 constexpr int kFaAhead = 3;   // 32-key tiles copied ahead (LDS ring of kFaAhead + 1)
 
 // max and sum over the two lane halves (lanes l and l ^ 32), without the LDS crossbar:
@@ -955,14 +943,16 @@ void qblock_geometry(QBlockParams& qp, int head_dim, int max_seq_len) {
 
 hipError_t launch_qblock(const QBlockParams& qp, int head_dim, QkPath path, hipStream_t stream) {
   if (qp.grid == 0) return hipSuccess;
-  hipError_t e;
   switch (head_dim) {
-    case 64: e = launch_d<64>(qp, path, stream); break;
-    case 128: e = launch_d<128>(qp, path, stream); break;
-    case 256: e = launch_d<256>(qp, path, stream); break;
+    case 64: return launch_d<64>(qp, path, stream);
+    case 128: return launch_d<128>(qp, path, stream);
+    case 256: return launch_d<256>(qp, path, stream);
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess || qp.splits == 1) return e;
+}
+
+hipError_t launch_qblock_merge(const QBlockParams& qp, int head_dim, hipStream_t stream) {
+  if (qp.grid == 0 || qp.splits == 1) return hipSuccess;
   switch (head_dim) {
     case 64: return launch_merge<64>(qp, stream);
     case 128: return launch_merge<128>(qp, stream);

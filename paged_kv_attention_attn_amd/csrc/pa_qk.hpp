@@ -413,7 +413,14 @@ __device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t x) {
 // one fp32 scale per tensor.  K and V are converted to bf16 in registers (exactly) and go
 // through the same MFMAs; the K scale is folded into the score scale by the host and the V
 // scale multiplies the output.  NT: K/V loads carry the non-temporal hint (rows read once).
-template <int D, int G, bool FP8, bool NT = true>
+// HP = 2 (one query token): a unit is a pair of adjacent KV heads, G = 2 * group columns
+// (the query heads of both, in order), and a tile holds both heads' 16-token K and V rows.  Each
+// head's K runs its own score MFMAs and each lane keeps the scores of its column's head; each
+// head's V runs its own P.V MFMAs into its own accumulators, whose rows of the other head's
+// columns are never read.  (Masking the operands instead would let 0 x NaN from one head's
+// rows reach the other's.)  A step then streams two heads' rows, the bytes of one head_dim-256
+// tile at head_dim 128, for the same per-byte work.
+template <int D, int G, bool FP8, bool NT = true, int HP = 1>
 struct QkMfmaPvT {
   static constexpr int KK = D / 32;
   static constexpr int W = RowGeom<D>::kWords;
@@ -425,13 +432,17 @@ struct QkMfmaPvT {
   // tile, so the per-tile instruction stream weighs twice as much) that pays; a floor of three
   // (168 registers at D = 128, with two spilled) measured no better.
   static constexpr int kMinWavesPerEu = FP8 && D <= 128 ? 2 : 1;
+  static_assert(HP == 1 || (HP == 2 && G <= 8), "head pairs: head-wise columns");
   static constexpr int VW = FP8 ? E / 4 : W;   // words a lane holds of one V row
   static_assert(!FP8 || E == 4 * VW, "an FP8 lane slice is whole words");
   // K: bf16, one 16-byte piece per score MFMA; FP8, one 16-byte piece per two (halves)
   static constexpr int KL = FP8 ? KK / 2 : KK;
-  struct Tile {
+  struct TileHead {
     u32x4_t k[KL];
     uint32_t v[kTileSteps][VW];
+  };
+  struct Tile {
+    TileHead x[HP];
   };
   // Columns: the N side of both contractions is (query token, head) pairs, n = i * group + h,
   // G of them at most (q_len * group <= G <= 16); with one query token a column is a head.
@@ -442,7 +453,10 @@ struct QkMfmaPvT {
   static constexpr bool kColumns = G == 16;
   static constexpr bool kQueryTokens = true;   // columns may be several query tokens
   static constexpr int kHalves = 1;
+  static constexpr int kHeads = HP;
   u32x4_t qb[KK];
+  bool half1;                        // head pairs: this lane's column belongs to the second head
+  int64_t pair_off;                  // head pairs: bytes from a pair's first head to its second
   float c2;
   float vs;   // FP8: V scale
   bool head_lane;
@@ -450,6 +464,7 @@ struct QkMfmaPvT {
   float m, l;
   float lsum;  // after merge_cols: the column's sum over the row groups
   f32x4_t cacc[E];
+  f32x4_t cacc1[HP == 2 ? E : 1];   // head pairs: P.V of the second head's V
   float up[(G > 4 && G <= 8) ? 4 : 1][E];   // G = 8: heads 4..7 brought up by merge_rows
 
   // q rows of the unit whose first head is h0 (= KV head * group): lane column n (col_base +
@@ -465,6 +480,7 @@ struct QkMfmaPvT {
     const char* qrow = reinterpret_cast<const char*>(
         p.q + (((size_t)b * qs.q_total + qs.q_first + (head_lane ? col_q : 0)) * p.num_q_heads +
                h0 + (head_lane ? hh : 0)) * D);
+    half1 = HP == 2 && n >= G / 2;
     const uint32_t keep = head_lane ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -485,6 +501,10 @@ struct QkMfmaPvT {
     l = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) cacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (HP == 2) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) cacc1[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
   }
   int rs;   // bytes between a block's consecutive K/V rows (the pool layout's row stride)
   __device__ __forceinline__ void init(const DecodeParams& p, const QShape& qs, int b, int h0,
@@ -492,11 +512,17 @@ struct QkMfmaPvT {
     c2 = c2_;
     rs = (int)p.kv_row_stride;
     vs = p.v_scale;
+    pair_off = p.kv_pair_off;
     load_q(p, qs, b, h0, lane, qflip, col_base);
     reset();
   }
 
   __device__ __forceinline__ void issue(Tile& t, const char* kb, const char* vb, int lane) const {
+    issue_head(t.x[0], kb, vb, lane);
+    if constexpr (HP == 2) issue_head(t.x[1], kb + pair_off, vb + pair_off, lane);
+  }
+  __device__ __forceinline__ void issue_head(TileHead& t, const char* kb, const char* vb,
+                                             int lane) const {
     const int mrow = lane & 15;
     const int tok = 4 * (mrow & 3) + (mrow >> 2);
     if constexpr (FP8) {
@@ -545,7 +571,14 @@ struct QkMfmaPvT {
            ((((off >> 4) ^ (row & kLdsSwizzle))) << 4) + (off & 15);
   }
   // Fill t from such a copy: the same pieces issue() reads from the pool.
-  __device__ __forceinline__ void fill_from_lds(Tile& t, const char* tile, int lane) const {
+  // A head pair's copy holds the second head's tile (K rows, then V rows) after the first's.
+  static constexpr int kHeadTileBytes = 2 * kTileTokens * kRowBytes;
+  __device__ __forceinline__ void fill_from_lds(Tile& tt, const char* tile, int lane) const {
+    fill_head_from_lds(tt.x[0], tile, lane);
+    if constexpr (HP == 2) fill_head_from_lds(tt.x[1], tile + kHeadTileBytes, lane);
+  }
+  __device__ __forceinline__ void fill_head_from_lds(TileHead& t, const char* tile,
+                                                     int lane) const {
     const int mrow = lane & 15;
     const int tok = 4 * (mrow & 3) + (mrow >> 2);
     const int g = lane >> 4, c = lane & 15;
@@ -602,28 +635,57 @@ struct QkMfmaPvT {
   template <bool MASKED>
   __device__ __forceinline__ void consume(Tile& t, int tok0, int lo, int hi, int vlo, int vhi,
                                           int lane) {
+    consume_impl<MASKED ? 1 : 0>(t, false, tok0, lo, hi, vlo, vhi, lane);
+  }
+  // One code path for every tile of a loop, masked unless `full` (wave-uniform: every key of
+  // the tile attended by every column).  Separate masked and unmasked paths through the
+  // matrix instructions leave the compiler two versions of the accumulators to merge after
+  // them, which it does by copying all of them, twice per tile; here only the masking step is
+  // conditional.
+  __device__ __forceinline__ void consume_flex(Tile& t, bool full, int tok0, int lo, int hi,
+                                               int vlo, int vhi, int lane) {
+    consume_impl<2>(t, full, tok0, lo, hi, vlo, vhi, lane);
+  }
+  // consume_flex with the column's own key range (as consume_cols)
+  __device__ __forceinline__ void consume_cols_flex(Tile& t, bool full, int tok0, int hi_base,
+                                                    int window, int vlo, int vhi, int lane) {
+    const int hi = hi_base + col_q;
+    const int lo = window > 0 ? max(hi - window, 0) : 0;
+    consume_impl<2>(t, full, tok0, lo, hi, vlo, vhi, lane);
+  }
+  // MODE 0: every key attended (the score scale folded into the exponent); 1: masked; 2:
+  // masked unless `full`.
+  template <int MODE>
+  __device__ __forceinline__ void consume_impl(Tile& t, bool full, int tok0, int lo, int hi,
+                                               int vlo, int vhi, int lane) {
+    constexpr bool MASKED = MODE != 0;
     const int g = lane >> 4;
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t sc = scores(t.x[0]);
+    if constexpr (HP == 2) {
+      const f32x4_t sc1 = scores(t.x[1]);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4_t kw;
-      if constexpr (FP8) {
-        const u32x4_t x = t.k[kk >> 1];
-        kw = fp8x8_to_bf16x8((kk & 1) ? u32x2_t{x.z, x.w} : u32x2_t{x.x, x.y});
-      } else {
-        kw = t.k[kk];
-      }
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw),
-                                                   __builtin_bit_cast(bf16x8_t, qb[kk]), sc, 0,
-                                                   0, 0);
+      for (int i = 0; i < 4; ++i) sc[i] = half1 ? sc1[i] : sc[i];
     }
-    if constexpr (MASKED) {
+    if constexpr (MODE == 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tk = tok0 + 4 * i + g;
         sc[i] = (tk >= lo && tk < hi) ? sc[i] * c2 : -INFINITY;
       }
-      mask_v_words<VW>(t.v, tok0, vlo, vhi, lane);
+#pragma unroll
+      for (int hp = 0; hp < HP; ++hp) mask_v_words<VW>(t.x[hp].v, tok0, vlo, vhi, lane);
+    } else if constexpr (MODE == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] *= c2;
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tk = tok0 + 4 * i + g;
+          sc[i] = (tk >= lo && tk < hi) ? sc[i] : -INFINITY;
+        }
+#pragma unroll
+        for (int hp = 0; hp < HP; ++hp) mask_v_words<VW>(t.x[hp].v, tok0, vlo, vhi, lane);
+      }
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     if constexpr (!MASKED) mx *= c2;
@@ -641,6 +703,10 @@ struct QkMfmaPvT {
             float, __builtin_amdgcn_ds_bpermute((4 * g + i) << 2, __builtin_bit_cast(int, alpha)));
 #pragma unroll
         for (int e = 0; e < E; ++e) cacc[e][i] *= a_i;
+        if constexpr (HP == 2) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) cacc1[e][i] *= a_i;
+        }
       }
     }
     const float mu = m == -INFINITY ? 0.f : m;
@@ -663,22 +729,50 @@ struct QkMfmaPvT {
     const s16x4_t a_hi = __builtin_bit_cast(s16x4_t, u32x2_t{uh01, uh23});
     const s16x4_t a_lo = __builtin_bit_cast(
         s16x4_t, u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
+    pv_head(t.x[0], a_hi, a_lo, cacc);
+    if constexpr (HP == 2) pv_head(t.x[1], a_hi, a_lo, cacc1);
+  }
+
+  // q.k of one head's tile: the scores of this lane's column for the four tokens of its row
+  // group (unscaled)
+  __device__ __forceinline__ f32x4_t scores(const TileHead& th) const {
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4_t kw;
+      if constexpr (FP8) {
+        const u32x4_t x = th.k[kk >> 1];
+        kw = fp8x8_to_bf16x8((kk & 1) ? u32x2_t{x.z, x.w} : u32x2_t{x.x, x.y});
+      } else {
+        kw = th.k[kk];
+      }
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw),
+                                                   __builtin_bit_cast(bf16x8_t, qb[kk]), sc, 0,
+                                                   0, 0);
+    }
+    return sc;
+  }
+
+  // P.V of one head's tile into acc: P as the two bf16 terms a_hi + a_lo
+  __device__ __forceinline__ static void pv_head(const TileHead& th, s16x4_t a_hi, s16x4_t a_lo,
+                                                 f32x4_t (&acc)[E]) {
     // B: element e of the slice of tokens 4j+g, j = 0..3, as bf16 pairs {token 4j+g of rows
     // j = 0, 1} and {j = 2, 3}
     const auto pv = [&](int e, uint32_t b01, uint32_t b23) {
       const s16x4_t bv = __builtin_bit_cast(s16x4_t, u32x2_t{b01, b23});
-      cacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, bv, cacc[e], 0, 0, 0);
-      cacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, bv, cacc[e], 0, 0, 0);
+      acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, bv, acc[e], 0, 0, 0);
+      acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, bv, acc[e], 0, 0, 0);
     };
+    const auto& v = th.v;
     if constexpr (FP8) {
       // word w holds elements 4w..4w+3 of a row: interleave the bytes of rows (0, 1) and (2, 3)
       // (x: elements 4w, 4w+1; y: 4w+2, 4w+3), then each half converts to one bf16 pair
 #pragma unroll
       for (int w = 0; w < VW; ++w) {
-        const uint32_t x01 = __builtin_amdgcn_perm(t.v[1][w], t.v[0][w], 0x05010400u);
-        const uint32_t y01 = __builtin_amdgcn_perm(t.v[1][w], t.v[0][w], 0x07030602u);
-        const uint32_t x23 = __builtin_amdgcn_perm(t.v[3][w], t.v[2][w], 0x05010400u);
-        const uint32_t y23 = __builtin_amdgcn_perm(t.v[3][w], t.v[2][w], 0x07030602u);
+        const uint32_t x01 = __builtin_amdgcn_perm(v[1][w], v[0][w], 0x05010400u);
+        const uint32_t y01 = __builtin_amdgcn_perm(v[1][w], v[0][w], 0x07030602u);
+        const uint32_t x23 = __builtin_amdgcn_perm(v[3][w], v[2][w], 0x05010400u);
+        const uint32_t y23 = __builtin_amdgcn_perm(v[3][w], v[2][w], 0x07030602u);
         pv(4 * w + 0, fp8x2_to_bf16x2<false>(x01), fp8x2_to_bf16x2<false>(x23));
         pv(4 * w + 1, fp8x2_to_bf16x2<true>(x01), fp8x2_to_bf16x2<true>(x23));
         pv(4 * w + 2, fp8x2_to_bf16x2<false>(y01), fp8x2_to_bf16x2<false>(y23));
@@ -689,8 +783,8 @@ struct QkMfmaPvT {
       for (int e = 0; e < E; ++e) {
         // bf16 halves gathered by v_perm
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        pv(e, __builtin_amdgcn_perm(t.v[1][e / 2], t.v[0][e / 2], sel),
-           __builtin_amdgcn_perm(t.v[3][e / 2], t.v[2][e / 2], sel));
+        pv(e, __builtin_amdgcn_perm(v[1][e / 2], v[0][e / 2], sel),
+           __builtin_amdgcn_perm(v[3][e / 2], v[2][e / 2], sel));
       }
     }
   }
@@ -709,7 +803,8 @@ struct QkMfmaPvT {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) up[i][e] = xor_lane(cacc[e][i], 16);
+        for (int e = 0; e < E; ++e)
+          up[i][e] = xor_lane(HP == 2 ? cacc1[e][i] : cacc[e][i], 16);
       }
     }
   }
@@ -717,7 +812,11 @@ struct QkMfmaPvT {
   // (times the V scale for an FP8 cache).
   __device__ __forceinline__ float out(int h, int e) const {
     static_assert(G <= 8, "out() covers eight columns");
-    const float x = h < 4 ? cacc[e][h & 3] : up[(h - 4) & 3][e];
+    // head pairs: heads h < G / 2 are the first KV head's, in cacc; the rest the second's (in
+    // cacc1, or for G = 8 brought up from row group 1 by merge_rows)
+    const float x = HP == 2 && G <= 4 ? (h < G / 2 ? cacc[e][h & 3] : cacc1[e][h & 3])
+                    : h < 4           ? cacc[e][h & 3]
+                                      : up[(h - 4) & 3][e];
     return FP8 ? x * vs : x;
   }
 
@@ -755,6 +854,7 @@ struct QkMfmaPvPair {
   static constexpr bool kColumns = true;
   static constexpr bool kQueryTokens = true;
   static constexpr int kHalves = 2;
+  static constexpr int kHeads = 1;
   Half h[2];
 
   __device__ __forceinline__ void init(const DecodeParams& p, const QShape& qs, int b, int h0,
@@ -789,6 +889,11 @@ struct QkMfmaPvPair {
     h[0].consume_cols(t, tok0, hi_base, window, vlo, vhi, lane);
     h[1].consume_cols(t, tok0, hi_base, window, vlo, vhi, lane);
   }
+  __device__ __forceinline__ void consume_cols_flex(Tile& t, bool full, int tok0, int hi_base,
+                                                    int window, int vlo, int vhi, int lane) {
+    h[0].consume_cols_flex(t, full, tok0, hi_base, window, vlo, vhi, lane);
+    h[1].consume_cols_flex(t, full, tok0, hi_base, window, vlo, vhi, lane);
+  }
 };
 
 // The policy of a path (32 columns: the matrix-core P.V pair).
@@ -799,7 +904,13 @@ using QkPolicy = typename std::conditional<
         PATH == QkPath::kValu, QkValu<D, G>,
         typename std::conditional<
             PATH == QkPath::kMfma, QkMfma<D, G>,
-            typename std::conditional<PATH == QkPath::kMfmaPv, QkMfmaPv<D, G>,
-                                      QkMfmaPvFp8<D, G>>::type>::type>::type>::type;
+            typename std::conditional<
+                PATH == QkPath::kMfmaPv, QkMfmaPv<D, G>,
+                typename std::conditional<
+                    PATH == QkPath::kMfmaPvHeads2, QkMfmaPvT<D, G, false, true, 2>,
+                    typename std::conditional<PATH == QkPath::kMfmaPvFp8Heads2,
+                                              QkMfmaPvT<D, G, true, true, 2>,
+                                              QkMfmaPvFp8<D, G>>::type>::type>::type>::type>::
+        type>::type;
 
 }  // namespace pa

@@ -1,5 +1,6 @@
-"""Test and measurement entry points (include/paged_attn_debug.h): the gather witness, the
-streaming-read and gather-read probes and the plain copy kernel.  Argument marshalling only."""
+"""Test and measurement entry points (include/paged_attn_debug.h): the gather witnesses, the
+streaming-read and gather-read probes, the plain copy kernel and a plan run with the decode
+kernel bracketed by HIP events.  Argument marshalling only."""
 from __future__ import annotations
 
 import ctypes
@@ -87,3 +88,27 @@ def copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
     st = lib().paged_attn_copy(_ptr(dst), _ptr(src), nbytes, _stream(src.device, stream))
     if st != PA_OK:
         raise PagedAttnError(st, "paged_attn_copy")
+
+
+def plan_run_timed(plan, q, k_cache, v_cache, block_table, seq_lens, scale: float, *, out,
+                   ev_before, ev_after, lse=None, sinks=None, workspace=None, stream=None,
+                   k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """Plan.run with ``ev_before`` / ``ev_after`` (torch.cuda.Event objects, already created:
+    record each once before the first call) recorded on the launch stream right before and
+    after the plan's decode kernel, so that ``ev_before.elapsed_time(ev_after)`` is that
+    kernel's own duration."""
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("seq_lens", seq_lens), ("out", out),
+                    ("lse", lse), ("sinks", sinks), ("workspace", workspace)):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    h0, h1 = ev_before.cuda_event, ev_after.cuda_event
+    if not h0 or not h1:
+        raise ValueError("record the events once before passing them")
+    st = lib().paged_attn_plan_run_timed(plan._h, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(block_table), _ptr(seq_lens), float(scale),
+                                         float(k_scale), float(v_scale), _ptr(sinks), _ptr(out),
+                                         _ptr(lse), _ptr(workspace),
+                                         _stream(out.device, stream), h0, h1)
+    if st != PA_OK:
+        raise PagedAttnError(st, "paged_attn_plan_run_timed")

@@ -394,15 +394,37 @@ def test_plan_create_and_workspace_sizes():
         a(rows * 128 * 4) + a(rows * 4) + a(2 * 2 * 4)
     assert b"last partition" in pa.lib().paged_attn_plan_name(h)
     pa.lib().paged_attn_plan_destroy(h)
+    # one bf16 token at head_dim 128: one KV head per unit, the eager call's workspace
     st, h = plan_create(shape(), schedule=2, workers=100)
     assert st == 0
     assert pa.lib().paged_attn_plan_workspace_size(h) == pa.balanced_workspace_size(shape(), 128,
                                                                                      100)
-    assert b"workers100" in pa.lib().paged_attn_plan_name(h)
+    assert b"mfmapv_d128_g4_workers100" in pa.lib().paged_attn_plan_name(h)
     pa.lib().paged_attn_plan_destroy(h)
-    # a length bound caps the workers: 2 seqs x 2 KV heads x (7 + 1) tiles / 4 = 8
+    # at head_dim 64 (bf16 or FP8), 2 KV heads of 4 query heads form one KV-head pair per
+    # sequence: 8 columns, the workspace of a shape with one KV head of 8
+    # query heads
+    for hd, kvd, tag in ((64, 0, b"mfmapv_headpairs_d64_g4_workers100"),
+                         (64, 1, b"mfmapv_fp8_headpairs_d64_g4_workers100")):
+        st, h = plan_create(shape(), schedule=2, workers=100, head_dim=hd, kv_dtype=kvd)
+        assert st == 0 and tag in pa.lib().paged_attn_plan_name(h)
+        assert pa.lib().paged_attn_plan_workspace_size(h) == pa.balanced_workspace_size(
+            shape(num_kv_heads=1), hd, 100)
+        pa.lib().paged_attn_plan_destroy(h)
+    # no pairs for an odd number of KV heads (the workspace of the eager call)
+    st, h = plan_create(shape(num_q_heads=12, num_kv_heads=3), schedule=2, workers=100,
+                        head_dim=64)
+    assert st == 0 and b"headpairs" not in pa.lib().paged_attn_plan_name(h)
+    assert pa.lib().paged_attn_plan_workspace_size(h) == pa.balanced_workspace_size(
+        shape(num_q_heads=12, num_kv_heads=3), 64, 100)
+    pa.lib().paged_attn_plan_destroy(h)
+    # a length bound caps the workers: 2 seqs x 2 KV heads x (7 + 1) tiles / 4 = 8, and 4 with
+    # KV-head pairs (one pair per sequence)
     st, h = plan_create(shape(), schedule=2, workers=100, max_len=100)
     assert st == 0 and b"workers8 " in pa.lib().paged_attn_plan_name(h)
+    pa.lib().paged_attn_plan_destroy(h)
+    st, h = plan_create(shape(), schedule=2, workers=100, max_len=100, head_dim=64)
+    assert st == 0 and b"workers4 " in pa.lib().paged_attn_plan_name(h)
     pa.lib().paged_attn_plan_destroy(h)
     # an FP8 cache: the FP8 path under every schedule, the same workspace as bf16
     for sched, sh in ((0, shape()), (1, s), (3, s)):

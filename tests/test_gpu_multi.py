@@ -175,3 +175,22 @@ def test_multi_graph_replay():
     compare(got[0].cpu().numpy().astype(np.float64), got[1].cpu().numpy().astype(np.float64),
             *oracle_full(wl), "multi graph replay")
     t["q"].copy_(q0)
+
+
+@pytest.mark.parametrize("workers", [7, 50])
+def test_multi_nan_key_reaches_only_the_tokens_that_attend_it(workers):
+    """Four query tokens per sequence and a NaN in the key at position L - 2 of sequence 1: the
+    two tokens before that position do not attend it and stay finite, the two at and after it
+    are NaN for that KV head's query heads (units cut into pieces that the fix-up merges)."""
+    wl = make_workload(name="multi nan", seq_lens=[200, 90, 333], num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, seed=[25], poison=True, q_len=4)
+    pos = 88
+    wl.k_cache[wl.block_table[1, pos // 16], 1, pos % 16, 5] = np.uint16(0x7FC0)
+    exp_o, exp_l = oracle_full(wl)
+    assert np.isnan(exp_o[1, 2:, 4:8]).all() and not np.isnan(exp_o[1, :2]).any()
+    got_o, got_l = run_plan(make_plan(wl, "balanced", num_workers=workers), wl, to_dev(wl))
+    bad_o = np.argwhere(np.isnan(got_o) != np.isnan(exp_o))
+    assert bad_o.size == 0, f"NaN pattern of out differs at {bad_o[:6].tolist()}"
+    assert np.array_equal(np.isnan(got_l), np.isnan(exp_l))
+    ok = ~np.isnan(exp_o)
+    assert np.abs(got_o[ok] - exp_o[ok]).max() <= 1e-3

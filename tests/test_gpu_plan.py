@@ -178,3 +178,52 @@ def test_auto_schedule(case):
     log(f"[auto] {case}: {plan.schedule} {plan.name}")
     assert plan.schedule == expected
     compare(*run_plan(plan, wl, to_dev(wl)), *oracle_full(wl), f"auto {case} -> {plan.name}")
+
+
+def _timed_case(case):
+    if case == "qblocks_split":   # two sequences: key splits and their merge
+        return make_workload(name="timed qblocks split", seq_lens=[3000, 2100], num_q_heads=8,
+                             num_kv_heads=2, head_dim=128, block_size=16, seed=[5, 1],
+                             poison=True, q_len=40), "query_blocks"
+    if case == "qblocks":
+        return make_workload(name="timed qblocks", seq_lens=[300, 17, 1000, 41] * 16,
+                             num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                             seed=[5, 2], poison=True, q_len=40), "query_blocks"
+    if case == "fp8":
+        return make_workload(name="timed fp8", seq_lens=[700, 1, 4000, 33], num_q_heads=16,
+                             num_kv_heads=4, head_dim=128, block_size=16, seed=[5, 3],
+                             poison=True, kv_format="fp8_e4m3",
+                             kv_scales=(0.0625, 0.05)), "balanced"
+    return make_config(5, poison=True), case
+
+
+@pytest.mark.parametrize("case", SCHEDULES + ["fp8", "qblocks", "qblocks_split"])
+def test_plan_run_timed_matches_run(case):
+    """The timed run launches what run() launches (bit-identical outputs) and its events
+    bracket a kernel of positive duration that is no longer than the whole step."""
+    from paged_kv_attention_attn_amd import debug
+    wl, schedule = _timed_case(case)
+    plan = make_plan(wl, schedule, partition_size=1024)
+    log(f"[timed] {case} {plan.name}")
+    t = to_dev(wl)
+    ws = plan.workspace("cuda")
+    want = run_plan(plan, wl, t, workspace=ws)
+    out = torch.full(wl.q.shape, float("nan"), device="cuda")
+    lse = torch.full(wl.q.shape[:-1], float("nan"), device="cuda")
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for x in e:
+        x.record()
+    e[2].record()
+    debug.plan_run_timed(plan, t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale),
+                         out=out, lse=lse, sinks=t["sinks"], workspace=ws, k_scale=wl.k_scale,
+                         v_scale=wl.v_scale, ev_before=e[0], ev_after=e[1])
+    e[3].record()
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), want[0].astype(np.float32), equal_nan=True)
+    assert np.array_equal(lse.cpu().numpy(), want[1].astype(np.float32), equal_nan=True)
+    kernel_ms, step_ms = e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3])
+    assert 0.0 < kernel_ms <= step_ms, (kernel_ms, step_ms)
+    with pytest.raises(ValueError):
+        debug.plan_run_timed(plan, t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale),
+                             out=out, ev_before=torch.cuda.Event(enable_timing=True),
+                             ev_after=e[1], sinks=t["sinks"], workspace=ws)
