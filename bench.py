@@ -470,13 +470,16 @@ def workload_label(config: int, D: int, Hq: int, kv: str, q_len: int, seq_lens=N
 
 def row_of(wl, label: str, m: dict, roof_flops: bool = False) -> dict:
     """One workload's figures for the JSON line: µs and KV GB/s per step, fraction of the HBM
-    peak, the decode kernel's µs and rate (the matrix-core rate for the query-block schedule)."""
+    peak, the decode kernel's µs and rate (the matrix-core rate for the query-block schedule),
+    and the decode kernel's measured HBM bytes per launch where the committed counter runs hold
+    them for the current kernel sources (else None)."""
     kv = wl.kv_bytes()
     r = {"workload": f"{label}: {wl.name}", **m, "kv_bytes_per_step": kv,
          "GBps": round(kv / m["us_per_step"] / 1e3, 2),
          "hbm_peak_frac": round(kv / m["us_per_step"] / 1e3 / HBM_PEAK_GBPS, 4),
          "decode_GBps": round(kv / m["decode_us_avg"] / 1e3, 2),
-         "decode_hbm_peak_frac": round(kv / m["decode_us_avg"] / 1e3 / HBM_PEAK_GBPS, 4)}
+         "decode_hbm_peak_frac": round(kv / m["decode_us_avg"] / 1e3 / HBM_PEAK_GBPS, 4),
+         "traffic": measured_traffic(label, m["schedule"])}
     if roof_flops:
         flops = attended_pairs(wl) * wl.num_q_heads * 4 * wl.head_dim
         r["decode_TFLOPs"] = round(flops / m["decode_us_avg"] / 1e6, 2)
