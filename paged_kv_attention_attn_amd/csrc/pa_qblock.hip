@@ -489,6 +489,10 @@ void qblock_fa_kernel(const QBlockParams qp) {
 
   // q rows as B operands of the score MFMAs: dims 16 ks + 8 h .. + 8 of row c
   const float c2 = fabsf(p.qk_scale_log2);
+  // the scale as applied to the scores: at least the smallest normal float, so that a masked
+  // (-inf) score stays -inf under it; with a zero scale every p is exp2 of a number below
+  // 1e-34 in magnitude, which is 1.0f, as with the scale itself
+  const float c2k = fmaxf(c2, 1.17549435e-38f);
   const uint32_t qflip = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
   u32x4_t qb[F::KS];
   {
@@ -580,13 +584,23 @@ void qblock_fa_kernel(const QBlockParams qp) {
   // must not meet p = 0
   const int z_lo = sw.start;
   const int z_hi = min(sw.L, t_end);
-  // LDS addresses of this lane's reads: the score operand of step ks is K row c, piece
-  // (2 ks + h) ^ (c % PR), at k_lane ^ 32 ks; the P.V operands are V rows 16 half + fa_key(j, h),
-  // slice 2 E c .. of each, at v_lane + (16 half + fa_key(j, 0)) * RB
+  // LDS addresses of this lane's reads.  The score operand of step ks is K row c, piece
+  // (2 ks + h) ^ (c % PR), at k_lane ^ 32 ks.  The P.V operand of MFMA e (head dims 32 e ..
+  // 32 e + 31) comes from two transposing reads (ds_read_b64_tr_b16): within each 16-lane
+  // group, lane L reads the 8 bytes of key row k0 + L / 4 at dims 32 e + 16 g + 4 (L % 4)
+  // (g = bit 4 of the lane), and lane j of the group receives dim 32 e + 16 g + j of key rows
+  // k0 .. k0 + 3, k0 = 4 h and 8 + 4 h of each 16-key half: exactly row l % 32 of V^T for the
+  // keys whose probabilities the lane holds
   const uint32_t k_lane = (uint32_t)(c * F::RB + ((h ^ (c & (F::PR - 1))) << 4));
-  const uint32_t v_lane =
-      (uint32_t)((F::kKeys + 4 * h) * F::RB + ((((2 * F::E * c) >> 4) ^ (h * (F::PR / 2))) << 4) +
-                 ((2 * F::E * c) & 15));
+  uint32_t vt_lane[F::E];
+  {
+    const int L = lane & 15, gq = (lane >> 4) & 1;
+#pragma unroll
+    for (int e = 0; e < F::E; ++e) {
+      const int piece = (4 * e + 2 * gq + ((L & 3) >> 1)) ^ F::swz(1, 4 * h);
+      vt_lane[e] = (uint32_t)((F::kKeys + 4 * h + (L >> 2)) * F::RB + (piece << 4) + 8 * (L & 1));
+    }
+  }
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(s_tiles);
 
   // fold tile k, which sits in ring slot SLOT, into this wave's rows
@@ -623,43 +637,38 @@ void qblock_fa_kernel(const QBlockParams qp) {
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kw[ks]),
                                                    __builtin_bit_cast(bf16x8_t, qb[ks]), sc, 0,
                                                    0, 0);
-    // the V reads of both halves go out now, under the softmax: head-dim slice E c .. E c + E
-    // of the eight V rows this lane's half contributes to each 16-key half
-    uint32_t vw[2][8][(F::E + 1) / 2];
+    // the V^T operands of both halves go out now, under the softmax (transposing LDS reads)
+    u32x4_t vt[2][F::E];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t at = tile + v_lane + (16 * half + 8 * (j >> 2) + (j & 3)) * F::RB;
-        if constexpr (F::E == 4) {
-          const u32x2_t x =
-              *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(
-                  (uintptr_t)at);
-          vw[half][j][0] = x.x;
-          vw[half][j][1] = x.y;
-        } else {
-          vw[half][j][0] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
-              (uintptr_t)at);
-        }
+      for (int e = 0; e < F::E; ++e) {
+        const uint32_t at = tile + vt_lane[e] + 16 * half * F::RB;
+        const s16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)at);
+        const s16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(at + 8 * F::RB));
+        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, r0), w1 = __builtin_bit_cast(u32x2_t, r1);
+        vt[half][e] = u32x4_t{w0.x, w0.y, w1.x, w1.y};
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     const int full = __builtin_amdgcn_readfirstlane(
         (tok0 >= lo_all && tok0 + F::kKeys <= min(hi_all, t_end)) ? 1 : 0);
-    float mx;
-    mx = -INFINITY;
-    if (full) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-      mx *= c2;
-    } else {
+    // one path: only the masking of keys outside the row's range is conditional (separate
+    // masked and unmasked paths made the compiler copy the scores between them); the score
+    // scale is applied inside the exponent's FMA, and c2k >= FLT_MIN keeps -inf * c2k = -inf
+    if (!full) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = tok0 + fa_key(v, h);
-        sc[v] = (key >= lo_row && key <= pos && key < t_end) ? sc[v] * c2 : -INFINITY;
-        mx = fmaxf(mx, sc[v]);
+        sc[v] = (key >= lo_row && key <= pos && key < t_end) ? sc[v] : -INFINITY;
       }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+    mx *= c2k;
     mx = halves_max(mx);   // the row's other 16 keys
     if (__builtin_amdgcn_ballot_w64(row_ok && mx > m + kRescaleSlack) != 0) {
       const float mn = fmaxf(m, mx);
@@ -673,13 +682,8 @@ void qblock_fa_kernel(const QBlockParams qp) {
     }
     const float mu = m == -INFINITY ? 0.f : m;
     float pr[16];
-    if (full) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) pr[v] = fast_exp2(fmaf(sc[v], c2, -mu));
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) pr[v] = fast_exp2(sc[v] - mu);
-    }
+    for (int v = 0; v < 16; ++v) pr[v] = fast_exp2(fmaf(sc[v], c2k, -mu));
     float ls = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) ls += pr[v];
@@ -704,15 +708,24 @@ void qblock_fa_kernel(const QBlockParams qp) {
       }
     }
     if (__builtin_amdgcn_readfirstlane((tok0 < z_lo || tok0 + F::kKeys > z_hi) ? 1 : 0)) {
+      // operand value j of a half is key 16 half + fa_key(j, h): keep it where that key is
+      // one some token attends (two bf16 values per word)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
+        uint32_t keep[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = tok0 + 16 * half + fa_key(j, h);
-          const bool keep = t >= z_lo && t < z_hi;
+        for (int w = 0; w < 4; ++w) {
+          const int t0 = tok0 + 16 * half + fa_key(2 * w, h);
+          const int t1 = tok0 + 16 * half + fa_key(2 * w + 1, h);
+          keep[w] = (t0 >= z_lo && t0 < z_hi ? 0x0000FFFFu : 0u) |
+                    (t1 >= z_lo && t1 < z_hi ? 0xFFFF0000u : 0u);
+        }
 #pragma unroll
-          for (int w = 0; w < (F::E + 1) / 2; ++w)
-            vw[half][j][w] = keep ? vw[half][j][w] : 0u;
+        for (int e = 0; e < F::E; ++e) {
+          vt[half][e].x &= keep[0];
+          vt[half][e].y &= keep[1];
+          vt[half][e].z &= keep[2];
+          vt[half][e].w &= keep[3];
         }
       }
     }
@@ -721,12 +734,7 @@ void qblock_fa_kernel(const QBlockParams qp) {
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int e = 0; e < F::E; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x4_t av;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          av[w] = __builtin_amdgcn_perm(vw[half][2 * w + 1][e >> 1], vw[half][2 * w][e >> 1],
-                                        sel);
+        const u32x4_t av = vt[half][e];
         o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                        __builtin_bit_cast(bf16x8_t, bhi[half]),
                                                        o[e], 0, 0, 0);
@@ -778,21 +786,17 @@ void qblock_fa_kernel(const QBlockParams qp) {
     dst = qp.part_out + slot * D;
     if (h == 0) qp.part_lse[slot] = lv;
   }
+  // o[e][v] is head dim 32 e + fa_key(v, h): four consecutive dims per group of four v
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int i = fa_key(v, h);   // head-dim slice E i .. E i + E
-    if constexpr (F::E == 4) {
+  for (int e = 0; e < F::E; ++e) {
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
       float4 x;
-      x.x = bad ? __builtin_nanf("") : o[0][v] * inv;
-      x.y = bad ? __builtin_nanf("") : o[1][v] * inv;
-      x.z = bad ? __builtin_nanf("") : o[2][v] * inv;
-      x.w = bad ? __builtin_nanf("") : o[3][v] * inv;
-      *reinterpret_cast<float4*>(dst + 4 * i) = x;
-    } else {
-      float2 x;
-      x.x = bad ? __builtin_nanf("") : o[0][v] * inv;
-      x.y = bad ? __builtin_nanf("") : o[1][v] * inv;
-      *reinterpret_cast<float2*>(dst + 2 * i) = x;
+      x.x = bad ? __builtin_nanf("") : o[e][4 * v4 + 0] * inv;
+      x.y = bad ? __builtin_nanf("") : o[e][4 * v4 + 1] * inv;
+      x.z = bad ? __builtin_nanf("") : o[e][4 * v4 + 2] * inv;
+      x.w = bad ? __builtin_nanf("") : o[e][4 * v4 + 3] * inv;
+      *reinterpret_cast<float4*>(dst + 32 * e + fa_key(4 * v4, h)) = x;
     }
   }
 }
