@@ -423,7 +423,12 @@ __device__ __forceinline__ constexpr int fa_key(int v, int h) {
   return 8 * (v >> 2) + 4 * h + (v & 3);
 }
 
-constexpr int kFaAhead = 3;   // 32-key tiles copied ahead (LDS ring of kFaAhead + 1)
+// From head_dim 128 on, a tile's P.V is issued a step late, behind the next tile's score MFMAs
+// (at head_dim 64 the score MFMAs are too few to hide it, and the ring is better spent on a third
+// tile in flight).  32-key tiles copied ahead: the ring holds them, the tile being folded and,
+// with P.V a step late, the one before it (its V read again from LDS): four in all.
+template <int D> constexpr bool fa_defer_pv() { return D >= 128; }
+template <int D> constexpr int fa_ahead() { return fa_defer_pv<D>() ? 2 : 3; }
 
 // max and sum over the two lane halves (lanes l and l ^ 32), without the LDS crossbar:
 // v_permlane32_swap exchanges the halves of its two operands, so the pair it returns holds, at
@@ -443,7 +448,8 @@ template <int D, bool HILO, int A>
 __global__ __launch_bounds__(kQbWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void qblock_fa_kernel(const QBlockParams qp) {
   using F = Fa<D>;
-  constexpr int NBUF = A + 1;
+  constexpr bool DEFER = fa_defer_pv<D>();
+  constexpr int NBUF = A + (DEFER ? 2 : 1);
   constexpr int PIECES = F::TB / 16;
   static_assert(PIECES % (kQbWaves * kWave) == 0, "a tile is whole workgroup copies");
   constexpr int PL = PIECES / (kQbWaves * kWave);   // copies per lane per tile
@@ -603,42 +609,10 @@ void qblock_fa_kernel(const QBlockParams qp) {
   }
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(s_tiles);
 
-  // fold tile k, which sits in ring slot SLOT, into this wave's rows
-  auto step = [&](int k, auto slot_c) {
-    constexpr int SLOT = decltype(slot_c)::value;
-    // this wave's copies of tile k are done once at most those of the A - 1 later tiles are
-    // outstanding; the barrier then makes the whole tile visible, and every wave has finished
-    // reading tile k - 1, whose slot the next copy reuses
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PL * (A - 1)) : "memory");
-    if ((k + A) % kTablePairs == 0 && k + A < npairs) fill_table(2 * (k + A));   // uniform
-    copy(k + A, (SLOT + A) % NBUF);
-    const int tok0 = (sw.t0 + 2 * k) * kTileTokens;
-    if (!active || tok0 + F::kKeys <= s.start || tok0 >= s.L) return;   // uniform per wave
-    // a table entry outside the pool in this wave's keys: never read through, NaN outputs
-    const uint32_t tb = badbits >> (2 * SLOT);
-    if (((tb & 1u) && tok0 + kTileTokens > s.start) ||
-        ((tb & 2u) && tok0 + kTileTokens < s.L)) {
-      bad = true;
-      return;
-    }
-    const uint32_t tile = lds0 + SLOT * F::TB;
-    // scores S^T: 32 keys x 32 rows; every K read is issued before the first MFMA that waits
-    u32x4_t kw[F::KS];
-#pragma unroll
-    for (int ks = 0; ks < F::KS; ++ks)
-      kw[ks] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
-          (uintptr_t)(tile + (k_lane ^ (32u * ks))));
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16_t sc;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sc[v] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < F::KS; ++ks)
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kw[ks]),
-                                                   __builtin_bit_cast(bf16x8_t, qb[ks]), sc, 0,
-                                                   0, 0);
-    // the V^T operands of both halves go out now, under the softmax (transposing LDS reads)
-    u32x4_t vt[2][F::E];
+  // P^T operands (p = hi + lo in bf16) of the tile whose P.V is still to be issued
+  u32x4_t pv_hi[2], pv_lo[2];
+  // V^T operands of both 16-key halves of the tile at LDS address TILE (transposing LDS reads)
+  auto read_vt = [&](uint32_t tile, u32x4_t (&vt)[2][F::E]) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -652,7 +626,107 @@ void qblock_fa_kernel(const QBlockParams qp) {
         vt[half][e] = u32x4_t{w0.x, w0.y, w1.x, w1.y};
       }
     }
+  };
+  // O^T += V^T P^T for the tile whose first key is TOK0
+  auto pv_mma = [&](u32x4_t (&vt)[2][F::E], int tok0) {
+    if (__builtin_amdgcn_readfirstlane((tok0 < z_lo || tok0 + F::kKeys > z_hi) ? 1 : 0)) {
+      // operand value j of a half is key 16 half + fa_key(j, h): keep it where that key is
+      // one some token attends (two bf16 values per word)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t keep[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int t0 = tok0 + 16 * half + fa_key(2 * w, h);
+          const int t1 = tok0 + 16 * half + fa_key(2 * w + 1, h);
+          keep[w] = (t0 >= z_lo && t0 < z_hi ? 0x0000FFFFu : 0u) |
+                    (t1 >= z_lo && t1 < z_hi ? 0xFFFF0000u : 0u);
+        }
+#pragma unroll
+        for (int e = 0; e < F::E; ++e) {
+          vt[half][e].x &= keep[0];
+          vt[half][e].y &= keep[1];
+          vt[half][e].z &= keep[2];
+          vt[half][e].w &= keep[3];
+        }
+      }
+    }
+    // O^T += V^T P^T, one 16-key half at a time
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int e = 0; e < F::E; ++e) {
+        o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vt[half][e]),
+                                                       __builtin_bit_cast(bf16x8_t, pv_hi[half]),
+                                                       o[e], 0, 0, 0);
+        if constexpr (HILO)
+          o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, vt[half][e]),
+              __builtin_bit_cast(bf16x8_t, pv_lo[half]), o[e], 0, 0, 0);
+      }
+    }
+  };
+  // With P.V a step late, the tile waiting for it is issued behind the next tile's score MFMAs,
+  // so that the matrix cores work through it while the vector ALUs run that tile's softmax.
+  // Its V^T operands are read again from its ring slot then (still resident: the copies in
+  // flight go to other slots), so only its P operands wait in registers.
+  bool pv_have = false;
+  int pv_tok0 = 0;
+  auto flush_pv = [&](auto slot_c) {   // the tile waiting for its P.V sits in slot SLOT
+    constexpr int SLOT = decltype(slot_c)::value;
+    if (!pv_have) return;   // uniform
+    pv_have = false;
+    u32x4_t vt[2][F::E];
+    read_vt(lds0 + SLOT * F::TB, vt);
+    pv_mma(vt, pv_tok0);
+  };
+
+  // fold tile k, which sits in ring slot SLOT, into this wave's rows
+  auto step = [&](int k, auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    const auto prev = std::integral_constant<int, (SLOT + NBUF - 1) % NBUF>{};   // tile k - 1
+    // this wave's copies of tile k are done once at most those of the A - 1 later tiles are
+    // outstanding; the barrier then makes the whole tile visible, and every wave has finished
+    // reading the tile whose slot the next copy reuses (tile k - 1; k - 2 with P.V a step late,
+    // its V read again then)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PL * (A - 1)) : "memory");
+    if ((k + A) % kTablePairs == 0 && k + A < npairs) fill_table(2 * (k + A));   // uniform
+    copy(k + A, (SLOT + A) % NBUF);
+    const int tok0 = (sw.t0 + 2 * k) * kTileTokens;
+    // whether this wave folds tile k (uniform per wave): its keys reach the wave's range, and
+    // no table entry outside the pool lies among them (never read through: NaN outputs)
+    bool fold = active && tok0 + F::kKeys > s.start && tok0 < s.L;
+    const uint32_t tb = badbits >> (2 * SLOT);
+    if (fold && (((tb & 1u) && tok0 + kTileTokens > s.start) ||
+                 ((tb & 2u) && tok0 + kTileTokens < s.L))) {
+      bad = true;
+      fold = false;
+    }
+    const uint32_t tile = lds0 + SLOT * F::TB;
+    f32x16_t sc;
+    if (fold) {
+      // scores S^T: 32 keys x 32 rows; every K read is issued before the first MFMA that waits
+      u32x4_t kw[F::KS];
+#pragma unroll
+      for (int ks = 0; ks < F::KS; ++ks)
+        kw[ks] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+            (uintptr_t)(tile + (k_lane ^ (32u * ks))));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < F::KS; ++ks)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kw[ks]),
+                                                     __builtin_bit_cast(bf16x8_t, qb[ks]), sc, 0,
+                                                     0, 0);
+    }
+    u32x4_t vt[2][F::E];
+    if constexpr (DEFER)
+      flush_pv(prev);   // the previous tile's P.V, behind these score MFMAs
+    else if (fold)
+      read_vt(tile, vt);   // this tile's V^T operands go out now, under the softmax
     __builtin_amdgcn_sched_barrier(0);
+    if (!fold) return;
     const int full = __builtin_amdgcn_readfirstlane(
         (tok0 >= lo_all && tok0 + F::kKeys <= min(hi_all, t_end)) ? 1 : 0);
     // one path: only the masking of keys outside the row's range is conditional (separate
@@ -689,7 +763,8 @@ void qblock_fa_kernel(const QBlockParams qp) {
     for (int v = 0; v < 16; ++v) ls += pr[v];
     l += ls;
     // P^T as B operands, p = hi + lo in bf16, eight keys per 16-key half of the tile
-    u32x4_t bhi[2], blo[2];
+    auto& bhi = pv_hi;
+    auto& blo = pv_lo;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -707,42 +782,11 @@ void qblock_fa_kernel(const QBlockParams qp) {
         }
       }
     }
-    if (__builtin_amdgcn_readfirstlane((tok0 < z_lo || tok0 + F::kKeys > z_hi) ? 1 : 0)) {
-      // operand value j of a half is key 16 half + fa_key(j, h): keep it where that key is
-      // one some token attends (two bf16 values per word)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t keep[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int t0 = tok0 + 16 * half + fa_key(2 * w, h);
-          const int t1 = tok0 + 16 * half + fa_key(2 * w + 1, h);
-          keep[w] = (t0 >= z_lo && t0 < z_hi ? 0x0000FFFFu : 0u) |
-                    (t1 >= z_lo && t1 < z_hi ? 0xFFFF0000u : 0u);
-        }
-#pragma unroll
-        for (int e = 0; e < F::E; ++e) {
-          vt[half][e].x &= keep[0];
-          vt[half][e].y &= keep[1];
-          vt[half][e].z &= keep[2];
-          vt[half][e].w &= keep[3];
-        }
-      }
-    }
-    // O^T += V^T P^T, one 16-key half at a time
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-      for (int e = 0; e < F::E; ++e) {
-        const u32x4_t av = vt[half][e];
-        o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                       __builtin_bit_cast(bf16x8_t, bhi[half]),
-                                                       o[e], 0, 0, 0);
-        if constexpr (HILO)
-          o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                         __builtin_bit_cast(bf16x8_t, blo[half]),
-                                                         o[e], 0, 0, 0);
-      }
+    if constexpr (DEFER) {
+      pv_have = true;
+      pv_tok0 = tok0;
+    } else {
+      pv_mma(vt, tok0);
     }
   };
 
@@ -757,6 +801,13 @@ void qblock_fa_kernel(const QBlockParams qp) {
     if (k + 3 < npairs) step(k + 3, std::integral_constant<int, 3>{});
   }
   static_assert(NBUF == 4, "the loop above is unrolled for a ring of four");
+  // the last tile's P.V, a step late: it sat in slot (npairs - 1) % NBUF
+  if constexpr (DEFER) switch ((npairs - 1) & 3) {
+    case 0: flush_pv(std::integral_constant<int, 0>{}); break;
+    case 1: flush_pv(std::integral_constant<int, 1>{}); break;
+    case 2: flush_pv(std::integral_constant<int, 2>{}); break;
+    default: flush_pv(std::integral_constant<int, 3>{}); break;
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the copies past the last tile
   if (!active) return;
   bad = bad || s.bad;
@@ -882,7 +933,7 @@ hipError_t launch_d(const QBlockParams& qp, QkPath path, hipStream_t stream) {
       hipLaunchKernelGGL((qblock_lds_kernel<D, QbQkFp8<D>, A>), dim3(qp.grid),
                          dim3(kQbWaves * kWave), 0, stream, qp);
     else if constexpr (D <= 128)
-      hipLaunchKernelGGL((qblock_fa_kernel<D, true, kFaAhead>), dim3(qp.grid),
+      hipLaunchKernelGGL((qblock_fa_kernel<D, true, fa_ahead<D>()>), dim3(qp.grid),
                          dim3(kQbWaves * kWave), 0, stream, qp);
     else
       hipLaunchKernelGGL((qblock_lds_kernel<D, QbQk<D>, A>), dim3(qp.grid),
