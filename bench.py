@@ -21,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -380,7 +381,8 @@ def measure(dv: Device, wl, *, schedule: str, partition: int, steps: int, warmup
                    window=wl.window, schedule=schedule, partition_size=partition,
                    max_seq_len=maxL, num_workers=workers, kv_dtype=wl.kv_format, q_len=wl.q_len)
     ws = plan.workspace(dv.dev)
-    nworkers = int(plan.name.split("workers")[1].split()[0]) if "workers" in plan.name else None
+    mw = re.search(r"_workers(\d+)", plan.name)
+    nworkers = int(mw.group(1)) if mw else None
 
     def run(i):
         c = i % copies

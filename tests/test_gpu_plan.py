@@ -3,6 +3,8 @@ paged_attn_plan_run for every schedule, NaN inputs inside the attended range, an
 capture and replay of a run."""
 from __future__ import annotations
 
+import re
+
 import numpy as np
 import pytest
 import torch
@@ -141,7 +143,8 @@ def test_plan_length_bound_caps_workers_and_a_violated_bound_stays_correct():
     B, Hq, D = wl.q.shape
     capped = pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
                      schedule="balanced", max_seq_len=100)
-    assert "workers" in capped.name and int(capped.name.split("workers")[1].split()[0]) <= 8
+    m = re.search(r"_workers(\d+)", capped.name)
+    assert m and int(m.group(1)) <= 8, capped.name
     low = pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
                   schedule="balanced", max_seq_len=16)    # below the real lengths (37, 100)
     t = to_dev(wl)
