@@ -295,7 +295,9 @@ int32_t paged_attn_suggest_partition_size(int32_t num_seqs, int32_t num_kv_heads
  *                  (a small batch then does not pay for thousands of idle workers); a length
  *                  above the bound still gives correct results, only fewer workers.
  *   num_workers    balanced only: 0 = paged_attn_balanced_default_workers (queries the current
- *                  device at creation), else 1 .. 2^20.
+ *                  device at creation; an FP8 plan at head_dim 128 for one query token takes
+ *                  half of it, 8 per compute unit, when num_seqs * num_kv_heads is below four
+ *                  per compute unit), else 1 .. 2^20.
  *   plan           receives a host-memory object owned by the caller until
  *                  paged_attn_plan_destroy.  A plan is immutable: several threads may run it at
  *                  once, each with its own workspace and outputs.

@@ -757,7 +757,8 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
       p.kv_head_stride *= 2;
     }
     if (num_workers == 0) {
-      num_workers = pa::balanced_default_workers(head_dim, columns, path, q_len > 1);
+      num_workers = pa::balanced_default_workers(head_dim, columns, path, q_len > 1,
+                                                  (int64_t)shape->num_seqs * p.num_kv_heads);
       if (num_workers <= 0) return PA_ERR_LAUNCH;
     }
     if (max_seq_len > 0) {

@@ -860,7 +860,8 @@ hipError_t launch_balanced_witness(const BalancedParams& bp, char* k_rows, char*
   return hipGetLastError();
 }
 
-int balanced_default_workers(int head_dim, int group, QkPath path, bool multi) {
+int balanced_default_workers(int head_dim, int group, QkPath path, bool multi,
+                             int64_t units) {
   const void* k = path == QkPath::kValu ? bal_ptr<QkPath::kValu>(head_dim, group, multi)
                   : path == QkPath::kMfma ? bal_ptr<QkPath::kMfma>(head_dim, group, multi)
                   : path == QkPath::kMfmaPvFp8
@@ -881,6 +882,15 @@ int balanced_default_workers(int head_dim, int group, QkPath path, bool multi) {
   // others runs each of its workers slower, and the launch waits for the slowest (measured:
   // ten FP8 workers per CU took 83 us where eight took 66)
   if (per_cu >= 4) per_cu &= ~3;
+  // FP8 tiles through the LDS ring at head_dim 128 (16 workers per CU fit): with fewer than
+  // four (sequence, KV head) units per CU, 8 workers per CU stream faster (decode µs at 8 / 16
+  // per CU, one query token: the B64 Llama-8B-shaped step, 512 units, 61.6 / 64.8 and 62.4 /
+  // 63.8 on two boxes; the B32 L8192 sweep point, 256 units, 91.2 / 92.0); with more units the
+  // extra workers pay (the B128 mixed batch, 1024 units of mostly short sequences, each switch
+  // of unit a flush and a q load: 115.6 / 110.7)
+  if (path == QkPath::kMfmaPvFp8 && head_dim == 128 && !multi && units > 0 &&
+      units < 4LL * cus && per_cu > 8)
+    per_cu = 8;
   const long long n = (long long)cus * (per_cu > 0 ? per_cu : 1);
   return (int)(n < (1 << 20) ? n : (1 << 20));
 }

@@ -162,7 +162,11 @@ hipError_t launch_balanced_witness(const BalancedParams& bp, char* k_rows, char*
                                    int row_bytes, int max_rows, hipStream_t stream);
 // Workers that fit on the current device at once (CUs x resident one-wave workgroups per CU),
 // or -1 if the query fails.
-int balanced_default_workers(int head_dim, int group, QkPath path, bool multi = false);
+// Default persistent workers for a balanced launch on the current device: as many as fit (a
+// whole number per SIMD); with `units` (sequences x KV heads, 0 = not known) some paths take
+// fewer when the batch has few units.
+int balanced_default_workers(int head_dim, int group, QkPath path, bool multi = false,
+                             int64_t units = 0);
 
 // Query-block grid: (token, head) columns per wave (32 at head_dim <= 128, 16 at 256; the
 // matrix-core P.V paths only), the grid for the shape, and the launch.
