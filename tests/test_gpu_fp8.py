@@ -143,3 +143,25 @@ def test_fp8_graph_replay_balanced():
     compare(got[0].cpu().numpy().astype(np.float64), got[1].cpu().numpy().astype(np.float64),
             *oracle_full(wl), "fp8 graph replay balanced")
     t["q"].copy_(q0)
+
+
+def test_fp8_default_workers_follow_the_units():
+    """A default FP8 plan at head_dim 128 (one query token) takes 8 workers per CU when the batch
+    has fewer than four (sequence, KV head) units per CU, and keeps the full count otherwise."""
+    import re
+
+    import paged_kv_attention_attn_amd as pa
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def workers(num_seqs):
+        plan = pa.Plan(num_seqs, 32, 8, 4096, 256, 128, 16, schedule="balanced", kv_dtype=FP8)
+        return int(re.search(r"_workers(\d+)", plan.name).group(1))
+
+    few = workers(max(1, cus // 4))    # 2 units per CU
+    many = workers(max(1, cus // 2))   # 4 units per CU
+    log(f"[fp8] default workers: {few} at 2 units per CU, {many} at 4")
+    assert few <= 8 * cus
+    assert many >= few
+    if many > 8 * cus:
+        assert few == 8 * cus
