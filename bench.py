@@ -359,7 +359,7 @@ def _graph_step(torch, plan, stream, copies, steps, q, ks, vs, bt, L, wl, out, l
 
 
 def measure(dv: Device, wl, *, schedule: str, partition: int, steps: int, warmup: int,
-            workers: int = 0, copies=None, graph: bool = True) -> dict:
+            workers: int = 0, copies=None, graph: bool = True, p_terms: int = 2) -> dict:
     """One workload on one schedule through a prepared plan (one library call per step: decode
     plus its merge).  Returns the wall time per step over ``steps`` back-to-back runs, the same
     steps replayed from a HIP graph, and the decode kernel's own duration from HIP events that
@@ -379,7 +379,8 @@ def measure(dv: Device, wl, *, schedule: str, partition: int, steps: int, warmup
     stream = torch.cuda.current_stream(dv.dev)
     plan = pa.Plan(B, Hq, wl.num_kv_heads, wl.num_blocks, wl.stride, D, wl.block_size,
                    window=wl.window, schedule=schedule, partition_size=partition,
-                   max_seq_len=maxL, num_workers=workers, kv_dtype=wl.kv_format, q_len=wl.q_len)
+                   max_seq_len=maxL, num_workers=workers, kv_dtype=wl.kv_format, q_len=wl.q_len,
+                   p_terms=p_terms)
     ws = plan.workspace(dv.dev)
     mw = re.search(r"_workers(\d+)", plan.name)
     nworkers = int(mw.group(1)) if mw else None
@@ -493,12 +494,14 @@ def row_of(wl, label: str, m: dict, roof_flops: bool = False) -> dict:
 # Further workloads the default run reports next to the headline: the mixed batch (window and
 # sinks), the long-context step on its stated 512-token partitions and on the balanced
 # schedule, the head-size sweep at group 4, the Llama-8B step with an FP8 cache, and the same
-# step with 512 new tokens per sequence on the query-block schedule.
+# step with 512 new tokens per sequence on the query-block schedule, with P as two bf16 terms
+# (the default) and as one (the plan option PA_PLAN_P_ONE_BF16).
 EXTRA_ROWS = [
     dict(config=5), dict(config=4, schedule="partitioned"), dict(config=4),
     dict(config=3, head_dim=64, q_heads=32), dict(config=3, head_dim=128, q_heads=32),
     dict(config=3, head_dim=256, q_heads=32), dict(config=2, kv="fp8_e4m3"),
     dict(config=2, q_len=512, schedule="query_blocks"),
+    dict(config=2, q_len=512, schedule="query_blocks", p_terms=1),
 ]
 
 
@@ -536,6 +539,9 @@ def main() -> int:
                     help="KV cache format")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per sequence (> 1: causal; balanced or query_blocks)")
+    ap.add_argument("--p-terms", type=int, choices=[1, 2], default=2,
+                    help="query-block schedule: P as two bf16 terms (default) or one "
+                         "(PA_PLAN_P_ONE_BF16)")
     ap.add_argument("--seq-lens", default=None,
                     help="replace the workload's lengths (its head geometry kept): 'BxL' for B "
                          "sequences of L tokens, or a comma-separated list")
@@ -592,9 +598,10 @@ def main() -> int:
           f"P={P}", file=sys.stderr, flush=True)
     m = measure(dv, wl, schedule=args.schedule, partition=P, steps=args.steps,
                 warmup=args.warmup, workers=args.workers, copies=args.copies,
-                graph=not args.no_graph)
+                graph=not args.no_graph, p_terms=args.p_terms)
     print(f"[bench] headline {m}", file=sys.stderr, flush=True)
-    label = workload_label(args.config, D, Hq, args.kv, args.q_len, args.seq_lens)
+    label = workload_label(args.config, D, Hq, args.kv, args.q_len, args.seq_lens) + \
+        ("_p1" if args.p_terms == 1 else "")
     qblocks = args.schedule == "query_blocks"
     # chunks of one 16-token tile of one KV head (the probe takes 2 to 8 KiB; an FP8 tile at
     # head_dim 64 is 1 KiB and is compared with 2 KiB chunks)
@@ -678,9 +685,10 @@ def main() -> int:
             w = workload(spec["config"], spec.get("head_dim", 128), spec.get("q_heads"),
                          spec.get("kv", "bf16"), spec.get("q_len", 1))
             lab = workload_label(spec["config"], w.head_dim, w.num_q_heads, w.kv_format,
-                                 w.q_len)
+                                 w.q_len) + ("_p1" if spec.get("p_terms", 2) == 1 else "")
             mm = measure(dv, w, schedule=sched, partition=partition_of(w, sched),
-                         steps=args.steps, warmup=args.warmup, graph=not args.no_graph)
+                         steps=args.steps, warmup=args.warmup, graph=not args.no_graph,
+                         p_terms=spec.get("p_terms", 2))
             r = row_of(w, lab, mm, roof_flops=sched == "query_blocks")
             print(f"[bench] row {r}", file=sys.stderr, flush=True)
             rows.append(r)

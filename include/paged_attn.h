@@ -371,6 +371,29 @@ pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_
                                  const pa_kv_layout* kv_layout, int32_t q_len,
                                  int32_t max_seq_len, int32_t num_workers, pa_plan** plan);
 
+/* Plan options for paged_attn_plan_create_flags (bits). */
+enum {
+  /* P.V with P rounded to one bf16 term (round to nearest: |p~ - p| <= 2^-8 p) instead of the
+     two terms hi + lo (|hi + lo - p| <= 2^-16 p).  Applies to the query-block schedule's 32-key
+     workgroup form (bf16 caches, head_dim 64 and 128, four or more blocks of tokens per
+     (sequence, KV head)); the plan name then ends in "_p1", and other plans ignore the bit.
+     The softmax denominator keeps fp32 p, so an output moves by at most 2^-8 times the largest
+     |v| the row attends: within the 3e-2 contract for N(0,1) values, not within 1e-3.  It
+     takes a third of the P.V matrix work and the vector work of the low term away: the 512-new-
+     token Llama-8B-shaped step runs about 18% faster on MI355X.  The pages give no precision for
+     P (the contract is the 3e-2 tolerance with fp32 accumulation); this option is this
+     library's. */
+  PA_PLAN_P_ONE_BF16 = 1
+};
+
+/* paged_attn_plan_create with option bits (PA_PLAN_*); unknown bits give PA_ERR_UNSUPPORTED.
+ * flags = 0 is paged_attn_plan_create. */
+pa_status paged_attn_plan_create_flags(const pa_shape* shape, int32_t head_dim,
+                                       int32_t block_size, int32_t window, int32_t schedule,
+                                       int32_t kv_dtype, const pa_kv_layout* kv_layout,
+                                       int32_t q_len, int32_t max_seq_len, int32_t num_workers,
+                                       int32_t flags, pa_plan** plan);
+
 /* Device workspace bytes a run needs (0 for the unsplit schedule): the partition partials and
  * their LSEs (plus one merge counter per (sequence, KV head) for the fused schedule), or the
  * balanced workspace.  Caller-owned and 256-byte aligned.  A fused plan's workspace must be

@@ -74,6 +74,8 @@ def _load() -> ctypes.CDLL:
         "paged_attn_balanced_default_workers": (i32, [i32, i32]),
         "paged_attn_plan_create": (i32, [sp, i32, i32, i32, i32, i32, vp, i32, i32, i32,
                                          ctypes.POINTER(vp)]),
+        "paged_attn_plan_create_flags": (i32, [sp, i32, i32, i32, i32, i32, vp, i32, i32, i32,
+                                               i32, ctypes.POINTER(vp)]),
         "paged_attn_plan_workspace_size": (ctypes.c_int64, [vp]),
         "paged_attn_plan_run": (i32, [vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp, vp,
                                       vp]),
@@ -108,7 +110,8 @@ EXPORTED = ("paged_attn_decode", "paged_attn_reduce", "paged_attn_decode_balance
             "paged_attn_gather_witness", "paged_attn_gather_witness_balanced",
             "paged_attn_stream_read", "paged_attn_gather_read",
             "paged_attn_copy",
-            "paged_attn_plan_create", "paged_attn_plan_workspace_size", "paged_attn_plan_run",
+            "paged_attn_plan_create", "paged_attn_plan_create_flags",
+            "paged_attn_plan_workspace_size", "paged_attn_plan_run",
             "paged_attn_plan_run_timed", "paged_attn_plan_name", "paged_attn_plan_destroy")
 
 
@@ -434,6 +437,7 @@ def _layout_ptr(layout):
         return None
     return ctypes.cast(ctypes.pointer(KvLayout(*[int(x) for x in layout])), ctypes.c_void_p)
 KV_DTYPES = {"bf16": 0, "fp8_e4m3": 1}
+PLAN_P_ONE_BF16 = 1   # PA_PLAN_P_ONE_BF16
 
 
 class Plan:
@@ -451,15 +455,18 @@ class Plan:
     ``kv_layout``: None for the pool [num_blocks][Hkv][bs][D], else (block, head, token) strides
     in elements of the cache type (pa_kv_layout).
     ``q_len`` > 1 (balanced or query_blocks): q_len causal query tokens per sequence,
-    q [B][q_len][Hq][D] -> out [B][q_len][Hq][D], lse [B][q_len][Hq].  run() records only
-    kernel launches on the stream, so it can be captured in a CUDA/HIP graph."""
+    q [B][q_len][Hq][D] -> out [B][q_len][Hq][D], lse [B][q_len][Hq].  ``p_terms``: 2 (the
+    default) forms P.V with P as two bf16 terms; 1 rounds P to one bf16 term where the query-block
+    schedule's 32-key form runs (PA_PLAN_P_ONE_BF16: faster, outputs within 2^-8 max|v| of the
+    two-term result; the name then ends in "_p1").  run() records only kernel launches on the
+    stream, so it can be captured in a CUDA/HIP graph."""
 
     def __init__(self, num_seqs: int, num_q_heads: int, num_kv_heads: int, num_blocks: int,
                  block_table_stride: int, head_dim: int, block_size: int, *, window: int = 0,
                  schedule: str = "balanced", partition_size: int = 0,
                  max_seq_len: Optional[int] = None, num_workers: int = 0,
                  kv_dtype: str = "bf16", q_len: int = 1,
-                 kv_layout: Optional[Tuple[int, int, int]] = None):
+                 kv_layout: Optional[Tuple[int, int, int]] = None, p_terms: int = 2):
         if schedule == "auto":
             schedule, partition_size = suggest_schedule(
                 num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, window=window,
@@ -482,11 +489,13 @@ class Plan:
                                 block_table_stride, partition_size, pmax)
         self.dims = (num_seqs, num_q_heads, head_dim)
         self._h = ctypes.c_void_p()
-        st = _lib.paged_attn_plan_create(ctypes.byref(self.shape), int(head_dim), int(block_size),
-                                         int(window), SCHEDULES[schedule], KV_DTYPES[kv_dtype],
-                                         _layout_ptr(kv_layout),
-                                         int(q_len), int(max_seq_len or 0), int(num_workers),
-                                         ctypes.byref(self._h))
+        if p_terms not in (1, 2):
+            raise ValueError("p_terms must be 1 or 2")
+        st = _lib.paged_attn_plan_create_flags(
+            ctypes.byref(self.shape), int(head_dim), int(block_size), int(window),
+            SCHEDULES[schedule], KV_DTYPES[kv_dtype], _layout_ptr(kv_layout), int(q_len),
+            int(max_seq_len or 0), int(num_workers), PLAN_P_ONE_BF16 if p_terms == 1 else 0,
+            ctypes.byref(self._h))
         if st != PA_OK:
             raise PagedAttnError(st, "paged_attn_plan_create")
         self.workspace_size = int(_lib.paged_attn_plan_workspace_size(self._h))

@@ -619,9 +619,11 @@ pa_status apply_kv_layout(pa::DecodeParams& p, const pa_kv_layout* kv_layout,
 
 pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size, int32_t window,
                      int32_t schedule, int32_t kv_dtype, const pa_kv_layout* kv_layout,
-                     int32_t q_len, int32_t max_seq_len, int32_t num_workers, pa_plan* pl) {
+                     int32_t q_len, int32_t max_seq_len, int32_t num_workers, int32_t flags,
+                     pa_plan* pl) {
   const pa_status st = check_shape(shape);
   if (st != PA_OK) return st;
+  if ((flags & ~PA_PLAN_P_ONE_BF16) != 0) return PA_ERR_UNSUPPORTED;
   if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
   const int group = shape->num_q_heads / shape->num_kv_heads;
   if (!pa::decode_supported(head_dim, group)) return PA_ERR_UNSUPPORTED;
@@ -707,6 +709,11 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
     pl->qb = pa::QBlockParams{};
     pl->qb.d = p;
     pa::qblock_geometry(pl->qb, head_dim, max_seq_len);
+    // one bf16 term of P where the 32-key workgroup form runs (bf16 caches, head_dim <= 128)
+    pl->qb.p_one_term = (flags & PA_PLAN_P_ONE_BF16) != 0 && pl->qb.waves > 1 &&
+                                path != pa::QkPath::kMfmaPvFp8 && head_dim <= 128
+                            ? 1
+                            : 0;
     pl->group = pa::qblock_columns(head_dim);
     if (pl->qb.splits > 1) {
       // key splits: normalised partial outputs, then their LSEs
@@ -716,9 +723,10 @@ pa_status plan_build(const pa_shape* shape, int32_t head_dim, int32_t block_size
     }
     char splits[16] = "";
     if (pl->qb.splits > 1) std::snprintf(splits, sizeof(splits), "_s%d", pl->qb.splits);
-    std::snprintf(pl->name, sizeof(pl->name), "pa_qblock_%s_d%d_g%d_q%d_t%d_w%d%s%s",
+    std::snprintf(pl->name, sizeof(pl->name), "pa_qblock_%s_d%d_g%d_q%d_t%d_w%d%s%s%s",
                   pa::qk_path_name(path), head_dim, group, q_len, pl->qb.tokens_per_block,
-                  pl->qb.waves, splits, pl->qb.xcd_pinned ? "_xcd" : "");
+                  pl->qb.waves, splits, pl->qb.xcd_pinned ? "_xcd" : "",
+                  pl->qb.p_one_term ? "_p1" : "");
   } else if (schedule == PA_SCHEDULE_PARTITIONED) {
     const size_t rows = (size_t)shape->num_seqs * shape->num_q_heads * shape->max_partitions;
     pl->part_bytes = align256(rows * head_dim * sizeof(float));
@@ -837,13 +845,22 @@ pa_status paged_attn_plan_create(const pa_shape* shape, int32_t head_dim, int32_
                                  int32_t window, int32_t schedule, int32_t kv_dtype,
                                  const pa_kv_layout* kv_layout, int32_t q_len,
                                  int32_t max_seq_len, int32_t num_workers, pa_plan** plan) {
+  return paged_attn_plan_create_flags(shape, head_dim, block_size, window, schedule, kv_dtype,
+                                      kv_layout, q_len, max_seq_len, num_workers, 0, plan);
+}
+
+pa_status paged_attn_plan_create_flags(const pa_shape* shape, int32_t head_dim,
+                                       int32_t block_size, int32_t window, int32_t schedule,
+                                       int32_t kv_dtype, const pa_kv_layout* kv_layout,
+                                       int32_t q_len, int32_t max_seq_len, int32_t num_workers,
+                                       int32_t flags, pa_plan** plan) {
   if (plan == nullptr) return PA_ERR_NULL;
   *plan = nullptr;
   pa_plan* pl = new (std::nothrow) pa_plan;
   if (pl == nullptr) return PA_ERR_LAUNCH;
   const pa_status st =
       plan_build(shape, head_dim, block_size, window, schedule, kv_dtype, kv_layout, q_len,
-                 max_seq_len, num_workers, pl);
+                 max_seq_len, num_workers, flags, pl);
   if (st != PA_OK) {
     delete pl;
     return st;

@@ -84,6 +84,7 @@ struct QBlockParams {
   int32_t blocks_per_seq;     // workgroup blocks per (sequence, KV head):
                               // ceil(q_total / (tokens_per_block * waves))
   int32_t xcd_pinned;         // 1: every workgroup of a (sequence, KV head) on one XCD
+  int32_t p_one_term;         // 1: the 32-key workgroup form takes P as one bf16 term
   int32_t splits;             // key splits per workgroup block (1 = none)
   int32_t split_tiles;        // splits > 1: tiles per split, counted from the first tile of the
                               // workgroup's key range; the last split takes the rest

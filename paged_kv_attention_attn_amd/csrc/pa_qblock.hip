@@ -770,11 +770,17 @@ void qblock_fa_kernel(const QBlockParams qp) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         // hi: the upper halves of the two floats (p truncated to bf16, one byte permute); lo:
-        // the exact remainder p - hi, rounded to bf16: |hi + lo - p| <= 2^-16 |p|
+        // the exact remainder p - hi, rounded to bf16: |hi + lo - p| <= 2^-16 |p|.  With one
+        // term, p rounded to the nearest bf16 instead: |hi - p| <= 2^-8 |p|
         const float a0 = pr[8 * half + 2 * w], a1 = pr[8 * half + 2 * w + 1];
         const uint32_t u0 = __builtin_bit_cast(uint32_t, a0);
         const uint32_t u1 = __builtin_bit_cast(uint32_t, a1);
-        bhi[half][w] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        if constexpr (HILO) {
+          bhi[half][w] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        } else {
+          const bf16x2_t hv = {(__bf16)a0, (__bf16)a1};
+          bhi[half][w] = __builtin_bit_cast(uint32_t, hv);
+        }
         if constexpr (HILO) {
           const bf16x2_t lv = {(__bf16)(a0 - __builtin_bit_cast(float, u0 & 0xFFFF0000u)),
                                (__bf16)(a1 - __builtin_bit_cast(float, u1 & 0xFFFF0000u))};
@@ -932,9 +938,14 @@ hipError_t launch_d(const QBlockParams& qp, QkPath path, hipStream_t stream) {
     if (path == QkPath::kMfmaPvFp8)
       hipLaunchKernelGGL((qblock_lds_kernel<D, QbQkFp8<D>, A>), dim3(qp.grid),
                          dim3(kQbWaves * kWave), 0, stream, qp);
-    else if constexpr (D <= 128)
-      hipLaunchKernelGGL((qblock_fa_kernel<D, true, fa_ahead<D>()>), dim3(qp.grid),
-                         dim3(kQbWaves * kWave), 0, stream, qp);
+    else if constexpr (D <= 128) {
+      if (qp.p_one_term)
+        hipLaunchKernelGGL((qblock_fa_kernel<D, false, fa_ahead<D>()>), dim3(qp.grid),
+                           dim3(kQbWaves * kWave), 0, stream, qp);
+      else
+        hipLaunchKernelGGL((qblock_fa_kernel<D, true, fa_ahead<D>()>), dim3(qp.grid),
+                           dim3(kQbWaves * kWave), 0, stream, qp);
+    }
     else
       hipLaunchKernelGGL((qblock_lds_kernel<D, QbQk<D>, A>), dim3(qp.grid),
                          dim3(kQbWaves * kWave), 0, stream, qp);

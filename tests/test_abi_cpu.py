@@ -295,6 +295,40 @@ def test_query_block_plans():
 
 
 
+def test_plan_flags_one_term_p():
+    """PA_PLAN_P_ONE_BF16 reaches the 32-key workgroup form only (bf16 caches, head_dim <= 128,
+    four or more blocks per (sequence, KV head)); other plans ignore it; unknown bits are
+    rejected."""
+    def create(flags, **kw):
+        h = ctypes.c_void_p()
+        st = pa.lib().paged_attn_plan_create_flags(
+            ctypes.byref(shape(**kw.pop("shape_kw", {}))), kw.get("head_dim", 128), 16, 0,
+            kw.get("schedule", 4), kw.get("kv_dtype", 0), None, kw.get("q_len", 70), 0, 100,
+            flags, ctypes.byref(h))
+        name = pa.lib().paged_attn_plan_name(h) if st == 0 else None
+        if st == 0:
+            pa.lib().paged_attn_plan_destroy(h)
+        return st, name
+
+    assert create(1) == (0, b"pa_qblock_mfmapv_d128_g4_q70_t8_w4_p1")
+    assert create(0) == (0, b"pa_qblock_mfmapv_d128_g4_q70_t8_w4")
+    assert create(1, head_dim=64) == (0, b"pa_qblock_mfmapv_d64_g4_q70_t8_w4_p1")
+    # FP8 caches, head_dim 256 and one wave per block keep both terms
+    assert create(1, kv_dtype=1)[1] == b"pa_qblock_mfmapv_fp8_d128_g4_q70_t8_w4"
+    assert not create(1, head_dim=256)[1].endswith(b"_p1")
+    assert create(1, q_len=5)[1] == b"pa_qblock_mfmapv_d128_g4_q5_t8_w1"
+    # other schedules ignore the bit
+    st, name = create(1, schedule=2, q_len=1)
+    assert st == 0 and b"_p1" not in name and b"workers100" in name
+    # unknown bits
+    assert create(2)[0] == -3
+    assert create(1 << 30)[0] == -3
+    # paged_attn_plan_create is the flags call with no bits
+    st, h = plan_create(shape(), schedule=4, q_len=70)
+    assert st == 0 and pa.lib().paged_attn_plan_name(h) == b"pa_qblock_mfmapv_d128_g4_q70_t8_w4"
+    pa.lib().paged_attn_plan_destroy(h)
+
+
 def test_query_block_key_splits():
     """Small batches cut each block's key range into key splits (about 2048 waves in all, at
     least 8 tiles a split, at most 64 splits) and take a workspace for the partials."""

@@ -226,3 +226,41 @@ def test_qblock_key_splits_with_lengths_above_the_bound():
     log(f"[qblock] {plan.name}")
     assert "_s" in plan.name
     compare(*run_plan(plan, wl, t), *oracle_full(wl), "qblock lengths above the bound")
+
+
+@pytest.mark.parametrize("D,g,Q,lens,window", [
+    (128, 4, 300, [300] * 4, 0),                    # whole prompts: the rows with fewest keys
+    (128, 4, 70, None, 11),                         # edge lengths, a window
+    (64, 2, 100, None, 0),
+    (128, 8, 64, [64, 2000, 700, 5], 0),
+    (64, 8, 40, [40, 41, 1000, 3], 300),
+])
+def test_qblock_one_term_p(D, g, Q, lens, window):
+    """Plans with p_terms=1 (PA_PLAN_P_ONE_BF16): P rounded to one bf16 term in the 32-key form.
+    |p~ - p| <= 2^-8 p and the denominator keeps fp32 p, so an output moves by at most 2^-8
+    max|v| from the two-term result (which meets the 1e-3 gate); the LSE does not move.  Both
+    bounds hold against the oracle, inside the 3e-2 contract."""
+    wl = qb_workload(D, g, Q, lens=lens, window=window, sinks=True, seed=11)
+    t = to_dev(wl)
+    one = pa.Plan(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.stride,
+                  wl.head_dim, wl.block_size, window=wl.window, schedule="query_blocks",
+                  q_len=wl.q_len, p_terms=1)
+    two = pa.Plan(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.stride,
+                  wl.head_dim, wl.block_size, window=wl.window, schedule="query_blocks",
+                  q_len=wl.q_len)
+    log(f"[qblock] {one.name} / {two.name}")
+    assert one.name == two.name + "_p1"
+    v = (wl.v_cache.astype(np.uint32) << 16).view(np.float32)
+    vmax = float(np.abs(v[np.isfinite(v)]).max())
+    bound = 2.0 ** -8 * vmax
+    ref = oracle_full(wl)
+    a = run_plan(one, wl, t)
+    b = run_plan(two, wl, t)
+    stats = compare(*a, *ref, f"qblock one-term P D={D} g={g} Q={Q}", strict=False)
+    compare(*b, *ref, f"qblock two-term P D={D} g={g} Q={Q}")
+    assert stats["max_abs"] <= bound + 1e-3, (stats, bound)
+    assert stats["lse_max_abs"] <= 1e-3, stats
+    assert np.abs(a[0] - b[0]).max() <= bound + 1e-5
+    fin = np.isfinite(b[1])
+    assert np.array_equal(fin, np.isfinite(a[1]))
+    assert np.abs(a[1][fin] - b[1][fin]).max() <= 1e-5
