@@ -885,9 +885,9 @@ int balanced_default_workers(int head_dim, int group, QkPath path, bool multi,
   // FP8 tiles through the LDS ring at head_dim 128 (16 workers per CU fit): with fewer than
   // four (sequence, KV head) units per CU, 8 workers per CU stream faster (decode µs at 8 / 16
   // per CU, one query token: the B64 Llama-8B-shaped step, 512 units, 61.6 / 64.8 and 62.4 /
-  // 63.8 on two boxes; the B32 L8192 sweep point, 256 units, 91.2 / 92.0); with more units the
-  // extra workers pay (the B128 mixed batch, 1024 units of mostly short sequences, each switch
-  // of unit a flush and a q load: 115.6 / 110.7)
+  // 63.8 on two boxes; the B32 L8192 sweep point, 256 units, 91.2 / 92.0; the B4 L131072 step,
+  // 32 units, 177.0 / 206.0); with more units the extra workers pay (the B128 mixed batch,
+  // 1024 units of 1 to 4096 keys: 115.6 / 110.7)
   if (path == QkPath::kMfmaPvFp8 && head_dim == 128 && !multi && units > 0 &&
       units < 4LL * cus && per_cu > 8)
     per_cu = 8;

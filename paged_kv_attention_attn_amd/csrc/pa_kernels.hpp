@@ -161,11 +161,10 @@ hipError_t launch_balanced_fixup(const BalancedParams& bp, int head_dim, int gro
 // k_rows / v_rows [B][Hkv][max_rows][row_bytes] instead of computing; bp.prefix is not used.
 hipError_t launch_balanced_witness(const BalancedParams& bp, char* k_rows, char* v_rows,
                                    int row_bytes, int max_rows, hipStream_t stream);
-// Workers that fit on the current device at once (CUs x resident one-wave workgroups per CU),
-// or -1 if the query fails.
-// Default persistent workers for a balanced launch on the current device: as many as fit (a
-// whole number per SIMD); with `units` (sequences x KV heads, 0 = not known) some paths take
-// fewer when the batch has few units.
+// Default persistent workers for a balanced launch on the current device: as many as fit at
+// once (CUs x resident one-wave workgroups per CU, a whole number per SIMD); with `units`
+// (sequences x KV heads, 0 = not known) some paths take fewer when the batch has few units.
+// -1 if the query fails.
 int balanced_default_workers(int head_dim, int group, QkPath path, bool multi = false,
                              int64_t units = 0);
 
