@@ -264,3 +264,41 @@ def test_qblock_one_term_p(D, g, Q, lens, window):
     fin = np.isfinite(b[1])
     assert np.array_equal(fin, np.isfinite(a[1]))
     assert np.abs(a[1][fin] - b[1][fin]).max() <= 1e-5
+
+
+def test_qblock_one_term_p_key_splits_graph_replay():
+    """One bf16 term of P with key splits (a small batch and a length bound) and their merge,
+    captured in a graph: every replay bit-equal to the eager run, which holds the one-term bound
+    against the oracle."""
+    wl = qb_workload(128, 4, 33, window=200, sinks=True, lens=[100, 33, 500, 7], seed=12)
+    t = to_dev(wl)
+    plan = pa.Plan(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.stride,
+                   wl.head_dim, wl.block_size, window=wl.window, schedule="query_blocks",
+                   max_seq_len=int(wl.seq_lens.max()), q_len=wl.q_len, p_terms=1)
+    log(f"[qblock] {plan.name}")
+    assert "_s" in plan.name and plan.name.endswith("_p1")
+    ws = plan.workspace("cuda")
+    args = (t["q"], t["k"], t["v"], t["bt"], t["L"], float(wl.scale))
+    out = torch.empty(wl.q.shape, device="cuda")
+    lse = torch.empty(wl.q.shape[:-1], device="cuda")
+    plan.run(*args, out=out, lse=lse, sinks=t["sinks"], workspace=ws)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            plan.run(*args, out=out, lse=lse, sinks=t["sinks"], workspace=ws)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+    v = (wl.v_cache.astype(np.uint32) << 16).view(np.float32)
+    bound = 2.0 ** -8 * float(np.abs(v[np.isfinite(v)]).max())
+    stats = compare(ref_out.cpu().numpy().astype(np.float64),
+                    ref_lse.cpu().numpy().astype(np.float64), *oracle_full(wl),
+                    "qblock one-term P, key splits (graph reference)", strict=False)
+    assert stats["max_abs"] <= bound + 1e-3 and stats["lse_max_abs"] <= 1e-3, (stats, bound)
