@@ -165,23 +165,51 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// Value of x in lane (lane ^ 16) and (lane ^ 32): crosses DPP rows, so it goes through the LDS
-// crossbar (ds_bpermute).  Both steps are needed to cover the four rows of a wave64; stopping at
-// xor 16 would only combine two rows.
-__device__ __forceinline__ float xor_lane(float x, int mask) {
-  const int lane = __lane_id();
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2,
-                                                                __builtin_bit_cast(int, x)));
+// Lanes l and l ^ MASK (MASK = 16: the two rows of a row pair; 32: the two halves of the wave)
+// cross DPP rows.  v_permlane16_swap / v_permlane32_swap exchange them without the LDS crossbar:
+// given x twice, each returns the pair (value of the pair's first row or half, value of its
+// second) at both lanes of the pair.
+template <int MASK>
+__device__ __forceinline__ void lane_pair(float x, float& first, float& second) {
+  static_assert(MASK == 16 || MASK == 32, "row pairs or wave halves");
+  const int xi = __builtin_bit_cast(int, x);
+  int a, b;
+  if constexpr (MASK == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+    a = (int)r[0];
+    b = (int)r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    a = (int)r[0];
+    b = (int)r[1];
+  }
+  first = __builtin_bit_cast(float, a);
+  second = __builtin_bit_cast(float, b);
 }
 
+// Value of x in lane (lane ^ MASK), MASK = 16 or 32.
+template <int MASK>
+__device__ __forceinline__ float xor_lane(float x) {
+  float first, second;
+  lane_pair<MASK>(x, first, second);
+  return (__lane_id() & MASK) == 0 ? second : first;
+}
+
+// Max / sum over the four rows of a wave64 (both steps are needed; stopping at the row pair
+// would only combine two rows).  Every lane of a pair combines the same two values in the same
+// order, so the four rows end with identical bits.
 __device__ __forceinline__ float rows_max(float x) {
-  x = fmaxf(x, xor_lane(x, 16));
-  return fmaxf(x, xor_lane(x, 32));
+  float a, b;
+  lane_pair<16>(x, a, b);
+  lane_pair<32>(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 
 __device__ __forceinline__ float rows_sum(float x) {
-  x += xor_lane(x, 16);
-  return x + xor_lane(x, 32);
+  float a, b;
+  lane_pair<16>(x, a, b);
+  lane_pair<32>(a + b, a, b);
+  return a + b;
 }
 
 // full-wave sum / max (every lane gets the result)

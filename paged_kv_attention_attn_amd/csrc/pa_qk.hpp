@@ -804,7 +804,7 @@ struct QkMfmaPvT {
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int e = 0; e < E; ++e)
-          up[i][e] = xor_lane(HP == 2 ? cacc1[e][i] : cacc[e][i], 16);
+          up[i][e] = xor_lane<16>(HP == 2 ? cacc1[e][i] : cacc[e][i]);
       }
     }
   }
